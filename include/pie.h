@@ -1,0 +1,271 @@
+/*
+ * pie.h -- C ABI of the batched paged-KV forward pass for AMD gfx950.
+ *
+ * One call, pie_forward, runs the Llama-style decoder of the Pie pages
+ * ("Write a model in Poem", section 5 Forward pass: embed, per layer
+ * RMSNorm -> RoPE'd grouped-query attention over the sequence's KV ->
+ * residual add -> RMSNorm -> SwiGLU -> residual add, then final RMSNorm,
+ * gather of the readout rows, lm_head) over a batch of forward passes from
+ * many sequences at once ("How Pie thinks", "Batching is still the engine's
+ * job"), then runs the fused epilogue of each readout row on the device and
+ * returns only a token id per row ("How Pie thinks", section 5 Epilogues).
+ *
+ * Each sequence's KV lives in a working set ("How Pie thinks", section 4
+ * Working sets): a page table over a pool of fixed-size KV pages, with a
+ * frozen prefix (committed tokens) and a writable buffer (uncommitted
+ * tokens).  pie_fork makes a new working set that shares the frozen prefix's
+ * pages without copying them.
+ *
+ * Conventions
+ *  - Every function returning int returns PIE_OK (0) or a negative pie_status;
+ *    pie_last_error() then gives a message (thread-local, valid until the next
+ *    call on the same thread).
+ *  - "device" pointers are HIP device memory of the GPU that is current when
+ *    pie_init is called; "host" pointers are ordinary process memory.
+ *  - The caller owns weights, the KV arena, the workspace and the stream; they
+ *    must outlive the context.  The library owns working-set and page-pool
+ *    metadata.  Host arrays passed in are read only during the call.
+ *  - A context is not thread-safe: one thread at a time per context.
+ *  - After PIE_EHIP a context is poisoned: every later call but pie_destroy
+ *    returns PIE_ESTATE.
+ */
+#ifndef PIE_H
+#define PIE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PIE_ABI_VERSION 1
+
+typedef struct pie_ctx pie_ctx;
+
+/* Working-set handle: (generation << 32) | (slot + 1).  0 is never valid; a
+ * handle whose working set was freed is stale and rejected with PIE_EINVAL. */
+typedef uint64_t pie_ws;
+
+enum pie_status {
+  PIE_OK = 0,
+  PIE_EINVAL = -1, /* bad argument, stale handle, or a batch that breaks a rule */
+  PIE_ENOMEM = -2, /* KV page pool exhausted, or a batch beyond the init limits  */
+  PIE_EHIP = -3,   /* a HIP runtime call failed (context is poisoned)            */
+  PIE_ESTATE = -4  /* context poisoned, or a call the context cannot serve       */
+};
+
+/* KV storage formats ("Write a model in Poem", section 2 Deployments). */
+enum pie_kv_dtype { PIE_KV_BF16 = 0, PIE_KV_E4M3 = 1 };
+
+/* Fused epilogues ("How Pie thinks", sections 3 and 5). */
+enum pie_epilogue_kind { PIE_EPI_ARGMAX = 0, PIE_EPI_GUMBEL_MAX = 1 };
+
+/* pie_forward flags */
+enum pie_forward_flags {
+  PIE_FLAG_NO_LAUNCH = 1,     /* validate, reserve, pack and update working sets, launch nothing;
+                                 out_tokens are set to -1.  The only mode of a host-only context. */
+  PIE_FLAG_LOGITS_DEVICE = 2, /* out_logits is a device pointer (default: host pointer)           */
+  PIE_FLAG_SYNC_DEBUG = 4     /* synchronise and check for errors after every kernel              */
+};
+
+/* Model shape ("Write a model in Poem", section 1 MODELS, section 4 caches).
+ * Constraints: head_dim = 64 or 128; n_q_heads % n_kv_heads == 0;
+ * d_model % 128 == 0; page_size = 16. */
+typedef struct pie_model_desc {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
+  float rms_eps;    /* epsilon inside the RMSNorm square root               */
+  float rope_theta; /* RoPE base; rotate-half pairs (j, j + head_dim/2)     */
+  int32_t kv_dtype; /* pie_kv_dtype                                          */
+  int32_t page_size;
+} pie_model_desc;
+
+/* Weights: caller-owned DEVICE pointers to bf16 tensors, row-major with the
+ * checkpoint layout [out][in] ("Write a model in Poem", section 3 Weights).
+ * The per-layer members are HOST arrays of n_layers device pointers; the
+ * library copies the pointer arrays during pie_init. */
+typedef struct pie_weights {
+  const void* embed;      /* [vocab][d_model]            */
+  const void* final_norm; /* [d_model]                   */
+  const void* lm_head;    /* [vocab][d_model]            */
+  const void* const* attn_norm; /* [L] -> [d_model]                     */
+  const void* const* wq;        /* [L] -> [n_q_heads*head_dim][d_model] */
+  const void* const* wk;        /* [L] -> [n_kv_heads*head_dim][d_model]*/
+  const void* const* wv;        /* [L] -> [n_kv_heads*head_dim][d_model]*/
+  const void* const* wo;        /* [L] -> [d_model][n_q_heads*head_dim] */
+  const void* const* mlp_norm;  /* [L] -> [d_model]                     */
+  const void* const* w_gate;    /* [L] -> [d_ffn][d_model]              */
+  const void* const* w_up;      /* [L] -> [d_ffn][d_model]              */
+  const void* const* w_down;    /* [L] -> [d_model][d_ffn]              */
+  /* e4m3 KV only: DEVICE float32 [L][2 (K, V)][n_kv_heads] dequantisation
+   * scales (stored code * scale = value); NULL for bf16 KV. */
+  const float* kv_scale;
+} pie_weights;
+
+/* Capacity of one pie_forward call; fixes the workspace size. */
+typedef struct pie_limits {
+  int32_t max_rows;    /* packed new tokens per call                          */
+  int32_t max_seqs;    /* passes (sequences) per call                         */
+  int32_t max_readout; /* readout rows per call                               */
+  int32_t max_ctx;     /* tokens in one working set, including the new ones  */
+} pie_limits;
+
+/* Bytes of one KV page over all layers (K and V, every KV head, page_size tokens). */
+size_t pie_kv_page_bytes(const pie_model_desc* desc);
+
+/* Device workspace bytes pie_init needs for these limits (0 on bad input). */
+size_t pie_workspace_bytes(const pie_model_desc* desc, const pie_limits* limits);
+
+/* Create a context.
+ *  kv_arena/kv_bytes: DEVICE memory for the page pool; pages = kv_bytes / pie_kv_page_bytes.
+ *  workspace/ws_bytes: DEVICE scratch of at least pie_workspace_bytes(desc, limits).
+ *  hip_stream: the hipStream_t every launch goes to (NULL = the null stream).
+ * With weights == NULL the context is host-only: it keeps working sets, page
+ * pool and batch packing but never touches the GPU (kv_arena and workspace may be
+ * NULL, kv_bytes still sizes the pool) and pie_forward needs PIE_FLAG_NO_LAUNCH.
+ * Errors: PIE_EINVAL (bad shape, limits or sizes), PIE_EHIP. */
+int pie_init(const pie_model_desc* desc, const pie_weights* weights, void* kv_arena,
+             size_t kv_bytes, void* workspace, size_t ws_bytes, const pie_limits* limits,
+             void* hip_stream, pie_ctx** out);
+
+/* Destroy a context; outstanding working sets are released.  NULL is a no-op. */
+int pie_destroy(pie_ctx* ctx);
+
+/* WorkingSet(): a new, empty working set (len = frozen_len = 0). */
+int pie_alloc_working_set(pie_ctx* ctx, pie_ws* out);
+
+/* ws.fork() ("How Pie thinks", section 4): a new working set that shares the
+ * parent's FROZEN prefix pages (reference counts +1, no KV bytes move) and has
+ * an empty writable buffer; the parent's uncommitted tokens are not inherited.
+ * A page shared this way is never written again: whoever appends next starts a
+ * fresh page, so a partly filled shared page stays partly filled in both. */
+int pie_fork(pie_ctx* ctx, pie_ws parent, pie_ws* child);
+
+/* Release a working set; pages whose reference count drops to 0 return to the pool. */
+int pie_free_working_set(pie_ctx* ctx, pie_ws ws);
+
+/* Roll the writable buffer back to new_len tokens (frozen_len <= new_len <= len).
+ * Pages left empty return to the pool.  Errors: PIE_EINVAL. */
+int pie_truncate(pie_ctx* ctx, pie_ws ws, int32_t new_len);
+
+typedef struct pie_ws_stats {
+  int32_t len;        /* tokens in the working set                    */
+  int32_t frozen_len; /* committed prefix length                      */
+  int32_t n_pages;    /* page-table entries                           */
+} pie_ws_stats;
+
+/* Working-set state; page_ids (nullable, host, n_pages entries) receives the
+ * page table's page ids in order. */
+int pie_ws_info(pie_ctx* ctx, pie_ws ws, pie_ws_stats* stats, int32_t* page_ids);
+
+typedef struct pie_pool_stats {
+  int64_t pages_total;
+  int64_t pages_free;
+  int64_t pages_ever_allocated; /* pages taken from the free list since init      */
+  int64_t kv_bytes_copied;      /* KV bytes ever copied between pages (always 0)  */
+} pie_pool_stats;
+
+int pie_pool_stats_get(pie_ctx* ctx, pie_pool_stats* out);
+
+/* Epilogue of one readout row.  ARGMAX: the lowest index of the largest logit.
+ * GUMBEL_MAX: the lowest index of the largest logit/temperature + G, where
+ * G = -ln(-ln u), u = ((x >> 9) + 0.5) * 2^-23 and x is word 0 of
+ * Philox4x32-10 with counter (vocab index, lane, 0, 0) and key (seed low 32
+ * bits, seed high 32 bits); lane is the row's index in its pass's readout list.
+ * temperature must be finite and > 0 for GUMBEL_MAX (ignored for ARGMAX). */
+typedef struct pie_epilogue {
+  int32_t kind;
+  float temperature;
+  uint64_t seed;
+} pie_epilogue;
+
+/* One ForwardPass ("How Pie thinks", section 3): new tokens for one working
+ * set, which rows to read out, the epilogue per readout row, and whether the
+ * appended tokens are committed (StateGeometry.folding(): append and freeze). */
+typedef struct pie_pass {
+  pie_ws ws;
+  const int32_t* tokens;    /* host [n_tokens]; 0 <= id < vocab                          */
+  const int32_t* positions; /* host [n_tokens] RoPE positions, or NULL for len + i      */
+  int32_t n_tokens;         /* >= 1                                                      */
+  const int32_t* readout;   /* host [n_readout] row indices into this pass's tokens      */
+  int32_t n_readout;        /* >= 0                                                      */
+  const pie_epilogue* epi;  /* host [n_readout]                                          */
+  int32_t commit;           /* 1: freeze everything appended so far; 0: writable buffer */
+} pie_pass;
+
+/* Run one batched forward over n_passes passes of distinct working sets.
+ *  out_tokens: host [sum n_readout] int32, pass order then readout order.
+ *  out_logits: NULL, or [sum n_readout][vocab] float32 (host pointer, or device
+ *              pointer with PIE_FLAG_LOGITS_DEVICE).
+ * All-or-nothing: every pass is validated and every page reserved before any
+ * launch; on an error no working set changes.
+ * Errors: PIE_EINVAL (stale handle, the same working set twice, token id out of
+ * range, readout index out of range, temperature <= 0 or not finite, positions
+ * not given when required, more rows/seqs/readouts than the limits, a sequence
+ * beyond max_ctx), PIE_ENOMEM (page pool exhausted), PIE_EHIP, PIE_ESTATE.
+ * Returns after the stream has finished the call's work. */
+int pie_forward(pie_ctx* ctx, const pie_pass* passes, int32_t n_passes, int32_t* out_tokens,
+                float* out_logits, int32_t flags);
+
+const char* pie_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Measurement hooks
+ * ------------------------------------------------------------------------- */
+
+/* Kernel classes a context can time with HIP events recorded on its stream. */
+enum pie_kernel_class {
+  PIE_K_EMBED = 0,      /* embedding gather                                 */
+  PIE_K_GEMM_QKV = 1,   /* RMSNorm-fused QKV projection + RoPE + KV append  */
+  PIE_K_ATTN_DECODE = 2,/* paged decode attention (split-KV + combine)      */
+  PIE_K_ATTN_PREFILL = 3,/* paged chunked-prefill attention                 */
+  PIE_K_GEMM_O = 4,     /* output projection + residual                     */
+  PIE_K_GEMM_GATEUP = 5,/* RMSNorm-fused gate/up projection + SwiGLU        */
+  PIE_K_GEMM_DOWN = 6,  /* down projection + residual                       */
+  PIE_K_LM_HEAD = 7,    /* final RMSNorm + gather + lm_head + epilogue      */
+  PIE_K_NUM_CLASSES = 8
+};
+
+/* Time every launch of the classes in class_mask (bit i = class i) from now on
+ * (0 turns timing off and clears totals). */
+int pie_profile_enable(pie_ctx* ctx, uint32_t class_mask);
+
+/* Per class: total milliseconds and number of launches timed since enabling.
+ * Synchronises the stream.  ms and counts are host arrays [PIE_K_NUM_CLASSES]. */
+int pie_profile_read(pie_ctx* ctx, double* ms, int64_t* counts);
+
+/* ---------------------------------------------------------------------------
+ * Debug views (used by tests)
+ * ------------------------------------------------------------------------- */
+
+/* The metadata the packer built for the last pie_forward of this context
+ * (host copies; valid until the next pie_forward or pie_destroy). */
+typedef struct pie_plan_view {
+  int32_t n_rows, n_seqs, n_readout, n_page_entries;
+  const int32_t* tok;      /* [n_rows]                                           */
+  const int32_t* pos;      /* [n_rows]                                           */
+  const int32_t* row_seq;  /* [n_rows] launch-local sequence of each row        */
+  const int32_t* slot;     /* [n_rows] page * page_size + offset the row's K/V goes to */
+  const int32_t* seq_row0; /* [n_seqs + 1] first packed row of each sequence    */
+  const int32_t* seq_ctx;  /* [n_seqs] tokens before this call                  */
+  const int32_t* seq_len;  /* [n_seqs] tokens after this call                   */
+  const int32_t* seq_pg0;  /* [n_seqs + 1] first page entry of each sequence    */
+  const int32_t* pg_id;    /* [n_page_entries] page id                          */
+  const int32_t* pg_valid; /* [n_page_entries] valid slots (1..page_size)       */
+  const int32_t* pg_start; /* [n_page_entries] logical index of the first slot  */
+  const int32_t* ro_row;   /* [n_readout] packed row of each readout            */
+  const int32_t* ro_lane;  /* [n_readout] index in its pass's readout list      */
+} pie_plan_view;
+
+int pie_debug_plan(pie_ctx* ctx, pie_plan_view* out);
+
+/* Word 0 of Philox4x32-10 for counters (v0 + i, lane, 0, 0), i in [0, n), key
+ * (seed lo, seed hi), computed by the device code the epilogue uses.
+ * out: DEVICE uint32 [n].  Runs on the context's stream and synchronises. */
+int pie_debug_philox(pie_ctx* ctx, uint64_t seed, uint32_t lane, uint32_t v0, int32_t n,
+                     uint32_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PIE_H */

@@ -1,0 +1,762 @@
+// The C ABI of include/pie.h: contexts, working sets and the batched forward.
+//
+// pie_forward packs the passes (packer.cpp), stages the packed metadata into
+// the device workspace with one host-to-device copy, and launches per call:
+//   rope table, embed, then per layer
+//     QKV GEMM (RMSNorm prologue; RoPE + KV append epilogue)
+//     decode attention (+ split combine) and/or chunked-prefill attention
+//     O GEMM (+ residual)
+//     gate/up GEMM (RMSNorm prologue; SwiGLU epilogue)
+//     down GEMM (+ residual)
+//   then the head GEMM (final RMSNorm of the gathered readout rows; fused
+//   argmax / Gumbel-max epilogue) and the cross-tile reduce,
+// and copies back only the token ids (and logits when asked).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "attention.h"
+#include "gemm.h"
+#include "kvstore.h"
+#include "misc.h"
+#include "packer.h"
+#include "pie.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int set_err(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+constexpr int GEMM_BN = 128;
+constexpr int GEMM_BK = 64;
+constexpr int MAX_SPLITS = 16;
+constexpr int LM_BN = 128;
+
+// Split-K policy for the small-M (decode) tile: enough workgroups to fill the
+// chip, each with at least 4 K-steps.
+struct SplitK {
+  int splits, k_split;
+};
+
+SplitK choose_split(int M, int n_tiles, int K) {
+  if (M > 64) return {1, K};
+  const int target = 512;
+  int s = (target + n_tiles - 1) / n_tiles;
+  s = std::max(1, std::min(s, MAX_SPLITS));
+  int max_by_k = std::max(1, K / (4 * GEMM_BK));
+  s = std::min(s, max_by_k);
+  int ks = (K + s - 1) / s;
+  ks = (ks + GEMM_BK - 1) / GEMM_BK * GEMM_BK;
+  s = (K + ks - 1) / ks;
+  return {s, ks};
+}
+
+struct Layout {
+  // int32 metadata offsets (in int32 units from meta base)
+  size_t tok, pos, row_seq, slot, seq_row0, seq_ctx, seq_len, seq_pg0, pg_id, pg_valid, pg_start,
+      ro_row, ro_lane, ro_kind, ro_temp, ro_seed_lo, ro_seed_hi, dec_items, comb_items, pre_items,
+      tokens_out, meta_ints;
+  int32_t max_pe, max_dec_items, max_pre_items;
+  // byte offsets into the workspace
+  size_t meta, y, ss, q, o, h, rope, part_o, part_ml, gpart, counters, tile_best, tile_idx, logits,
+      total;
+  size_t gpart_floats;
+  int n_counters;
+};
+
+bool desc_ok(const pie_model_desc* d, std::string* why) {
+  if (!d) { *why = "null model desc"; return false; }
+  if (d->n_layers < 1 || d->d_model < 128 || d->d_model % 128 || d->n_q_heads < 1 ||
+      d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads || d->d_ffn < 8 || d->d_ffn % 8 ||
+      d->vocab < 2) {
+    *why = "model desc: bad dimensions (d_model % 128, d_ffn % 8, heads)";
+    return false;
+  }
+  if (d->head_dim != 64 && d->head_dim != 128) { *why = "model desc: head_dim must be 64 or 128"; return false; }
+  if ((d->n_q_heads * d->head_dim) % 128 || (d->n_kv_heads * d->head_dim) % 128) {
+    *why = "model desc: q and kv widths must be multiples of 128";
+    return false;
+  }
+  if (d->n_q_heads / d->n_kv_heads > 16) { *why = "model desc: at most 16 query heads per KV head"; return false; }
+  if (d->page_size != 16) { *why = "model desc: page_size must be 16"; return false; }
+  if (d->kv_dtype != PIE_KV_BF16 && d->kv_dtype != PIE_KV_E4M3) { *why = "model desc: kv_dtype"; return false; }
+  if (!(d->rms_eps > 0.f) || !(d->rope_theta > 1.f)) { *why = "model desc: eps / theta"; return false; }
+  return true;
+}
+
+bool limits_ok(const pie_limits* l, std::string* why) {
+  if (!l || l->max_rows < 1 || l->max_seqs < 1 || l->max_readout < 0 || l->max_ctx < 1 ||
+      l->max_seqs > l->max_rows) {
+    *why = "bad limits (max_rows >= max_seqs >= 1, max_ctx >= 1)";
+    return false;
+  }
+  return true;
+}
+
+size_t kv_elem_bytes(const pie_model_desc& d) { return d.kv_dtype == PIE_KV_E4M3 ? 1 : 2; }
+long page_stride_elems(const pie_model_desc& d) { return 2L * d.n_kv_heads * d.page_size * d.head_dim; }
+
+Layout make_layout(const pie_model_desc& d, const pie_limits& l) {
+  Layout L{};
+  const size_t R = (size_t)l.max_rows, S = (size_t)l.max_seqs, RO = (size_t)std::max(l.max_readout, 1);
+  L.max_pe = (int32_t)std::min<int64_t>((int64_t)S * ((l.max_ctx + d.page_size - 1) / d.page_size + 4),
+                                        (int64_t)1 << 30);
+  L.max_dec_items = L.max_pe / 8 + 2 * (int32_t)S;
+  L.max_pre_items = (int32_t)(R + S);
+  size_t o = 0;
+  auto take = [&](size_t n) { size_t at = o; o += (n + 63) / 64 * 64; return at; };
+  L.tok = take(R); L.pos = take(R); L.row_seq = take(R); L.slot = take(R);
+  L.seq_row0 = take(S + 1); L.seq_ctx = take(S); L.seq_len = take(S); L.seq_pg0 = take(S + 1);
+  L.pg_id = take(L.max_pe); L.pg_valid = take(L.max_pe); L.pg_start = take(L.max_pe);
+  L.ro_row = take(RO); L.ro_lane = take(RO); L.ro_kind = take(RO); L.ro_temp = take(RO);
+  L.ro_seed_lo = take(RO); L.ro_seed_hi = take(RO);
+  L.dec_items = take(4 * (size_t)L.max_dec_items); L.comb_items = take(4 * S);
+  L.pre_items = take(4 * (size_t)L.max_pre_items);
+  L.tokens_out = take(RO);
+  L.meta_ints = o;
+
+  const size_t qw = (size_t)d.n_q_heads * d.head_dim;
+  const int n_ss = d.d_model / 128;
+  size_t b = 0;
+  auto take_b = [&](size_t bytes) { size_t at = b; b = align_up(b + bytes); return at; };
+  L.meta = take_b(L.meta_ints * 4);
+  L.y = take_b(R * d.d_model * 4);
+  L.ss = take_b(R * n_ss * 4);
+  L.q = take_b(R * qw * 2);
+  L.o = take_b(R * qw * 2);
+  L.h = take_b(R * (size_t)d.d_ffn * 2);
+  L.rope = take_b(R * (size_t)d.head_dim * 4);
+  L.part_o = take_b((size_t)L.max_dec_items * d.n_kv_heads * 16 * d.head_dim * 4);
+  L.part_ml = take_b((size_t)L.max_dec_items * d.n_kv_heads * 16 * 2 * 4);
+  // split-K partials for the worst case over the four layer GEMMs at M <= 64
+  const int kvw = d.n_kv_heads * d.head_dim;
+  struct G { int n_tiles, K; } gs[4] = {
+      {(int)((qw + 2 * kvw + GEMM_BN - 1) / GEMM_BN), d.d_model},
+      {(d.d_model + GEMM_BN - 1) / GEMM_BN, (int)qw},
+      {(d.d_ffn + GEMM_BN / 2 - 1) / (GEMM_BN / 2), d.d_model},
+      {(d.d_model + GEMM_BN - 1) / GEMM_BN, d.d_ffn}};
+  size_t worst = 0;
+  int max_tiles = 0;
+  for (auto& g : gs) {
+    SplitK sk = choose_split(64, g.n_tiles, g.K);
+    worst = std::max(worst, (size_t)g.n_tiles * sk.splits);
+    max_tiles = std::max(max_tiles, g.n_tiles);
+  }
+  L.gpart_floats = worst * 64 * GEMM_BN;
+  L.gpart = take_b(L.gpart_floats * 4);
+  L.n_counters = max_tiles;
+  L.counters = take_b((size_t)max_tiles * 4);
+  const size_t vt = (size_t)(d.vocab + LM_BN - 1) / LM_BN;
+  L.tile_best = take_b(vt * RO * 4);
+  L.tile_idx = take_b(vt * RO * 4);
+  L.logits = take_b(RO * (size_t)d.vocab * 4);
+  L.total = b;
+  return L;
+}
+
+}  // namespace
+
+struct pie_ctx {
+  pie_model_desc d{};
+  pie_limits lim{};
+  bool host_only = false, poisoned = false;
+  const uint16_t *embed = nullptr, *final_norm = nullptr, *lm_head = nullptr;
+  std::vector<const uint16_t*> attn_norm, wq, wk, wv, wo, mlp_norm, wg, wu, wd;
+  const float* kv_scale = nullptr;
+  uint8_t* kv = nullptr;
+  int64_t n_pages = 0;
+  long page_stride = 0;
+  uint8_t* ws = nullptr;
+  Layout lay{};
+  hipStream_t stream = nullptr;
+  pie::KVStore store{16};
+  pie::Plan plan;
+  int32_t* pinned = nullptr;
+  std::vector<int32_t> dec, comb, pre;  // int4 items, flattened
+  int n_parts = 0;
+  // profiling
+  uint32_t prof_mask = 0;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<std::pair<int, size_t>> ev_marks;  // (class, index of start event)
+  double prof_ms[PIE_K_NUM_CLASSES] = {0};
+  int64_t prof_n[PIE_K_NUM_CLASSES] = {0};
+};
+
+namespace {
+
+int hip_fail(pie_ctx* c, hipError_t e, const char* what) {
+  if (c) c->poisoned = true;
+  return set_err(PIE_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HIP_TRY(c, call)                                   \
+  do {                                                     \
+    hipError_t e_ = (call);                                \
+    if (e_ != hipSuccess) return hip_fail((c), e_, #call); \
+  } while (0)
+
+hipEvent_t next_event(pie_ctx* c) {
+  if (c->ev_used == c->ev_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    c->ev_pool.push_back(e);
+  }
+  return c->ev_pool[c->ev_used++];
+}
+
+// Brackets one launch of class k with events when that class is being timed.
+struct Timed {
+  pie_ctx* c;
+  int k;
+  bool on;
+  Timed(pie_ctx* c_, int k_) : c(c_), k(k_), on((c_->prof_mask >> k_) & 1u) {
+    if (on) {
+      hipEvent_t a = next_event(c), b = next_event(c);
+      if (!a || !b) { on = false; return; }
+      c->ev_marks.push_back({k, c->ev_used - 2});
+      (void)hipEventRecord(a, c->stream);
+    }
+  }
+  ~Timed() {
+    if (on) (void)hipEventRecord(c->ev_pool[c->ev_marks.back().second + 1], c->stream);
+  }
+};
+
+void collect_profile(pie_ctx* c) {
+  for (auto& m : c->ev_marks) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, c->ev_pool[m.second], c->ev_pool[m.second + 1]) == hipSuccess) {
+      c->prof_ms[m.first] += ms;
+      c->prof_n[m.first] += 1;
+    }
+  }
+  c->ev_marks.clear();
+  c->ev_used = 0;
+}
+
+int check_launch(pie_ctx* c, int flags, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(c, e, what);
+  if (flags & PIE_FLAG_SYNC_DEBUG) {
+    e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, what);
+  }
+  return PIE_OK;
+}
+
+void build_work(pie_ctx* c) {
+  const pie::Plan& p = c->plan;
+  const int G = c->d.n_q_heads / c->d.n_kv_heads;
+  const int tpw = std::max(1, pie::PREFILL_ROWS / G);
+  c->dec.clear();
+  c->comb.clear();
+  c->pre.clear();
+  c->n_parts = 0;
+  int n_dec = 0;
+  int64_t dec_entries = 0;
+  for (int s = 0; s < p.n_seqs; ++s)
+    if (p.seq_row0[s + 1] - p.seq_row0[s] == 1) {
+      ++n_dec;
+      dec_entries += p.seq_pg0[s + 1] - p.seq_pg0[s];
+    }
+  int pps = 1 << 30;
+  if (n_dec) {
+    const int64_t target = std::max<int64_t>(n_dec, (2048 + c->d.n_kv_heads - 1) / c->d.n_kv_heads);
+    int64_t v = (dec_entries + target - 1) / target;
+    v = std::max<int64_t>(v, 8);
+    pps = (int)((v + 1) / 2 * 2);
+  }
+  for (int s = 0; s < p.n_seqs; ++s) {
+    const int n_new = p.seq_row0[s + 1] - p.seq_row0[s];
+    const int e0 = p.seq_pg0[s], e1 = p.seq_pg0[s + 1];
+    if (n_new == 1) {
+      const int ns = std::max(1, (e1 - e0 + pps - 1) / pps);
+      if (ns == 1) {
+        c->dec.insert(c->dec.end(), {s, e0, e1, -1});
+      } else {
+        for (int k = 0; k < ns; ++k)
+          c->dec.insert(c->dec.end(), {s, e0 + k * pps, std::min(e1, e0 + (k + 1) * pps), c->n_parts + k});
+        c->comb.insert(c->comb.end(), {s, c->n_parts, ns, 0});
+        c->n_parts += ns;
+      }
+    } else {
+      for (int tb = 0; tb < n_new; tb += tpw)
+        c->pre.insert(c->pre.end(), {s, tb, std::min(tpw, n_new - tb), 0});
+    }
+  }
+}
+
+template <typename T>
+void put(int32_t* base, size_t off, const std::vector<T>& v) {
+  if (!v.empty()) std::memcpy(base + off, v.data(), v.size() * sizeof(T));
+}
+
+int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
+  const pie::Plan& p = c->plan;
+  const pie_model_desc& d = c->d;
+  const Layout& L = c->lay;
+  hipStream_t st = c->stream;
+  build_work(c);
+  if ((int)(c->dec.size() / 4) > L.max_dec_items || (int)(c->pre.size() / 4) > L.max_pre_items)
+    return set_err(PIE_ENOMEM, "pie_forward: attention work list exceeds the workspace");
+
+  // ---- stage metadata (one H2D copy) ----
+  int32_t* h = c->pinned;
+  put(h, L.tok, p.tok); put(h, L.pos, p.pos); put(h, L.row_seq, p.row_seq); put(h, L.slot, p.slot);
+  put(h, L.seq_row0, p.seq_row0); put(h, L.seq_ctx, p.seq_ctx); put(h, L.seq_len, p.seq_len);
+  put(h, L.seq_pg0, p.seq_pg0); put(h, L.pg_id, p.pg_id); put(h, L.pg_valid, p.pg_valid);
+  put(h, L.pg_start, p.pg_start); put(h, L.ro_row, p.ro_row); put(h, L.ro_lane, p.ro_lane);
+  put(h, L.ro_kind, p.ro_kind); put(h, L.ro_temp, p.ro_temp); put(h, L.ro_seed_lo, p.ro_seed_lo);
+  put(h, L.ro_seed_hi, p.ro_seed_hi); put(h, L.dec_items, c->dec); put(h, L.comb_items, c->comb);
+  put(h, L.pre_items, c->pre);
+  const size_t meta_used = L.tokens_out;  // everything before the token output slot
+  int32_t* dmeta = reinterpret_cast<int32_t*>(c->ws + L.meta);
+  HIP_TRY(c, hipMemcpyAsync(dmeta, h, meta_used * 4, hipMemcpyHostToDevice, st));
+  auto M32 = [&](size_t off) { return dmeta + off; };
+
+  float* y = reinterpret_cast<float*>(c->ws + L.y);
+  float* ss = reinterpret_cast<float*>(c->ws + L.ss);
+  uint16_t* q = reinterpret_cast<uint16_t*>(c->ws + L.q);
+  uint16_t* o = reinterpret_cast<uint16_t*>(c->ws + L.o);
+  uint16_t* hb = reinterpret_cast<uint16_t*>(c->ws + L.h);
+  float* rope = reinterpret_cast<float*>(c->ws + L.rope);
+  const int T = p.n_rows, R = p.n_readout;
+  const int qw = d.n_q_heads * d.head_dim, kvw = d.n_kv_heads * d.head_dim;
+  const int n_ss = d.d_model / 128;
+  int rc;
+
+  pie::launch_rope_table(M32(L.pos), T, d.head_dim, (double)d.rope_theta, rope, st);
+  if ((rc = check_launch(c, flags, "rope table"))) return rc;
+  {
+    Timed tm(c, PIE_K_EMBED);
+    pie::launch_embed(c->embed, M32(L.tok), T, d.d_model, y, ss, st);
+  }
+  if ((rc = check_launch(c, flags, "embed"))) return rc;
+
+  const int tile = T <= 64 ? pie::TILE_64x128 : pie::TILE_128x128;
+  float* gpart = reinterpret_cast<float*>(c->ws + L.gpart);
+  int* counters = reinterpret_cast<int*>(c->ws + L.counters);
+  const size_t elem = kv_elem_bytes(d);
+
+  pie::GemmArgs base{};
+  base.M = T;
+  base.ss = ss;
+  base.n_ss = n_ss;
+  base.y = y;
+  base.ldy = d.d_model;
+  base.eps = d.rms_eps;
+  base.partial = gpart;
+  base.counters = counters;
+  base.y_out = y;
+  base.ss_out = ss;
+
+  auto set_split = [&](pie::GemmArgs& g, int n_tiles) {
+    SplitK sk = choose_split(T, n_tiles, g.K);
+    if ((size_t)n_tiles * sk.splits * 64 * GEMM_BN > L.gpart_floats || n_tiles > L.n_counters)
+      sk = {1, g.K};
+    g.splits = sk.splits;
+    g.k_split = sk.k_split;
+  };
+
+  pie::AttnArgs at{};
+  at.q = q;
+  at.o = o;
+  at.page_stride = c->page_stride;
+  at.nq = d.n_q_heads;
+  at.nkv = d.n_kv_heads;
+  at.hd = d.head_dim;
+  at.page_size = d.page_size;
+  at.kv_e4m3 = d.kv_dtype == PIE_KV_E4M3;
+  at.sm_scale = 1.0f / std::sqrt((float)d.head_dim);
+  at.seq_row0 = M32(L.seq_row0);
+  at.seq_ctx = M32(L.seq_ctx);
+  at.seq_pg0 = M32(L.seq_pg0);
+  at.pg_id = M32(L.pg_id);
+  at.pg_valid = M32(L.pg_valid);
+  at.pg_start = M32(L.pg_start);
+  at.part_o = reinterpret_cast<float*>(c->ws + L.part_o);
+  at.part_ml = reinterpret_cast<float*>(c->ws + L.part_ml);
+
+  for (int l = 0; l < d.n_layers; ++l) {
+    void* kv_layer = c->kv + (size_t)l * c->n_pages * c->page_stride * elem;
+    const float* kvs = c->kv_scale ? c->kv_scale + (size_t)l * 2 * d.n_kv_heads : nullptr;
+    // QKV
+    {
+      pie::GemmArgs g = base;
+      g.N = qw + 2 * kvw;
+      g.K = d.d_model;
+      g.gain = c->attn_norm[l];
+      g.w[0] = c->wq[l]; g.w[1] = c->wk[l]; g.w[2] = c->wv[l];
+      g.seg_n0[0] = 0; g.seg_n0[1] = qw; g.seg_n0[2] = qw + kvw; g.seg_n0[3] = qw + 2 * kvw;
+      g.q_out = q;
+      g.rope_cs = rope;
+      g.slot = M32(L.slot);
+      g.kv_layer = kv_layer;
+      g.page_stride = c->page_stride;
+      g.nq = d.n_q_heads; g.nkv = d.n_kv_heads; g.hd = d.head_dim; g.page_size = d.page_size;
+      g.kv_e4m3 = d.kv_dtype == PIE_KV_E4M3;
+      g.kv_scale = kvs;
+      set_split(g, (g.N + GEMM_BN - 1) / GEMM_BN);
+      Timed tm(c, PIE_K_GEMM_QKV);
+      pie::launch_gemm(pie::A_NORM, pie::EPI_QKV, tile, g, st);
+    }
+    if ((rc = check_launch(c, flags, "qkv gemm"))) return rc;
+    // attention
+    at.kv_layer = kv_layer;
+    at.kv_scale = kvs;
+    if (!c->dec.empty()) {
+      at.items = reinterpret_cast<const int4*>(M32(L.dec_items));
+      at.n_items = (int)(c->dec.size() / 4);
+      at.combine = reinterpret_cast<const int4*>(M32(L.comb_items));
+      at.n_combine = (int)(c->comb.size() / 4);
+      {
+        Timed tm(c, PIE_K_ATTN_DECODE);
+        pie::launch_attn_decode(at, st);
+        pie::launch_attn_combine(at, st);
+      }
+      if ((rc = check_launch(c, flags, "decode attention"))) return rc;
+    }
+    if (!c->pre.empty()) {
+      at.items = reinterpret_cast<const int4*>(M32(L.pre_items));
+      at.n_items = (int)(c->pre.size() / 4);
+      {
+        Timed tm(c, PIE_K_ATTN_PREFILL);
+        pie::launch_attn_prefill(at, st);
+      }
+      if ((rc = check_launch(c, flags, "prefill attention"))) return rc;
+    }
+    // O projection + residual
+    {
+      pie::GemmArgs g = base;
+      g.N = d.d_model;
+      g.K = qw;
+      g.a = o;
+      g.lda = qw;
+      g.w[0] = g.w[1] = g.w[2] = c->wo[l];
+      g.seg_n0[0] = 0; g.seg_n0[1] = g.seg_n0[2] = g.seg_n0[3] = d.d_model;
+      set_split(g, (g.N + GEMM_BN - 1) / GEMM_BN);
+      Timed tm(c, PIE_K_GEMM_O);
+      pie::launch_gemm(pie::A_BF16, pie::EPI_RESID, tile, g, st);
+    }
+    if ((rc = check_launch(c, flags, "o gemm"))) return rc;
+    // gate/up + SwiGLU
+    {
+      pie::GemmArgs g = base;
+      g.N = d.d_ffn;
+      g.K = d.d_model;
+      g.gain = c->mlp_norm[l];
+      g.w[0] = c->wg[l]; g.w[1] = c->wu[l]; g.w[2] = c->wu[l];
+      g.h_out = hb;
+      set_split(g, (g.N + GEMM_BN / 2 - 1) / (GEMM_BN / 2));
+      Timed tm(c, PIE_K_GEMM_GATEUP);
+      pie::launch_gemm(pie::A_NORM, pie::EPI_SWIGLU, tile, g, st);
+    }
+    if ((rc = check_launch(c, flags, "gate/up gemm"))) return rc;
+    // down + residual
+    {
+      pie::GemmArgs g = base;
+      g.N = d.d_model;
+      g.K = d.d_ffn;
+      g.a = hb;
+      g.lda = d.d_ffn;
+      g.w[0] = g.w[1] = g.w[2] = c->wd[l];
+      g.seg_n0[0] = 0; g.seg_n0[1] = g.seg_n0[2] = g.seg_n0[3] = d.d_model;
+      set_split(g, (g.N + GEMM_BN - 1) / GEMM_BN);
+      Timed tm(c, PIE_K_GEMM_DOWN);
+      pie::launch_gemm(pie::A_BF16, pie::EPI_RESID, tile, g, st);
+    }
+    if ((rc = check_launch(c, flags, "down gemm"))) return rc;
+  }
+
+  int32_t* dtok = M32(L.tokens_out);
+  if (R > 0) {
+    float* logits = nullptr;
+    if (out_logits) logits = (flags & PIE_FLAG_LOGITS_DEVICE) ? out_logits : reinterpret_cast<float*>(c->ws + L.logits);
+    pie::GemmArgs g = base;
+    g.M = R;
+    g.N = d.vocab;
+    g.K = d.d_model;
+    g.gain = c->final_norm;
+    g.a_rows = M32(L.ro_row);
+    g.w[0] = g.w[1] = g.w[2] = c->lm_head;
+    g.seg_n0[0] = 0; g.seg_n0[1] = g.seg_n0[2] = g.seg_n0[3] = d.vocab;
+    g.splits = 1;
+    g.k_split = g.K;
+    g.logits = logits;
+    g.ro_kind = M32(L.ro_kind);
+    g.ro_temp = reinterpret_cast<const float*>(M32(L.ro_temp));
+    g.ro_seed_lo = reinterpret_cast<const uint32_t*>(M32(L.ro_seed_lo));
+    g.ro_seed_hi = reinterpret_cast<const uint32_t*>(M32(L.ro_seed_hi));
+    g.ro_lane = M32(L.ro_lane);
+    g.tile_best = reinterpret_cast<float*>(c->ws + L.tile_best);
+    g.tile_idx = reinterpret_cast<int32_t*>(c->ws + L.tile_idx);
+    const int vt = (d.vocab + LM_BN - 1) / LM_BN;
+    {
+      Timed tm(c, PIE_K_LM_HEAD);
+      pie::launch_gemm(pie::A_NORM, pie::EPI_LOGITS, R <= 64 ? pie::TILE_64x128 : pie::TILE_128x128, g, st);
+      pie::launch_argmax_reduce(g.tile_best, g.tile_idx, vt, R, dtok, st);
+    }
+    if ((rc = check_launch(c, flags, "lm_head"))) return rc;
+    HIP_TRY(c, hipMemcpyAsync(h + L.tokens_out, dtok, (size_t)R * 4, hipMemcpyDeviceToHost, st));
+    if (out_logits && !(flags & PIE_FLAG_LOGITS_DEVICE))
+      HIP_TRY(c, hipMemcpyAsync(out_logits, logits, (size_t)R * d.vocab * 4, hipMemcpyDeviceToHost, st));
+  }
+  HIP_TRY(c, hipStreamSynchronize(st));
+  if (c->prof_mask) collect_profile(c);
+  if (R > 0) std::memcpy(out_tokens, h + L.tokens_out, (size_t)R * 4);
+  return PIE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pie_kv_page_bytes(const pie_model_desc* desc) {
+  std::string why;
+  if (!desc_ok(desc, &why)) return 0;
+  return (size_t)desc->n_layers * page_stride_elems(*desc) * kv_elem_bytes(*desc);
+}
+
+size_t pie_workspace_bytes(const pie_model_desc* desc, const pie_limits* limits) {
+  std::string why;
+  if (!desc_ok(desc, &why) || !limits_ok(limits, &why)) return 0;
+  return make_layout(*desc, *limits).total;
+}
+
+int pie_init(const pie_model_desc* desc, const pie_weights* w, void* kv_arena, size_t kv_bytes,
+             void* workspace, size_t ws_bytes, const pie_limits* limits, void* hip_stream,
+             pie_ctx** out) {
+  std::string why;
+  if (!out) return set_err(PIE_EINVAL, "pie_init: null output");
+  *out = nullptr;
+  if (!desc_ok(desc, &why) || !limits_ok(limits, &why)) return set_err(PIE_EINVAL, "pie_init: " + why);
+  const size_t page_bytes = pie_kv_page_bytes(desc);
+  const int64_t n_pages = (int64_t)(kv_bytes / page_bytes);
+  if (n_pages < 1) return set_err(PIE_EINVAL, "pie_init: KV arena smaller than one page");
+  if (n_pages * desc->page_size >= ((int64_t)1 << 31))
+    return set_err(PIE_EINVAL, "pie_init: too many pages for 32-bit slot ids");
+  auto* c = new pie_ctx();
+  c->d = *desc;
+  c->lim = *limits;
+  c->store = pie::KVStore(desc->page_size);
+  c->store.reset(n_pages);
+  c->n_pages = n_pages;
+  c->page_stride = page_stride_elems(*desc);
+  c->lay = make_layout(*desc, *limits);
+  c->host_only = (w == nullptr);
+  if (c->host_only) {
+    c->pinned = static_cast<int32_t*>(std::malloc(c->lay.meta_ints * 4));
+    *out = c;
+    return PIE_OK;
+  }
+  const int L = desc->n_layers;
+  if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv ||
+      !w->wo || !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down) {
+    delete c;
+    return set_err(PIE_EINVAL, "pie_init: missing weight pointer");
+  }
+  if (desc->kv_dtype == PIE_KV_E4M3 && !w->kv_scale) {
+    delete c;
+    return set_err(PIE_EINVAL, "pie_init: e4m3 KV needs kv_scale");
+  }
+  if (!kv_arena || !workspace || ws_bytes < c->lay.total) {
+    size_t need = c->lay.total;
+    delete c;
+    return set_err(PIE_EINVAL, "pie_init: workspace too small (need " + std::to_string(need) + " bytes)");
+  }
+  auto cp = [&](std::vector<const uint16_t*>& dst, const void* const* src, const char* nm) {
+    dst.resize(L);
+    for (int l = 0; l < L; ++l) {
+      if (!src[l]) return std::string("pie_init: null ") + nm + " weight";
+      dst[l] = static_cast<const uint16_t*>(src[l]);
+    }
+    return std::string();
+  };
+  for (auto& e : {cp(c->attn_norm, w->attn_norm, "attn_norm"), cp(c->wq, w->wq, "q"), cp(c->wk, w->wk, "k"),
+                  cp(c->wv, w->wv, "v"), cp(c->wo, w->wo, "o"), cp(c->mlp_norm, w->mlp_norm, "mlp_norm"),
+                  cp(c->wg, w->w_gate, "gate"), cp(c->wu, w->w_up, "up"), cp(c->wd, w->w_down, "down")})
+    if (!e.empty()) { delete c; return set_err(PIE_EINVAL, e); }
+  c->embed = static_cast<const uint16_t*>(w->embed);
+  c->final_norm = static_cast<const uint16_t*>(w->final_norm);
+  c->lm_head = static_cast<const uint16_t*>(w->lm_head);
+  c->kv_scale = desc->kv_dtype == PIE_KV_E4M3 ? w->kv_scale : nullptr;
+  c->kv = static_cast<uint8_t*>(kv_arena);
+  c->ws = static_cast<uint8_t*>(workspace);
+  c->stream = static_cast<hipStream_t>(hip_stream);
+
+  int dev = 0;
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) { delete c; return set_err(PIE_EHIP, std::string("pie_init: ") + hipGetErrorString(e)); }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    delete c;
+    return set_err(PIE_ESTATE, std::string("pie_init: kernels are built for gfx950, device is ") + prop.gcnArchName);
+  }
+  e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned), c->lay.meta_ints * 4, hipHostMallocDefault);
+  if (e != hipSuccess) { delete c; return set_err(PIE_EHIP, std::string("pie_init: hipHostMalloc: ") + hipGetErrorString(e)); }
+  // counters of the split-K reduction start at zero (a fill kernel, not a memset)
+  pie::launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws + c->lay.counters), (size_t)c->lay.n_counters, 0u, c->stream);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) {
+    (void)hipHostFree(c->pinned);
+    delete c;
+    return set_err(PIE_EHIP, std::string("pie_init: ") + hipGetErrorString(e));
+  }
+  *out = c;
+  return PIE_OK;
+}
+
+int pie_destroy(pie_ctx* c) {
+  if (!c) return PIE_OK;
+  if (c->host_only) std::free(c->pinned);
+  else if (c->pinned) (void)hipHostFree(c->pinned);
+  for (auto e : c->ev_pool) (void)hipEventDestroy(e);
+  delete c;
+  return PIE_OK;
+}
+
+#define CTX_OK(c)                                                         \
+  do {                                                                    \
+    if (!(c)) return set_err(PIE_EINVAL, "null context");                 \
+    if ((c)->poisoned) return set_err(PIE_ESTATE, "context is poisoned"); \
+  } while (0)
+
+int pie_alloc_working_set(pie_ctx* c, pie_ws* out) {
+  CTX_OK(c);
+  std::string err;
+  int rc = c->store.alloc(out, &err);
+  return rc ? set_err(rc, err) : PIE_OK;
+}
+
+int pie_fork(pie_ctx* c, pie_ws parent, pie_ws* child) {
+  CTX_OK(c);
+  std::string err;
+  int rc = c->store.fork(parent, child, &err);
+  return rc ? set_err(rc, err) : PIE_OK;
+}
+
+int pie_free_working_set(pie_ctx* c, pie_ws ws) {
+  CTX_OK(c);
+  std::string err;
+  int rc = c->store.release(ws, &err);
+  return rc ? set_err(rc, err) : PIE_OK;
+}
+
+int pie_truncate(pie_ctx* c, pie_ws ws, int32_t new_len) {
+  CTX_OK(c);
+  std::string err;
+  int rc = c->store.truncate(ws, new_len, &err);
+  return rc ? set_err(rc, err) : PIE_OK;
+}
+
+int pie_ws_info(pie_ctx* c, pie_ws ws, pie_ws_stats* stats, int32_t* page_ids) {
+  CTX_OK(c);
+  const pie::WorkingSet* w = c->store.get(ws);
+  if (!w) return set_err(PIE_EINVAL, "ws_info: invalid or stale working set");
+  if (stats) {
+    stats->len = w->len;
+    stats->frozen_len = w->frozen_len;
+    stats->n_pages = (int32_t)w->pages.size();
+  }
+  if (page_ids)
+    for (size_t i = 0; i < w->pages.size(); ++i) page_ids[i] = w->pages[i].page;
+  return PIE_OK;
+}
+
+int pie_pool_stats_get(pie_ctx* c, pie_pool_stats* out) {
+  CTX_OK(c);
+  if (!out) return set_err(PIE_EINVAL, "null output");
+  out->pages_total = c->store.pool().total();
+  out->pages_free = c->store.pool().free_count();
+  out->pages_ever_allocated = c->store.pool().ever_allocated();
+  out->kv_bytes_copied = 0;  // no code path copies KV bytes between pages
+  return PIE_OK;
+}
+
+int pie_forward(pie_ctx* c, const pie_pass* passes, int32_t n_passes, int32_t* out_tokens,
+                float* out_logits, int32_t flags) {
+  CTX_OK(c);
+  if (!(flags & PIE_FLAG_NO_LAUNCH) && c->host_only)
+    return set_err(PIE_ESTATE, "pie_forward: a host-only context can only plan (PIE_FLAG_NO_LAUNCH)");
+  pie::PackLimits pl{c->lim.max_rows, c->lim.max_seqs, c->lim.max_readout, c->lim.max_ctx,
+                     c->lay.max_pe, c->d.vocab};
+  int64_t want_ro = 0;
+  if (passes && n_passes > 0)
+    for (int i = 0; i < n_passes; ++i) want_ro += passes[i].n_readout > 0 ? passes[i].n_readout : 0;
+  if (want_ro > 0 && !out_tokens) return set_err(PIE_EINVAL, "pie_forward: null out_tokens");
+  std::string err;
+  int rc = pie::pack_batch(c->store, passes, n_passes, pl, &c->plan, &err);
+  if (rc) return set_err(rc, err);
+  if (flags & PIE_FLAG_NO_LAUNCH) {
+    for (int i = 0; i < c->plan.n_readout; ++i) out_tokens[i] = -1;
+    return PIE_OK;
+  }
+  return run_forward(c, out_tokens, out_logits, flags);
+}
+
+const char* pie_last_error(void) { return g_err.c_str(); }
+
+int pie_profile_enable(pie_ctx* c, uint32_t mask) {
+  CTX_OK(c);
+  c->prof_mask = mask & ((1u << PIE_K_NUM_CLASSES) - 1);
+  for (int k = 0; k < PIE_K_NUM_CLASSES; ++k) {
+    c->prof_ms[k] = 0;
+    c->prof_n[k] = 0;
+  }
+  c->ev_marks.clear();
+  c->ev_used = 0;
+  return PIE_OK;
+}
+
+int pie_profile_read(pie_ctx* c, double* ms, int64_t* counts) {
+  CTX_OK(c);
+  if (!c->host_only) {
+    hipError_t e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "pie_profile_read");
+    collect_profile(c);
+  }
+  for (int k = 0; k < PIE_K_NUM_CLASSES; ++k) {
+    if (ms) ms[k] = c->prof_ms[k];
+    if (counts) counts[k] = c->prof_n[k];
+  }
+  return PIE_OK;
+}
+
+int pie_debug_plan(pie_ctx* c, pie_plan_view* v) {
+  CTX_OK(c);
+  if (!v) return set_err(PIE_EINVAL, "null output");
+  const pie::Plan& p = c->plan;
+  v->n_rows = p.n_rows; v->n_seqs = p.n_seqs; v->n_readout = p.n_readout; v->n_page_entries = p.n_pe;
+  v->tok = p.tok.data(); v->pos = p.pos.data(); v->row_seq = p.row_seq.data(); v->slot = p.slot.data();
+  v->seq_row0 = p.seq_row0.data(); v->seq_ctx = p.seq_ctx.data(); v->seq_len = p.seq_len.data();
+  v->seq_pg0 = p.seq_pg0.data(); v->pg_id = p.pg_id.data(); v->pg_valid = p.pg_valid.data();
+  v->pg_start = p.pg_start.data(); v->ro_row = p.ro_row.data(); v->ro_lane = p.ro_lane.data();
+  return PIE_OK;
+}
+
+int pie_debug_philox(pie_ctx* c, uint64_t seed, uint32_t lane, uint32_t v0, int32_t n, uint32_t* out) {
+  CTX_OK(c);
+  if (c->host_only) return set_err(PIE_ESTATE, "pie_debug_philox: host-only context");
+  if (n < 0 || (n > 0 && !out)) return set_err(PIE_EINVAL, "pie_debug_philox: bad arguments");
+  pie::launch_philox(seed, lane, v0, n, out, c->stream);
+  HIP_TRY(c, hipGetLastError());
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  return PIE_OK;
+}
+
+}  // extern "C"

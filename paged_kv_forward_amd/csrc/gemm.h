@@ -1,0 +1,80 @@
+// Dense projections of the decoder (ops.linear.matmul / glu / lm_head on the
+// "Poem ops" page) as one MFMA GEMM kernel with fused prologues and epilogues:
+//   C[M, N] = A[M, K] * W[N, K]^T,  W in checkpoint layout [out][in], bf16.
+// Prologue A_NORM computes the RMSNorm of the residual stream on the fly:
+//   A[m, k] = bf16(y[m, k] * rsqrt(sum_sq[m] / K + eps) * gain[k]),
+// with sum_sq[m] summed from per-128-column partials that the producer of y
+// wrote; with a_rows it also gathers rows (the readout rows of the head).
+// Epilogues:
+//   EPI_QKV     RoPE on q and k, q -> bf16 buffer, k and v -> KV page slots
+//   EPI_RESID   y += C, and the per-128-column sums of squares of the new y
+//   EPI_SWIGLU  h = bf16(silu(gate) * up), gate/up tiles interleaved
+//   EPI_LOGITS  logits (optional) and the per-tile maximum of the epilogue's
+//               decision value (argmax, or logit/T + Gumbel noise)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pie {
+
+enum { A_BF16 = 0, A_NORM = 1 };
+enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+struct GemmArgs {
+  int M, N, K;  // N: output columns (EPI_SWIGLU: d_ffn, the gated width)
+  // A operand
+  const uint16_t* a;    // A_BF16: [M][lda] bf16
+  int lda;
+  const float* y;       // A_NORM: residual stream [rows][ldy] fp32
+  int ldy;
+  const float* ss;      // A_NORM: sum-of-squares partials [rows][n_ss]
+  int n_ss;
+  const uint16_t* gain; // A_NORM: [K] bf16
+  const int32_t* a_rows;// A_NORM: optional row gather (A row m = y row a_rows[m])
+  float eps;
+  // W segments: output column n in [seg_n0[s], seg_n0[s+1]) reads row n - seg_n0[s] of w[s].
+  // EPI_SWIGLU: w[0] = gate, w[1] = up, both [N][K].
+  const uint16_t* w[3];
+  int seg_n0[4];
+  // split-K (splits > 1): K range of split z is [z*k_split, min(K, (z+1)*k_split))
+  int splits, k_split;
+  float* partial;   // [tiles][splits][BM*BN] fp32
+  int* counters;    // [tiles], zero between calls
+  // EPI_RESID
+  float* y_out;     // [rows][ldy]
+  float* ss_out;    // [rows][n_ss]
+  // EPI_SWIGLU
+  uint16_t* h_out;  // [M][N] bf16
+  // EPI_QKV
+  uint16_t* q_out;  // [M][nq*hd] bf16
+  const float* rope_cs;  // [M][hd/2][2] (cos, sin)
+  const int32_t* slot;   // [M] page * page_size + offset
+  void* kv_layer;        // base of this layer's pages
+  long page_stride;      // elements per page per layer (2 * nkv * P * hd)
+  int nq, nkv, hd, page_size, kv_e4m3;
+  const float* kv_scale; // [2][nkv] for this layer (e4m3)
+  // EPI_LOGITS
+  float* logits;         // [M][N] or NULL
+  const int32_t* ro_kind;
+  const float* ro_temp;
+  const uint32_t* ro_seed_lo;
+  const uint32_t* ro_seed_hi;
+  const int32_t* ro_lane;
+  float* tile_best;      // [n_tiles][M] decision value
+  int32_t* tile_idx;     // [n_tiles][M] its index
+};
+
+// Tile configurations
+enum GemmTile { TILE_64x128 = 0, TILE_128x128 = 1 };
+
+void launch_gemm(int amode, int epi, int tile, const GemmArgs& g, hipStream_t stream);
+
+// Reduce the per-tile maxima of EPI_LOGITS into one token per row.
+void launch_argmax_reduce(const float* tile_best, const int32_t* tile_idx, int n_tiles, int M,
+                          int32_t* tokens, hipStream_t stream);
+
+int gemm_tile_bm(int tile);
+int gemm_tile_bn(int tile);
+
+}  // namespace pie

@@ -1,0 +1,231 @@
+"""Python-side owner of one pie context: device buffers come from PyTorch
+(plumbing only -- every step of the forward runs in the HIP library), passes
+are marshalled into the C structs of include/pie.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _native as N
+from ._native import check
+
+
+@dataclass
+class Pass:
+    """One ForwardPass: new tokens of one working set, readout rows and their epilogues."""
+    ws: int
+    tokens: Sequence[int]
+    readout: Sequence[int] = ()
+    epi: Sequence[Tuple[int, float, int]] = ()   # (kind, temperature, seed) per readout row
+    positions: Optional[Sequence[int]] = None
+    commit: bool = True
+
+
+def model_desc(shape) -> N.pie_model_desc:
+    return N.pie_model_desc(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads,
+                            shape.head_dim, shape.d_ffn, shape.vocab, shape.rms_eps,
+                            shape.rope_theta, shape.kv_dtype, shape.page_size)
+
+
+LAYER_KEYS = ["attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up", "down"]
+
+
+def upload_weights(recipe, device="cuda", progress=None) -> Dict:
+    """Draw the seeded bf16 weights of `recipe` (a synth.WeightRecipe) on the
+    host and copy them to `device`, one tensor at a time through pinned memory."""
+    import torch
+    shape = recipe.shape
+    biggest = max(shape.vocab * shape.d_model, 3 * shape.d_model * shape.d_ffn)
+    stage = torch.empty(biggest, dtype=torch.int16, pin_memory=True)
+    stage_np = stage.numpy().view(np.uint16)
+
+    def one(name, shp):
+        n = int(np.prod(shp))
+        recipe.tensor_bits(name, shp, out=stage_np[:n])
+        t = torch.empty(shp, dtype=torch.bfloat16, device=device)
+        t.view(torch.int16).view(-1).copy_(stage[:n], non_blocking=False)
+        return t
+
+    import synth
+    w = {"embed": one("embed", (shape.vocab, shape.d_model)),
+         "final_norm": one("final_norm", (shape.d_model,)),
+         "lm_head": one("head", (shape.vocab, shape.d_model)), "layers": []}
+    for l in range(shape.n_layers):
+        w["layers"].append({k: one("layers.%d.%s" % (l, k), s)
+                            for k, s in synth.layer_tensor_shapes(shape)})
+        if progress:
+            progress(l)
+    if shape.kv_dtype == synth.KV_E4M3:
+        w["kv_scale"] = torch.from_numpy(synth.kv_scales(shape)).to(device)
+    return w
+
+
+class PieRuntime:
+    """One context over torch-owned device memory (or a host-only context when
+    weights is None: working sets and packing without the GPU)."""
+
+    def __init__(self, shape, weights: Optional[Dict], kv_bytes: int, max_rows: int,
+                 max_seqs: int, max_readout: int, max_ctx: int, device="cuda", stream=None):
+        self.shape = shape
+        self.desc = model_desc(shape)
+        self.limits = N.pie_limits(max_rows, max_seqs, max_readout, max_ctx)
+        self._keep = []
+        L = N.lib()
+        self.page_bytes = L.pie_kv_page_bytes(ctypes.byref(self.desc))
+        self.ws_bytes = L.pie_workspace_bytes(ctypes.byref(self.desc), ctypes.byref(self.limits))
+        if self.page_bytes == 0 or self.ws_bytes == 0:
+            raise N.PieError(N.PIE_EINVAL, "bad model shape or limits")
+        ctx = ctypes.c_void_p()
+        if weights is None:
+            check(L.pie_init(ctypes.byref(self.desc), None, None, kv_bytes, None, 0,
+                             ctypes.byref(self.limits), None, ctypes.byref(ctx)))
+            self.kv = self.workspace = None
+            self.stream = None
+        else:
+            import torch
+            self.device = torch.device(device)
+            self.kv = torch.empty(kv_bytes, dtype=torch.uint8, device=self.device)
+            self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+            self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+            self.weights = weights
+            pw = self._weights_struct(weights)
+            check(L.pie_init(ctypes.byref(self.desc), ctypes.byref(pw), self.kv.data_ptr(),
+                             kv_bytes, self.workspace.data_ptr(), self.ws_bytes,
+                             ctypes.byref(self.limits), ctypes.c_void_p(self.stream.cuda_stream),
+                             ctypes.byref(ctx)))
+        self.ctx = ctx
+
+    def _weights_struct(self, w):
+        L = self.shape.n_layers
+        arrs = {}
+        for k in LAYER_KEYS:
+            a = (ctypes.c_void_p * L)(*[w["layers"][l][k].data_ptr() for l in range(L)])
+            arrs[k] = a
+        self._keep.append(arrs)
+        ks = w.get("kv_scale")
+        return N.pie_weights(w["embed"].data_ptr(), w["final_norm"].data_ptr(),
+                             w["lm_head"].data_ptr(), arrs["attn_norm"], arrs["q"], arrs["k"],
+                             arrs["v"], arrs["o"], arrs["mlp_norm"], arrs["gate"], arrs["up"],
+                             arrs["down"], ks.data_ptr() if ks is not None else None)
+
+    # ------------------------------------------------------------ working sets
+    def alloc(self) -> int:
+        h = ctypes.c_uint64()
+        check(N.lib().pie_alloc_working_set(self.ctx, ctypes.byref(h)))
+        return h.value
+
+    def fork(self, parent: int) -> int:
+        h = ctypes.c_uint64()
+        check(N.lib().pie_fork(self.ctx, parent, ctypes.byref(h)))
+        return h.value
+
+    def free(self, ws: int) -> None:
+        check(N.lib().pie_free_working_set(self.ctx, ws))
+
+    def truncate(self, ws: int, new_len: int) -> None:
+        check(N.lib().pie_truncate(self.ctx, ws, new_len))
+
+    def ws_info(self, ws: int):
+        st = N.pie_ws_stats()
+        check(N.lib().pie_ws_info(self.ctx, ws, ctypes.byref(st), None))
+        ids = (ctypes.c_int32 * max(st.n_pages, 1))()
+        check(N.lib().pie_ws_info(self.ctx, ws, ctypes.byref(st), ids))
+        return {"len": st.len, "frozen_len": st.frozen_len,
+                "pages": np.frombuffer(ids, dtype=np.int32)[:st.n_pages].copy()}
+
+    def pool_stats(self) -> Dict[str, int]:
+        st = N.pie_pool_stats()
+        check(N.lib().pie_pool_stats_get(self.ctx, ctypes.byref(st)))
+        return {k: getattr(st, k) for k, _ in N.pie_pool_stats._fields_}
+
+    # ------------------------------------------------------------ forward
+    def _marshal(self, passes: Sequence[Pass]):
+        arr = (N.pie_pass * len(passes))()
+        keep = []
+        for i, p in enumerate(passes):
+            tok = np.ascontiguousarray(p.tokens, dtype=np.int32)
+            ro = np.ascontiguousarray(p.readout, dtype=np.int32)
+            epi = (N.pie_epilogue * max(len(p.readout), 1))()
+            for j, e in enumerate(p.epi):
+                epi[j] = N.pie_epilogue(int(e[0]), float(e[1]), int(e[2]) & 0xFFFFFFFFFFFFFFFF)
+            pos = None if p.positions is None else np.ascontiguousarray(p.positions, dtype=np.int32)
+            keep += [tok, ro, epi, pos]
+            ip = ctypes.POINTER(ctypes.c_int32)
+            arr[i] = N.pie_pass(p.ws, tok.ctypes.data_as(ip),
+                                pos.ctypes.data_as(ip) if pos is not None else None, len(tok),
+                                ro.ctypes.data_as(ip) if len(ro) else None, len(ro),
+                                epi if len(ro) else None, 1 if p.commit else 0)
+        return arr, keep
+
+    def forward(self, passes: Sequence[Pass], want_logits: bool = False, flags: int = 0,
+                logits_out=None):
+        """Returns (tokens int32[R], logits float32[R, V] or None)."""
+        arr, keep = self._marshal(passes)
+        if os.environ.get("PIE_SYNC_DEBUG"):
+            flags |= N.PIE_FLAG_SYNC_DEBUG
+        R = sum(len(p.readout) for p in passes)
+        toks = np.full(max(R, 1), -1, dtype=np.int32)
+        logits_ptr = None
+        logits = None
+        if logits_out is not None:
+            logits_ptr = logits_out.data_ptr()
+            flags |= N.PIE_FLAG_LOGITS_DEVICE
+            logits = logits_out
+        elif want_logits and R:
+            logits = np.empty((R, self.shape.vocab), dtype=np.float32)
+            logits_ptr = logits.ctypes.data
+        check(N.lib().pie_forward(self.ctx, arr, len(passes),
+                                  toks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                  logits_ptr, flags))
+        del keep
+        return toks[:R], logits
+
+    def plan(self) -> Dict[str, np.ndarray]:
+        v = N.pie_plan_view()
+        check(N.lib().pie_debug_plan(self.ctx, ctypes.byref(v)))
+        sizes = {"tok": v.n_rows, "pos": v.n_rows, "row_seq": v.n_rows, "slot": v.n_rows,
+                 "seq_row0": v.n_seqs + 1, "seq_ctx": v.n_seqs, "seq_len": v.n_seqs,
+                 "seq_pg0": v.n_seqs + 1, "pg_id": v.n_page_entries,
+                 "pg_valid": v.n_page_entries, "pg_start": v.n_page_entries,
+                 "ro_row": v.n_readout, "ro_lane": v.n_readout}
+        out = {}
+        for k, n in sizes.items():
+            ptr = getattr(v, k)
+            out[k] = np.ctypeslib.as_array(ptr, shape=(n,)).copy() if n else np.zeros(0, np.int32)
+        return out
+
+    # ------------------------------------------------------------ measurement
+    def profile_enable(self, classes: Sequence[str]) -> None:
+        mask = 0
+        for c in classes:
+            mask |= 1 << N.KERNEL_CLASSES.index(c)
+        check(N.lib().pie_profile_enable(self.ctx, mask))
+
+    def profile_read(self) -> Dict[str, Tuple[float, int]]:
+        ms = (ctypes.c_double * N.PIE_K_NUM_CLASSES)()
+        cnt = (ctypes.c_int64 * N.PIE_K_NUM_CLASSES)()
+        check(N.lib().pie_profile_read(self.ctx, ms, cnt))
+        return {c: (ms[i], cnt[i]) for i, c in enumerate(N.KERNEL_CLASSES)}
+
+    def philox(self, seed: int, lane: int, v0: int, n: int) -> np.ndarray:
+        import torch
+        out = torch.empty(n, dtype=torch.int32, device=self.device)
+        check(N.lib().pie_debug_philox(self.ctx, seed & 0xFFFFFFFFFFFFFFFF, lane, v0, n,
+                                       out.data_ptr()))
+        return out.cpu().numpy().view(np.uint32)
+
+    def close(self):
+        if getattr(self, "ctx", None) is not None and self.ctx.value:
+            N.lib().pie_destroy(self.ctx)
+            self.ctx = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,59 @@
+"""Shared helpers of the GPU parity tests: the comparison rule and drivers that
+run the same seeded workload through the HIP path and through the oracle.
+
+Parity rule: token ids bit-exact, except rows whose oracle top-2 margin (over
+logits for argmax, over logit/T + G for Gumbel-max) is below TAU_LOGIT (/T for
+Gumbel); those are excluded and counted.  Logits: max |err| <= TOL_LOGITS.
+"""
+from __future__ import annotations
+
+import os
+import sys
+from dataclasses import dataclass, field
+from typing import List, Sequence
+
+import numpy as np
+
+TAU_LOGIT = 2e-2
+TOL_LOGITS = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@dataclass
+class Report:
+    rows: int = 0
+    excluded: int = 0
+    mismatched: List[tuple] = field(default_factory=list)
+    max_err: float = 0.0
+
+    def add(self, gpu_tok, ref_tok, margin, tau, gpu_logits=None, ref_logits=None, tag=""):
+        self.rows += 1
+        if gpu_logits is not None and ref_logits is not None:
+            self.max_err = max(self.max_err, float(np.max(np.abs(gpu_logits - ref_logits))))
+        if margin < tau:
+            self.excluded += 1
+            return
+        if int(gpu_tok) != int(ref_tok):
+            self.mismatched.append((tag, int(gpu_tok), int(ref_tok), float(margin)))
+
+    def check(self, tol=TOL_LOGITS, max_excluded_frac=0.6):
+        say("parity: rows=%d excluded=%d mismatched=%d max|dlogit|=%.3g" %
+            (self.rows, self.excluded, len(self.mismatched), self.max_err))
+        assert not self.mismatched, self.mismatched[:10]
+        assert self.max_err <= tol, self.max_err
+        assert self.excluded <= max_excluded_frac * max(self.rows, 1)
+
+
+def tau_for(kind, temperature):
+    return TAU_LOGIT if kind == 0 else TAU_LOGIT / temperature
+
+
+def gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False

@@ -1,0 +1,222 @@
+"""GPU parity at the tiny 2-layer shape (every row checked) through the C ABI.
+
+The oracle runs first; GPU decode passes are then fed the oracle's tokens
+(teacher forcing by the oracle), so every GPU readout is compared with the
+oracle on identical inputs.  A free-running loop is checked too, up to the
+first near-tie.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from oracle.epilogue import apply
+from oracle.run import Chunk, Session, SynthWeights, default_numerics, forward_chunks
+from tests.parity import Report, say, tau_for
+
+pytestmark = pytest.mark.gpu
+
+N_SEQ, PROMPT, STEPS = 4, 32, 8
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def make_runtime(shape, recipe, torch_cuda, max_rows=512, max_seqs=16, max_readout=64, max_ctx=1024,
+                 pages=2048):
+    from paged_kv_forward_amd.runtime import PieRuntime, upload_weights
+    w = upload_weights(recipe)
+    page_bytes = shape.n_layers * 2 * shape.n_kv_heads * 16 * shape.head_dim * (
+        1 if shape.kv_dtype == synth.KV_E4M3 else 2)
+    return PieRuntime(shape, w, page_bytes * pages, max_rows, max_seqs, max_readout, max_ctx)
+
+
+RECIPES = {
+    "gains1": synth.WeightRecipe(synth.TINY),
+    "gains_spread": synth.WeightRecipe(synth.TINY, weight_seed=99, gain_std=0.02),
+}
+
+
+def oracle_greedy(recipe, prompts, steps, kinds, temps, seeds_fn):
+    """Oracle free-running loop per sequence: returns per seq list of (token, margin, logits)."""
+    w = SynthWeights(recipe, cache_layers=True)
+    num = default_numerics(recipe.shape)
+    out = []
+    for s, pr in enumerate(prompts):
+        sess = Session(w, num)
+        lg = sess.step(pr)[0]
+        rows = []
+        for k in range(steps + 1):
+            tok, margin = apply(lg, kinds[s], temps[s], seeds_fn(s, k), 0)
+            rows.append((tok, margin, lg))
+            if k < steps:
+                lg = sess.step([tok])[0]
+        out.append(rows)
+    return out
+
+
+@pytest.mark.parametrize("rname", list(RECIPES))
+@pytest.mark.parametrize("kind", [0, 1])
+def test_tiny_prefill_then_decode_teacher_forced(torch_cuda, rname, kind):
+    from paged_kv_forward_amd.runtime import Pass
+    recipe = RECIPES[rname]
+    shape = recipe.shape
+    prompts = [synth.prompt_tokens(1, s, PROMPT, shape.vocab) for s in range(N_SEQ)]
+    kinds = [kind] * N_SEQ
+    temps = [0.7] * N_SEQ
+    seed = lambda s, k: synth.epilogue_seed(0x1000 + s, k)
+    say("tiny %s kind=%d: oracle" % (rname, kind))
+    ref = oracle_greedy(recipe, prompts, STEPS, kinds, temps, seed)
+    say("tiny %s kind=%d: gpu" % (rname, kind))
+    rt = make_runtime(shape, recipe, torch_cuda)
+    ws = [rt.alloc() for _ in range(N_SEQ)]
+    rep = Report()
+    toks, logits = rt.forward([Pass(ws[s], prompts[s], [PROMPT - 1], [(kind, 0.7, seed(s, 0))])
+                               for s in range(N_SEQ)], want_logits=True)
+    for s in range(N_SEQ):
+        t, m, lg = ref[s][0]
+        rep.add(toks[s], t, m, tau_for(kind, 0.7), logits[s], lg, ("prefill", s))
+    for k in range(1, STEPS + 1):
+        feed = [ref[s][k - 1][0] for s in range(N_SEQ)]
+        toks, logits = rt.forward([Pass(ws[s], [feed[s]], [0], [(kind, 0.7, seed(s, k))])
+                                   for s in range(N_SEQ)], want_logits=True)
+        for s in range(N_SEQ):
+            t, m, lg = ref[s][k]
+            rep.add(toks[s], t, m, tau_for(kind, 0.7), logits[s], lg, ("decode", k, s))
+    rep.check()
+    for s in range(N_SEQ):
+        info = rt.ws_info(ws[s])
+        assert info["len"] == PROMPT + STEPS and info["frozen_len"] == PROMPT + STEPS
+    rt.close()
+
+
+def test_tiny_free_running_agrees_until_a_near_tie(torch_cuda):
+    from paged_kv_forward_amd.runtime import Pass
+    recipe = RECIPES["gains1"]
+    shape = recipe.shape
+    prompts = [synth.prompt_tokens(1, s, PROMPT, shape.vocab) for s in range(N_SEQ)]
+    ref = oracle_greedy(recipe, prompts, STEPS, [0] * N_SEQ, [1.0] * N_SEQ, lambda s, k: 0)
+    rt = make_runtime(shape, recipe, torch_cuda)
+    ws = [rt.alloc() for _ in range(N_SEQ)]
+    toks, _ = rt.forward([Pass(ws[s], prompts[s], [PROMPT - 1], [(0, 1.0, 0)]) for s in range(N_SEQ)])
+    gen = [[int(t)] for t in toks]
+    for k in range(STEPS):
+        toks, _ = rt.forward([Pass(ws[s], [gen[s][-1]], [0], [(0, 1.0, 0)]) for s in range(N_SEQ)])
+        for s in range(N_SEQ):
+            gen[s].append(int(toks[s]))
+    agree = 0
+    for s in range(N_SEQ):
+        for k in range(STEPS + 1):
+            t, m, _ = ref[s][k]
+            if gen[s][k] != t:
+                assert m < 2e-2, (s, k, gen[s][k], t, m)
+                break
+            agree += 1
+    say("free-running: %d of %d steps agree before any near-tie" % (agree, N_SEQ * (STEPS + 1)))
+
+
+def test_tiny_determinism_and_batch_invariance(torch_cuda):
+    from paged_kv_forward_amd.runtime import Pass
+    recipe = RECIPES["gains_spread"]
+    shape = recipe.shape
+    prompts = [synth.prompt_tokens(1, 10 + s, 20 + 3 * s, shape.vocab) for s in range(3)]
+    outs = []
+    for rep in range(2):
+        rt = make_runtime(shape, recipe, torch_cuda)
+        ws = [rt.alloc() for _ in range(3)]
+        _, lg = rt.forward([Pass(ws[s], prompts[s], [len(prompts[s]) - 1], [(0, 1, 0)])
+                            for s in range(3)], want_logits=True)
+        outs.append(lg)
+        # each pass alone, in a fresh working set
+        alone = []
+        for s in range(3):
+            w = rt.alloc()
+            _, l1 = rt.forward([Pass(w, prompts[s], [len(prompts[s]) - 1], [(0, 1, 0)])],
+                               want_logits=True)
+            alone.append(l1[0])
+        np.testing.assert_allclose(np.stack(alone), lg, rtol=0, atol=2e-3)
+        rt.close()
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def test_tiny_fork_partial_page_and_mixed_launch(torch_cuda):
+    """Prefix of 21 tokens (a partly filled page), forked 3 ways; suffixes and a
+    decode row of another sequence share one launch.  Compared with the
+    oracle's tree of chunks; no KV bytes copied, shared pages kept."""
+    from paged_kv_forward_amd.runtime import Pass
+    recipe = RECIPES["gains_spread"]
+    shape = recipe.shape
+    pre = synth.prompt_tokens(1, 20, 21, shape.vocab)
+    sufs = [synth.prompt_tokens(1, 21 + b, 5 + 7 * b, shape.vocab) for b in range(3)]
+    other = synth.prompt_tokens(1, 30, 40, shape.vocab)
+    nxt = int(synth.prompt_tokens(1, 31, 1, shape.vocab)[0])
+    rt = make_runtime(shape, recipe, torch_cuda)
+    p = rt.alloc()
+    o = rt.alloc()
+    rt.forward([Pass(p, pre, [], []), Pass(o, other, [], [])])
+    st0 = rt.pool_stats()
+    kids = [rt.fork(p) for _ in range(3)]
+    st1 = rt.pool_stats()
+    assert st1["pages_ever_allocated"] == st0["pages_ever_allocated"]
+    parent_pages = rt.ws_info(p)["pages"]
+    for k in kids:
+        np.testing.assert_array_equal(rt.ws_info(k)["pages"], parent_pages)
+    passes = [Pass(kids[b], sufs[b], [len(sufs[b]) - 1], [(1, 0.7, 77 + b)]) for b in range(3)]
+    passes.append(Pass(o, [nxt], [0], [(0, 1.0, 0)]))
+    toks, logits = rt.forward(passes, want_logits=True)
+    for b, k in enumerate(kids):
+        np.testing.assert_array_equal(rt.ws_info(k)["pages"][:len(parent_pages)], parent_pages)
+    assert rt.pool_stats()["kv_bytes_copied"] == 0
+    # oracle
+    w = SynthWeights(recipe, cache_layers=True)
+    num = default_numerics(shape)
+    tree = [Chunk(pre, np.arange(21), -1, [])]
+    tree += [Chunk(s, 21 + np.arange(len(s)), 0, [len(s) - 1]) for s in sufs]
+    tree += [Chunk(other, np.arange(40), -1, []), Chunk(np.array([nxt]), np.array([40]), 4, [0])]
+    ref = forward_chunks(w, tree, num)
+    rep = Report()
+    for b in range(3):
+        t, m = apply(ref[1 + b][0], 1, 0.7, 77 + b, 0)
+        rep.add(toks[b], t, m, tau_for(1, 0.7), logits[b], ref[1 + b][0], ("fork", b))
+    t, m = apply(ref[5][0], 0)
+    rep.add(toks[3], t, m, tau_for(0, 1), logits[3], ref[5][0], ("decode-in-mix",))
+    rep.check()
+    rt.close()
+
+
+def test_tiny_e4m3_kv(torch_cuda):
+    from paged_kv_forward_amd.runtime import Pass
+    shape = dataclasses.replace(synth.TINY, kv_dtype=synth.KV_E4M3)
+    recipe = synth.WeightRecipe(shape, weight_seed=5)
+    prompts = [synth.prompt_tokens(1, 40 + s, PROMPT, shape.vocab) for s in range(N_SEQ)]
+    ref = oracle_greedy(recipe, prompts, 4, [0] * N_SEQ, [1.0] * N_SEQ, lambda s, k: 0)
+    rt = make_runtime(shape, recipe, torch_cuda)
+    ws = [rt.alloc() for _ in range(N_SEQ)]
+    rep = Report()
+    toks, lg = rt.forward([Pass(ws[s], prompts[s], [PROMPT - 1], [(0, 1, 0)]) for s in range(N_SEQ)],
+                          want_logits=True)
+    for s in range(N_SEQ):
+        rep.add(toks[s], ref[s][0][0], ref[s][0][1], 2e-2, lg[s], ref[s][0][2])
+    for k in range(1, 5):
+        toks, lg = rt.forward([Pass(ws[s], [ref[s][k - 1][0]], [0], [(0, 1, 0)]) for s in range(N_SEQ)],
+                              want_logits=True)
+        for s in range(N_SEQ):
+            rep.add(toks[s], ref[s][k][0], ref[s][k][1], 2e-2, lg[s], ref[s][k][2])
+    rep.check()
+    rt.close()
+
+
+def test_device_philox_matches_oracle(torch_cuda):
+    from oracle.philox import philox4x32_10
+    rt = make_runtime(synth.TINY, RECIPES["gains1"], torch_cuda)
+    for seed, lane, v0 in [(0, 0, 0), (0xDEADBEEF12345678, 3, 1000), (2**64 - 1, 77, 2**32 - 5000)]:
+        got = rt.philox(seed, lane, v0, 4096)
+        v = (np.arange(4096, dtype=np.uint64) + np.uint64(v0)) & np.uint64(0xFFFFFFFF)
+        ref = philox4x32_10(v, lane, 0, 0, seed & 0xFFFFFFFF, seed >> 32)[0]
+        np.testing.assert_array_equal(got, ref)
+    rt.close()
