@@ -1,0 +1,197 @@
+"""Decode benchmark of the batched paged-KV forward pass on one MI355X.
+
+Workload (synthetic, seeded): the Llama-3.1-8B shape (32 layers, d 4096,
+32 q / 8 kv heads, head_dim 128, ffn 14336, vocab 128256), bf16 weights
+N(0, 0.02), bf16 paged KV (page 16).  64 sequences of 2048 uniform random
+prompt tokens are prefilled (setup, reported as prefill tokens/s), then greedy
+(argmax) decode steps run with batch 64, each sequence feeding back its own
+token.  A step is one pie_forward over the 64 decode rows: host packing, the
+whole forward, the fused argmax epilogue and the token copy-back.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Prints one JSON line.  The decode-attention kernel's achieved HBM bandwidth
+is measured with HIP events on the library's stream over the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+N_SEQ = 64
+PROMPT = 2048
+PREFILL_SEQS_PER_LAUNCH = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(shape, recipe, n_seq=2, n_layers=2):
+    """The oracle's decode step on a bounded sample, scaled to a full step:
+    `n_seq` decode rows (context 2048, synthetic bf16 K/V) through `n_layers`
+    layers plus the head, timed on the host cores."""
+    import synth
+    from oracle.model import Numerics, head_logits, layer_forward
+    from oracle.run import SynthWeights
+    w = SynthWeights(recipe)
+    num = Numerics(exact=False, kv_dtype=shape.kv_dtype)
+    rng = np.random.default_rng(3)
+    from oracle.numerics import round_bf16
+    ctxK = [round_bf16(rng.standard_normal((PROMPT, shape.n_kv_heads, shape.head_dim))) for _ in range(n_seq)]
+    ctxV = [round_bf16(rng.standard_normal((PROMPT, shape.n_kv_heads, shape.head_dim))) for _ in range(n_seq)]
+    h0 = [w.embed_rows(np.array([7 + s])).astype(np.float64) for s in range(n_seq)]
+    layers = [w.layer(l) for l in range(n_layers)]
+    head, fin = w.head(), w.final_norm()
+    t0 = time.perf_counter()
+    for s in range(n_seq):
+        h = h0[s]
+        for l in range(n_layers):
+            h, _, _ = layer_forward(layers[l], h, np.array([PROMPT]), ctxK[s], ctxV[s], shape, num, l)
+    t_layers = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for s in range(n_seq):
+        head_logits(h0[s], fin, head, shape, num)
+    t_head = time.perf_counter() - t0
+    per_row_step = t_layers / n_seq / n_layers * shape.n_layers + t_head / n_seq
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    return {"value": round(1.0 / per_row_step, 4), "unit": "decode tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d decode rows at context %d through %d of %d layers + lm_head (float64 "
+                      "numpy, synthetic K/V), scaled to one 64-row step; %.1f s of CPU work" %
+                      (n_seq, PROMPT, n_layers, shape.n_layers, t_layers + t_head)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=125)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="time every kernel class (extra pass)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path runs on a single MI355X "
+              "(multi-GPU sharding is a design note, not built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from paged_kv_forward_amd import _native as N
+    from paged_kv_forward_amd.runtime import Pass, PieRuntime, upload_weights
+
+    torch.cuda.set_device(0)
+    shape = synth.LLAMA_8B
+    recipe = synth.WeightRecipe(shape)
+    wl = synth.workload(2)
+    t0 = time.perf_counter()
+    log("bench: drawing and uploading %.2f B seeded weights" % (shape.n_params() / 1e9))
+    weights = upload_weights(recipe, "cuda:0", progress=lambda l: (l % 8 == 7) and log("  layer", l + 1))
+    log("bench: weights ready in %.1f s" % (time.perf_counter() - t0))
+    K, W = args.steps, args.warmup
+    max_ctx = PROMPT + W + K + 8
+    pages = N_SEQ * ((max_ctx + 15) // 16 + 1)
+    page_bytes = shape.n_layers * 2 * shape.n_kv_heads * 16 * shape.head_dim * 2
+    rt = PieRuntime(shape, weights, pages * page_bytes, max_rows=PREFILL_SEQS_PER_LAUNCH * PROMPT,
+                    max_seqs=N_SEQ, max_readout=N_SEQ, max_ctx=max_ctx)
+    ws = [rt.alloc() for _ in range(N_SEQ)]
+    prompts = [wl.prompt(s) for s in range(N_SEQ)]
+
+    # ---- prefill (setup) ----
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    nxt = np.zeros(N_SEQ, dtype=np.int32)
+    for b in range(0, N_SEQ, PREFILL_SEQS_PER_LAUNCH):
+        ss = range(b, b + PREFILL_SEQS_PER_LAUNCH)
+        toks, _ = rt.forward([Pass(ws[s], prompts[s], [PROMPT - 1], [(0, 1.0, 0)]) for s in ss])
+        nxt[b:b + PREFILL_SEQS_PER_LAUNCH] = toks
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    log("bench: prefill %d x %d tokens in %.2f s" % (N_SEQ, PROMPT, t_prefill))
+
+    def step():
+        toks, _ = rt.forward([Pass(ws[s], [int(nxt[s])], [0], [(0, 1.0, 0)]) for s in range(N_SEQ)])
+        nxt[:] = toks
+
+    for _ in range(W):
+        step()
+    ctx_first = rt.ws_info(ws[0])["len"] + 1
+    rt.profile_enable(["attn_decode"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    t_dec = time.perf_counter() - t0
+    prof = rt.profile_read()
+    rt.profile_enable([])
+    log("bench: %d decode steps in %.3f s" % (K, t_dec))
+
+    # algorithmic bytes of decode attention: every K and V element of every
+    # sequence's context once, plus q in and o out
+    kv_tok = shape.n_kv_heads * shape.head_dim * 2 * 2
+    qo = N_SEQ * shape.q_width * 2 * 2
+    ctx_sum = sum(N_SEQ * (ctx_first + i) for i in range(K))
+    attn_bytes = (ctx_sum * kv_tok + K * qo) * shape.n_layers
+    attn_ms, attn_n = prof["attn_decode"]
+    attn_gbs = attn_bytes / (attn_ms / 1e3) / 1e9 if attn_ms > 0 else 0.0
+    per_launch = attn_bytes / max(attn_n, 1)
+    weight_bytes = 2 * (shape.n_params() - shape.vocab * shape.d_model)  # all but the embedding table
+    step_bytes = weight_bytes + (ctx_sum / K) * kv_tok * shape.n_layers
+    ms_step = t_dec / K * 1e3
+
+    breakdown = None
+    if args.breakdown:
+        rt.profile_enable(N.KERNEL_CLASSES)
+        for _ in range(3):
+            step()
+        pb = rt.profile_read()
+        rt.profile_enable([])
+        breakdown = {k: round(v[0] / 3, 4) for k, v in pb.items() if v[1]}
+
+    out = {
+        "metric": "decode tokens/s + HBM-roofline fraction, Llama-3.1-8B shape, batch 64, 1 GPU",
+        "value": round(N_SEQ * K / t_dec, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, uniform random tokens)",
+        "config": {"workload": "llama31-8b decode: batch 64, context %d..%d, bf16 paged KV (page 16), "
+                               "argmax epilogue" % (ctx_first, ctx_first + K - 1),
+                   "global_batch": N_SEQ, "seq_len": PROMPT, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "paged decode attention (split-KV + combine)",
+                     "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(per_launch),
+                     "avg_launch_ms": round(attn_ms / max(attn_n, 1), 5)},
+        "step_hbm": {"bytes_per_step": int(step_bytes),
+                     "achieved_gbs": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
+                     "frac": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "prefill_tokens_per_s": round(N_SEQ * PROMPT / t_prefill, 1),
+    }
+    if breakdown:
+        out["ms_per_step_by_kernel"] = breakdown
+    rt.close()
+    del weights
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(shape, recipe)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,7 +13,16 @@
 // for P*V group g takes tokens 4g..4g+3 of both pages.
 // Softmax is online (running max and sum per row, in log2 units), in fp32;
 // P enters the MFMA rounded to bf16.
+//
+// Memory: a wave first loads a slice of its sequence's page table into lane
+// registers (entry base + l in lane l) and reads entries back with readlane,
+// so page ids are never a dependent load in the inner loop.  K and V come
+// through a wave-uniform buffer descriptor per page (a missing second page of
+// a pair gets a zero-size descriptor and reads zeros), and pairs run through a
+// two-slot register ring in straight-line code: the loads of the next pair are
+// in flight while the current pair is computed.
 #include <climits>
+#include <type_traits>
 
 #include "attention.h"
 #include "common.h"
@@ -23,73 +32,134 @@ namespace pie {
 constexpr int PS = 16;  // page size
 constexpr float LOG2E = 1.4426950408889634f;
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Raw K / V fragments of one pair of entries, as loaded.
 template <int HD, bool E4M3>
-__device__ __forceinline__ uint4 load_k_frag(const void* kv, size_t elem) {
-  if constexpr (E4M3) {
-    uint2 c = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(kv) + elem);
-    uint32_t w[4];
+struct PairRaw {
+  static constexpr int STEPS = HD / 32, DB = HD / 16;
+  // K: per page and k-step, 8 elements (bf16: 16 B; e4m3: 8 B)
+  typename std::conditional<E4M3, uint2, uint4>::type k[2][STEPS];
+  // V^T: per page and 16-row block, 4 tokens (bf16: 8 B; e4m3: 4 B)
+  typename std::conditional<E4M3, uint32_t, uint2>::type v[2][DB];
+  int valid0, valid1, start0, start1;
+};
+
+// Page-table slice of up to 64 entries in lane registers.
+struct PtSlice {
+  int base, n;        // entries [base, base + n)
+  int pg, valid, start;
+};
+
+__device__ __forceinline__ void load_slice(PtSlice& sl, const AttnArgs& a, int base, int end, int lane) {
+  sl.base = base;
+  sl.n = min(64, end - base);
+  const int e = base + lane;
+  const bool ok = lane < sl.n;
+  sl.pg = ok ? a.pg_id[e] : 0;
+  sl.valid = ok ? a.pg_valid[e] : 0;
+  sl.start = ok ? a.pg_start[e] : 0;
+}
+
+// Issue the loads of entries (e, e+1); entries at or past e_end are absent.
+template <int HD, bool E4M3>
+__device__ __forceinline__ void load_pair(PairRaw<HD, E4M3>& f, const AttnArgs& a, const PtSlice& sl, int e,
+                                          int e_end, uint32_t kofs, uint32_t vofs, int lane) {
+  constexpr int STEPS = HD / 32, DB = HD / 16, EB = E4M3 ? 1 : 2;
+  const int t = lane & 15, g = lane >> 4;
+  const uint32_t page_bytes = (uint32_t)a.page_stride * EB;
+  const uint8_t* kv = reinterpret_cast<const uint8_t*>(a.kv_layer);
+  __amdgpu_buffer_rsrc_t r[2];
+  int vl[2], st[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t src = j < 2 ? c.x : c.y;
-      uint32_t b0 = (src >> (16 * (j & 1))) & 0xffu, b1 = (src >> (16 * (j & 1) + 8)) & 0xffu;
-      w[j] = e4m3_to_bf16(b0) | (e4m3_to_bf16(b1) << 16);
+  for (int p = 0; p < 2; ++p) {
+    const int ee = e + p;
+    const bool live = ee < e_end;
+    const int li = live ? ee - sl.base : 0;  // wave-uniform lane index
+    const int pg = __builtin_amdgcn_readlane(sl.pg, li);
+    vl[p] = live ? __builtin_amdgcn_readlane(sl.valid, li) : 0;
+    st[p] = live ? __builtin_amdgcn_readlane(sl.start, li) : 0;
+    r[p] = page_rsrc(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
+  }
+  f.valid0 = vl[0]; f.valid1 = vl[1]; f.start0 = st[0]; f.start1 = st[1];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+      const uint32_t off = kofs + ((uint32_t)t * HD + (uint32_t)(g * STEPS + i) * 8) * EB;
+      if constexpr (E4M3)
+        f.k[p][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r[p], off, 0, 0));
+      else
+        f.k[p][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r[p], off, 0, 0));
     }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-    return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(kv) + elem);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const uint32_t off = vofs + ((uint32_t)(16 * b + t) * PS + 4 * g) * EB;
+      if constexpr (E4M3)
+        f.v[p][b] = __builtin_amdgcn_raw_buffer_load_b32(r[p], off, 0, 0);
+      else
+        f.v[p][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r[p], off, 0, 0));
+    }
   }
 }
 
-// 4 consecutive V^T elements (tokens 4g..4g+3 of one page), slots >= nvalid zeroed; as 2 bf16x2 words.
-template <bool E4M3>
-__device__ __forceinline__ uint2 load_v4(const void* kv, size_t elem, int nvalid) {
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t src = j < 2 ? c.x : c.y;
+    const uint32_t b0 = (src >> (16 * (j & 1))) & 0xffu, b1 = (src >> (16 * (j & 1) + 8)) & 0xffu;
+    w[j] = e4m3_to_bf16(b0) | (e4m3_to_bf16(b1) << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// 4 V^T tokens (4g .. 4g+3) as 2 bf16x2 words with slots >= nvalid zeroed
+// (slots past a page's valid count may hold another working set's data or
+// never-written memory).
+template <bool E4M3, typename T>
+__device__ __forceinline__ uint2 v4_bf16(T raw, int nvalid) {
   uint32_t w0, w1;
   if constexpr (E4M3) {
-    uint32_t c = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(kv) + elem);
-    uint32_t keep = nvalid >= 4 ? 0xffffffffu : (nvalid <= 0 ? 0u : ((1u << (8 * nvalid)) - 1u));
+    uint32_t c = raw;
+    const uint32_t keep = nvalid >= 4 ? 0xffffffffu : (nvalid <= 0 ? 0u : ((1u << (8 * nvalid)) - 1u));
     c &= keep;
     w0 = e4m3_to_bf16(c & 0xffu) | (e4m3_to_bf16((c >> 8) & 0xffu) << 16);
     w1 = e4m3_to_bf16((c >> 16) & 0xffu) | (e4m3_to_bf16(c >> 24) << 16);
   } else {
-    uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(kv) + elem);
-    w0 = v.x;
-    w1 = v.y;
-    if (nvalid < 4) {
-      w0 &= nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0xffffu : 0u);
-      w1 &= nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0xffffu : 0u);
-    }
+    w0 = raw.x;
+    w1 = raw.y;
+    w0 &= nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0xffffu : 0u);
+    w1 &= nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0xffffu : 0u);
   }
   return make_uint2(w0, w1);
 }
 
-// Process entries (p0, p1) of a page table for RB row blocks of 16 query rows.
+// Online-softmax update of RB row blocks with one pair of entries.
 // qidx[rb]: logical index of this lane's query row (keys with a larger logical
 // index are masked), or -1 for an unused row.
 template <int HD, bool E4M3, int RB>
-__device__ __forceinline__ void attend_pair(const uint4 (&qf)[RB][HD / 32], f32x4 (&oacc)[RB][HD / 16],
-                                            float (&m_run)[RB], float (&l_run)[RB],
-                                            const void* kv, size_t kbase0, size_t kbase1,
-                                            size_t vbase0, size_t vbase1, int valid0, int valid1,
-                                            int start0, int start1, const int (&qidx)[RB],
-                                            float scale_log2, int lane) {
+__device__ __forceinline__ void compute_pair(const PairRaw<HD, E4M3>& f, const uint4 (&qf)[RB][HD / 32],
+                                             f32x4 (&oacc)[RB][HD / 16], float (&m_run)[RB],
+                                             float (&l_run)[RB], const int (&qidx)[RB], float scale_log2,
+                                             int lane) {
   constexpr int STEPS = HD / 32, DB = HD / 16;
-  const int t = lane & 15, g = lane >> 4;
-  const bool has1 = valid1 > 0;
-  // K fragments of both pages
+  const int g = lane >> 4;
   uint4 kf[2][STEPS];
 #pragma unroll
-  for (int i = 0; i < STEPS; ++i) {
-    size_t off = (size_t)t * HD + (size_t)(g * STEPS + i) * 8;
-    kf[0][i] = load_k_frag<HD, E4M3>(kv, kbase0 + off);
-    kf[1][i] = has1 ? load_k_frag<HD, E4M3>(kv, kbase1 + off) : make_uint4(0, 0, 0, 0);
-  }
-  // V^T fragments of both pages
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+      if constexpr (E4M3) kf[p][i] = e4m3x8_to_bf16(f.k[p][i]);
+      else kf[p][i] = f.k[p][i];
+    }
   uint4 vf[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
-    size_t off = (size_t)(16 * b + t) * PS + 4 * g;
-    uint2 a0 = load_v4<E4M3>(kv, vbase0 + off, valid0 - 4 * g);
-    uint2 a1 = has1 ? load_v4<E4M3>(kv, vbase1 + off, valid1 - 4 * g) : make_uint2(0, 0);
+    const uint2 a0 = v4_bf16<E4M3>(f.v[0][b], f.valid0 - 4 * g);
+    const uint2 a1 = v4_bf16<E4M3>(f.v[1][b], f.valid1 - 4 * g);
     vf[b] = make_uint4(a0.x, a0.y, a1.x, a1.y);
   }
 #pragma unroll
@@ -104,9 +174,9 @@ __device__ __forceinline__ void attend_pair(const uint4 (&qf)[RB][HD / 32], f32x
     const int qi = qidx[rb];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int tok = 4 * g + j;
-      bool ok0 = tok < valid0 && start0 + tok <= qi;
-      bool ok1 = tok < valid1 && start1 + tok <= qi;
+      const int tok = 4 * g + j;
+      const bool ok0 = tok < f.valid0 && f.start0 + tok <= qi;
+      const bool ok1 = tok < f.valid1 && f.start1 + tok <= qi;
       sc[j] = ok0 ? s0[j] * scale_log2 : -INFINITY;
       sc[4 + j] = ok1 ? s1[j] * scale_log2 : -INFINITY;
     }
@@ -116,27 +186,47 @@ __device__ __forceinline__ void attend_pair(const uint4 (&qf)[RB][HD / 32], f32x
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run[rb], mx);
+    const bool any = m_new != -INFINITY;
+    const float alpha = any ? exp2f(m_run[rb] - m_new) : 1.f;
     float p[8];
-    float alpha = 1.f;
-    if (m_new == -INFINITY) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = 0.f;
-    } else {
-      alpha = exp2f(m_run[rb] - m_new);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = exp2f(sc[j] - m_new);
-    }
+    for (int j = 0; j < 8; ++j) p[j] = any ? exp2f(sc[j] - m_new) : 0.f;
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ps += p[j];
     l_run[rb] = l_run[rb] * alpha + ps;
     m_run[rb] = m_new;
-    uint4 pb = make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]),
-                          pack_bf2(p[6], p[7]));
+    const uint4 pb = make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]),
+                                pack_bf2(p[6], p[7]));
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       oacc[rb][b] *= alpha;
       oacc[rb][b] = mfma16(vf[b], pb, oacc[rb][b]);
+    }
+  }
+}
+
+// Entries [e_begin, e_end) of sequence s, two at a time through a two-slot ring.
+template <int HD, bool E4M3, int RB>
+__device__ __forceinline__ void attend_range(const AttnArgs& a, int e_begin, int e_end, uint32_t kofs,
+                                             uint32_t vofs, const uint4 (&qf)[RB][HD / 32],
+                                             f32x4 (&oacc)[RB][HD / 16], float (&m_run)[RB],
+                                             float (&l_run)[RB], const int (&qidx)[RB], float scale_log2,
+                                             int lane) {
+  for (int sb = e_begin; sb < e_end; sb += 64) {
+    const int se = min(e_end, sb + 64);
+    PtSlice sl;
+    load_slice(sl, a, sb, se, lane);
+    const int n_pairs = (se - sb + 1) / 2;
+    PairRaw<HD, E4M3> s0, s1;
+    load_pair<HD, E4M3>(s0, a, sl, sb, se, kofs, vofs, lane);
+    load_pair<HD, E4M3>(s1, a, sl, sb + 2, se, kofs, vofs, lane);
+    // straight-line pairs of slots; pairs past n_pairs are absent (all masked)
+    for (int pp = 0; pp < n_pairs; pp += 2) {
+      compute_pair<HD, E4M3, RB>(s0, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
+      load_pair<HD, E4M3>(s0, a, sl, sb + 2 * (pp + 2), se, kofs, vofs, lane);
+      compute_pair<HD, E4M3, RB>(s1, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
+      load_pair<HD, E4M3>(s1, a, sl, sb + 2 * (pp + 3), se, kofs, vofs, lane);
     }
   }
 }
@@ -151,10 +241,16 @@ __device__ __forceinline__ void load_q(uint4 (&qf)[HD / 32], const uint16_t* qro
 
 // ---------------------------------------------------------------- decode
 
+// One workgroup (4 waves) per (item, KV head).  The waves split the item's
+// entries into 4 contiguous runs of pairs and merge their running
+// (max, sum, O) through LDS.  part < 0: the item covers its sequence and the
+// workgroup writes o; else it writes an unnormalised partial for the combine.
 template <int HD, bool E4M3>
-__global__ __launch_bounds__(64) void attn_decode_kernel(AttnArgs a) {
-  constexpr int DB = HD / 16;
-  const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
+__global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
+  constexpr int DB = HD / 16, EB = E4M3 ? 1 : 2;
+  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ float s_o[4][16][HD + 4];
+  const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4;
   const int4 it = a.items[blockIdx.x];
   const int kvh = blockIdx.y;
   const int s = it.x, e_begin = it.y, e_end = it.z, part = it.w;
@@ -170,64 +266,85 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(AttnArgs a) {
   float m_run[1] = {-INFINITY}, l_run[1] = {0.f};
   const float ks = E4M3 ? a.kv_scale[kvh] : 1.f;
   const float scale_log2 = a.sm_scale * ks * LOG2E;
-  const size_t kofs = (size_t)kvh * PS * HD, vofs = (size_t)a.nkv * PS * HD + (size_t)kvh * HD * PS;
+  const uint32_t kofs = (uint32_t)(kvh * PS * HD) * EB;
+  const uint32_t vofs = (uint32_t)(a.nkv * PS * HD + kvh * HD * PS) * EB;
 
-  for (int e = e_begin; e < e_end; e += 2) {
-    const int pg0 = a.pg_id[e], v0 = a.pg_valid[e];
-    const bool two = e + 1 < e_end;
-    const int pg1 = two ? a.pg_id[e + 1] : pg0, v1 = two ? a.pg_valid[e + 1] : 0;
-    const size_t b0 = (size_t)pg0 * a.page_stride, b1 = (size_t)pg1 * a.page_stride;
-    attend_pair<HD, E4M3, 1>(qf, oacc, m_run, l_run, a.kv_layer, b0 + kofs, b1 + kofs, b0 + vofs,
-                             b1 + vofs, v0, v1, 0, 0, qidx, scale_log2, lane);
-  }
+  const int n_pairs = (e_end - e_begin + 1) / 2;
+  const int ppw = (n_pairs + 3) / 4;
+  const int wb = e_begin + 2 * min(n_pairs, wave * ppw);
+  const int we = min(e_end, e_begin + 2 * min(n_pairs, (wave + 1) * ppw));
+  attend_range<HD, E4M3, 1>(a, wb, we, kofs, vofs, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
+
   float l = l_run[0];
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (n >= G) return;
+  if (g == 0) {
+    s_m[wave][n] = m_run[0];
+    s_l[wave][n] = l;
+  }
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[wave][n][16 * b + 4 * g + i] = oacc[0][b][i];
+  __syncthreads();
+
   const float vs = E4M3 ? a.kv_scale[a.nkv + kvh] : 1.f;
-  if (part < 0) {
-    const float inv = vs / l;
-    uint16_t* o = a.o + ((size_t)row * a.nq + kvh * G + n) * HD;
+  for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
+    const int r = idx / HD, d = idx % HD;
+    float M = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      uint2 w = make_uint2(pack_bf2(oacc[0][b][0] * inv, oacc[0][b][1] * inv),
-                           pack_bf2(oacc[0][b][2] * inv, oacc[0][b][3] * inv));
-      *reinterpret_cast<uint2*>(o + 16 * b + 4 * g) = w;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][r]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = s_m[w][r] == -INFINITY ? 0.f : exp2f(s_m[w][r] - M);
+      num += s_o[w][r][d] * wt;
+      den += s_l[w][r] * wt;
     }
-  } else {
-    float* po = a.part_o + (((size_t)part * a.nkv + kvh) * 16 + n) * HD;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-      *reinterpret_cast<float4*>(po + 16 * b + 4 * g) =
-          make_float4(oacc[0][b][0] * vs, oacc[0][b][1] * vs, oacc[0][b][2] * vs, oacc[0][b][3] * vs);
-    if (g == 0) {
-      float* pm = a.part_ml + (((size_t)part * a.nkv + kvh) * 16 + n) * 2;
-      pm[0] = m_run[0];
-      pm[1] = l;
+    if (part < 0) {
+      a.o[((size_t)row * a.nq + kvh * G + r) * HD + d] = f2bf(num * vs / den);
+    } else {
+      const size_t base = ((size_t)part * a.nkv + kvh) * 16 + r;
+      a.part_o[base * HD + d] = num * vs;
+      if (d == 0) {
+        a.part_ml[base * 2] = M;
+        a.part_ml[base * 2 + 1] = den;
+      }
     }
   }
 }
 
-__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+// Merges the partials of a sequence split over several workgroups.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  constexpr int MAXP = 64;
+  __shared__ float s_w[MAXP][16];
+  __shared__ float s_den[16];
   const int4 c = a.combine[blockIdx.x];
   const int kvh = blockIdx.y;
-  const int s = c.x, p0 = c.y, np = c.z;
+  const int s = c.x, p0 = c.y, np = min(c.z, MAXP);
   const int G = a.nq / a.nkv, HD = a.hd;
   const int row = a.seq_row0[s];
-  for (int idx = threadIdx.x; idx < G * HD; idx += 64) {
-    const int n = idx / HD, d = idx % HD;
+  if (threadIdx.x < G) {
+    const int n = threadIdx.x;
     float M = -INFINITY;
-    for (int p = 0; p < np; ++p)
-      M = fmaxf(M, a.part_ml[(((size_t)(p0 + p) * a.nkv + kvh) * 16 + n) * 2]);
-    float num = 0.f, den = 0.f;
+    for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_ml[(((size_t)(p0 + p) * a.nkv + kvh) * 16 + n) * 2]);
+    float den = 0.f;
     for (int p = 0; p < np; ++p) {
       const size_t base = ((size_t)(p0 + p) * a.nkv + kvh) * 16 + n;
-      const float m = a.part_ml[base * 2], l = a.part_ml[base * 2 + 1];
+      const float m = a.part_ml[base * 2];
       const float w = m == -INFINITY ? 0.f : exp2f(m - M);
-      num += a.part_o[base * HD + d] * w;
-      den += l * w;
+      s_w[p][n] = w;
+      den += a.part_ml[base * 2 + 1] * w;
     }
-    a.o[((size_t)row * a.nq + kvh * G + n) * HD + d] = f2bf(num / den);
+    s_den[n] = den;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
+    const int n = idx / HD, d = idx % HD;
+    float num = 0.f;
+    for (int p = 0; p < np; ++p)
+      num += a.part_o[(((size_t)(p0 + p) * a.nkv + kvh) * 16 + n) * HD + d] * s_w[p][n];
+    a.o[((size_t)row * a.nq + kvh * G + n) * HD + d] = f2bf(num / s_den[n]);
   }
 }
 
@@ -236,8 +353,8 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 template <int HD, bool E4M3>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
   constexpr int RB = PREFILL_ROWS / 64;  // row blocks per wave (4 waves)
-  constexpr int DB = HD / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
+  constexpr int DB = HD / 16, EB = E4M3 ? 1 : 2;
+  const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4;
   const int4 it = a.items[blockIdx.x];
   const int kvh = blockIdx.y;
   const int s = it.x, tb = it.y, nt = it.z;
@@ -272,19 +389,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
   }
   const float ks = E4M3 ? a.kv_scale[kvh] : 1.f;
   const float scale_log2 = a.sm_scale * ks * LOG2E;
-  const size_t kofs = (size_t)kvh * PS * HD, vofs = (size_t)a.nkv * PS * HD + (size_t)kvh * HD * PS;
-  const int e_begin = a.seq_pg0[s], e_stop = a.seq_pg0[s + 1];
-  for (int e = e_begin; e < e_stop; e += 2) {
-    const int st0 = a.pg_start[e];
-    if (st0 > qmax) break;
-    const int pg0 = a.pg_id[e], v0 = a.pg_valid[e];
-    const bool two = e + 1 < e_stop && a.pg_start[e + 1] <= qmax;
-    const int pg1 = two ? a.pg_id[e + 1] : pg0, v1 = two ? a.pg_valid[e + 1] : 0;
-    const int st1 = two ? a.pg_start[e + 1] : 0;
-    const size_t b0 = (size_t)pg0 * a.page_stride, b1 = (size_t)pg1 * a.page_stride;
-    attend_pair<HD, E4M3, RB>(qf, oacc, m_run, l_run, a.kv_layer, b0 + kofs, b1 + kofs, b0 + vofs,
-                              b1 + vofs, v0, v1, st0, st1, qidx, scale_log2, lane);
-  }
+  const uint32_t kofs = (uint32_t)(kvh * PS * HD) * EB;
+  const uint32_t vofs = (uint32_t)(a.nkv * PS * HD + kvh * HD * PS) * EB;
+  // entries whose first slot is visible to some row of this wave
+  const int e_begin = a.seq_pg0[s];
+  int e_end = a.seq_pg0[s + 1];
+  while (e_end > e_begin && a.pg_start[e_end - 1] > qmax) --e_end;
+  attend_range<HD, E4M3, RB>(a, e_begin, e_end, kofs, vofs, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
   const float vs = E4M3 ? a.kv_scale[a.nkv + kvh] : 1.f;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -309,17 +420,17 @@ void launch_attn_decode(const AttnArgs& a, hipStream_t st) {
   if (a.n_items == 0) return;
   dim3 grid(a.n_items, a.nkv);
   if (a.hd == 128) {
-    if (a.kv_e4m3) hipLaunchKernelGGL((attn_decode_kernel<128, true>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((attn_decode_kernel<128, false>), grid, dim3(64), 0, st, a);
+    if (a.kv_e4m3) hipLaunchKernelGGL((attn_decode_kernel<128, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_decode_kernel<128, false>), grid, dim3(256), 0, st, a);
   } else {
-    if (a.kv_e4m3) hipLaunchKernelGGL((attn_decode_kernel<64, true>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((attn_decode_kernel<64, false>), grid, dim3(64), 0, st, a);
+    if (a.kv_e4m3) hipLaunchKernelGGL((attn_decode_kernel<64, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_decode_kernel<64, false>), grid, dim3(256), 0, st, a);
   }
 }
 
 void launch_attn_combine(const AttnArgs& a, hipStream_t st) {
   if (a.n_combine == 0) return;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.n_combine, a.nkv), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.n_combine, a.nkv), dim3(256), 0, st, a);
 }
 
 void launch_attn_prefill(const AttnArgs& a, hipStream_t st) {

@@ -64,6 +64,20 @@ __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c)
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- sync
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
+// memory, which makes the compiler wait for every outstanding global load
+// (s_waitcnt vmcnt(0)) at each barrier and drains software prefetch rings.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Index of the calling wave in its workgroup, as a wave-uniform value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // ---------------------------------------------------------------- reductions
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -52,13 +52,15 @@ struct SplitK {
 
 SplitK choose_split(int M, int n_tiles, int K) {
   if (M > 64) return {1, K};
-  const int target = 512;
-  int s = (target + n_tiles - 1) / n_tiles;
+  // About one 8-wave workgroup per CU (measured best for the decode shapes),
+  // and at least 4 chunks of 64 per split.
+  const int target = 256;
+  int s = (target + n_tiles / 2) / n_tiles;
   s = std::max(1, std::min(s, MAX_SPLITS));
   int max_by_k = std::max(1, K / (4 * GEMM_BK));
   s = std::min(s, max_by_k);
   int ks = (K + s - 1) / s;
-  ks = (ks + GEMM_BK - 1) / GEMM_BK * GEMM_BK;
+  ks = (ks + GEMM_BK - 1) / GEMM_BK * GEMM_BK;  // whole 64-wide chunks
   s = (K + ks - 1) / ks;
   return {s, ks};
 }
@@ -70,10 +72,8 @@ struct Layout {
       tokens_out, meta_ints;
   int32_t max_pe, max_dec_items, max_pre_items;
   // byte offsets into the workspace
-  size_t meta, y, ss, q, o, h, rope, part_o, part_ml, gpart, counters, tile_best, tile_idx, logits,
-      total;
+  size_t meta, y, ss, x, q, o, h, rope, part_o, part_ml, gpart, tile_best, tile_idx, logits, total;
   size_t gpart_floats;
-  int n_counters;
 };
 
 bool desc_ok(const pie_model_desc* d, std::string* why) {
@@ -128,12 +128,13 @@ Layout make_layout(const pie_model_desc& d, const pie_limits& l) {
   L.meta_ints = o;
 
   const size_t qw = (size_t)d.n_q_heads * d.head_dim;
-  const int n_ss = d.d_model / 128;
+  const int n_ss = d.d_model / 64;
   size_t b = 0;
   auto take_b = [&](size_t bytes) { size_t at = b; b = align_up(b + bytes); return at; };
   L.meta = take_b(L.meta_ints * 4);
   L.y = take_b(R * d.d_model * 4);
   L.ss = take_b(R * n_ss * 4);
+  L.x = take_b(R * d.d_model * 2);
   L.q = take_b(R * qw * 2);
   L.o = take_b(R * qw * 2);
   L.h = take_b(R * (size_t)d.d_ffn * 2);
@@ -148,16 +149,12 @@ Layout make_layout(const pie_model_desc& d, const pie_limits& l) {
       {(d.d_ffn + GEMM_BN / 2 - 1) / (GEMM_BN / 2), d.d_model},
       {(d.d_model + GEMM_BN - 1) / GEMM_BN, d.d_ffn}};
   size_t worst = 0;
-  int max_tiles = 0;
   for (auto& g : gs) {
     SplitK sk = choose_split(64, g.n_tiles, g.K);
     worst = std::max(worst, (size_t)g.n_tiles * sk.splits);
-    max_tiles = std::max(max_tiles, g.n_tiles);
   }
   L.gpart_floats = worst * 64 * GEMM_BN;
   L.gpart = take_b(L.gpart_floats * 4);
-  L.n_counters = max_tiles;
-  L.counters = take_b((size_t)max_tiles * 4);
   const size_t vt = (size_t)(d.vocab + LM_BN - 1) / LM_BN;
   L.tile_best = take_b(vt * RO * 4);
   L.tile_idx = take_b(vt * RO * 4);
@@ -274,7 +271,8 @@ void build_work(pie_ctx* c) {
     }
   int pps = 1 << 30;
   if (n_dec) {
-    const int64_t target = std::max<int64_t>(n_dec, (2048 + c->d.n_kv_heads - 1) / c->d.n_kv_heads);
+    // one workgroup (4 waves) per (item, KV head); aim for >= 512 workgroups
+    const int64_t target = std::max<int64_t>(n_dec, (512 + c->d.n_kv_heads - 1) / c->d.n_kv_heads);
     int64_t v = (dec_entries + target - 1) / target;
     v = std::max<int64_t>(v, 8);
     pps = (int)((v + 1) / 2 * 2);
@@ -335,7 +333,7 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
   float* rope = reinterpret_cast<float*>(c->ws + L.rope);
   const int T = p.n_rows, R = p.n_readout;
   const int qw = d.n_q_heads * d.head_dim, kvw = d.n_kv_heads * d.head_dim;
-  const int n_ss = d.d_model / 128;
+  const int n_ss = d.d_model / 64;
   int rc;
 
   pie::launch_rope_table(M32(L.pos), T, d.head_dim, (double)d.rope_theta, rope, st);
@@ -346,9 +344,10 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
   }
   if ((rc = check_launch(c, flags, "embed"))) return rc;
 
-  const int tile = T <= 64 ? pie::TILE_64x128 : pie::TILE_128x128;
+  const bool small = T <= 64;  // decode-sized: the weight-streaming skinny GEMM with split-K
+  const int tile = small ? pie::TILE_SKINNY : pie::TILE_128x128;
   float* gpart = reinterpret_cast<float*>(c->ws + L.gpart);
-  int* counters = reinterpret_cast<int*>(c->ws + L.counters);
+  uint16_t* xb = reinterpret_cast<uint16_t*>(c->ws + L.x);
   const size_t elem = kv_elem_bytes(d);
 
   pie::GemmArgs base{};
@@ -359,14 +358,12 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
   base.ldy = d.d_model;
   base.eps = d.rms_eps;
   base.partial = gpart;
-  base.counters = counters;
   base.y_out = y;
   base.ss_out = ss;
 
   auto set_split = [&](pie::GemmArgs& g, int n_tiles) {
     SplitK sk = choose_split(T, n_tiles, g.K);
-    if ((size_t)n_tiles * sk.splits * 64 * GEMM_BN > L.gpart_floats || n_tiles > L.n_counters)
-      sk = {1, g.K};
+    if ((size_t)n_tiles * sk.splits * 64 * GEMM_BN > L.gpart_floats) sk = {1, g.K};
     g.splits = sk.splits;
     g.k_split = sk.k_split;
   };
@@ -409,9 +406,12 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
       g.nq = d.n_q_heads; g.nkv = d.n_kv_heads; g.hd = d.head_dim; g.page_size = d.page_size;
       g.kv_e4m3 = d.kv_dtype == PIE_KV_E4M3;
       g.kv_scale = kvs;
-      set_split(g, (g.N + GEMM_BN - 1) / GEMM_BN);
+      set_split(g, pie::gemm_n_tiles(pie::EPI_QKV, g.N, tile));
       Timed tm(c, PIE_K_GEMM_QKV);
-      pie::launch_gemm(pie::A_NORM, pie::EPI_QKV, tile, g, st);
+      pie::launch_rmsnorm(y, ss, n_ss, c->attn_norm[l], T, d.d_model, d.rms_eps, nullptr, xb, st);
+      g.a = xb;
+      g.lda = d.d_model;
+      pie::launch_gemm(pie::A_BF16, pie::EPI_QKV, tile, g, st);
     }
     if ((rc = check_launch(c, flags, "qkv gemm"))) return rc;
     // attention
@@ -447,7 +447,7 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
       g.lda = qw;
       g.w[0] = g.w[1] = g.w[2] = c->wo[l];
       g.seg_n0[0] = 0; g.seg_n0[1] = g.seg_n0[2] = g.seg_n0[3] = d.d_model;
-      set_split(g, (g.N + GEMM_BN - 1) / GEMM_BN);
+      set_split(g, pie::gemm_n_tiles(pie::EPI_RESID, g.N, tile));
       Timed tm(c, PIE_K_GEMM_O);
       pie::launch_gemm(pie::A_BF16, pie::EPI_RESID, tile, g, st);
     }
@@ -460,9 +460,12 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
       g.gain = c->mlp_norm[l];
       g.w[0] = c->wg[l]; g.w[1] = c->wu[l]; g.w[2] = c->wu[l];
       g.h_out = hb;
-      set_split(g, (g.N + GEMM_BN / 2 - 1) / (GEMM_BN / 2));
+      set_split(g, pie::gemm_n_tiles(pie::EPI_SWIGLU, g.N, tile));
       Timed tm(c, PIE_K_GEMM_GATEUP);
-      pie::launch_gemm(pie::A_NORM, pie::EPI_SWIGLU, tile, g, st);
+      pie::launch_rmsnorm(y, ss, n_ss, c->mlp_norm[l], T, d.d_model, d.rms_eps, nullptr, xb, st);
+      g.a = xb;
+      g.lda = d.d_model;
+      pie::launch_gemm(pie::A_BF16, pie::EPI_SWIGLU, tile, g, st);
     }
     if ((rc = check_launch(c, flags, "gate/up gemm"))) return rc;
     // down + residual
@@ -474,7 +477,7 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
       g.lda = d.d_ffn;
       g.w[0] = g.w[1] = g.w[2] = c->wd[l];
       g.seg_n0[0] = 0; g.seg_n0[1] = g.seg_n0[2] = g.seg_n0[3] = d.d_model;
-      set_split(g, (g.N + GEMM_BN - 1) / GEMM_BN);
+      set_split(g, pie::gemm_n_tiles(pie::EPI_RESID, g.N, tile));
       Timed tm(c, PIE_K_GEMM_DOWN);
       pie::launch_gemm(pie::A_BF16, pie::EPI_RESID, tile, g, st);
     }
@@ -506,7 +509,14 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
     const int vt = (d.vocab + LM_BN - 1) / LM_BN;
     {
       Timed tm(c, PIE_K_LM_HEAD);
-      pie::launch_gemm(pie::A_NORM, pie::EPI_LOGITS, R <= 64 ? pie::TILE_64x128 : pie::TILE_128x128, g, st);
+      if (R <= 64) {  // gather + final RMSNorm of the readout rows, then the weight stream
+        pie::launch_rmsnorm(y, ss, n_ss, c->final_norm, R, d.d_model, d.rms_eps, g.a_rows, xb, st);
+        g.a = xb;
+        g.lda = d.d_model;
+        pie::launch_gemm(pie::A_BF16, pie::EPI_LOGITS, pie::TILE_SKINNY, g, st);
+      } else {
+        pie::launch_gemm(pie::A_NORM, pie::EPI_LOGITS, pie::TILE_128x128, g, st);
+      }
       pie::launch_argmax_reduce(g.tile_best, g.tile_idx, vt, R, dtok, st);
     }
     if ((rc = check_launch(c, flags, "lm_head"))) return rc;
@@ -608,15 +618,6 @@ int pie_init(const pie_model_desc* desc, const pie_weights* w, void* kv_arena, s
   }
   e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned), c->lay.meta_ints * 4, hipHostMallocDefault);
   if (e != hipSuccess) { delete c; return set_err(PIE_EHIP, std::string("pie_init: hipHostMalloc: ") + hipGetErrorString(e)); }
-  // counters of the split-K reduction start at zero (a fill kernel, not a memset)
-  pie::launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws + c->lay.counters), (size_t)c->lay.n_counters, 0u, c->stream);
-  e = hipGetLastError();
-  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
-  if (e != hipSuccess) {
-    (void)hipHostFree(c->pinned);
-    delete c;
-    return set_err(PIE_EHIP, std::string("pie_init: ") + hipGetErrorString(e));
-  }
   *out = c;
   return PIE_OK;
 }

@@ -3,11 +3,11 @@
 //   C[M, N] = A[M, K] * W[N, K]^T,  W in checkpoint layout [out][in], bf16.
 // Prologue A_NORM computes the RMSNorm of the residual stream on the fly:
 //   A[m, k] = bf16(y[m, k] * rsqrt(sum_sq[m] / K + eps) * gain[k]),
-// with sum_sq[m] summed from per-128-column partials that the producer of y
+// with sum_sq[m] summed from per-64-column partials that the producer of y
 // wrote; with a_rows it also gathers rows (the readout rows of the head).
 // Epilogues:
 //   EPI_QKV     RoPE on q and k, q -> bf16 buffer, k and v -> KV page slots
-//   EPI_RESID   y += C, and the per-128-column sums of squares of the new y
+//   EPI_RESID   y += C, and the per-64-column sums of squares of the new y
 //   EPI_SWIGLU  h = bf16(silu(gate) * up), gate/up tiles interleaved
 //   EPI_LOGITS  logits (optional) and the per-tile maximum of the epilogue's
 //               decision value (argmax, or logit/T + Gumbel noise)
@@ -37,10 +37,11 @@ struct GemmArgs {
   // EPI_SWIGLU: w[0] = gate, w[1] = up, both [N][K].
   const uint16_t* w[3];
   int seg_n0[4];
-  // split-K (splits > 1): K range of split z is [z*k_split, min(K, (z+1)*k_split))
+  // split-K (splits > 1): K range of split z is [z*k_split, min(K, (z+1)*k_split));
+  // split partials go to partial[split][BM][n_tiles * BN] and a reduce kernel
+  // runs the epilogue (only with a single M tile).
   int splits, k_split;
-  float* partial;   // [tiles][splits][BM*BN] fp32
-  int* counters;    // [tiles], zero between calls
+  float* partial;
   // EPI_RESID
   float* y_out;     // [rows][ldy]
   float* ss_out;    // [rows][n_ss]
@@ -65,10 +66,18 @@ struct GemmArgs {
   int32_t* tile_idx;     // [n_tiles][M] its index
 };
 
-// Tile configurations
-enum GemmTile { TILE_64x128 = 0, TILE_128x128 = 1 };
+// Tile configurations.  TILE_SKINNY: M <= 64 with a bf16 A operand, 128 output
+// columns per workgroup, weights streamed through registers (decode).
+enum GemmTile { TILE_64x128 = 0, TILE_128x128 = 1, TILE_SKINNY = 2 };
 
 void launch_gemm(int amode, int epi, int tile, const GemmArgs& g, hipStream_t stream);
+
+// x[m] = bf16(rmsnorm(y[rows ? rows[m] : m]) * gain) for M rows.
+void launch_rmsnorm(const float* y, const float* ss, int n_ss, const uint16_t* gain, int M, int d,
+                    float eps, const int32_t* rows, uint16_t* x, hipStream_t stream);
+
+// Output tiles of a GEMM along N (EPI_SWIGLU tiles hold half gate, half up columns).
+int gemm_n_tiles(int epi, int N, int tile);
 
 // Reduce the per-tile maxima of EPI_LOGITS into one token per row.
 void launch_argmax_reduce(const float* tile_best, const int32_t* tile_idx, int n_tiles, int M,

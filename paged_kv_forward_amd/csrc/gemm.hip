@@ -1,16 +1,24 @@
 // MFMA GEMM with fused RMSNorm prologue, split-K and the decoder's epilogues.
 // See gemm.h for the operation.  Tiles are staged through LDS with double
 // buffering; each of the 4 waves of a workgroup owns a WM x WN block of the
-// BM x BN tile and issues 16x16x32 bf16 MFMAs.  With split-K, every split
-// writes its fp32 partial tile, and the last split to finish (counted with a
-// device-scope atomic) sums all partials in split order -- so the result does
-// not depend on which split finishes last -- and runs the epilogue.
+// BM x BN tile and issues 16x16x32 bf16 MFMAs.
+//
+// Split-K: every split writes its fp32 partial tile and exits; a second,
+// small kernel sums the partials in split order (so the result does not
+// depend on scheduling) and runs the epilogue.  The kernel boundary is what
+// makes the partials visible: on gfx950 each XCD has its own L2, and an
+// in-kernel device-scope fence would write back and invalidate the whole L2
+// of the XCD for every workgroup.
 #include <climits>
 
 #include "common.h"
 #include "gemm.h"
 
 namespace pie {
+
+struct uint4x2 {
+  uint4 a, b;
+};
 
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;  // bf16 elements per LDS row (16 B pad against bank conflicts)
@@ -31,13 +39,127 @@ struct Cfg {
   static constexpr int LDS_BYTES = LDS_AB > LDS_C ? LDS_AB : LDS_C;
 };
 
+// Epilogue over rows [m0, m0 + rows) of output tile n_tile, whose fp32 values
+// are in sC (row stride ldc).  Called by all 256 threads of a workgroup.
+template <int EPI, int BN, int NTH = 256>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int ldc, int m0, int rows,
+                                         int n_tile) {
+  constexpr int NW = NTH / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (EPI == EPI_RESID) {
+    // y += C; per-64-column sums of squares of the new y for the next RMSNorm
+    const int n0 = n_tile * BN;
+    constexpr int CH = BN / 64;
+    for (int p = wave; p < rows * CH; p += NW) {
+      int row = p / CH, ch = p % CH, m = m0 + row;
+      if (m >= g.M) continue;
+      const int col = ch * 64 + lane;
+      const size_t off = (size_t)m * g.ldy + n0 + col;
+      const float v = g.y_out[off] + sC[row * ldc + col];
+      g.y_out[off] = v;
+      const float s = wave_sum(v * v);
+      if (lane == 0) g.ss_out[(size_t)m * g.n_ss + n0 / 64 + ch] = s;
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    constexpr int HALF = BN / 2;
+    const int j0 = n_tile * HALF;
+    for (int idx = tid; idx < rows * HALF; idx += NTH) {
+      int row = idx / HALF, j = idx % HALF, m = m0 + row, n = j0 + j;
+      if (m < g.M && n < g.N) {
+        float gt = sC[row * ldc + j], up = sC[row * ldc + HALF + j];
+        float h = gt / (1.0f + expf(-gt)) * up;
+        g.h_out[(size_t)m * g.N + n] = f2bf(h);
+      }
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    const int n0 = n_tile * BN;
+    const int hd = g.hd, hd2 = hd >> 1, P = g.page_size;
+    const int qw = g.nq * hd, kw = g.nkv * hd;
+    const int kind = n0 < qw ? 0 : (n0 < qw + kw ? 1 : 2);
+    if (kind < 2) {
+      for (int idx = tid; idx < rows * (BN / 2); idx += NTH) {
+        int row = idx / (BN / 2), pr = idx % (BN / 2), m = m0 + row;
+        if (m >= g.M) continue;
+        int hl = pr / hd2, dd = pr % hd2;
+        int c1 = hl * hd + dd, c2 = c1 + hd2;
+        float cs = g.rope_cs[((size_t)m * hd2 + dd) * 2], sn = g.rope_cs[((size_t)m * hd2 + dd) * 2 + 1];
+        float x1 = sC[row * ldc + c1], x2 = sC[row * ldc + c2];
+        float o1 = x1 * cs - x2 * sn, o2 = x2 * cs + x1 * sn;
+        if (kind == 0) {
+          int head = (n0 + c1) / hd;
+          uint16_t* q = g.q_out + (size_t)m * qw + head * hd;
+          q[dd] = f2bf(o1);
+          q[dd + hd2] = f2bf(o2);
+        } else {
+          int kvh = (n0 - qw + c1) / hd;
+          int sl = g.slot[m], page = sl / P, off = sl % P;
+          size_t base = (size_t)page * g.page_stride + (size_t)kvh * P * hd + (size_t)off * hd;
+          if (g.kv_e4m3) {
+            float s = g.kv_scale[kvh];
+            uint8_t* kv = reinterpret_cast<uint8_t*>(g.kv_layer);
+            kv[base + dd] = f2e4m3(o1 / s);
+            kv[base + dd + hd2] = f2e4m3(o2 / s);
+          } else {
+            uint16_t* kv = reinterpret_cast<uint16_t*>(g.kv_layer);
+            kv[base + dd] = f2bf(o1);
+            kv[base + dd + hd2] = f2bf(o2);
+          }
+        }
+      }
+    } else {
+      for (int idx = tid; idx < rows * BN; idx += NTH) {
+        int row = idx / BN, c = idx % BN, m = m0 + row;
+        if (m >= g.M) continue;
+        int vc = n0 - qw - kw + c, kvh = vc / hd, dd = vc % hd;
+        int sl = g.slot[m], page = sl / P, off = sl % P;
+        size_t idx_v = (size_t)page * g.page_stride + (size_t)g.nkv * P * hd + (size_t)kvh * hd * P +
+                       (size_t)dd * P + off;
+        float x = sC[row * ldc + c];
+        if (g.kv_e4m3) {
+          reinterpret_cast<uint8_t*>(g.kv_layer)[idx_v] = f2e4m3(x / g.kv_scale[g.nkv + kvh]);
+        } else {
+          reinterpret_cast<uint16_t*>(g.kv_layer)[idx_v] = f2bf(x);
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_LOGITS) {
+    const int n0 = n_tile * BN;
+    for (int row = wave; row < rows; row += NW) {
+      int m = m0 + row;
+      if (m >= g.M) continue;
+      const int kind = g.ro_kind[m];
+      const float T = g.ro_temp[m];
+      const uint32_t lo = g.ro_seed_lo[m], hi = g.ro_seed_hi[m], ln = (uint32_t)g.ro_lane[m];
+      float best = -INFINITY;
+      int bi = INT_MAX;
+      for (int c = lane; c < BN; c += 64) {
+        int v = n0 + c;
+        if (v >= g.N) break;
+        float l = sC[row * ldc + c];
+        if (g.logits) g.logits[(size_t)m * g.N + v] = l;
+        float s = kind == 0 ? l : l / T + gumbel((uint32_t)v, ln, lo, hi);
+        if (s > best) { best = s; bi = v; }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        float ob = __shfl_xor(best, o, 64);
+        int oi = __shfl_xor(bi, o, 64);
+        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+      }
+      if (lane == 0) {
+        g.tile_best[(size_t)n_tile * g.M + m] = best;
+        g.tile_idx[(size_t)n_tile * g.M + m] = bi;
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int AMODE, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   using C = Cfg<BM, BN>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
   __shared__ float s_rstd[BM];
   __shared__ int s_rows[BM];
-  __shared__ int s_last;
 
   uint16_t* sA = reinterpret_cast<uint16_t*>(smem);
   uint16_t* sB = sA + 2 * BM * LDK;
@@ -178,47 +300,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
           for (int b = 0; b < C::FN; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
       }
       if (t + 1 < nk) store((t + 1) & 1);
-      __syncthreads();
+      lds_barrier();
     }
   }
 
-  // ---- split-K: publish the partial; the last split sums them in order ----
   if (g.splits > 1) {
-    const int tile_id = m_tile * gridDim.x + n_tile;
-    constexpr int PER = C::FM * C::FN * 4;
-    float* part = g.partial + (size_t)tile_id * g.splits * (BM * BN);
-    float* mine = part + (size_t)split * (BM * BN);
+    // partial layout: [split][m < BM][n < n_tiles * BN], row-major
+    const size_t ld = (size_t)gridDim.x * BN;
+    float* part = g.partial + (size_t)split * BM * ld + (size_t)n_tile * BN;
 #pragma unroll
     for (int a = 0; a < C::FM; ++a)
 #pragma unroll
       for (int b = 0; b < C::FN; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mine[((a * C::FN + b) * 4 + i) * 256 + tid] = acc[a][b][i];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&g.counters[tile_id], 1) == g.splits - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-#pragma unroll
-    for (int a = 0; a < C::FM; ++a)
-#pragma unroll
-      for (int b = 0; b < C::FN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int z = 0; z < g.splits; ++z) {
-      const float* pz = part + (size_t)z * (BM * BN);
-#pragma unroll
-      for (int a = 0; a < C::FM; ++a)
-#pragma unroll
-        for (int b = 0; b < C::FN; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[a][b][i] += __builtin_nontemporal_load(pz + ((a * C::FN + b) * 4 + i) * 256 + tid);
-    }
-    (void)PER;
-    if (tid == 0) g.counters[tile_id] = 0;
+        for (int i = 0; i < 4; ++i) {
+          int row = wm * C::WM + a * 16 + 4 * (lane >> 4) + i;
+          int col = wn * C::WN + b * 16 + (lane & 15);
+          part[(size_t)row * ld + col] = acc[a][b][i];
+        }
+    return;
   }
 
-  // ---- stage the fp32 tile in LDS ----
   float* sC = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int a = 0; a < C::FM; ++a)
@@ -231,116 +333,190 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         sC[row * C::LDC + col] = acc[a][b][i];
       }
   __syncthreads();
+  epilogue<EPI, BN>(g, sC, C::LDC, m0, BM, n_tile);
+}
 
-  if constexpr (EPI == EPI_RESID) {
-    const int n0 = n_tile * BN;
-    constexpr int CH = BN / 128;
-    for (int p = wave; p < BM * CH; p += 4) {
-      int row = p / CH, ch = p % CH, m = m0 + row;
-      if (m >= g.M) continue;
-      float s = 0.f;
+// ---------------------------------------------------------------------------
+// Skinny variant for M <= 64 (decode): A is bf16 [M][K], at most 64 rows, and
+// every weight byte is used by exactly one workgroup, so the kernel is a
+// weight stream.  A workgroup of 8 waves computes a 64 x 128 output tile over
+// its K range in 64-wide chunks; wave w owns output columns 16w .. 16w+15.
+//  - Weights: each lane loads its row's chunk (k-groups g and 4+g of the
+//    chunk, the MFMA B layout) into a ring of SK_DEPTH chunks, so several
+//    chunks of loads are always in flight.
+//  - Activations: the 64 x 64 chunk, the same for all waves, travels in the
+//    same ring (one 16-byte piece per thread) and is staged through a
+//    double-buffered LDS tile, one barrier per chunk.
+//  - All loads are raw buffer loads with wave-uniform descriptors: a masked
+//    load uses an out-of-range offset and reads zeros (the hardware bounds
+//    check), so the loop has no branches and the compiler waits for exactly
+//    the chunk it consumes.
+constexpr int SK_BN = 128, SK_NT = 512, SK_KC = 64, SK_DEPTH = 8, SK_LDX = SK_KC + 8, SK_LDC = SK_BN + 4;
+constexpr uint32_t OOB = 0xFFFFFFF0u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <int EPI>
+__global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][64 * SK_LDX];
+  __shared__ __attribute__((aligned(16))) float sC[64 * SK_LDC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), gq = lane >> 4, r16 = lane & 15;
+  const int t = blockIdx.x, split = blockIdx.y;
+  const int kb = g.splits > 1 ? split * g.k_split : 0;
+  const int ke = g.splits > 1 ? min(g.K, kb + g.k_split) : g.K;
+  const int nc = ke > kb ? (ke - kb + SK_KC - 1) / SK_KC : 0;
+
+  // The wave's weight tensor (uniform per wave) and this lane's row in it.
+  const uint16_t* wt;
+  int wrow, wrows;
+  if (EPI == EPI_SWIGLU) {
+    const bool up = wave >= 4;
+    wt = up ? g.w[1] : g.w[0];
+    wrow = t * (SK_BN / 2) + (wave & 3) * 16 + r16;
+    wrows = g.N;
+  } else {
+    const int n0 = t * SK_BN;  // whole tiles lie in one segment
+    const int sg = n0 >= g.seg_n0[1] ? (n0 >= g.seg_n0[2] ? 2 : 1) : 0;
+    wt = g.w[sg];
+    wrow = n0 - g.seg_n0[sg] + wave * 16 + r16;
+    wrows = min(g.N, g.seg_n0[sg + 1]) - g.seg_n0[sg];
+  }
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wt, (uint32_t)((size_t)wrows * g.K * 2));
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(g.a, (uint32_t)((size_t)g.M * g.lda * 2));
+  const bool wok = wrow < wrows;
+  const uint32_t wbase = (uint32_t)wrow * (uint32_t)g.K;
+  const int xr = tid >> 3, xk = (tid & 7) * 8;  // this thread's activation piece
+  const bool xok = xr < g.M;
+
+  struct Slot {
+    uint4 w0, w1, x;
+  };
+  auto load = [&](Slot& sl, int j) {
+    const int k0 = kb + j * SK_KC;
+    const bool live = j < nc;
+    const int kw = k0 + gq * 8;
+    sl.w0 = bload16(wrs, live && wok && kw < ke ? (wbase + (uint32_t)kw) * 2u : OOB);
+    sl.w1 = bload16(wrs, live && wok && kw + 32 < ke ? (wbase + (uint32_t)(kw + 32)) * 2u : OOB);
+    const int kx = k0 + xk;
+    sl.x = bload16(xrs, live && xok && kx < ke ? (uint32_t)(xr * g.lda + kx) * 2u : OOB);
+  };
+
+  f32x4 acc[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int col = ch * 128 + lane + 64 * h;
-        size_t off = (size_t)m * g.ldy + n0 + col;
-        float v = g.y_out[off] + sC[row * C::LDC + col];
-        g.y_out[off] = v;
-        s += v * v;
-      }
-      s = wave_sum(s);
-      if (lane == 0) g.ss_out[(size_t)m * g.n_ss + n0 / 128 + ch] = s;
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    constexpr int HALF = BN / 2;
-    const int j0 = n_tile * HALF;
-    for (int idx = tid; idx < BM * HALF; idx += 256) {
-      int row = idx / HALF, j = idx % HALF, m = m0 + row, n = j0 + j;
-      if (m < g.M && n < g.N) {
-        float gt = sC[row * C::LDC + j], up = sC[row * C::LDC + HALF + j];
-        float h = gt / (1.0f + expf(-gt)) * up;
-        g.h_out[(size_t)m * g.N + n] = f2bf(h);
-      }
-    }
-  } else if constexpr (EPI == EPI_QKV) {
-    const int n0 = n_tile * BN;
-    const int hd = g.hd, hd2 = hd >> 1, P = g.page_size;
-    const int qw = g.nq * hd, kw = g.nkv * hd;
-    const int kind = n0 < qw ? 0 : (n0 < qw + kw ? 1 : 2);
-    if (kind < 2) {
-      for (int idx = tid; idx < BM * (BN / 2); idx += 256) {
-        int row = idx / (BN / 2), pr = idx % (BN / 2), m = m0 + row;
-        if (m >= g.M) continue;
-        int hl = pr / hd2, dd = pr % hd2;
-        int c1 = hl * hd + dd, c2 = c1 + hd2;
-        float cs = g.rope_cs[((size_t)m * hd2 + dd) * 2], sn = g.rope_cs[((size_t)m * hd2 + dd) * 2 + 1];
-        float x1 = sC[row * C::LDC + c1], x2 = sC[row * C::LDC + c2];
-        float o1 = x1 * cs - x2 * sn, o2 = x2 * cs + x1 * sn;
-        if (kind == 0) {
-          int head = (n0 + c1) / hd;
-          uint16_t* q = g.q_out + (size_t)m * qw + head * hd;
-          q[dd] = f2bf(o1);
-          q[dd + hd2] = f2bf(o2);
-        } else {
-          int kvh = (n0 - qw + c1) / hd;
-          int sl = g.slot[m], page = sl / P, off = sl % P;
-          size_t base = (size_t)page * g.page_stride + (size_t)kvh * P * hd + (size_t)off * hd;
-          if (g.kv_e4m3) {
-            float s = g.kv_scale[kvh];
-            uint8_t* kv = reinterpret_cast<uint8_t*>(g.kv_layer);
-            kv[base + dd] = f2e4m3(o1 / s);
-            kv[base + dd + hd2] = f2e4m3(o2 / s);
-          } else {
-            uint16_t* kv = reinterpret_cast<uint16_t*>(g.kv_layer);
-            kv[base + dd] = f2bf(o1);
-            kv[base + dd + hd2] = f2bf(o2);
-          }
-        }
-      }
-    } else {
-      for (int idx = tid; idx < BM * BN; idx += 256) {
-        int row = idx / BN, c = idx % BN, m = m0 + row;
-        if (m >= g.M) continue;
-        int vc = n0 - qw - kw + c, kvh = vc / hd, dd = vc % hd;
-        int sl = g.slot[m], page = sl / P, off = sl % P;
-        size_t idx_v = (size_t)page * g.page_stride + (size_t)g.nkv * P * hd + (size_t)kvh * hd * P +
-                       (size_t)dd * P + off;
-        float x = sC[row * C::LDC + c];
-        if (g.kv_e4m3) {
-          reinterpret_cast<uint8_t*>(g.kv_layer)[idx_v] = f2e4m3(x / g.kv_scale[g.nkv + kvh]);
-        } else {
-          reinterpret_cast<uint16_t*>(g.kv_layer)[idx_v] = f2bf(x);
-        }
-      }
-    }
-  } else if constexpr (EPI == EPI_LOGITS) {
-    const int n0 = n_tile * BN;
-    for (int row = wave; row < BM; row += 4) {
-      int m = m0 + row;
-      if (m >= g.M) continue;
-      const int kind = g.ro_kind[m];
-      const float T = g.ro_temp[m];
-      const uint32_t lo = g.ro_seed_lo[m], hi = g.ro_seed_hi[m], ln = (uint32_t)g.ro_lane[m];
-      float best = -INFINITY;
-      int bi = INT_MAX;
-      for (int c = lane; c < BN; c += 64) {
-        int v = n0 + c;
-        if (v >= g.N) break;
-        float l = sC[row * C::LDC + c];
-        if (g.logits) g.logits[(size_t)m * g.N + v] = l;
-        float s = kind == 0 ? l : l / T + gumbel((uint32_t)v, ln, lo, hi);
-        if (s > best) { best = s; bi = v; }
-      }
+  for (int a = 0; a < 4; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nc > 0) {
+    // Whole groups of SK_DEPTH chunks, with no branches inside a group:
+    // chunks past nc load zeros (out-of-range offsets) and add nothing.
+    // Straight-line code lets the compiler wait for exactly the slot it is
+    // about to consume.
+    Slot ring[SK_DEPTH];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        float ob = __shfl_xor(best, o, 64);
-        int oi = __shfl_xor(bi, o, 64);
-        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-      }
-      if (lane == 0) {
-        g.tile_best[(size_t)n_tile * g.M + m] = best;
-        g.tile_idx[(size_t)n_tile * g.M + m] = bi;
+    for (int j = 0; j < SK_DEPTH; ++j) load(ring[j], j);
+    const int ngroups = (nc + SK_DEPTH - 1) / SK_DEPTH;
+    for (int gi = 0; gi < ngroups; ++gi) {
+#pragma unroll
+      for (int j = 0; j < SK_DEPTH; ++j) {
+        const int c = gi * SK_DEPTH + j;
+        uint16_t* X = sX[j & 1];
+        *reinterpret_cast<uint4*>(&X[xr * SK_LDX + xk]) = ring[j].x;
+        lds_barrier();
+        uint4 af[2][4];  // all eight A fragments in flight before the first MFMA
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            af[ks][a] = *reinterpret_cast<const uint4*>(&X[(a * 16 + r16) * SK_LDX + ks * 32 + gq * 8]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) acc[a] = mfma16(af[ks][a], ks ? ring[j].w1 : ring[j].w0, acc[a]);
+        load(ring[j], c + SK_DEPTH);
       }
     }
+  }
+
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sC[(a * 16 + 4 * gq + i) * SK_LDC + wave * 16 + r16] = acc[a][i];
+  __syncthreads();
+  if (g.splits > 1) {
+    const size_t ld = (size_t)gridDim.x * SK_BN;
+    float* part = g.partial + (size_t)split * 64 * ld + (size_t)t * SK_BN;
+    for (int idx = tid; idx < 64 * SK_BN; idx += SK_NT) {
+      const int row = idx / SK_BN, col = idx % SK_BN;
+      part[(size_t)row * ld + col] = sC[row * SK_LDC + col];
+    }
+    return;
+  }
+  epilogue<EPI, SK_BN, SK_NT>(g, sC, SK_LDC, 0, 64, t);
+}
+
+// Split-K reduce of the skinny kernel: one workgroup per 16 rows of a 64 x 128
+// tile; each thread sums 8 elements, the 8 loads of one split in flight
+// together, splits added in split order; then the epilogue on those rows.
+template <int EPI>
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, int n_tiles) {
+  constexpr int ROWS = 16, PER = ROWS * SK_BN / 256;
+  __shared__ __attribute__((aligned(16))) float sC[ROWS * SK_LDC];
+  const int t = blockIdx.x, r0 = blockIdx.y * ROWS;
+  const size_t ld = (size_t)n_tiles * SK_BN, zs = 64 * ld;
+  const float* base = g.partial + (size_t)r0 * ld + (size_t)t * SK_BN;
+  float v[PER];
+  size_t off[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + 256 * i, row = e / SK_BN, col = e % SK_BN;
+    off[i] = (size_t)row * ld + col;
+    v[i] = 0.f;
+  }
+  for (int z = 0; z < g.splits; ++z) {
+    float x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) x[i] = base[z * zs + off[i]];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] += x[i];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + 256 * i, row = e / SK_BN, col = e % SK_BN;
+    sC[row * SK_LDC + col] = v[i];
+  }
+  __syncthreads();
+  epilogue<EPI, SK_BN, 256>(g, sC, SK_LDC, r0, ROWS, t);
+}
+
+// x[m, :] = bf16(y[m, :] * rsqrt(sum_sq[m] / d + eps) * gain), one workgroup per row.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ y, const float* __restrict__ ss,
+                                                      int n_ss, const uint16_t* __restrict__ gain, int d,
+                                                      float eps, const int32_t* __restrict__ rows,
+                                                      uint16_t* __restrict__ x) {
+  const int m = blockIdx.x;
+  const int src = rows ? rows[m] : m;
+  __shared__ float s_r;
+  if (threadIdx.x == 0) {
+    float s = 0.f;
+    for (int c = 0; c < n_ss; ++c) s += ss[(size_t)src * n_ss + c];
+    s_r = 1.0f / sqrtf(s / (float)d + eps);
+  }
+  __syncthreads();
+  const float r = s_r;
+  for (int k = threadIdx.x * 8; k < d; k += 256 * 8) {
+    const float4* p = reinterpret_cast<const float4*>(y + (size_t)src * d + k);
+    float4 a = p[0], b = p[1];
+    uint4 gw = *reinterpret_cast<const uint4*>(gain + k);
+    uint4 o;
+    o.x = pack_bf2(a.x * r * bf2f(gw.x & 0xffffu), a.y * r * bf2f(gw.x >> 16));
+    o.y = pack_bf2(a.z * r * bf2f(gw.y & 0xffffu), a.w * r * bf2f(gw.y >> 16));
+    o.z = pack_bf2(b.x * r * bf2f(gw.z & 0xffffu), b.y * r * bf2f(gw.z >> 16));
+    o.w = pack_bf2(b.z * r * bf2f(gw.w & 0xffffu), b.w * r * bf2f(gw.w >> 16));
+    *reinterpret_cast<uint4*>(x + (size_t)m * d + k) = o;
   }
 }
 
@@ -366,11 +542,28 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* tile_bes
 int gemm_tile_bm(int tile) { return tile == TILE_64x128 ? 64 : 128; }
 int gemm_tile_bn(int) { return 128; }
 
+int gemm_n_tiles(int epi, int N, int) {
+  return epi == EPI_SWIGLU ? (N + 63) / 64 : (N + 127) / 128;
+}
+
+// Large tiles (prefill-sized M) never split K: there are enough output tiles.
 template <int BM, int BN, int AMODE, int EPI>
-static void launch_t(const GemmArgs& g, hipStream_t st) {
-  int n_tiles = EPI == EPI_SWIGLU ? (g.N + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
-  dim3 grid(n_tiles, (g.M + BM - 1) / BM, g.splits > 1 ? g.splits : 1);
+static void launch_t(const GemmArgs& g0, hipStream_t st) {
+  GemmArgs g = g0;
+  g.splits = 1;
+  g.k_split = g.K;
+  const int n_tiles = EPI == EPI_SWIGLU ? (g.N + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
+  dim3 grid(n_tiles, (g.M + BM - 1) / BM, 1);
   hipLaunchKernelGGL((gemm_kernel<BM, BN, AMODE, EPI>), grid, dim3(256), 0, st, g);
+}
+
+template <int EPI>
+static void launch_skinny(const GemmArgs& g, hipStream_t st) {
+  const int n_tiles = gemm_n_tiles(EPI, g.N, TILE_SKINNY);
+  hipLaunchKernelGGL((gemm_skinny_kernel<EPI>), dim3(n_tiles, g.splits > 1 ? g.splits : 1), dim3(SK_NT), 0,
+                     st, g);
+  if (g.splits > 1)
+    hipLaunchKernelGGL((skinny_reduce_kernel<EPI>), dim3(n_tiles, (g.M + 15) / 16), dim3(256), 0, st, g, n_tiles);
 }
 
 template <int BM, int BN>
@@ -383,12 +576,32 @@ static void launch_tile(int amode, int epi, const GemmArgs& g, hipStream_t st) {
       default: return;
     }
   }
-  if (epi == EPI_RESID) return launch_t<BM, BN, A_BF16, EPI_RESID>(g, st);
+  switch (epi) {
+    case EPI_QKV: return launch_t<BM, BN, A_BF16, EPI_QKV>(g, st);
+    case EPI_SWIGLU: return launch_t<BM, BN, A_BF16, EPI_SWIGLU>(g, st);
+    case EPI_RESID: return launch_t<BM, BN, A_BF16, EPI_RESID>(g, st);
+    default: return;
+  }
 }
 
 void launch_gemm(int amode, int epi, int tile, const GemmArgs& g, hipStream_t st) {
+  if (tile == TILE_SKINNY) {
+    switch (epi) {
+      case EPI_QKV: return launch_skinny<EPI_QKV>(g, st);
+      case EPI_RESID: return launch_skinny<EPI_RESID>(g, st);
+      case EPI_SWIGLU: return launch_skinny<EPI_SWIGLU>(g, st);
+      case EPI_LOGITS: return launch_skinny<EPI_LOGITS>(g, st);
+    }
+    return;
+  }
   if (tile == TILE_64x128) launch_tile<64, 128>(amode, epi, g, st);
   else launch_tile<128, 128>(amode, epi, g, st);
+}
+
+void launch_rmsnorm(const float* y, const float* ss, int n_ss, const uint16_t* gain, int M, int d,
+                    float eps, const int32_t* rows, uint16_t* x, hipStream_t st) {
+  if (M <= 0) return;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, st, y, ss, n_ss, gain, d, eps, rows, x);
 }
 
 void launch_argmax_reduce(const float* tile_best, const int32_t* tile_idx, int n_tiles, int M,

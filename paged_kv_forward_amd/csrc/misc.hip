@@ -6,8 +6,8 @@
 
 namespace pie {
 
-// y[t, :] = float(E[tok[t], :]); ss[t, c] = sum of y[t, 128c : 128c + 128]^2.
-// One workgroup (4 waves) per row; each wave takes 128-column chunks.
+// y[t, :] = float(E[tok[t], :]); ss[t, c] = sum of y[t, 64c : 64c + 64]^2.
+// One workgroup (4 waves) per row; each wave takes 64-column chunks.
 __global__ __launch_bounds__(256) void embed_kernel(const uint16_t* __restrict__ E,
                                                     const int32_t* __restrict__ tok, int d,
                                                     float* __restrict__ y, float* __restrict__ ss,
@@ -16,11 +16,10 @@ __global__ __launch_bounds__(256) void embed_kernel(const uint16_t* __restrict__
   const uint16_t* src = E + (size_t)tok[t] * d;
   float* dst = y + (size_t)t * d;
   for (int c = wave; c < n_ss; c += 4) {
-    const int k = c * 128 + 2 * lane;
-    uint32_t w = *reinterpret_cast<const uint32_t*>(src + k);
-    float a = bf2f(w & 0xffffu), b = bf2f(w >> 16);
-    *reinterpret_cast<float2*>(dst + k) = make_float2(a, b);
-    float s = wave_sum(a * a + b * b);
+    const int k = c * 64 + lane;
+    const float a = bf2f(src[k]);
+    dst[k] = a;
+    const float s = wave_sum(a * a);
     if (lane == 0) ss[(size_t)t * n_ss + c] = s;
   }
 }
@@ -52,7 +51,7 @@ __global__ void philox_kernel(uint32_t seed_lo, uint32_t seed_hi, uint32_t lane,
 void launch_embed(const uint16_t* E, const int32_t* tok, int n_rows, int d, float* y, float* ss,
                   hipStream_t st) {
   if (n_rows <= 0) return;
-  hipLaunchKernelGGL(embed_kernel, dim3(n_rows), dim3(256), 0, st, E, tok, d, y, ss, d / 128);
+  hipLaunchKernelGGL(embed_kernel, dim3(n_rows), dim3(256), 0, st, E, tok, d, y, ss, d / 64);
 }
 
 void launch_rope_table(const int32_t* pos, int n_rows, int hd, double theta, float* cs,
