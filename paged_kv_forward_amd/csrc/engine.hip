@@ -15,6 +15,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
+#include <map>
+#include <tuple>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -163,6 +166,29 @@ Layout make_layout(const pie_model_desc& d, const pie_limits& l) {
   return L;
 }
 
+// Events of the timed launches of one call (timed calls are never captured).
+struct EventSink {
+  std::vector<hipEvent_t> ev;
+  std::vector<std::pair<int, size_t>> marks;  // (class, index of the start event)
+  size_t used = 0;
+};
+
+// What determines the launch sequence of a call (everything else the kernels
+// read comes from the metadata staged in device memory).
+struct GraphKey {
+  int T, R, n_dec, n_comb, n_pre, flags;
+  const void* logits;
+  bool operator<(const GraphKey& o) const {
+    return std::tie(T, R, n_dec, n_comb, n_pre, flags, logits) <
+           std::tie(o.T, o.R, o.n_dec, o.n_comb, o.n_pre, o.flags, o.logits);
+  }
+};
+
+struct GraphEntry {
+  int seen = 0;
+  hipGraphExec_t exec = nullptr;
+};
+
 }  // namespace
 
 struct pie_ctx {
@@ -183,19 +209,23 @@ struct pie_ctx {
   int32_t* pinned = nullptr;
   std::vector<int32_t> dec, comb, pre;  // int4 items, flattened
   int n_parts = 0;
-  // profiling
+  // profiling: events bracketing timed launches, recorded into a sink
   uint32_t prof_mask = 0;
-  std::vector<hipEvent_t> ev_pool;
-  size_t ev_used = 0;
-  std::vector<std::pair<int, size_t>> ev_marks;  // (class, index of start event)
+  EventSink sink;
+  hipStream_t cur = nullptr;    // stream launches go to while enqueueing
   double prof_ms[PIE_K_NUM_CLASSES] = {0};
   int64_t prof_n[PIE_K_NUM_CLASSES] = {0};
+  // graphs of the per-call launch sequence, by launch shape
+  hipStream_t cap_stream = nullptr;
+  std::map<GraphKey, GraphEntry> graphs;
+  bool use_graphs = true;
+  bool capturing = false;
 };
 
 namespace {
 
 int hip_fail(pie_ctx* c, hipError_t e, const char* what) {
-  if (c) c->poisoned = true;
+  if (c && !c->capturing) c->poisoned = true;
   return set_err(PIE_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
@@ -205,50 +235,57 @@ int hip_fail(pie_ctx* c, hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail((c), e_, #call); \
   } while (0)
 
-hipEvent_t next_event(pie_ctx* c) {
-  if (c->ev_used == c->ev_pool.size()) {
+hipEvent_t next_event(EventSink* k) {
+  if (k->used == k->ev.size()) {
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
-    c->ev_pool.push_back(e);
+    k->ev.push_back(e);
   }
-  return c->ev_pool[c->ev_used++];
+  return k->ev[k->used++];
 }
 
 // Brackets one launch of class k with events when that class is being timed.
 struct Timed {
   pie_ctx* c;
-  int k;
   bool on;
-  Timed(pie_ctx* c_, int k_) : c(c_), k(k_), on((c_->prof_mask >> k_) & 1u) {
+  size_t first = 0;
+  Timed(pie_ctx* c_, int k) : c(c_), on(((c_->prof_mask >> k) & 1u) && !c_->capturing) {
     if (on) {
-      hipEvent_t a = next_event(c), b = next_event(c);
+      hipEvent_t a = next_event(&c->sink), b = next_event(&c->sink);
       if (!a || !b) { on = false; return; }
-      c->ev_marks.push_back({k, c->ev_used - 2});
-      (void)hipEventRecord(a, c->stream);
+      first = c->sink.used - 2;
+      c->sink.marks.push_back({k, first});
+      (void)hipEventRecord(a, c->cur);
     }
   }
   ~Timed() {
-    if (on) (void)hipEventRecord(c->ev_pool[c->ev_marks.back().second + 1], c->stream);
+    if (on) (void)hipEventRecord(c->sink.ev[first + 1], c->cur);
   }
 };
 
-void collect_profile(pie_ctx* c) {
-  for (auto& m : c->ev_marks) {
+void collect_profile(pie_ctx* c, EventSink& k) {
+  for (auto& m : k.marks) {
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, c->ev_pool[m.second], c->ev_pool[m.second + 1]) == hipSuccess) {
+    if (hipEventElapsedTime(&ms, k.ev[m.second], k.ev[m.second + 1]) == hipSuccess) {
       c->prof_ms[m.first] += ms;
       c->prof_n[m.first] += 1;
     }
   }
-  c->ev_marks.clear();
-  c->ev_used = 0;
+  (void)hipGetLastError();  // a failed timing query must not surface in a later call
+}
+
+void release_graphs(pie_ctx* c) {
+  for (auto& kv : c->graphs) {
+    if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
+  }
+  c->graphs.clear();
 }
 
 int check_launch(pie_ctx* c, int flags, const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(c, e, what);
   if (flags & PIE_FLAG_SYNC_DEBUG) {
-    e = hipStreamSynchronize(c->stream);
+    e = hipStreamSynchronize(c->cur);
     if (e != hipSuccess) return hip_fail(c, e, what);
   }
   return PIE_OK;
@@ -302,16 +339,13 @@ void put(int32_t* base, size_t off, const std::vector<T>& v) {
   if (!v.empty()) std::memcpy(base + off, v.data(), v.size() * sizeof(T));
 }
 
-int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
+// Pack the plan and the attention work lists into the pinned staging buffer.
+int stage(pie_ctx* c) {
   const pie::Plan& p = c->plan;
-  const pie_model_desc& d = c->d;
   const Layout& L = c->lay;
-  hipStream_t st = c->stream;
   build_work(c);
   if ((int)(c->dec.size() / 4) > L.max_dec_items || (int)(c->pre.size() / 4) > L.max_pre_items)
     return set_err(PIE_ENOMEM, "pie_forward: attention work list exceeds the workspace");
-
-  // ---- stage metadata (one H2D copy) ----
   int32_t* h = c->pinned;
   put(h, L.tok, p.tok); put(h, L.pos, p.pos); put(h, L.row_seq, p.row_seq); put(h, L.slot, p.slot);
   put(h, L.seq_row0, p.seq_row0); put(h, L.seq_ctx, p.seq_ctx); put(h, L.seq_len, p.seq_len);
@@ -320,6 +354,17 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
   put(h, L.ro_kind, p.ro_kind); put(h, L.ro_temp, p.ro_temp); put(h, L.ro_seed_lo, p.ro_seed_lo);
   put(h, L.ro_seed_hi, p.ro_seed_hi); put(h, L.dec_items, c->dec); put(h, L.comb_items, c->comb);
   put(h, L.pre_items, c->pre);
+  return PIE_OK;
+}
+
+// Enqueue one call's work on c->cur: metadata upload, every kernel, token
+// copy-back (and the logits copy to a host buffer when asked).
+int enqueue(pie_ctx* c, float* out_logits, int flags) {
+  const pie::Plan& p = c->plan;
+  const pie_model_desc& d = c->d;
+  const Layout& L = c->lay;
+  hipStream_t st = c->cur;
+  int32_t* h = c->pinned;
   const size_t meta_used = L.tokens_out;  // everything before the token output slot
   int32_t* dmeta = reinterpret_cast<int32_t*>(c->ws + L.meta);
   HIP_TRY(c, hipMemcpyAsync(dmeta, h, meta_used * 4, hipMemcpyHostToDevice, st));
@@ -524,9 +569,62 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
     if (out_logits && !(flags & PIE_FLAG_LOGITS_DEVICE))
       HIP_TRY(c, hipMemcpyAsync(out_logits, logits, (size_t)R * d.vocab * 4, hipMemcpyDeviceToHost, st));
   }
-  HIP_TRY(c, hipStreamSynchronize(st));
-  if (c->prof_mask) collect_profile(c);
-  if (R > 0) std::memcpy(out_tokens, h + L.tokens_out, (size_t)R * 4);
+  return PIE_OK;
+}
+
+// Run a call: enqueue directly, or replay (after capturing it the second
+// time its launch shape comes up) a graph of the whole launch sequence.
+// Graphs are captured on an internal stream and launched on the caller's.
+int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
+  int rc = stage(c);
+  if (rc) return rc;
+  const pie::Plan& p = c->plan;
+  const bool host_logits = out_logits && !(flags & PIE_FLAG_LOGITS_DEVICE);
+  // timed calls launch directly: kernel timing uses events between launches
+  const bool graphable = c->use_graphs && c->cap_stream && !host_logits && !c->prof_mask &&
+                         !(flags & PIE_FLAG_SYNC_DEBUG);
+  GraphEntry* ge = nullptr;
+  if (graphable) {
+    GraphKey key{p.n_rows, p.n_readout, (int)(c->dec.size() / 4), (int)(c->comb.size() / 4),
+                 (int)(c->pre.size() / 4), flags, out_logits};
+    if (c->graphs.size() >= 64 && !c->graphs.count(key)) release_graphs(c);
+    ge = &c->graphs[key];
+    if (!ge->exec && ++ge->seen >= 2) {
+      // capture; any failure leaves this shape on direct launches
+      c->cur = c->cap_stream;
+      c->capturing = true;
+      hipGraph_t graph = nullptr;
+      hipError_t e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
+      if (e == hipSuccess) {
+        rc = enqueue(c, out_logits, flags);
+        e = hipStreamEndCapture(c->cap_stream, &graph);
+        if (rc == PIE_OK && e == hipSuccess && graph)
+          e = hipGraphInstantiate(&ge->exec, graph, nullptr, nullptr, 0);
+        else if (e == hipSuccess)
+          e = hipErrorUnknown;
+      }
+      if (graph) (void)hipGraphDestroy(graph);
+      c->capturing = false;
+      if (e != hipSuccess || !ge->exec) {
+        (void)hipGetLastError();
+        ge->exec = nullptr;
+        ge->seen = -(1 << 30);
+        g_err.clear();
+      }
+    }
+  }
+  if (ge && ge->exec) {
+    HIP_TRY(c, hipGraphLaunch(ge->exec, c->stream));
+  } else {
+    c->cur = c->stream;
+    c->sink.used = 0;
+    c->sink.marks.clear();
+    rc = enqueue(c, out_logits, flags);
+    if (rc) return rc;
+  }
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  if (c->prof_mask) collect_profile(c, c->sink);
+  if (p.n_readout > 0) std::memcpy(out_tokens, c->pinned + c->lay.tokens_out, (size_t)p.n_readout * 4);
   return PIE_OK;
 }
 
@@ -618,15 +716,26 @@ int pie_init(const pie_model_desc* desc, const pie_weights* w, void* kv_arena, s
   }
   e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned), c->lay.meta_ints * 4, hipHostMallocDefault);
   if (e != hipSuccess) { delete c; return set_err(PIE_EHIP, std::string("pie_init: hipHostMalloc: ") + hipGetErrorString(e)); }
+  // a default-priority stream of our own, used only to capture launch graphs
+  if (hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess) c->cap_stream = nullptr;
+  const char* ng = std::getenv("PIE_NO_GRAPH");
+  c->use_graphs = !(ng && ng[0] && ng[0] != '0');
+  c->cur = c->stream;
   *out = c;
   return PIE_OK;
 }
 
 int pie_destroy(pie_ctx* c) {
   if (!c) return PIE_OK;
-  if (c->host_only) std::free(c->pinned);
-  else if (c->pinned) (void)hipHostFree(c->pinned);
-  for (auto e : c->ev_pool) (void)hipEventDestroy(e);
+  if (c->host_only) {
+    std::free(c->pinned);
+  } else {
+    (void)hipStreamSynchronize(c->stream);
+    release_graphs(c);
+    if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+    if (c->pinned) (void)hipHostFree(c->pinned);
+    for (auto e : c->sink.ev) (void)hipEventDestroy(e);
+  }
   delete c;
   return PIE_OK;
 }
@@ -719,8 +828,6 @@ int pie_profile_enable(pie_ctx* c, uint32_t mask) {
     c->prof_ms[k] = 0;
     c->prof_n[k] = 0;
   }
-  c->ev_marks.clear();
-  c->ev_used = 0;
   return PIE_OK;
 }
 
@@ -729,7 +836,6 @@ int pie_profile_read(pie_ctx* c, double* ms, int64_t* counts) {
   if (!c->host_only) {
     hipError_t e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "pie_profile_read");
-    collect_profile(c);
   }
   for (int k = 0; k < PIE_K_NUM_CLASSES; ++k) {
     if (ms) ms[k] = c->prof_ms[k];

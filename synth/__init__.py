@@ -236,6 +236,12 @@ def prompt_tokens(config_id: int, seq_id: int, n: int, vocab: int, salt: int = 7
     return uniform_int(n, key_of("tokens/%d/%d/%d" % (config_id, seq_id, salt)), 0, vocab)
 
 
+def teacher_tokens(config_id: int, seq_id: int, n: int, vocab: int) -> np.ndarray:
+    """Seeded tokens fed to decode steps of parity runs (instead of the model's own
+    choice), so that a whole trajectory is known in advance."""
+    return prompt_tokens(config_id, 1000 + seq_id, n, vocab, salt=11)
+
+
 def epilogue_seed(branch_seed: int, step: int) -> int:
     """Fresh 64-bit seed per pass: (branch_seed << 32) | step."""
     return ((branch_seed & 0xFFFFFFFF) << 32) | (step & 0xFFFFFFFF)

@@ -1,0 +1,181 @@
+"""Writes the stored expected values of the full-size GPU parity tests.
+
+Calls only the oracle (oracle/) and the seeded input generator (synth/).  Every
+decode step of a checked sequence is fed a seeded "teacher" token, so the
+whole trajectory of a sequence is one chunk of known tokens and the oracle can
+run it layer-major in one pass (weights drawn once per layer); the GPU test
+feeds the same tokens.  By the incremental-decode invariant of the oracle,
+reading out row i of that chunk equals decoding token by token.
+
+    python tests/golden/make_golden.py c2 [c3 c4 c5]
+
+Output: tests/golden/<name>.npz with, per checked readout row, the oracle's
+token, its top-2 margin, the float32 logits at a fixed seeded subset of
+vocabulary indices, and the full float32 logits for a few rows.
+"""
+from __future__ import annotations
+
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from oracle.epilogue import scores, top2_margin, argmax_lowest  # noqa: E402
+from oracle.run import Chunk, SynthWeights, default_numerics, forward_chunks  # noqa: E402
+
+SUBSET = 2048  # logits kept for every row at these seeded vocabulary indices
+
+
+def subset_idx(vocab):
+    return np.sort(synth.uniform_int(SUBSET, synth.key_of("golden/subset"), 0, vocab))
+
+
+teacher_tokens = synth.teacher_tokens
+
+
+def finish(name, rows, full_rows, vocab, meta):
+    """rows: list of dicts (seq, step, kind, temp, seed, lane, logits)."""
+    idx = subset_idx(vocab)
+    out = {"subset_idx": idx}
+    toks, margins, subs = [], [], []
+    for r in rows:
+        s32, s64 = scores(r["logits"], r["kind"], r["temp"], r["seed"], r["lane"])
+        toks.append(argmax_lowest(s32))
+        margins.append(top2_margin(s64))
+        subs.append(r["logits"][idx].astype(np.float32))
+    out["token"] = np.array(toks, dtype=np.int32)
+    out["margin"] = np.array(margins)
+    out["logits_subset"] = np.stack(subs)
+    out["row_seq"] = np.array([r["seq"] for r in rows], dtype=np.int32)
+    out["row_step"] = np.array([r["step"] for r in rows], dtype=np.int32)
+    out["row_kind"] = np.array([r["kind"] for r in rows], dtype=np.int32)
+    out["full_rows"] = np.array(full_rows, dtype=np.int32)
+    out["logits_full"] = np.stack([rows[i]["logits"].astype(np.float32) for i in full_rows])
+    for k, v in meta.items():
+        out["meta_" + k] = np.asarray(v)
+    path = os.path.join(HERE, name + ".npz")
+    np.savez_compressed(path, **out)
+    print("wrote", path, "rows", len(rows), "excluded(margin<2e-2)",
+          int(np.sum(out["margin"] < 2e-2)), flush=True)
+
+
+def c2(decode_steps=3, seqs=(0, 63)):
+    """Llama-3.1-8B decode: sequences of 2048 prompt tokens + teacher-fed decode steps."""
+    wl = synth.workload(2)
+    shape = wl.shape
+    w = SynthWeights(synth.WeightRecipe(shape))
+    num = default_numerics(shape)
+    chunks = []
+    for s in seqs:
+        toks = np.concatenate([wl.prompt(s), teacher_tokens(2, s, decode_steps, shape.vocab)])
+        n = len(toks)
+        ro = list(range(wl.prompt_len[s] - 1, n))
+        chunks.append(Chunk(toks, np.arange(n), -1, ro))
+    t0 = time.time()
+    logits = forward_chunks(w, chunks, num)
+    print("c2 oracle %.0f s" % (time.time() - t0), flush=True)
+    rows = []
+    for ci, s in enumerate(seqs):
+        for k in range(decode_steps + 1):
+            rows.append(dict(seq=s, step=k, kind=synth.EPI_ARGMAX, temp=1.0, seed=0, lane=0,
+                             logits=logits[ci][k]))
+    full = [0, decode_steps, decode_steps + 1, 2 * decode_steps + 1]
+    finish("c2_decode_8b", rows, full, shape.vocab,
+           dict(seqs=list(seqs), decode_steps=decode_steps))
+
+
+def c3(decode_steps=2, branches=(0, 4, 9)):
+    """Fork at the 8B shape: 8192-token prefix, 256-token suffix per branch, Gumbel T=0.7."""
+    wl = synth.workload(3)
+    shape = wl.shape
+    w = SynthWeights(synth.WeightRecipe(shape))
+    num = default_numerics(shape)
+    pre = wl.prefix()
+    P = len(pre)
+    chunks = [Chunk(pre, np.arange(P), -1, [])]
+    for b in branches:
+        toks = np.concatenate([wl.prompt(b), teacher_tokens(3, b, decode_steps, shape.vocab)])
+        n = len(toks)
+        chunks.append(Chunk(toks, P + np.arange(n), 0, list(range(wl.prompt_len[b] - 1, n))))
+    t0 = time.time()
+    logits = forward_chunks(w, chunks, num)
+    print("c3 oracle %.0f s" % (time.time() - t0), flush=True)
+    rows = []
+    for ci, b in enumerate(branches):
+        for k in range(decode_steps + 1):
+            rows.append(dict(seq=b, step=k, kind=synth.EPI_GUMBEL, temp=0.7,
+                             seed=synth.epilogue_seed(wl.branch_seed[b], k), lane=0,
+                             logits=logits[1 + ci][k]))
+    finish("c3_fork_8b", rows, [0, decode_steps + 1], shape.vocab,
+           dict(branches=list(branches), decode_steps=decode_steps))
+
+
+def c4(seqs=None):
+    """Mix at the 8B shape: prompts 0 and 7 (4096 tokens, read out at the end of the
+    last 512-chunk), and two decode rows (the shortest context and one other) read out
+    at each of the 8 launches."""
+    wl = synth.workload(4)
+    shape = wl.shape
+    w = SynthWeights(synth.WeightRecipe(shape))
+    num = default_numerics(shape)
+    dec_ctx = np.array(wl.prompt_len[8:])
+    shortest = 8 + int(np.argmin(dec_ctx))
+    other = 8 + 37
+    seqs = seqs or [0, 7, shortest, other]
+    chunks, meta_rows = [], []
+    for s in seqs:
+        if s < 8:
+            toks = wl.prompt(s)
+            chunks.append(Chunk(toks, np.arange(len(toks)), -1, [len(toks) - 1]))
+            meta_rows.append([(s, 7)])
+        else:
+            ctx = wl.prompt(s)
+            toks = np.concatenate([ctx, teacher_tokens(4, s, 8, shape.vocab)])
+            n = len(toks)
+            # the context is prefilled in setup; launch k feeds teacher token k
+            chunks.append(Chunk(toks, np.arange(n), -1, list(range(len(ctx), n))))
+            meta_rows.append([(s, k) for k in range(8)])
+    t0 = time.time()
+    logits = forward_chunks(w, chunks, num)
+    print("c4 oracle %.0f s" % (time.time() - t0), flush=True)
+    rows = []
+    for ci, s in enumerate(seqs):
+        for j, (_, k) in enumerate(meta_rows[ci]):
+            rows.append(dict(seq=s, step=k, kind=wl.epi_kind[s], temp=1.0,
+                             seed=synth.epilogue_seed(wl.branch_seed[s], k), lane=0,
+                             logits=logits[ci][j]))
+    finish("c4_mix_8b", rows, [0, 1, 2, len(rows) - 1], shape.vocab, dict(seqs=seqs))
+
+
+def c5(decode_steps=2, seqs=(0,)):
+    """Llama-3.3-70B decode with e4m3 KV: 4096 prompt tokens + teacher-fed decode steps."""
+    wl = synth.workload(5)
+    shape = wl.shape
+    w = SynthWeights(synth.WeightRecipe(shape))
+    num = default_numerics(shape)
+    chunks = []
+    for s in seqs:
+        toks = np.concatenate([wl.prompt(s), teacher_tokens(5, s, decode_steps, shape.vocab)])
+        n = len(toks)
+        chunks.append(Chunk(toks, np.arange(n), -1, list(range(wl.prompt_len[s] - 1, n))))
+    t0 = time.time()
+    logits = forward_chunks(w, chunks, num)
+    print("c5 oracle %.0f s" % (time.time() - t0), flush=True)
+    rows = []
+    for ci, s in enumerate(seqs):
+        for k in range(decode_steps + 1):
+            rows.append(dict(seq=s, step=k, kind=synth.EPI_ARGMAX, temp=1.0, seed=0, lane=0,
+                             logits=logits[ci][k]))
+    finish("c5_decode_70b", rows, [0, decode_steps], shape.vocab,
+           dict(seqs=list(seqs), decode_steps=decode_steps))
+
+
+if __name__ == "__main__":
+    for name in sys.argv[1:] or ["c2"]:
+        globals()[name]()

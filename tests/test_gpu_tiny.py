@@ -220,3 +220,32 @@ def test_device_philox_matches_oracle(torch_cuda):
         ref = philox4x32_10(v, lane, 0, 0, seed & 0xFFFFFFFF, seed >> 32)[0]
         np.testing.assert_array_equal(got, ref)
     rt.close()
+
+
+def test_graph_replays_match_direct_launches(torch_cuda, monkeypatch):
+    """The same decode loop with launch graphs (captured on the second call of a
+    shape, replayed after) and without: every step's logits bitwise equal."""
+    from paged_kv_forward_amd.runtime import Pass
+    recipe = RECIPES["gains_spread"]
+    shape = recipe.shape
+    prompts = [synth.prompt_tokens(1, 50 + s, 24 + s, shape.vocab) for s in range(3)]
+    feeds = [synth.teacher_tokens(1, s, 6, shape.vocab) for s in range(3)]
+    runs = []
+    for no_graph in ("1", "0"):
+        monkeypatch.setenv("PIE_NO_GRAPH", no_graph)
+        rt = make_runtime(shape, recipe, torch_cuda)
+        ws = [rt.alloc() for _ in range(3)]
+        out = []
+        _, lg = rt.forward([Pass(ws[s], prompts[s], [len(prompts[s]) - 1], [(0, 1, 0)]) for s in range(3)],
+                           want_logits=True)
+        out.append(lg)
+        dev = torch_cuda.empty((3, shape.vocab), dtype=torch_cuda.float32, device="cuda")
+        for k in range(6):
+            rt.forward([Pass(ws[s], [int(feeds[s][k])], [0], [(1, 0.7, 99 + k)]) for s in range(3)],
+                       logits_out=dev)
+            torch_cuda.cuda.synchronize()
+            out.append(dev.cpu().numpy().copy())
+        runs.append(out)
+        rt.close()
+    for a, b in zip(*runs):
+        np.testing.assert_array_equal(a, b)
