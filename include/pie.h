@@ -199,10 +199,12 @@ typedef struct pie_pass {
  *              pointer with PIE_FLAG_LOGITS_DEVICE).
  * All-or-nothing: every pass is validated and every page reserved before any
  * launch; on an error no working set changes.
- * Errors: PIE_EINVAL (stale handle, the same working set twice, token id out of
- * range, readout index out of range, temperature <= 0 or not finite, positions
- * not given when required, more rows/seqs/readouts than the limits, a sequence
- * beyond max_ctx), PIE_ENOMEM (page pool exhausted), PIE_EHIP, PIE_ESTATE.
+ * Errors: PIE_EINVAL (no passes, stale handle, the same working set twice, a
+ * pass without tokens, token id out of range, negative position, readout index
+ * out of range, unknown epilogue kind, temperature <= 0 or not finite, a
+ * sequence beyond max_ctx), PIE_ENOMEM (page pool exhausted, or more
+ * rows/passes/readouts/page-table entries than the init limits), PIE_EHIP,
+ * PIE_ESTATE (poisoned or host-only context without PIE_FLAG_NO_LAUNCH).
  * Returns after the stream has finished the call's work. */
 int pie_forward(pie_ctx* ctx, const pie_pass* passes, int32_t n_passes, int32_t* out_tokens,
                 float* out_logits, int32_t flags);
