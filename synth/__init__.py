@@ -155,6 +155,12 @@ LLAMA_70B = ModelShape("llama33-70b", n_layers=80, d_model=8192, n_q_heads=64, n
 SHAPES = {s.name: s for s in (TINY, LLAMA_8B, LLAMA_70B)}
 
 
+def first_layers(shape: ModelShape, n_layers: int) -> ModelShape:
+    """The same model cut to its first n_layers layers (weights are drawn by
+    tensor name, so the kept layers, embedding and head are identical)."""
+    return replace(shape, name="%s-first%d" % (shape.name, n_layers), n_layers=n_layers)
+
+
 def layer_tensor_shapes(m: ModelShape) -> List[Tuple[str, Tuple[int, ...]]]:
     """Per-layer weights, row-major [out][in] for matrices (the checkpoint layout)."""
     d, f = m.d_model, m.d_ffn

@@ -7,9 +7,10 @@ run it layer-major in one pass (weights drawn once per layer); the GPU test
 feeds the same tokens.  By the incremental-decode invariant of the oracle,
 reading out row i of that chunk equals decoding token by token.
 
-    python tests/golden/make_golden.py c2 [c3 c4 c5]
+    python tests/golden/make_golden.py c2 [c3 c4 c5] [c2:2 ...]
 
-Output: tests/golden/<name>.npz with, per checked readout row, the oracle's
+"cN:L" writes the same case for the model cut to its first L layers
+(<name>_first<L>.npz).  Output: tests/golden/<name>.npz with, per checked readout row, the oracle's
 token, its top-2 margin, the float32 logits at a fixed seeded subset of
 vocabulary indices, and the full float32 logits for a few rows.
 """
@@ -39,8 +40,19 @@ def subset_idx(vocab):
 teacher_tokens = synth.teacher_tokens
 
 
+LAYERS = None  # set by "cN:L" on the command line
+
+
+def model(wl):
+    """The workload's model, cut to LAYERS layers when asked."""
+    return wl.shape if LAYERS is None else synth.first_layers(wl.shape, LAYERS)
+
+
 def finish(name, rows, full_rows, vocab, meta):
     """rows: list of dicts (seq, step, kind, temp, seed, lane, logits)."""
+    if LAYERS is not None:
+        name = "%s_first%d" % (name, LAYERS)
+        meta = dict(meta, n_layers=LAYERS)
     idx = subset_idx(vocab)
     out = {"subset_idx": idx}
     toks, margins, subs = [], [], []
@@ -68,7 +80,9 @@ def finish(name, rows, full_rows, vocab, meta):
 def c2(decode_steps=3, seqs=(0, 63)):
     """Llama-3.1-8B decode: sequences of 2048 prompt tokens + teacher-fed decode steps."""
     wl = synth.workload(2)
-    shape = wl.shape
+    shape = model(wl)
+    if LAYERS is not None:
+        seqs = (0, 21, 42, 63)
     w = SynthWeights(synth.WeightRecipe(shape))
     num = default_numerics(shape)
     chunks = []
@@ -93,7 +107,7 @@ def c2(decode_steps=3, seqs=(0, 63)):
 def c3(decode_steps=2, branches=(0, 4, 9)):
     """Fork at the 8B shape: 8192-token prefix, 256-token suffix per branch, Gumbel T=0.7."""
     wl = synth.workload(3)
-    shape = wl.shape
+    shape = model(wl)
     w = SynthWeights(synth.WeightRecipe(shape))
     num = default_numerics(shape)
     pre = wl.prefix()
@@ -121,7 +135,7 @@ def c4(seqs=None):
     last 512-chunk), and two decode rows (the shortest context and one other) read out
     at each of the 8 launches."""
     wl = synth.workload(4)
-    shape = wl.shape
+    shape = model(wl)
     w = SynthWeights(synth.WeightRecipe(shape))
     num = default_numerics(shape)
     dec_ctx = np.array(wl.prompt_len[8:])
@@ -156,7 +170,7 @@ def c4(seqs=None):
 def c5(decode_steps=2, seqs=(0,)):
     """Llama-3.3-70B decode with e4m3 KV: 4096 prompt tokens + teacher-fed decode steps."""
     wl = synth.workload(5)
-    shape = wl.shape
+    shape = model(wl)
     w = SynthWeights(synth.WeightRecipe(shape))
     num = default_numerics(shape)
     chunks = []
@@ -177,5 +191,7 @@ def c5(decode_steps=2, seqs=(0,)):
 
 
 if __name__ == "__main__":
-    for name in sys.argv[1:] or ["c2"]:
+    for arg in sys.argv[1:] or ["c2"]:
+        name, _, layers = arg.partition(":")
+        LAYERS = int(layers) if layers else None
         globals()[name]()

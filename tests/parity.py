@@ -17,6 +17,16 @@ import numpy as np
 TAU_LOGIT = 2e-2
 TOL_LOGITS = 2e-2
 
+# Full depth (32 or 80 random-init layers): a one-ulp bf16 change in 0.1 % of
+# the embedding values moves the oracle's own logits by up to ~0.19 (largest)
+# and ~0.03 (mean) at the 8B shape (tests/golden/conditioning.py).  Any
+# implementation that sums in another order than the fp64 oracle differs from
+# it by that much, so at full depth the bounds are set from that measurement:
+# logits within twice the largest measured change, and tokens compared where
+# the oracle's top-2 margin exceeds the largest measured change.
+TOL_FULL_DEPTH = 0.4
+TAU_FULL_DEPTH = 0.2
+
 
 def say(*a):
     print(*a, flush=True)
@@ -28,6 +38,7 @@ class Report:
     excluded: int = 0
     mismatched: List[tuple] = field(default_factory=list)
     max_err: float = 0.0
+    sum_err: float = 0.0
 
     def add(self, gpu_tok, ref_tok, margin, tau, gpu_logits=None, ref_logits=None, tag=""):
         self.rows += 1
@@ -40,8 +51,9 @@ class Report:
             self.mismatched.append((tag, int(gpu_tok), int(ref_tok), float(margin)))
 
     def check(self, tol=TOL_LOGITS, max_excluded_frac=0.6):
-        say("parity: rows=%d excluded=%d mismatched=%d max|dlogit|=%.3g" %
-            (self.rows, self.excluded, len(self.mismatched), self.max_err))
+        say("parity: rows=%d excluded=%d mismatched=%d max|dlogit|=%.3g mean|dlogit|=%.3g" %
+            (self.rows, self.excluded, len(self.mismatched), self.max_err,
+             self.sum_err / max(self.rows, 1)))
         assert not self.mismatched, self.mismatched[:10]
         assert self.max_err <= tol, self.max_err
         assert self.excluded <= max_excluded_frac * max(self.rows, 1)

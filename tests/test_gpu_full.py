@@ -3,15 +3,25 @@ benchmark times, against stored oracle values (tests/golden/*.npz, written by
 tests/golden/make_golden.py from the oracle alone).
 
 Checked sequences are fed seeded teacher tokens at every decode step (the
-others are computed in the same launches but not compared).
+others run in the same launches and are not compared).
+
+Two depths per workload:
+  * the model cut to its first 2 layers, at full width, batch, context and
+    launch shape: every kernel runs at its real size and the 2e-2 bounds on
+    logits and on the token margin hold;
+  * the full depth (32 or 80 layers): tokens and logits against the bounds
+    of tests/parity.py for full depth, which follow from how strongly these
+    random-init models amplify one-ulp bf16 differences
+    (tests/golden/conditioning.py measures it with the oracle).
 """
+import ctypes
 import os
 
 import numpy as np
 import pytest
 
 import synth
-from tests.parity import Report, say, tau_for
+from tests.parity import (TAU_FULL_DEPTH, TAU_LOGIT, TOL_FULL_DEPTH, TOL_LOGITS, Report, say)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -24,12 +34,29 @@ def golden(name):
     return np.load(path, allow_pickle=False)
 
 
-def compare(rep, g, row, tok, logits, tag):
-    kind = int(g["row_kind"][row])
-    tau = tau_for(kind, 0.7 if kind else 1.0)
+def shape_of(wl, g):
+    if "meta_n_layers" in g.files:
+        return synth.first_layers(wl.shape, int(g["meta_n_layers"]))
+    return wl.shape
+
+
+def bounds(g):
+    return (TOL_LOGITS, TAU_LOGIT) if "meta_n_layers" in g.files else (TOL_FULL_DEPTH, TAU_FULL_DEPTH)
+
+
+def row_of(g, seq, step):
+    hit = np.nonzero((g["row_seq"] == seq) & (g["row_step"] == step))[0]
+    assert len(hit) == 1, (seq, step)
+    return int(hit[0])
+
+
+def compare(rep, g, row, tok, logits, tag, tau):
+    """tau: the margin below which the row's token is not compared (already
+    divided by the temperature for Gumbel-max rows)."""
     sub = logits[g["subset_idx"]]
-    err = float(np.max(np.abs(sub - g["logits_subset"][row])))
-    rep.max_err = max(rep.max_err, err)
+    err = np.abs(sub - g["logits_subset"][row])
+    rep.max_err = max(rep.max_err, float(err.max()))
+    rep.sum_err += float(err.mean())
     fr = list(g["full_rows"])
     if row in fr:
         full = g["logits_full"][fr.index(row)]
@@ -37,42 +64,192 @@ def compare(rep, g, row, tok, logits, tag):
     rep.add(tok, g["token"][row], float(g["margin"][row]), tau, tag=tag)
 
 
-def test_c2_llama8b_decode_batch64():
-    import torch
-    from paged_kv_forward_amd.runtime import Pass, PieRuntime, upload_weights
-    g = golden("c2_decode_8b")
-    wl = synth.workload(2)
-    shape = wl.shape
-    steps = int(g["meta_decode_steps"])
-    checked = list(g["meta_seqs"])
-    say("c2: uploading 8B weights")
+def make_runtime(shape, n_seqs, max_ctx, max_rows, max_readout, pages=None):
+    from paged_kv_forward_amd import _native as N
+    from paged_kv_forward_amd.runtime import PieRuntime, model_desc, upload_weights
+    say("uploading %s weights (%d layers)" % (shape.name, shape.n_layers))
     w = upload_weights(synth.WeightRecipe(shape))
-    n = wl.n_seqs
-    max_ctx = wl.prompt_len[0] + steps + 8
-    page_bytes = shape.n_layers * 2 * shape.n_kv_heads * 16 * shape.head_dim * 2
-    pages = n * ((max_ctx + 15) // 16 + 1)
-    rt = PieRuntime(shape, w, pages * page_bytes, max_rows=4 * 2048, max_seqs=n, max_readout=n,
-                    max_ctx=max_ctx)
+    page_bytes = N.lib().pie_kv_page_bytes(ctypes.byref(model_desc(shape)))
+    if pages is None:
+        pages = n_seqs * ((max_ctx + 15) // 16 + 1)
+    return PieRuntime(shape, w, pages * page_bytes, max_rows=max_rows, max_seqs=n_seqs,
+                      max_readout=max_readout, max_ctx=max_ctx)
+
+
+def decode_case(name, config_id, per_launch):
+    """Batch decode: every sequence prefilled (launches of `per_launch`
+    sequences, readout at the last prompt token), then teacher-fed decode
+    steps over the whole batch, logits written to device memory."""
+    import torch
+    from paged_kv_forward_amd.runtime import Pass
+    g = golden(name)
+    wl = synth.workload(config_id)
+    shape = shape_of(wl, g)
+    tol, tau = bounds(g)
+    steps = int(g["meta_decode_steps"])
+    checked = [int(s) for s in g["meta_seqs"]]
+    n, ctx = wl.n_seqs, wl.prompt_len[0]
+    rt = make_runtime(shape, n, ctx + steps + 8, per_launch * ctx, n)
     ws = [rt.alloc() for _ in range(n)]
     rep = Report()
-    logits_dev = torch.empty((n, shape.vocab), dtype=torch.float32, device="cuda")
-    say("c2: prefill 64 x 2048 in launches of 4 sequences")
-    for b in range(0, n, 4):
-        ss = list(range(b, b + 4))
-        toks, _ = rt.forward([Pass(ws[s], wl.prompt(s), [wl.prompt_len[s] - 1], [(0, 1.0, 0)]) for s in ss],
-                             logits_out=logits_dev[:4])
-        lg = logits_dev[:4].cpu().numpy()
+    logits = torch.empty((n, shape.vocab), dtype=torch.float32, device="cuda")
+    say("%s: prefill %d x %d in launches of %d" % (name, n, ctx, per_launch))
+    for b in range(0, n, per_launch):
+        ss = list(range(b, b + per_launch))
+        toks, _ = rt.forward([Pass(ws[s], wl.prompt(s), [ctx - 1], [(0, 1.0, 0)]) for s in ss],
+                             logits_out=logits[:per_launch])
+        lg = logits[:per_launch].cpu().numpy()
         for j, s in enumerate(ss):
             if s in checked:
-                row = checked.index(s) * (steps + 1)
-                compare(rep, g, row, toks[j], lg[j], ("prefill", s))
-    teach = [synth.teacher_tokens(2, s, steps, shape.vocab) for s in range(n)]
-    for k in range(steps):
-        say("c2: decode step", k + 1)
-        toks, _ = rt.forward([Pass(ws[s], [int(teach[s][k])], [0], [(0, 1.0, 0)]) for s in range(n)],
-                             logits_out=logits_dev)
-        lg = logits_dev.cpu().numpy()
-        for ci, s in enumerate(checked):
-            compare(rep, g, ci * (steps + 1) + k + 1, toks[s], lg[s], ("decode", k + 1, s))
-    rep.check()
+                compare(rep, g, row_of(g, s, 0), toks[j], lg[j], ("prefill", s), tau)
+    teach = [synth.teacher_tokens(config_id, s, steps, shape.vocab) for s in range(n)]
+    for k in range(1, steps + 1):
+        say("%s: decode step %d" % (name, k))
+        toks, _ = rt.forward([Pass(ws[s], [int(teach[s][k - 1])], [0], [(0, 1.0, 0)]) for s in range(n)],
+                             logits_out=logits)
+        lg = logits.cpu().numpy()
+        for s in checked:
+            compare(rep, g, row_of(g, s, k), toks[s], lg[s], ("decode", k, s), tau)
     rt.close()
+    rep.check(tol=tol)
+
+
+def fork_case(name):
+    """Prefix sharing: an 8192-token prefix committed once, forked into 10
+    branches that prefill their own 256-token suffixes in one launch and then
+    decode with Gumbel-max at T = 0.7; no shared page is ever copied."""
+    import torch
+    from paged_kv_forward_amd.runtime import Pass
+    g = golden(name)
+    wl = synth.workload(3)
+    shape = shape_of(wl, g)
+    tol, tau = bounds(g)
+    steps = int(g["meta_decode_steps"])
+    checked = [int(b) for b in g["meta_branches"]]
+    pre = wl.prefix()
+    P, nb, T = len(pre), wl.n_seqs, wl.temperature[0]
+    suffix = wl.prompt_len[0]
+    rt = make_runtime(shape, nb, P + suffix + steps + 8, P, nb)
+    root = rt.alloc()
+    say("%s: prefix %d" % (name, P))
+    rt.forward([Pass(root, pre)])
+    st0 = rt.pool_stats()
+    prefix_pages = list(rt.ws_info(root)["pages"])
+    br = [rt.fork(root) for _ in range(nb)]
+    assert rt.pool_stats()["pages_free"] == st0["pages_free"]
+    for h in br:
+        assert list(rt.ws_info(h)["pages"]) == prefix_pages
+    rep = Report()
+    logits = torch.empty((nb, shape.vocab), dtype=torch.float32, device="cuda")
+    teach = [synth.teacher_tokens(3, b, steps, shape.vocab) for b in range(nb)]
+    for k in range(steps + 1):
+        passes = []
+        for b in range(nb):
+            seed = synth.epilogue_seed(wl.branch_seed[b], k)
+            if k == 0:
+                passes.append(Pass(br[b], wl.prompt(b), [suffix - 1], [(1, T, seed)]))
+            else:
+                passes.append(Pass(br[b], [int(teach[b][k - 1])], [0], [(1, T, seed)]))
+        say("%s: launch %d" % (name, k))
+        toks, _ = rt.forward(passes, logits_out=logits)
+        lg = logits.cpu().numpy()
+        for b in checked:
+            compare(rep, g, row_of(g, b, k), toks[b], lg[b], ("branch", b, k), tau / T)
+    st = rt.pool_stats()
+    assert st["kv_bytes_copied"] == 0
+    # the prefix pages are still shared by every branch; each branch owns only its tail
+    for h in br:
+        assert list(rt.ws_info(h)["pages"][:len(prefix_pages)]) == prefix_pages
+    own = (suffix + steps + 15) // 16
+    assert st["pages_ever_allocated"] == len(prefix_pages) + nb * own
+    rt.close()
+    rep.check(tol=tol)
+
+
+def mix_case(name):
+    """Continuous batching: 8 prompts of 4096 tokens prefilled in 512-token
+    chunks, packed into the same 8 launches as 120 decode rows whose
+    contexts (128..8192 tokens) were prefilled beforehand; per-row epilogue
+    argmax or Gumbel-max (T = 1)."""
+    import torch
+    from paged_kv_forward_amd.runtime import Pass
+    g = golden(name)
+    wl = synth.workload(4)
+    shape = shape_of(wl, g)
+    tol, tau = bounds(g)
+    checked = sorted(set(int(s) for s in g["row_seq"]))
+    n, C = wl.n_seqs, wl.chunk
+    max_ctx = max(wl.prompt_len) + 8 + 8
+    pages = sum((L + 8 + 15) // 16 + 1 for L in wl.prompt_len)
+    rt = make_runtime(shape, n, max_ctx, 8192, n, pages=pages)
+    ws = [rt.alloc() for _ in range(n)]
+    say("%s: prefill of the decode rows' contexts" % name)
+    batch, rows = [], 0
+    for s in range(8, n):
+        L = wl.prompt_len[s]
+        if rows + L > 8192:
+            rt.forward(batch)
+            batch, rows = [], 0
+        batch.append(Pass(ws[s], wl.prompt(s)))
+        rows += L
+    if batch:
+        rt.forward(batch)
+    rep = Report()
+    logits = torch.empty((n, shape.vocab), dtype=torch.float32, device="cuda")
+    teach = {s: synth.teacher_tokens(4, s, 8, shape.vocab) for s in range(8, n)}
+    n_launch = wl.prompt_len[0] // C
+    for k in range(n_launch):
+        passes, ro_seq = [], []
+        for s in range(8):
+            toks = wl.prompt(s)[k * C:(k + 1) * C]
+            if k == n_launch - 1:
+                seed = synth.epilogue_seed(wl.branch_seed[s], k)
+                passes.append(Pass(ws[s], toks, [C - 1], [(wl.epi_kind[s], 1.0, seed)]))
+                ro_seq.append(s)
+            else:
+                passes.append(Pass(ws[s], toks))
+        for s in range(8, n):
+            seed = synth.epilogue_seed(wl.branch_seed[s], k)
+            passes.append(Pass(ws[s], [int(teach[s][k])], [0], [(wl.epi_kind[s], 1.0, seed)]))
+            ro_seq.append(s)
+        say("%s: launch %d (%d rows)" % (name, k, sum(len(p.tokens) for p in passes)))
+        toks, _ = rt.forward(passes, logits_out=logits[:len(ro_seq)])
+        lg = logits[:len(ro_seq)].cpu().numpy()
+        for i, s in enumerate(ro_seq):
+            if s in checked:
+                compare(rep, g, row_of(g, s, k if s >= 8 else n_launch - 1), toks[i], lg[i],
+                        ("mix", s, k), tau)
+    rt.close()
+    rep.check(tol=tol)
+
+
+def test_c2_first2_llama8b_decode_batch64():
+    decode_case("c2_decode_8b_first2", 2, 4)
+
+
+def test_c5_first2_llama70b_decode_e4m3():
+    decode_case("c5_decode_70b_first2", 5, 2)
+
+
+def test_c3_first2_fork_gumbel():
+    fork_case("c3_fork_8b_first2")
+
+
+def test_c4_first2_mix():
+    mix_case("c4_mix_8b_first2")
+
+
+def test_c2_llama8b_decode_batch64():
+    decode_case("c2_decode_8b", 2, 4)
+
+
+def test_c3_fork_gumbel():
+    fork_case("c3_fork_8b")
+
+
+def test_c4_mix():
+    mix_case("c4_mix_8b")
+
+
+def test_c5_llama70b_decode_e4m3():
+    decode_case("c5_decode_70b", 5, 2)
