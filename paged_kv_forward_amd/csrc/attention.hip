@@ -12,7 +12,8 @@
 // same sum): for Q*K^T group g takes head-dim chunks g*STEPS .. g*STEPS+STEPS-1,
 // for P*V group g takes tokens 4g..4g+3 of both pages.
 // Softmax is online (running max and sum per row, in log2 units), in fp32;
-// P enters the MFMA rounded to bf16.
+// P enters the P*V MFMA as two bf16 parts, hi = bf16(P) and lo = bf16(P - hi),
+// so the product sees P to about 16 significant bits.
 //
 // Memory: a wave first loads a slice of its sequence's page table into lane
 // registers (entry base + l in lane l) and reads entries back with readlane,
@@ -196,12 +197,24 @@ __device__ __forceinline__ void compute_pair(const PairRaw<HD, E4M3>& f, const u
     for (int j = 0; j < 8; ++j) ps += p[j];
     l_run[rb] = l_run[rb] * alpha + ps;
     m_run[rb] = m_new;
-    const uint4 pb = make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]),
+    // P as the sum of two bf16 values (hi + lo, about 16 significant bits):
+    // one bf16 rounding of P would move the 8B-shape logits by up to ~0.04.
+    const uint4 ph = make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]),
                                 pack_bf2(p[6], p[7]));
+    const uint32_t hw[4] = {ph.x, ph.y, ph.z, ph.w};
+    float lo[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[2 * j] = p[2 * j] - bf2f(hw[j] & 0xffffu);
+      lo[2 * j + 1] = p[2 * j + 1] - bf2f(hw[j] >> 16);
+    }
+    const uint4 pl = make_uint4(pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(lo[4], lo[5]),
+                                pack_bf2(lo[6], lo[7]));
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       oacc[rb][b] *= alpha;
-      oacc[rb][b] = mfma16(vf[b], pb, oacc[rb][b]);
+      oacc[rb][b] = mfma16(vf[b], ph, oacc[rb][b]);
+      oacc[rb][b] = mfma16(vf[b], pl, oacc[rb][b]);
     }
   }
 }

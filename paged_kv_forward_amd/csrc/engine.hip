@@ -44,7 +44,6 @@ inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 constexpr int GEMM_BN = 128;
 constexpr int GEMM_BK = 64;
-constexpr int MAX_SPLITS = 16;
 constexpr int LM_BN = 128;
 
 // Split-K policy for the small-M (decode) tile: enough workgroups to fill the
@@ -59,7 +58,7 @@ SplitK choose_split(int M, int n_tiles, int K) {
   // and at least 4 chunks of 64 per split.
   const int target = 256;
   int s = (target + n_tiles / 2) / n_tiles;
-  s = std::max(1, std::min(s, MAX_SPLITS));
+  s = std::max(1, std::min(s, pie::SK_MAX_SPLITS));
   int max_by_k = std::max(1, K / (4 * GEMM_BK));
   s = std::min(s, max_by_k);
   int ks = (K + s - 1) / s;
@@ -218,7 +217,7 @@ struct pie_ctx {
   // graphs of the per-call launch sequence, by launch shape
   hipStream_t cap_stream = nullptr;
   std::map<GraphKey, GraphEntry> graphs;
-  bool use_graphs = true;
+  bool use_graphs = false;
   bool capturing = false;
 };
 
@@ -357,17 +356,32 @@ int stage(pie_ctx* c) {
   return PIE_OK;
 }
 
-// Enqueue one call's work on c->cur: metadata upload, every kernel, token
-// copy-back (and the logits copy to a host buffer when asked).
+// Metadata upload (pinned staging -> device), on the caller's stream.
+int upload_meta(pie_ctx* c) {
+  int32_t* dmeta = reinterpret_cast<int32_t*>(c->ws + c->lay.meta);
+  HIP_TRY(c, hipMemcpyAsync(dmeta, c->pinned, c->lay.tokens_out * 4, hipMemcpyHostToDevice, c->stream));
+  return PIE_OK;
+}
+
+// Token copy-back (device -> pinned staging), on the caller's stream.
+int download_tokens(pie_ctx* c) {
+  const int R = c->plan.n_readout;
+  if (R <= 0) return PIE_OK;
+  int32_t* dmeta = reinterpret_cast<int32_t*>(c->ws + c->lay.meta);
+  HIP_TRY(c, hipMemcpyAsync(c->pinned + c->lay.tokens_out, dmeta + c->lay.tokens_out, (size_t)R * 4,
+                            hipMemcpyDeviceToHost, c->stream));
+  return PIE_OK;
+}
+
+// Enqueue every kernel of one call on c->cur (and the logits copy to a host
+// buffer when asked).  The metadata must already be in device memory; the
+// kernels write the token ids to its token slot.
 int enqueue(pie_ctx* c, float* out_logits, int flags) {
   const pie::Plan& p = c->plan;
   const pie_model_desc& d = c->d;
   const Layout& L = c->lay;
   hipStream_t st = c->cur;
-  int32_t* h = c->pinned;
-  const size_t meta_used = L.tokens_out;  // everything before the token output slot
   int32_t* dmeta = reinterpret_cast<int32_t*>(c->ws + L.meta);
-  HIP_TRY(c, hipMemcpyAsync(dmeta, h, meta_used * 4, hipMemcpyHostToDevice, st));
   auto M32 = [&](size_t off) { return dmeta + off; };
 
   float* y = reinterpret_cast<float*>(c->ws + L.y);
@@ -453,7 +467,10 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       g.kv_scale = kvs;
       set_split(g, pie::gemm_n_tiles(pie::EPI_QKV, g.N, tile));
       Timed tm(c, PIE_K_GEMM_QKV);
-      pie::launch_rmsnorm(y, ss, n_ss, c->attn_norm[l], T, d.d_model, d.rms_eps, nullptr, xb, st);
+      // decode-sized calls: the previous layer's down projection already wrote
+      // this layer's normed rows (fused into its split-K reduce)
+      if (!small || l == 0)
+        pie::launch_rmsnorm(y, ss, n_ss, c->attn_norm[l], T, d.d_model, d.rms_eps, nullptr, xb, st);
       g.a = xb;
       g.lda = d.d_model;
       pie::launch_gemm(pie::A_BF16, pie::EPI_QKV, tile, g, st);
@@ -493,6 +510,10 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       g.w[0] = g.w[1] = g.w[2] = c->wo[l];
       g.seg_n0[0] = 0; g.seg_n0[1] = g.seg_n0[2] = g.seg_n0[3] = d.d_model;
       set_split(g, pie::gemm_n_tiles(pie::EPI_RESID, g.N, tile));
+      if (small) {  // and the MLP RMSNorm of the new rows
+        g.next_gain = c->mlp_norm[l];
+        g.x_out = xb;
+      }
       Timed tm(c, PIE_K_GEMM_O);
       pie::launch_gemm(pie::A_BF16, pie::EPI_RESID, tile, g, st);
     }
@@ -507,7 +528,8 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       g.h_out = hb;
       set_split(g, pie::gemm_n_tiles(pie::EPI_SWIGLU, g.N, tile));
       Timed tm(c, PIE_K_GEMM_GATEUP);
-      pie::launch_rmsnorm(y, ss, n_ss, c->mlp_norm[l], T, d.d_model, d.rms_eps, nullptr, xb, st);
+      if (!small)  // decode-sized: the O projection's reduce wrote the normed rows
+        pie::launch_rmsnorm(y, ss, n_ss, c->mlp_norm[l], T, d.d_model, d.rms_eps, nullptr, xb, st);
       g.a = xb;
       g.lda = d.d_model;
       pie::launch_gemm(pie::A_BF16, pie::EPI_SWIGLU, tile, g, st);
@@ -523,6 +545,10 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       g.w[0] = g.w[1] = g.w[2] = c->wd[l];
       g.seg_n0[0] = 0; g.seg_n0[1] = g.seg_n0[2] = g.seg_n0[3] = d.d_model;
       set_split(g, pie::gemm_n_tiles(pie::EPI_RESID, g.N, tile));
+      if (small && l + 1 < d.n_layers) {  // and the next layer's attention RMSNorm
+        g.next_gain = c->attn_norm[l + 1];
+        g.x_out = xb;
+      }
       Timed tm(c, PIE_K_GEMM_DOWN);
       pie::launch_gemm(pie::A_BF16, pie::EPI_RESID, tile, g, st);
     }
@@ -565,7 +591,6 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       pie::launch_argmax_reduce(g.tile_best, g.tile_idx, vt, R, dtok, st);
     }
     if ((rc = check_launch(c, flags, "lm_head"))) return rc;
-    HIP_TRY(c, hipMemcpyAsync(h + L.tokens_out, dtok, (size_t)R * 4, hipMemcpyDeviceToHost, st));
     if (out_logits && !(flags & PIE_FLAG_LOGITS_DEVICE))
       HIP_TRY(c, hipMemcpyAsync(out_logits, logits, (size_t)R * d.vocab * 4, hipMemcpyDeviceToHost, st));
   }
@@ -613,6 +638,7 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
       }
     }
   }
+  if ((rc = upload_meta(c))) return rc;
   if (ge && ge->exec) {
     HIP_TRY(c, hipGraphLaunch(ge->exec, c->stream));
   } else {
@@ -622,6 +648,7 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
     rc = enqueue(c, out_logits, flags);
     if (rc) return rc;
   }
+  if ((rc = download_tokens(c))) return rc;
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   if (c->prof_mask) collect_profile(c, c->sink);
   if (p.n_readout > 0) std::memcpy(out_tokens, c->pinned + c->lay.tokens_out, (size_t)p.n_readout * 4);
@@ -718,8 +745,10 @@ int pie_init(const pie_model_desc* desc, const pie_weights* w, void* kv_arena, s
   if (e != hipSuccess) { delete c; return set_err(PIE_EHIP, std::string("pie_init: hipHostMalloc: ") + hipGetErrorString(e)); }
   // a default-priority stream of our own, used only to capture launch graphs
   if (hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess) c->cap_stream = nullptr;
-  const char* ng = std::getenv("PIE_NO_GRAPH");
-  c->use_graphs = !(ng && ng[0] && ng[0] != '0');
+  // Graph replay is opt-in: on the measured ROCm stack a replay of the
+  // ~300-launch decode sequence started later than direct launches did.
+  const char* ug = std::getenv("PIE_GRAPHS");
+  c->use_graphs = ug && ug[0] && ug[0] != '0';
   c->cur = c->stream;
   *out = c;
   return PIE_OK;

@@ -45,6 +45,10 @@ struct GemmArgs {
   // EPI_RESID
   float* y_out;     // [rows][ldy]
   float* ss_out;    // [rows][n_ss]
+  // EPI_RESID with TILE_SKINNY only: when x_out is set, also the RMSNorm that
+  // follows, x_out[m][:] = bf16(rmsnorm(y[m][:]) * next_gain) (N = d_model)
+  const uint16_t* next_gain;
+  uint16_t* x_out;
   // EPI_SWIGLU
   uint16_t* h_out;  // [M][N] bf16
   // EPI_QKV
@@ -69,6 +73,9 @@ struct GemmArgs {
 // Tile configurations.  TILE_SKINNY: M <= 64 with a bf16 A operand, 128 output
 // columns per workgroup, weights streamed through registers (decode).
 enum GemmTile { TILE_64x128 = 0, TILE_128x128 = 1, TILE_SKINNY = 2 };
+
+// Most K splits of one skinny GEMM.
+constexpr int SK_MAX_SPLITS = 16;
 
 void launch_gemm(int amode, int epi, int tile, const GemmArgs& g, hipStream_t stream);
 

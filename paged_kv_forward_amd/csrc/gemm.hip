@@ -449,47 +449,106 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   if (g.splits > 1) {
     const size_t ld = (size_t)gridDim.x * SK_BN;
     float* part = g.partial + (size_t)split * 64 * ld + (size_t)t * SK_BN;
-    for (int idx = tid; idx < 64 * SK_BN; idx += SK_NT) {
-      const int row = idx / SK_BN, col = idx % SK_BN;
-      part[(size_t)row * ld + col] = sC[row * SK_LDC + col];
+    for (int idx = tid; idx < 64 * SK_BN / 4; idx += SK_NT) {
+      const int row = idx / (SK_BN / 4), col = (idx % (SK_BN / 4)) * 4;
+      *reinterpret_cast<float4*>(&part[(size_t)row * ld + col]) =
+          *reinterpret_cast<const float4*>(&sC[row * SK_LDC + col]);
     }
     return;
   }
   epilogue<EPI, SK_BN, SK_NT>(g, sC, SK_LDC, 0, 64, t);
 }
 
-// Split-K reduce of the skinny kernel: one workgroup per 16 rows of a 64 x 128
-// tile; each thread sums 8 elements, the 8 loads of one split in flight
-// together, splits added in split order; then the epilogue on those rows.
+// Split-K reduce of the skinny kernel: one workgroup per 8 rows of a 64 x 128
+// tile; each thread owns 4 consecutive columns of one row and issues the loads
+// of every split before it adds them, in split order; then the epilogue on
+// those rows.
+constexpr int SK_RED_ROWS = 8;
 template <int EPI>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, int n_tiles) {
-  constexpr int ROWS = 16, PER = ROWS * SK_BN / 256;
-  __shared__ __attribute__((aligned(16))) float sC[ROWS * SK_LDC];
-  const int t = blockIdx.x, r0 = blockIdx.y * ROWS;
+  __shared__ __attribute__((aligned(16))) float sC[SK_RED_ROWS * SK_LDC];
+  const int t = blockIdx.x, r0 = blockIdx.y * SK_RED_ROWS;
+  const int row = threadIdx.x / (SK_BN / 4), col = (threadIdx.x % (SK_BN / 4)) * 4;
   const size_t ld = (size_t)n_tiles * SK_BN, zs = 64 * ld;
-  const float* base = g.partial + (size_t)r0 * ld + (size_t)t * SK_BN;
-  float v[PER];
-  size_t off[PER];
+  const float* base = g.partial + (size_t)(r0 + row) * ld + (size_t)t * SK_BN + col;
+  float4 x[SK_MAX_SPLITS];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = threadIdx.x + 256 * i, row = e / SK_BN, col = e % SK_BN;
-    off[i] = (size_t)row * ld + col;
-    v[i] = 0.f;
+  for (int z = 0; z < SK_MAX_SPLITS; ++z)
+    x[z] = z < g.splits ? *reinterpret_cast<const float4*>(base + z * zs) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 v = x[0];
+#pragma unroll
+  for (int z = 1; z < SK_MAX_SPLITS; ++z) {
+    v.x += x[z].x;
+    v.y += x[z].y;
+    v.z += x[z].z;
+    v.w += x[z].w;
   }
-  for (int z = 0; z < g.splits; ++z) {
-    float x[PER];
+  *reinterpret_cast<float4*>(&sC[row * SK_LDC + col]) = v;
+  __syncthreads();
+  epilogue<EPI, SK_BN, 256>(g, sC, SK_LDC, r0, SK_RED_ROWS, t);
+}
+
+// Split-K reduce of an EPI_RESID skinny GEMM fused with the RMSNorm that
+// follows it: one workgroup per row holds the whole new row of y.  It adds
+// the partials in split order, writes y and the per-64-column sums of
+// squares exactly as the EPI_RESID epilogue does, sums those partials in
+// column order as rmsnorm_kernel does, and writes the normed bf16 row.
+constexpr int RN_NT = 512;
+__global__ __launch_bounds__(RN_NT) void skinny_reduce_norm_kernel(GemmArgs g, int n_tiles) {
+  extern __shared__ __attribute__((aligned(16))) float s_row[];  // [N] new y, then [N / 64] sums
+  __shared__ float s_r;
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int N = g.N, n_grp = N / 64;
+  float* s_ssq = s_row + N;
+  const size_t ld = (size_t)n_tiles * SK_BN, zs = 64 * ld;
+  for (int c = tid * 4; c < N; c += RN_NT * 4) {
+    const float* p = g.partial + (size_t)m * ld + c;
+    float4 x[SK_MAX_SPLITS];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) x[i] = base[z * zs + off[i]];
+    for (int z = 0; z < SK_MAX_SPLITS; ++z)
+      x[z] = z < g.splits ? *reinterpret_cast<const float4*>(p + z * zs) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 v = x[0];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] += x[i];
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = threadIdx.x + 256 * i, row = e / SK_BN, col = e % SK_BN;
-    sC[row * SK_LDC + col] = v[i];
+    for (int z = 1; z < SK_MAX_SPLITS; ++z) {
+      v.x += x[z].x;
+      v.y += x[z].y;
+      v.z += x[z].z;
+      v.w += x[z].w;
+    }
+    float4* yp = reinterpret_cast<float4*>(g.y_out + (size_t)m * g.ldy + c);
+    const float4 yo = *yp;
+    const float4 yn = make_float4(yo.x + v.x, yo.y + v.y, yo.z + v.z, yo.w + v.w);
+    *yp = yn;
+    *reinterpret_cast<float4*>(&s_row[c]) = yn;
   }
   __syncthreads();
-  epilogue<EPI, SK_BN, 256>(g, sC, SK_LDC, r0, ROWS, t);
+  for (int grp = wave; grp < n_grp; grp += RN_NT / 64) {
+    const float v = s_row[grp * 64 + lane];
+    const float sq = wave_sum(v * v);
+    if (lane == 0) {
+      g.ss_out[(size_t)m * g.n_ss + grp] = sq;
+      s_ssq[grp] = sq;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float sum = 0.f;
+    for (int c = 0; c < n_grp; ++c) sum += s_ssq[c];
+    s_r = 1.0f / sqrtf(sum / (float)N + g.eps);
+  }
+  __syncthreads();
+  const float r = s_r;
+  for (int k = tid * 8; k < N; k += RN_NT * 8) {
+    const float4 a = *reinterpret_cast<const float4*>(&s_row[k]);
+    const float4 b = *reinterpret_cast<const float4*>(&s_row[k + 4]);
+    const uint4 gw = *reinterpret_cast<const uint4*>(g.next_gain + k);
+    uint4 o;
+    o.x = pack_bf2(a.x * r * bf2f(gw.x & 0xffffu), a.y * r * bf2f(gw.x >> 16));
+    o.y = pack_bf2(a.z * r * bf2f(gw.y & 0xffffu), a.w * r * bf2f(gw.y >> 16));
+    o.z = pack_bf2(b.x * r * bf2f(gw.z & 0xffffu), b.y * r * bf2f(gw.z >> 16));
+    o.w = pack_bf2(b.z * r * bf2f(gw.w & 0xffffu), b.w * r * bf2f(gw.w >> 16));
+    *reinterpret_cast<uint4*>(g.x_out + (size_t)m * g.N + k) = o;
+  }
 }
 
 // x[m, :] = bf16(y[m, :] * rsqrt(sum_sq[m] / d + eps) * gain), one workgroup per row.
@@ -562,8 +621,16 @@ static void launch_skinny(const GemmArgs& g, hipStream_t st) {
   const int n_tiles = gemm_n_tiles(EPI, g.N, TILE_SKINNY);
   hipLaunchKernelGGL((gemm_skinny_kernel<EPI>), dim3(n_tiles, g.splits > 1 ? g.splits : 1), dim3(SK_NT), 0,
                      st, g);
-  if (g.splits > 1)
-    hipLaunchKernelGGL((skinny_reduce_kernel<EPI>), dim3(n_tiles, (g.M + 15) / 16), dim3(256), 0, st, g, n_tiles);
+  const bool norm = EPI == EPI_RESID && g.x_out;
+  if (g.splits > 1 && norm) {
+    const size_t lds = ((size_t)g.N + g.N / 64) * 4;
+    hipLaunchKernelGGL(skinny_reduce_norm_kernel, dim3(g.M), dim3(RN_NT), lds, st, g, n_tiles);
+  } else if (g.splits > 1) {
+    hipLaunchKernelGGL((skinny_reduce_kernel<EPI>), dim3(n_tiles, (g.M + SK_RED_ROWS - 1) / SK_RED_ROWS),
+                       dim3(256), 0, st, g, n_tiles);
+  }
+  if (g.splits <= 1 && norm)
+    launch_rmsnorm(g.y_out, g.ss_out, g.n_ss, g.next_gain, g.M, g.N, g.eps, nullptr, g.x_out, st);
 }
 
 template <int BM, int BN>

@@ -55,12 +55,15 @@ def compare(rep, g, row, tok, logits, tag, tau):
     divided by the temperature for Gumbel-max rows)."""
     sub = logits[g["subset_idx"]]
     err = np.abs(sub - g["logits_subset"][row])
-    rep.max_err = max(rep.max_err, float(err.max()))
+    row_max = float(err.max())
     rep.sum_err += float(err.mean())
     fr = list(g["full_rows"])
     if row in fr:
         full = g["logits_full"][fr.index(row)]
-        rep.max_err = max(rep.max_err, float(np.max(np.abs(logits - full))))
+        row_max = max(row_max, float(np.max(np.abs(logits - full))))
+    rep.max_err = max(rep.max_err, row_max)
+    say("  row %s: max|dlogit| %.4f mean %.5f token %d/%d margin %.4f" %
+        (tag, row_max, float(err.mean()), int(tok), int(g["token"][row]), float(g["margin"][row])))
     rep.add(tok, g["token"][row], float(g["margin"][row]), tau, tag=tag)
 
 

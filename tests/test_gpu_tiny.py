@@ -231,8 +231,8 @@ def test_graph_replays_match_direct_launches(torch_cuda, monkeypatch):
     prompts = [synth.prompt_tokens(1, 50 + s, 24 + s, shape.vocab) for s in range(3)]
     feeds = [synth.teacher_tokens(1, s, 6, shape.vocab) for s in range(3)]
     runs = []
-    for no_graph in ("1", "0"):
-        monkeypatch.setenv("PIE_NO_GRAPH", no_graph)
+    for graphs in ("0", "1"):
+        monkeypatch.setenv("PIE_GRAPHS", graphs)
         rt = make_runtime(shape, recipe, torch_cuda)
         ws = [rt.alloc() for _ in range(3)]
         out = []
