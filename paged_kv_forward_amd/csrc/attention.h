@@ -3,9 +3,12 @@
 // thinks", section 4).
 //
 // KV page layout, per layer and page (elements of the KV dtype):
-//   K: [n_kv_heads][page_size][head_dim]     token-major
+//   K: [n_kv_heads][head_dim / 8][page_size][8]   head-dim groups of 8, token
+//                                            within a group: the Q*K^T MFMA
+//                                            operand of a k-step is one
+//                                            contiguous run
 //   V: [n_kv_heads][head_dim][page_size]     transposed, so that the P*V
-//                                            MFMA reads 8 consecutive tokens
+//                                            MFMA reads consecutive tokens
 // Per layer the pages follow each other (page_stride elements apart); layers
 // follow each other (n_pages * page_stride apart).
 #pragma once

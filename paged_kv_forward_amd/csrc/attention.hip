@@ -9,13 +9,16 @@
 // query row for 8 tokens, exactly the B operand of the P*V MFMA, so P never
 // leaves registers.  The 8 k-slots of a lane group are matched between the two
 // operands of each MFMA (any fixed assignment of k values to slots gives the
-// same sum): for Q*K^T group g takes head-dim chunks g*STEPS .. g*STEPS+STEPS-1,
-// for P*V group g takes tokens 4g..4g+3 of both pages.
+// same sum): in k-step i of Q*K^T group g takes head-dim group 4i + g (8
+// values), for P*V group g takes tokens 4g..4g+3 of both pages.
 // Softmax is online (running max and sum per row, in log2 units), in fp32;
 // P enters the P*V MFMA as two bf16 parts, hi = bf16(P) and lo = bf16(P - hi),
 // so the product sees P to about 16 significant bits.
 //
-// Memory: a wave first loads a slice of its sequence's page table into lane
+// Memory: K and V are read with streaming (non-temporal) loads, each load
+// instruction covering whole 128-byte lines (K's page layout makes a k-step's
+// operand one contiguous run).  A wave first loads a slice of its sequence's
+// page table into lane
 // registers (entry base + l in lane l) and reads entries back with readlane,
 // so page ids are never a dependent load in the inner loop.  K and V come
 // through a wave-uniform buffer descriptor per page (a missing second page of
@@ -31,6 +34,7 @@
 namespace pie {
 
 constexpr int PS = 16;  // page size
+
 constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, uint32_t bytes) {
@@ -89,19 +93,20 @@ __device__ __forceinline__ void load_pair(PairRaw<HD, E4M3>& f, const AttnArgs& 
   for (int p = 0; p < 2; ++p) {
 #pragma unroll
     for (int i = 0; i < STEPS; ++i) {
-      const uint32_t off = kofs + ((uint32_t)t * HD + (uint32_t)(g * STEPS + i) * 8) * EB;
+      // head-dim group 4i + g of token t: one contiguous run of 64 x 8 elements per step
+      const uint32_t off = kofs + ((uint32_t)i * 64 + (uint32_t)lane) * 8 * EB;
       if constexpr (E4M3)
-        f.k[p][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r[p], off, 0, 0));
+        f.k[p][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r[p], off, 0, CPOL_NT));
       else
-        f.k[p][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r[p], off, 0, 0));
+        f.k[p][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r[p], off, 0, CPOL_NT));
     }
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       const uint32_t off = vofs + ((uint32_t)(16 * b + t) * PS + 4 * g) * EB;
       if constexpr (E4M3)
-        f.v[p][b] = __builtin_amdgcn_raw_buffer_load_b32(r[p], off, 0, 0);
+        f.v[p][b] = __builtin_amdgcn_raw_buffer_load_b32(r[p], off, 0, CPOL_NT);
       else
-        f.v[p][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r[p], off, 0, 0));
+        f.v[p][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r[p], off, 0, CPOL_NT));
     }
   }
 }
@@ -249,7 +254,7 @@ __device__ __forceinline__ void load_q(uint4 (&qf)[HD / 32], const uint16_t* qro
   constexpr int STEPS = HD / 32;
 #pragma unroll
   for (int i = 0; i < STEPS; ++i)
-    qf[i] = ok ? *reinterpret_cast<const uint4*>(qrow + (g * STEPS + i) * 8) : make_uint4(0, 0, 0, 0);
+    qf[i] = ok ? *reinterpret_cast<const uint4*>(qrow + (4 * i + g) * 8) : make_uint4(0, 0, 0, CPOL_NT);
 }
 
 // ---------------------------------------------------------------- decode

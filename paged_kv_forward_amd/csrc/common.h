@@ -10,6 +10,12 @@ namespace pie {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Cache-policy operand of the raw buffer loads: non-temporal (streaming).
+// Data read once per call (weights of the decode GEMMs, KV pages) bypasses
+// the normal L2 retention; a plain streaming read measured ~7.0 TB/s with it
+// against ~6.2 TB/s without.
+constexpr int CPOL_NT = 2;
+
 // ---------------------------------------------------------------- formats
 
 // float32 -> bf16 bits, round to nearest even (NaN stays NaN).

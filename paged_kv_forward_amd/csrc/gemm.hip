@@ -93,16 +93,19 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int
         } else {
           int kvh = (n0 - qw + c1) / hd;
           int sl = g.slot[m], page = sl / P, off = sl % P;
-          size_t base = (size_t)page * g.page_stride + (size_t)kvh * P * hd + (size_t)off * hd;
+          // K page layout [kv head][hd / 8][token][8]
+          size_t base = (size_t)page * g.page_stride + (size_t)kvh * P * hd + (size_t)off * 8;
+          const size_t i1 = base + (size_t)(dd >> 3) * P * 8 + (dd & 7);
+          const size_t i2 = base + (size_t)((dd + hd2) >> 3) * P * 8 + ((dd + hd2) & 7);
           if (g.kv_e4m3) {
             float s = g.kv_scale[kvh];
             uint8_t* kv = reinterpret_cast<uint8_t*>(g.kv_layer);
-            kv[base + dd] = f2e4m3(o1 / s);
-            kv[base + dd + hd2] = f2e4m3(o2 / s);
+            kv[i1] = f2e4m3(o1 / s);
+            kv[i2] = f2e4m3(o2 / s);
           } else {
             uint16_t* kv = reinterpret_cast<uint16_t*>(g.kv_layer);
-            kv[base + dd] = f2bf(o1);
-            kv[base + dd + hd2] = f2bf(o2);
+            kv[i1] = f2bf(o1);
+            kv[i2] = f2bf(o2);
           }
         }
       }
@@ -342,29 +345,41 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 // weight stream.  A workgroup of 8 waves computes a 64 x 128 output tile over
 // its K range in 64-wide chunks; wave w owns output columns 16w .. 16w+15.
 //  - Weights: each lane loads its row's chunk (k-groups g and 4+g of the
-//    chunk, the MFMA B layout) into a ring of SK_DEPTH chunks, so several
-//    chunks of loads are always in flight.
-//  - Activations: the 64 x 64 chunk, the same for all waves, travels in the
-//    same ring (one 16-byte piece per thread) and is staged through a
-//    double-buffered LDS tile, one barrier per chunk.
+//    chunk, the MFMA B layout) into a ring of SK_DEPTH chunks with streaming
+//    loads, so several chunks are always in flight.
+//  - Activations: staged in LDS a group of SK_DEPTH chunks (64 x 512) at a
+//    time, double-buffered.  The next group's pieces are loaded into
+//    registers at the start of a group and written to LDS at its end, so
+//    there is one barrier per group and waiting for them never drains the
+//    weight ring.
 //  - All loads are raw buffer loads with wave-uniform descriptors: a masked
 //    load uses an out-of-range offset and reads zeros (the hardware bounds
 //    check), so the loop has no branches and the compiler waits for exactly
 //    the chunk it consumes.
-constexpr int SK_BN = 128, SK_NT = 512, SK_KC = 64, SK_DEPTH = 8, SK_LDX = SK_KC + 8, SK_LDC = SK_BN + 4;
+constexpr int SK_BN = 128, SK_NT = 512, SK_KC = 64, SK_DEPTH = 8, SK_LDC = SK_BN + 4;
+constexpr int SK_GK = SK_KC * SK_DEPTH;          // K of one activation group (512)
+constexpr int SK_LDX = SK_GK + 8;                // bf16 per LDS row (16-byte pad)
+constexpr int SK_XP = 64 * SK_GK / 8 / SK_NT;    // 16-byte activation pieces per thread per group (8)
+constexpr int SK_LDS = 2 * 64 * SK_LDX * 2 > 64 * SK_LDC * 4 ? 2 * 64 * SK_LDX * 2 : 64 * SK_LDC * 4;
 constexpr uint32_t OOB = 0xFFFFFFF0u;
+#ifndef SK_WPOL
+#define SK_WPOL 0
+#endif
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+template <int CPOL = 0>
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
 }
 
 template <int EPI>
 __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][64 * SK_LDX];
-  __shared__ __attribute__((aligned(16))) float sC[64 * SK_LDC];
+  // activation groups (two buffers), later reused for the output tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SK_LDS];
+  uint16_t* sX = reinterpret_cast<uint16_t*>(smem);
+  float* sC = reinterpret_cast<float*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), gq = lane >> 4, r16 = lane & 15;
   const int t = blockIdx.x, split = blockIdx.y;
   const int kb = g.splits > 1 ? split * g.k_split : 0;
@@ -390,20 +405,30 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(g.a, (uint32_t)((size_t)g.M * g.lda * 2));
   const bool wok = wrow < wrows;
   const uint32_t wbase = (uint32_t)wrow * (uint32_t)g.K;
-  const int xr = tid >> 3, xk = (tid & 7) * 8;  // this thread's activation piece
-  const bool xok = xr < g.M;
+  // this thread's activation pieces of a group: rows xr0 + 8i, columns xk .. xk + 7
+  const int xr0 = tid / (SK_GK / 8), xk = (tid % (SK_GK / 8)) * 8;
 
-  struct Slot {
-    uint4 w0, w1, x;
+  struct WSlot {
+    uint4 w0, w1;
   };
-  auto load = [&](Slot& sl, int j) {
-    const int k0 = kb + j * SK_KC;
-    const bool live = j < nc;
-    const int kw = k0 + gq * 8;
-    sl.w0 = bload16(wrs, live && wok && kw < ke ? (wbase + (uint32_t)kw) * 2u : OOB);
-    sl.w1 = bload16(wrs, live && wok && kw + 32 < ke ? (wbase + (uint32_t)(kw + 32)) * 2u : OOB);
-    const int kx = k0 + xk;
-    sl.x = bload16(xrs, live && xok && kx < ke ? (uint32_t)(xr * g.lda + kx) * 2u : OOB);
+  auto load_w = [&](WSlot& sl, int j) {
+    const int kw = kb + j * SK_KC + gq * 8;
+    const bool live = j < nc && wok;
+    sl.w0 = bload16<SK_WPOL>(wrs, live && kw < ke ? (wbase + (uint32_t)kw) * 2u : OOB);
+    sl.w1 = bload16<SK_WPOL>(wrs, live && kw + 32 < ke ? (wbase + (uint32_t)(kw + 32)) * 2u : OOB);
+  };
+  auto load_x = [&](uint4 (&xv)[SK_XP], int gi) {
+    const int kx = kb + gi * SK_GK + xk;
+#pragma unroll
+    for (int i = 0; i < SK_XP; ++i) {
+      const int r = xr0 + 8 * i;
+      xv[i] = bload16(xrs, r < g.M && kx < ke ? (uint32_t)(r * g.lda + kx) * 2u : OOB);
+    }
+  };
+  auto store_x = [&](const uint4 (&xv)[SK_XP], int buf) {
+    uint16_t* X = sX + buf * 64 * SK_LDX;
+#pragma unroll
+    for (int i = 0; i < SK_XP; ++i) *reinterpret_cast<uint4*>(&X[(xr0 + 8 * i) * SK_LDX + xk]) = xv[i];
   };
 
   f32x4 acc[4];
@@ -413,34 +438,37 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   if (nc > 0) {
     // Whole groups of SK_DEPTH chunks, with no branches inside a group:
     // chunks past nc load zeros (out-of-range offsets) and add nothing.
-    // Straight-line code lets the compiler wait for exactly the slot it is
-    // about to consume.
-    Slot ring[SK_DEPTH];
+    WSlot ring[SK_DEPTH];
 #pragma unroll
-    for (int j = 0; j < SK_DEPTH; ++j) load(ring[j], j);
+    for (int j = 0; j < SK_DEPTH; ++j) load_w(ring[j], j);
+    uint4 xv[SK_XP];
+    load_x(xv, 0);
+    store_x(xv, 0);
+    lds_barrier();
     const int ngroups = (nc + SK_DEPTH - 1) / SK_DEPTH;
     for (int gi = 0; gi < ngroups; ++gi) {
+      load_x(xv, gi + 1);  // the next group, in flight during this one
+      const uint16_t* X = sX + (gi & 1) * 64 * SK_LDX;
 #pragma unroll
       for (int j = 0; j < SK_DEPTH; ++j) {
-        const int c = gi * SK_DEPTH + j;
-        uint16_t* X = sX[j & 1];
-        *reinterpret_cast<uint4*>(&X[xr * SK_LDX + xk]) = ring[j].x;
-        lds_barrier();
         uint4 af[2][4];  // all eight A fragments in flight before the first MFMA
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int a = 0; a < 4; ++a)
-            af[ks][a] = *reinterpret_cast<const uint4*>(&X[(a * 16 + r16) * SK_LDX + ks * 32 + gq * 8]);
+            af[ks][a] = *reinterpret_cast<const uint4*>(&X[(a * 16 + r16) * SK_LDX + j * SK_KC + ks * 32 + gq * 8]);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int a = 0; a < 4; ++a) acc[a] = mfma16(af[ks][a], ks ? ring[j].w1 : ring[j].w0, acc[a]);
-        load(ring[j], c + SK_DEPTH);
+        load_w(ring[j], (gi + 1) * SK_DEPTH + j);
       }
+      store_x(xv, (gi + 1) & 1);  // that buffer was last read in group gi - 1
+      lds_barrier();
     }
   }
 
+  // the loop ended with a barrier: the activation buffers are free for sC
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
