@@ -17,15 +17,27 @@ import numpy as np
 TAU_LOGIT = 2e-2
 TOL_LOGITS = 2e-2
 
-# Full depth (32 or 80 random-init layers): a one-ulp bf16 change in 0.1 % of
-# the embedding values moves the oracle's own logits by up to ~0.19 (largest)
-# and ~0.03 (mean) at the 8B shape (tests/golden/conditioning.py).  Any
-# implementation that sums in another order than the fp64 oracle differs from
-# it by that much, so at full depth the bounds are set from that measurement:
-# logits within twice the largest measured change, and tokens compared where
-# the oracle's top-2 margin exceeds the largest measured change.
-TOL_FULL_DEPTH = 0.4
-TAU_FULL_DEPTH = 0.2
+# At the 8B and 70B widths the 2e-2 bounds lie below the noise floor of
+# float32 accumulation itself: the oracle run twice -- as is, and with its
+# weight products taken in float32 -- differs by more than 2e-2 in the logits
+# already at 2 layers (tests/golden/conditioning.py writes the measured
+# difference to tests/golden/conditioning_<name>.json).  The GPU sums in
+# float32, so for those configurations the bounds are set from that
+# measurement: logits within twice the twin's largest difference, and tokens
+# compared where the oracle's top-2 margin is at least the twin's largest
+# difference.
+NOISE_FACTOR = 2.0
+
+
+def noise_bounds(conditioning_jsons):
+    """(logit tolerance, token margin) from the measured float32-twin noise of
+    the given conditioning files (the largest of them), never below 2e-2."""
+    import json
+    twin = 0.0
+    for path in conditioning_jsons:
+        with open(path) as f:
+            twin = max(twin, float(json.load(f)["max_abs_dlogit"]))
+    return max(TOL_LOGITS, NOISE_FACTOR * twin), max(TAU_LOGIT, twin)
 
 
 def say(*a):

@@ -290,3 +290,27 @@ def test_working_set_churn_keeps_pool_consistent():
     st = rt.pool_stats()
     assert st["pages_free"] == st["pages_total"] and st["kv_bytes_copied"] == 0
     rt.close()
+
+
+def test_noise_bounds_rule(tmp_path):
+    """Full-size parity bounds: twice the largest measured float32-twin
+    difference for logits, the difference itself for the token margin, never
+    below the 2e-2 of the tiny configuration."""
+    import json
+    from tests.parity import noise_bounds
+    a, b = tmp_path / "a.json", tmp_path / "b.json"
+    a.write_text(json.dumps({"max_abs_dlogit": 0.031}))
+    b.write_text(json.dumps({"max_abs_dlogit": 0.004}))
+    tol, tau = noise_bounds([str(a), str(b)])
+    assert abs(tol - 0.062) < 1e-12 and abs(tau - 0.031) < 1e-12
+    assert noise_bounds([str(b)]) == (2e-2, 2e-2)
+
+
+def test_stored_conditioning_files_are_complete():
+    import glob
+    import json
+    for path in glob.glob(os.path.join(ROOT, "tests", "golden", "conditioning_*.json")):
+        d = json.load(open(path))
+        for k in ("model", "n_layers", "context", "max_abs_dlogit", "mean_abs_dlogit", "twin"):
+            assert k in d, (path, k)
+        assert 0 < d["mean_abs_dlogit"] <= d["max_abs_dlogit"] < 1.0
