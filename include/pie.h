@@ -80,8 +80,12 @@ typedef struct pie_model_desc {
   int32_t page_size;
 } pie_model_desc;
 
-/* Weights: caller-owned DEVICE pointers to bf16 tensors, row-major with the
- * checkpoint layout [out][in] ("Write a model in Poem", section 3 Weights).
+/* Weights: caller-owned DEVICE pointers to bf16 tensors ("Write a model in
+ * Poem", section 3 Weights: the checkpoint layout is [out][in]).
+ *  - embed, final_norm and the norm gains: plain row-major, as in the checkpoint.
+ *  - the projections wq, wk, wv, wo, w_gate, w_up, w_down and lm_head: the
+ *    library's tiled layout, made from the [out][in] tensor by pie_pack_weight
+ *    (pie_packed_weight_bytes gives its size).
  * The per-layer members are HOST arrays of n_layers device pointers; the
  * library copies the pointer arrays during pie_init. */
 typedef struct pie_weights {
@@ -109,6 +113,21 @@ typedef struct pie_limits {
   int32_t max_readout; /* readout rows per call                               */
   int32_t max_ctx;     /* tokens in one working set, including the new ones  */
 } pie_limits;
+
+/* Tiled weight layout of the projections and lm_head.  An [n][k] bf16 matrix
+ * (row-major, the checkpoint's [out][in]) is zero-padded to n and k rounded
+ * up to 64 and stored as 8 KiB blocks: block (r / 64, c / 64) sits at block
+ * index (r / 64) * ceil(k / 64) + c / 64 and holds its 64 x 64 elements as
+ * [4 panels of 16 rows][2 halves of 32 columns][4 groups of 8 columns]
+ * [16 rows][8 columns].  A decode GEMM then reads every weight tile in
+ * address order.  Returns the packed size in bytes (0 if n or k <= 0). */
+size_t pie_packed_weight_bytes(int32_t n, int32_t k);
+
+/* Convert one weight matrix to the tiled layout: src is DEVICE bf16 [n][k]
+ * row-major, dst DEVICE memory of pie_packed_weight_bytes(n, k) bytes; they
+ * must not overlap.  Runs on hip_stream (NULL = the null stream) and
+ * synchronises it.  Needs no context.  Errors: PIE_EINVAL, PIE_EHIP. */
+int pie_pack_weight(const void* src, void* dst, int32_t n, int32_t k, void* hip_stream);
 
 /* Bytes of one KV page over all layers (K and V, every KV head, page_size tokens). */
 size_t pie_kv_page_bytes(const pie_model_desc* desc);

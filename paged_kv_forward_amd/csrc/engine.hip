@@ -895,4 +895,22 @@ int pie_debug_philox(pie_ctx* c, uint64_t seed, uint32_t lane, uint32_t v0, int3
   return PIE_OK;
 }
 
+size_t pie_packed_weight_bytes(int32_t n, int32_t k) {
+  if (n <= 0 || k <= 0) return 0;
+  return pie::packed_elems(n, k) * 2;
+}
+
+int pie_pack_weight(const void* src, void* dst, int32_t n, int32_t k, void* hip_stream) {
+  if (!src || !dst || n <= 0 || k <= 0) return set_err(PIE_EINVAL, "pie_pack_weight: bad arguments");
+  const size_t src_bytes = (size_t)n * k * 2, dst_bytes = pie::packed_elems(n, k) * 2;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + dst_bytes && b < a + src_bytes) return set_err(PIE_EINVAL, "pie_pack_weight: src and dst overlap");
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  pie::launch_pack_weight(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), n, k, st);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return set_err(PIE_EHIP, std::string("pie_pack_weight: ") + hipGetErrorString(e));
+  return PIE_OK;
+}
+
 }  // extern "C"

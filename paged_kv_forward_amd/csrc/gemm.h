@@ -19,6 +19,24 @@
 namespace pie {
 
 enum { A_BF16 = 0, A_NORM = 1 };
+
+// Tiled ("packed") layout of the projection and lm_head weights.  An [N][K]
+// bf16 matrix is zero-padded to Np = N rounded up to 64 and Kp = K rounded up
+// to 64 and stored as 8 KiB blocks, block (n / 64, k / 64) at index
+// (n / 64) * (Kp / 64) + k / 64, each block laid out
+//   [4 panels of 16 rows][2 halves of 32 k][4 groups of 8 k][16 rows][8 k].
+// One MFMA B-operand load of a 16-row panel over 32 k (lane = group * 16 +
+// row) is then one contiguous KiB, and a 64-row tile streams through memory
+// in order as its K loop advances.
+__host__ __device__ inline size_t packed_index(int n, int k, int kc) {
+  const int r = n & 63, kk = k & 63;
+  return ((size_t)(n >> 6) * kc + (k >> 6)) * 4096 + (size_t)(r >> 4) * 1024 + (size_t)(kk >> 5) * 512 +
+         (size_t)((kk >> 3) & 3) * 128 + (size_t)(r & 15) * 8 + (kk & 7);
+}
+__host__ __device__ inline size_t packed_elems(int N, int K) { return (size_t)((N + 63) / 64) * 64 * (size_t)((K + 63) / 64) * 64; }
+
+// dst (packed, packed_elems(N, K) bf16) <- src ([N][K] row-major bf16).
+void launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t stream);
 enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
 struct GemmArgs {
@@ -33,8 +51,9 @@ struct GemmArgs {
   const uint16_t* gain; // A_NORM: [K] bf16
   const int32_t* a_rows;// A_NORM: optional row gather (A row m = y row a_rows[m])
   float eps;
-  // W segments: output column n in [seg_n0[s], seg_n0[s+1]) reads row n - seg_n0[s] of w[s].
-  // EPI_SWIGLU: w[0] = gate, w[1] = up, both [N][K].
+  // W segments, each a packed [rows][K] matrix: output column n in
+  // [seg_n0[s], seg_n0[s+1]) reads row n - seg_n0[s] of w[s]; segment sizes
+  // are multiples of 64.  EPI_SWIGLU: w[0] = gate, w[1] = up, both [N][K].
   const uint16_t* w[3];
   int seg_n0[4];
   // split-K (splits > 1): K range of split z is [z*k_split, min(K, (z+1)*k_split));

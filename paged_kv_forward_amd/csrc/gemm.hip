@@ -191,23 +191,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // Row pointers of this thread's W chunks (nullptr = zero row).
-  const uint16_t* wrow[C::B_CH];
+  // This thread's W pieces: piece c of the BN x 64 tile lies in 64-row block
+  // c / 512 (a packed 8 KiB block per K chunk) at element (c % 512) * 8, so a
+  // wave's loads are one contiguous KiB.  wblk: block base at K chunk 0
+  // (nullptr = rows past N, read as zeros).
+  static_assert(BN == 128, "two 64-row packed blocks per tile");
+  const int kc = (g.K + 63) / 64;
+  const uint16_t* wblk[C::B_CH];
 #pragma unroll
   for (int i = 0; i < C::B_CH; ++i) {
-    int r = (tid + 256 * i) >> 3;
+    const int c = tid + 256 * i, bsel = c >> 9;
     const uint16_t* p = nullptr;
     if (EPI == EPI_SWIGLU) {
-      int j = n_tile * (BN / 2) + (r % (BN / 2));
-      if (j < g.N) p = (r < BN / 2 ? g.w[0] : g.w[1]) + (size_t)j * g.K;
+      if (n_tile * 64 < g.N) p = g.w[bsel] + (size_t)n_tile * kc * 4096;
     } else {
-      int n = n_tile * BN + r;
+      const int n = n_tile * BN + bsel * 64;
       if (n < g.N) {
-        int s = n >= g.seg_n0[1] ? (n >= g.seg_n0[2] ? 2 : 1) : 0;
-        p = g.w[s] + (size_t)(n - g.seg_n0[s]) * g.K;
+        const int s = n >= g.seg_n0[1] ? (n >= g.seg_n0[2] ? 2 : 1) : 0;
+        p = g.w[s] + (size_t)((n - g.seg_n0[s]) >> 6) * kc * 4096;
       }
     }
-    wrow[i] = p;
+    wblk[i] = p ? p + (size_t)(c & 511) * 8 : nullptr;
   }
 
   uint4 ra[C::A_CH];
@@ -237,11 +241,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) {
-      int c = tid + 256 * i, k = k0 + (c & 7) * 8;
-      rb[i] = (wrow[i] && k < ke) ? *reinterpret_cast<const uint4*>(wrow[i] + k)
-                                  : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < C::B_CH; ++i)
+      rb[i] = wblk[i] ? *reinterpret_cast<const uint4*>(wblk[i] + (size_t)(k0 >> 6) * 4096)
+                      : make_uint4(0, 0, 0, 0);
   };
 
   auto store = [&](int buf) {
@@ -267,7 +269,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int i = 0; i < C::B_CH; ++i) {
-      int c = tid + 256 * i, row = c >> 3, kk = (c & 7) * 8;
+      const int c = tid + 256 * i, q = c & 511;
+      const int row = (c >> 9) * 64 + (q >> 7) * 16 + (q & 15), kk = ((q >> 6) & 1) * 32 + ((q >> 4) & 3) * 8;
       *reinterpret_cast<uint4*>(B + row * LDK + kk) = rb[i];
     }
   };
@@ -386,25 +389,27 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   const int ke = g.splits > 1 ? min(g.K, kb + g.k_split) : g.K;
   const int nc = ke > kb ? (ke - kb + SK_KC - 1) / SK_KC : 0;
 
-  // The wave's weight tensor (uniform per wave) and this lane's row in it.
+  // The wave's packed weight tensor, its 64-row block and 16-row panel.
   const uint16_t* wt;
-  int wrow, wrows;
+  int wblk, wrows;
   if (EPI == EPI_SWIGLU) {
     const bool up = wave >= 4;
     wt = up ? g.w[1] : g.w[0];
-    wrow = t * (SK_BN / 2) + (wave & 3) * 16 + r16;
+    wblk = t;
     wrows = g.N;
   } else {
     const int n0 = t * SK_BN;  // whole tiles lie in one segment
     const int sg = n0 >= g.seg_n0[1] ? (n0 >= g.seg_n0[2] ? 2 : 1) : 0;
     wt = g.w[sg];
-    wrow = n0 - g.seg_n0[sg] + wave * 16 + r16;
+    wblk = (n0 - g.seg_n0[sg]) / 64 + (wave >> 2);
     wrows = min(g.N, g.seg_n0[sg + 1]) - g.seg_n0[sg];
   }
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wt, (uint32_t)((size_t)wrows * g.K * 2));
+  const int kc = (g.K + 63) / 64;
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wt, (uint32_t)(packed_elems(wrows, g.K) * 2));
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(g.a, (uint32_t)((size_t)g.M * g.lda * 2));
-  const bool wok = wrow < wrows;
-  const uint32_t wbase = (uint32_t)wrow * (uint32_t)g.K;
+  // element of this lane's piece in half 0 of K chunk 0 (half 1 is 512 further)
+  const uint32_t wbase = (uint32_t)wblk * (uint32_t)kc * 4096u + (uint32_t)(wave & 3) * 1024u + (uint32_t)lane * 8u;
+  const int c0 = kb / SK_KC;
   // this thread's activation pieces of a group: rows xr0 + 8i, columns xk .. xk + 7
   const int xr0 = tid / (SK_GK / 8), xk = (tid % (SK_GK / 8)) * 8;
 
@@ -412,10 +417,10 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
     uint4 w0, w1;
   };
   auto load_w = [&](WSlot& sl, int j) {
-    const int kw = kb + j * SK_KC + gq * 8;
-    const bool live = j < nc && wok;
-    sl.w0 = bload16<SK_WPOL>(wrs, live && kw < ke ? (wbase + (uint32_t)kw) * 2u : OOB);
-    sl.w1 = bload16<SK_WPOL>(wrs, live && kw + 32 < ke ? (wbase + (uint32_t)(kw + 32)) * 2u : OOB);
+    // chunks past nc (this split's end) read zeros; a chunk's padding past K is stored as zeros
+    const uint32_t e = wbase + (uint32_t)(c0 + j) * 4096u;
+    sl.w0 = bload16<SK_WPOL>(wrs, j < nc ? e * 2u : OOB);
+    sl.w1 = bload16<SK_WPOL>(wrs, j < nc ? (e + 512u) * 2u : OOB);
   };
   auto load_x = [&](uint4 (&xv)[SK_XP], int gi) {
     const int kx = kb + gi * SK_GK + xk;
@@ -691,6 +696,34 @@ void launch_gemm(int amode, int epi, int tile, const GemmArgs& g, hipStream_t st
   }
   if (tile == TILE_64x128) launch_tile<64, 128>(amode, epi, g, st);
   else launch_tile<128, 128>(amode, epi, g, st);
+}
+
+// One thread per 16-byte piece of the packed matrix (see packed_index).
+__global__ void pack_weight_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int N, int K,
+                                   size_t n_pieces) {
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= n_pieces) return;
+  const int kc = (K + 63) / 64;
+  const size_t blk = q >> 9;
+  const int w = (int)(q & 511);
+  const int n = (int)(blk / kc) * 64 + (w >> 7) * 16 + (w & 15);
+  const int k = (int)(blk % kc) * 64 + ((w >> 6) & 1) * 32 + ((w >> 4) & 3) * 8;
+  uint16_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (n < N && k + e < K) ? src[(size_t)n * K + k + e] : (uint16_t)0;
+  uint4 o;
+  o.x = v[0] | ((uint32_t)v[1] << 16);
+  o.y = v[2] | ((uint32_t)v[3] << 16);
+  o.z = v[4] | ((uint32_t)v[5] << 16);
+  o.w = v[6] | ((uint32_t)v[7] << 16);
+  *reinterpret_cast<uint4*>(dst + q * 8) = o;
+}
+
+void launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t st) {
+  const size_t pieces = packed_elems(N, K) / 8;
+  if (pieces == 0) return;
+  hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st, src, dst, N, K,
+                     pieces);
 }
 
 void launch_rmsnorm(const float* y, const float* ss, int n_ss, const uint16_t* gain, int M, int d,

@@ -35,31 +35,48 @@ def model_desc(shape) -> N.pie_model_desc:
 LAYER_KEYS = ["attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up", "down"]
 
 
+PACKED_KEYS = {"q", "k", "v", "o", "gate", "up", "down"}
+
+
 def upload_weights(recipe, device="cuda", progress=None) -> Dict:
     """Draw the seeded bf16 weights of `recipe` (a synth.WeightRecipe) on the
-    host and copy them to `device`, one tensor at a time through pinned memory."""
+    host and copy them to `device`, one tensor at a time through pinned
+    memory.  Projections and lm_head are converted on the device to the
+    library's tiled layout (pie_pack_weight) through one staging buffer, so
+    the checkpoint-layout copy never exists for more than one tensor."""
     import torch
+    import synth
     shape = recipe.shape
     biggest = max(shape.vocab * shape.d_model, 3 * shape.d_model * shape.d_ffn)
     stage = torch.empty(biggest, dtype=torch.int16, pin_memory=True)
     stage_np = stage.numpy().view(np.uint16)
+    dev_stage = torch.empty(max(shape.vocab * shape.d_model, shape.d_model * shape.d_ffn,
+                                shape.d_model * shape.q_width), dtype=torch.int16, device=device)
+    L = N.lib()
 
-    def one(name, shp):
+    def one(name, shp, packed=False):
         n = int(np.prod(shp))
         recipe.tensor_bits(name, shp, out=stage_np[:n])
-        t = torch.empty(shp, dtype=torch.bfloat16, device=device)
-        t.view(torch.int16).view(-1).copy_(stage[:n], non_blocking=False)
+        if not packed:
+            t = torch.empty(shp, dtype=torch.bfloat16, device=device)
+            t.view(torch.int16).view(-1).copy_(stage[:n], non_blocking=False)
+            return t
+        rows, cols = shp
+        dev_stage[:n].copy_(stage[:n], non_blocking=False)
+        t = torch.empty(L.pie_packed_weight_bytes(rows, cols) // 2, dtype=torch.bfloat16, device=device)
+        check(L.pie_pack_weight(dev_stage.data_ptr(), t.data_ptr(), rows, cols,
+                                torch.cuda.current_stream(device).cuda_stream))
         return t
 
-    import synth
     w = {"embed": one("embed", (shape.vocab, shape.d_model)),
          "final_norm": one("final_norm", (shape.d_model,)),
-         "lm_head": one("head", (shape.vocab, shape.d_model)), "layers": []}
+         "lm_head": one("head", (shape.vocab, shape.d_model), packed=True), "layers": []}
     for l in range(shape.n_layers):
-        w["layers"].append({k: one("layers.%d.%s" % (l, k), s)
+        w["layers"].append({k: one("layers.%d.%s" % (l, k), s, packed=k in PACKED_KEYS)
                             for k, s in synth.layer_tensor_shapes(shape)})
         if progress:
             progress(l)
+    del dev_stage
     if shape.kv_dtype == synth.KV_E4M3:
         w["kv_scale"] = torch.from_numpy(synth.kv_scales(shape)).to(device)
     return w

@@ -249,3 +249,32 @@ def test_graph_replays_match_direct_launches(torch_cuda, monkeypatch):
         rt.close()
     for a, b in zip(*runs):
         np.testing.assert_array_equal(a, b)
+
+
+def packed_reference(w):
+    """The tiled weight layout as include/pie.h describes it, built with numpy
+    from the row-major [n][k] matrix: zero padding to multiples of 64, 64 x 64
+    blocks in (row block, column block) order, each block as
+    [4 panels of 16 rows][2 halves of 32 columns][4 groups of 8][16 rows][8]."""
+    n, k = w.shape
+    np_, kp = -(-n // 64) * 64, -(-k // 64) * 64
+    pad = np.zeros((np_, kp), dtype=w.dtype)
+    pad[:n, :k] = w
+    b = pad.reshape(np_ // 64, 4, 16, kp // 64, 2, 4, 8)  # [rb][panel][row][cb][half][group][8]
+    return b.transpose(0, 3, 1, 4, 5, 2, 6).reshape(-1)
+
+
+@pytest.mark.parametrize("n,k", [(64, 64), (200, 136), (688, 256), (128, 4096 + 8)])
+def test_pack_weight_layout(torch_cuda, n, k):
+    from paged_kv_forward_amd import _native as N
+    rng = np.random.default_rng(n * 7 + k)
+    w = rng.integers(0, 1 << 16, size=(n, k), dtype=np.uint16)
+    src = torch_cuda.from_numpy(w.view(np.int16)).to("cuda")
+    nbytes = N.lib().pie_packed_weight_bytes(n, k)
+    assert nbytes == (-(-n // 64) * 64) * (-(-k // 64) * 64) * 2
+    dst = torch_cuda.full((nbytes // 2,), -1, dtype=torch_cuda.int16, device="cuda")
+    N.check(N.lib().pie_pack_weight(src.data_ptr(), dst.data_ptr(), n, k, None))
+    got = dst.cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, packed_reference(w))
+    # overlapping buffers are refused
+    assert N.lib().pie_pack_weight(dst.data_ptr(), dst.data_ptr(), n, k, None) == N.PIE_EINVAL
