@@ -13,7 +13,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Cache-policy operand of the raw buffer loads: non-temporal (streaming).
 // Data read once per call (weights of the decode GEMMs, KV pages) bypasses
 // the normal L2 retention; a plain streaming read measured ~7.0 TB/s with it
-// against ~6.2 TB/s without.
+// against ~6.2 TB/s without.  It only pays when each load instruction covers
+// whole 128-byte lines (the tiled weight layout, the K page layout): with
+// half-line accesses it was slower than plain loads.
 constexpr int CPOL_NT = 2;
 
 // ---------------------------------------------------------------- formats

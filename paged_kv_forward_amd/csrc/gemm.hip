@@ -347,9 +347,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 // every weight byte is used by exactly one workgroup, so the kernel is a
 // weight stream.  A workgroup of 8 waves computes a 64 x 128 output tile over
 // its K range in 64-wide chunks; wave w owns output columns 16w .. 16w+15.
-//  - Weights: each lane loads its row's chunk (k-groups g and 4+g of the
-//    chunk, the MFMA B layout) into a ring of SK_DEPTH chunks with streaming
-//    loads, so several chunks are always in flight.
+//  - Weights (tiled layout, see packed_index): per chunk a wave reads its
+//    16-row panel's two contiguous KiB (the MFMA B operands of the chunk's
+//    two k-halves) with streaming loads into a ring of SK_DEPTH chunks, so
+//    several chunks are always in flight and each 64-row tile is read in
+//    address order.
 //  - Activations: staged in LDS a group of SK_DEPTH chunks (64 x 512) at a
 //    time, double-buffered.  The next group's pieces are loaded into
 //    registers at the start of a group and written to LDS at its end, so
@@ -365,9 +367,6 @@ constexpr int SK_LDX = SK_GK + 8;                // bf16 per LDS row (16-byte pa
 constexpr int SK_XP = 64 * SK_GK / 8 / SK_NT;    // 16-byte activation pieces per thread per group (8)
 constexpr int SK_LDS = 2 * 64 * SK_LDX * 2 > 64 * SK_LDC * 4 ? 2 * 64 * SK_LDX * 2 : 64 * SK_LDC * 4;
 constexpr uint32_t OOB = 0xFFFFFFF0u;
-#ifndef SK_WPOL
-#define SK_WPOL 0
-#endif
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -419,8 +418,8 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   auto load_w = [&](WSlot& sl, int j) {
     // chunks past nc (this split's end) read zeros; a chunk's padding past K is stored as zeros
     const uint32_t e = wbase + (uint32_t)(c0 + j) * 4096u;
-    sl.w0 = bload16<SK_WPOL>(wrs, j < nc ? e * 2u : OOB);
-    sl.w1 = bload16<SK_WPOL>(wrs, j < nc ? (e + 512u) * 2u : OOB);
+    sl.w0 = bload16<CPOL_NT>(wrs, j < nc ? e * 2u : OOB);
+    sl.w1 = bload16<CPOL_NT>(wrs, j < nc ? (e + 512u) * 2u : OOB);
   };
   auto load_x = [&](uint4 (&xv)[SK_XP], int gi) {
     const int kx = kb + gi * SK_GK + xk;
