@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, int n_ti
 // the partials in split order, writes y and the per-64-column sums of
 // squares exactly as the EPI_RESID epilogue does, sums those partials in
 // column order as rmsnorm_kernel does, and writes the normed bf16 row.
-constexpr int RN_NT = 512;
+constexpr int RN_NT = 1024;
 __global__ __launch_bounds__(RN_NT) void skinny_reduce_norm_kernel(GemmArgs g, int n_tiles) {
   extern __shared__ __attribute__((aligned(16))) float s_row[];  // [N] new y, then [N / 64] sums
   __shared__ float s_r;
