@@ -71,6 +71,116 @@ def cpu_baseline(shape, recipe, n_seq=2, n_layers=2):
                       (n_seq, PROMPT, n_layers, shape.n_layers, t_layers + t_head)}
 
 
+# ---------------------------------------------------------------- profiles
+ATTN_SOURCES = ["paged_kv_forward_amd/csrc/attention.hip", "paged_kv_forward_amd/csrc/attention.h",
+                "paged_kv_forward_amd/csrc/common.h"]
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attn_decode_hbm_counters.json")
+TRACE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace_c2 -o c2 -- "
+             "python3 <repo>/bench.py --steps 20 --warmup 5 --no-cpu-baseline")
+PMC_CMDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch -o f -- python3 <repo>/bench.py "
+    "--steps 3 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write -o w -- python3 <repo>/bench.py "
+    "--steps 3 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_copy_f -o cf -- python3 <repo>/bench.py "
+    "--calibrate-copy",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_copy_w -o cw -- python3 <repo>/bench.py "
+    "--calibrate-copy"]
+
+
+def sources_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(name):
+    return name.split("(")[0].replace("void ", "").strip()
+
+
+def summarize(out_dir):
+    """Write the committed summaries under profiles/ from a rocprofv3 kernel
+    trace (out_dir/trace_c2) and the FETCH_SIZE / WRITE_SIZE counter runs
+    (out_dir/pmc_*) of this benchmark."""
+    import csv
+    import glob
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(out_dir, "trace_c2", "*kernel_stats.csv"))[0])))
+    lines = ["# Kernel trace of the decode benchmark (Llama-3.1-8B shape, batch 64)", "",
+             "Command (on one MI355X, from the repository root):", "", "    " + TRACE_CMD, "",
+             "The run includes the 64 x 2048-token prefill (16 launches of 4 sequences) and 45 decode",
+             "steps (5 warm-up + 20 timed + 20 with HIP events).  Per kernel: calls, average and total",
+             "duration from `c2_kernel_stats.csv`.", "",
+             "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
+    for r in stats[:24]:
+        lines.append("| `%s` | %s | %.2f | %.2f | %s |" % (short_name(r["Name"]), r["Calls"],
+                     float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6, r["Percentage"][:5]))
+    with open(os.path.join(prof, "decode_llama8b_b64_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(csv_path):
+        agg = {}
+        for r in csv.DictReader(open(csv_path)):
+            k = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+            agg.setdefault(k, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fetch = per_kernel(glob.glob(os.path.join(out_dir, "pmc_fetch", "*counter_collection.csv"))[0])
+    write = per_kernel(glob.glob(os.path.join(out_dir, "pmc_write", "*counter_collection.csv"))[0])
+    cf = per_kernel(glob.glob(os.path.join(out_dir, "pmc_copy_f", "*counter_collection.csv"))[0])
+    cw = per_kernel(glob.glob(os.path.join(out_dir, "pmc_copy_w", "*counter_collection.csv"))[0])
+    copy_kib = (1 << 30) / 1024.0
+    cf_k = [v for k, v in cf.items() if "copyBuffer" in k[0]][0]
+    cw_k = [v for k, v in cw.items() if "copyBuffer" in k[0]][0]
+    f_scale, w_scale = copy_kib / cf_k, copy_kib / cw_k
+    rows = ["# HBM bytes per dispatch of the decode kernels (Llama-3.1-8B shape, batch 64)", "",
+            "Commands (on one MI355X, each its own run, from /tmp):", ""]
+    rows += ["    " + c for c in PMC_CMDS]
+    rows += ["", "Scale factors from the plain 1 GiB device copy (`bench.py --calibrate-copy`): "
+             "FETCH_SIZE read %.1f KiB for 1048576 KiB moved (x %.4f), WRITE_SIZE %.1f KiB (x %.4f)."
+             % (cf_k, f_scale, cw_k, w_scale), "",
+             "Decode step contexts in these runs: 2049..2055 tokens.", "",
+             "| kernel | grid (threads) | fetch KiB | write KiB | HBM MB per dispatch (scaled) |",
+             "|---|---|---|---|---|"]
+    attn = None
+    for k in sorted(fetch, key=lambda k: -fetch[k]):
+        if k[1] < 8192:
+            continue
+        fb, wb = fetch[k], write.get(k, 0.0)
+        mb = (fb * f_scale + wb * w_scale) * 1024 / 1e6
+        rows.append("| `%s` | %d | %.1f | %.1f | %.1f |" % (k[0], k[1], fb, wb, mb))
+        if k[0].startswith("pie::attn_decode_kernel") and k[1] == 64 * 8 * 256:
+            attn = {"kernel": k[0], "grid_threads": k[1], "fetch_kib": fb, "write_kib": wb,
+                    "fetch_scale": f_scale, "write_scale": w_scale,
+                    "bytes_per_dispatch": (fb * f_scale + wb * w_scale) * 1024,
+                    "context_tokens": [2049, 2055]}
+    with open(os.path.join(prof, "decode_llama8b_b64_hbm_counters.md"), "w") as f:
+        f.write("\n".join(rows) + "\n")
+    if attn:
+        attn["sources_sha256"] = sources_digest(ATTN_SOURCES)
+        with open(TRAFFIC_JSON, "w") as f:
+            json.dump(attn, f, indent=1)
+    print("wrote summaries under", prof)
+
+
+def measured_traffic():
+    """Counter-measured HBM bytes per decode-attention dispatch, or None when
+    the kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("sources_sha256") != sources_digest(ATTN_SOURCES):
+        return None
+    return t
+
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,10 +188,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel class (extra pass)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write profiles/ summaries from the rocprofv3 outputs under DIR and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the known-size "
                          "kernel that scales HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path runs on a single MI355X "
               "(multi-GPU sharding is a design note, not built); use --gpus 1", file=sys.stderr)
@@ -180,6 +295,7 @@ def main():
         rt.profile_enable([])
         breakdown = {k: round(v[0] / 3, 4) for k, v in pb.items() if v[1]}
 
+    traffic = measured_traffic()
     out = {
         "metric": "decode tokens/s + HBM-roofline fraction, Llama-3.1-8B shape, batch 64, 1 GPU",
         "value": round(N_SEQ * K / t_dec, 2),
@@ -196,7 +312,11 @@ def main():
                    "global_batch": N_SEQ, "seq_len": PROMPT, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "paged decode attention (split-KV + combine)",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": round(traffic["bytes_per_dispatch"]) if traffic else None,
+                     "traffic_note": ("HBM bytes per dispatch from FETCH_SIZE + WRITE_SIZE (scaled by a "
+                                      "plain copy), at context %d..%d" % tuple(traffic["context_tokens"])
+                                      if traffic else "counters not taken for this kernel's sources"),
                      "bytes_per_launch": int(per_launch),
                      "avg_launch_ms": round(attn_ms / max(attn_n, 1), 5),
                      "timed_over": "a second pass of %d decode steps (context %d..%d) with HIP events "
