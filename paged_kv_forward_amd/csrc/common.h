@@ -67,6 +67,16 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
 // D = A * B + C for one 16x16x32 bf16 tile (wave-wide).  Lane l holds, for
 // A, row (l % 16) and 8 k-values of group (l / 16); for B, column (l % 16)
 // and the same 8 k-values; D gives lane l column (l % 16), rows 4*(l/16)+i.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// D[32x32] += A[32x16] * B[16x32], bf16 in, fp32 accumulate.  Lane l holds A
+// row l % 32 and B column l % 32, k values 8 * (l / 32) .. + 7; D value i of
+// lane l is row 8 * (i / 4) + 4 * (l / 32) + i % 4, column l % 32.
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

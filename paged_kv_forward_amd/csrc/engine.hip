@@ -404,7 +404,9 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
   if ((rc = check_launch(c, flags, "embed"))) return rc;
 
   const bool small = T <= 64;  // decode-sized: the weight-streaming skinny GEMM with split-K
-  const int tile = small ? pie::TILE_SKINNY : pie::TILE_128x128;
+  // prefill-sized calls: 256 x 256 tiles once there are enough rows for them
+  const int tile = small ? pie::TILE_SKINNY : (T >= 256 ? pie::TILE_256x256 : pie::TILE_128x128);
+  const int qkv_tile = tile == pie::TILE_256x256 && (qw % 256 || kvw % 256) ? pie::TILE_128x128 : tile;
   float* gpart = reinterpret_cast<float*>(c->ws + L.gpart);
   uint16_t* xb = reinterpret_cast<uint16_t*>(c->ws + L.x);
   const size_t elem = kv_elem_bytes(d);
@@ -465,7 +467,7 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       g.nq = d.n_q_heads; g.nkv = d.n_kv_heads; g.hd = d.head_dim; g.page_size = d.page_size;
       g.kv_e4m3 = d.kv_dtype == PIE_KV_E4M3;
       g.kv_scale = kvs;
-      set_split(g, pie::gemm_n_tiles(pie::EPI_QKV, g.N, tile));
+      set_split(g, pie::gemm_n_tiles(pie::EPI_QKV, g.N, qkv_tile));
       Timed tm(c, PIE_K_GEMM_QKV);
       // decode-sized calls: the previous layer's down projection already wrote
       // this layer's normed rows (fused into its split-K reduce)
@@ -473,7 +475,7 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
         pie::launch_rmsnorm(y, ss, n_ss, c->attn_norm[l], T, d.d_model, d.rms_eps, nullptr, xb, st);
       g.a = xb;
       g.lda = d.d_model;
-      pie::launch_gemm(pie::A_BF16, pie::EPI_QKV, tile, g, st);
+      pie::launch_gemm(pie::A_BF16, pie::EPI_QKV, qkv_tile, g, st);
     }
     if ((rc = check_launch(c, flags, "qkv gemm"))) return rc;
     // attention

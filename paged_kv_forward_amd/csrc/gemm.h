@@ -91,7 +91,9 @@ struct GemmArgs {
 
 // Tile configurations.  TILE_SKINNY: M <= 64 with a bf16 A operand, 128 output
 // columns per workgroup, weights streamed through registers (decode).
-enum GemmTile { TILE_64x128 = 0, TILE_128x128 = 1, TILE_SKINNY = 2 };
+// TILE_256x256: prefill-sized M with a bf16 A operand and EPI_QKV, EPI_RESID
+// or EPI_SWIGLU (for EPI_QKV the q and k/v widths must be multiples of 256).
+enum GemmTile { TILE_64x128 = 0, TILE_128x128 = 1, TILE_SKINNY = 2, TILE_256x256 = 3 };
 
 // Most K splits of one skinny GEMM.
 constexpr int SK_MAX_SPLITS = 16;

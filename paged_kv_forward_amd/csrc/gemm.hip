@@ -1,9 +1,10 @@
 // MFMA GEMM with fused RMSNorm prologue, split-K and the decoder's epilogues.
-// See gemm.h for the operation.  Tiles are staged through LDS with double
-// buffering; each of the 4 waves of a workgroup owns a WM x WN block of the
-// BM x BN tile and issues 16x16x32 bf16 MFMAs.
+// See gemm.h for the operation.  The tiled kernel (prefill-sized M) stages
+// tiles through LDS with double buffering; each of the 4 waves of a workgroup
+// owns a WM x WN block of the BM x BN tile and issues 16x16x32 bf16 MFMAs.
+// The skinny kernel (decode-sized M) is a weight stream, described below.
 //
-// Split-K: every split writes its fp32 partial tile and exits; a second,
+// Split-K (skinny kernel): every split writes its fp32 partial tile and exits; a second,
 // small kernel sums the partials in split order (so the result does not
 // depend on scheduling) and runs the epilogue.  The kernel boundary is what
 // makes the partials visible: on gfx950 each XCD has its own L2, and an
@@ -157,6 +158,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int
   }
 }
 
+constexpr int GROUP_M = 16;
+
+// Output tiles along N of the tiled kernel (EPI_SWIGLU tiles hold BN/2 gate and BN/2 up columns).
+template <int EPI>
+__device__ __forceinline__ int tiles_n(const GemmArgs& g, int BN) {
+  return EPI == EPI_SWIGLU ? (g.N + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
+}
+
 template <int BM, int BN, int AMODE, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   using C = Cfg<BM, BN>;
@@ -169,10 +178,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const int n_tile = blockIdx.x, m_tile = blockIdx.y, split = blockIdx.z;
+  // Grouped raster: consecutive workgroups sweep GROUP_M row tiles for each
+  // column tile, so the ~256 workgroups in flight share 16 row tiles and 16
+  // column tiles and read each from HBM about once per window (row-major
+  // order would read every column tile once per row tile).
+  int n_tile, m_tile;
+  {
+    const int n_tiles = tiles_n<EPI>(g, BN), m_tiles = (g.M + BM - 1) / BM;
+    const int pid = blockIdx.x, per_group = GROUP_M * n_tiles;
+    const int grp = pid / per_group, m0g = grp * GROUP_M, gm = min(GROUP_M, m_tiles - m0g);
+    const int r = pid - grp * per_group;
+    m_tile = m0g + r % gm;
+    n_tile = r / gm;
+  }
   const int m0 = m_tile * BM;
-  const int kb = g.splits > 1 ? split * g.k_split : 0;
-  const int ke = g.splits > 1 ? min(g.K, kb + g.k_split) : g.K;
+  const int kb = 0, ke = g.K;  // the tiled kernel does not split K
 
   if (AMODE == A_NORM) {
     for (int i = tid; i < BM; i += 256) {
@@ -310,22 +330,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
   }
 
-  if (g.splits > 1) {
-    // partial layout: [split][m < BM][n < n_tiles * BN], row-major
-    const size_t ld = (size_t)gridDim.x * BN;
-    float* part = g.partial + (size_t)split * BM * ld + (size_t)n_tile * BN;
-#pragma unroll
-    for (int a = 0; a < C::FM; ++a)
-#pragma unroll
-      for (int b = 0; b < C::FN; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int row = wm * C::WM + a * 16 + 4 * (lane >> 4) + i;
-          int col = wn * C::WN + b * 16 + (lane & 15);
-          part[(size_t)row * ld + col] = acc[a][b][i];
-        }
-    return;
-  }
 
   float* sC = reinterpret_cast<float*>(smem);
 #pragma unroll
@@ -340,6 +344,142 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       }
   __syncthreads();
   epilogue<EPI, BN>(g, sC, C::LDC, m0, BM, n_tile);
+}
+
+// ---------------------------------------------------------------------------
+// Large variant for prefill-sized M: a 256 x 256 output tile per workgroup of
+// 4 waves, each wave a 128 x 128 block of 4 x 4 32x32x16 MFMAs (256 fp32
+// accumulators per lane), K in stages of 64 staged through double-buffered
+// LDS.  Per k16 step a wave reads 4 A and 4 B fragments for 16 MFMAs, so LDS
+// traffic is half of what 64 x 64 wave blocks of 16x16 MFMAs need.  The next
+// stage's global loads are in flight while the current stage is computed.
+// The epilogue runs in four passes of 64 rows through LDS.
+constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 64, BG_NT = 256, BG_LDK = BG_BK + 8, BG_LDC = BG_BN + 4;
+constexpr int BG_PIECES = BG_BM * BG_BK / 8 / BG_NT;  // 16-byte pieces per thread per operand per stage (8)
+constexpr int BG_LDS = 2 * (BG_BM + BG_BN) * BG_LDK * 2;
+static_assert(64 * BG_LDC * 4 <= BG_LDS, "epilogue pass fits in the operand buffers");
+
+template <int EPI>
+__device__ __forceinline__ int big_tiles_n(const GemmArgs& g) {
+  return EPI == EPI_SWIGLU ? (g.N + BG_BN / 2 - 1) / (BG_BN / 2) : (g.N + BG_BN - 1) / BG_BN;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[BG_LDS];
+  uint16_t* sA = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* sB = sA + 2 * BG_BM * BG_LDK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, lh = lane >> 5;
+
+  int n_tile, m_tile;
+  {
+    const int n_tiles = big_tiles_n<EPI>(g), m_tiles = (g.M + BG_BM - 1) / BG_BM;
+    constexpr int GM = 8;
+    const int pid = blockIdx.x, per_group = GM * n_tiles;
+    const int grp = pid / per_group, m0g = grp * GM, gm = min(GM, m_tiles - m0g);
+    const int r = pid - grp * per_group;
+    m_tile = m0g + r % gm;
+    n_tile = r / gm;
+  }
+  const int m0 = m_tile * BG_BM;
+  const int kc = (g.K + 63) / 64;
+  const int nk = kc;
+
+  // A pieces: row p / 8, columns (p % 8) * 8; B pieces: packed 64-row block p / 512.
+  const uint16_t* bblk[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint16_t* p = nullptr;
+    if (EPI == EPI_SWIGLU) {
+      const int t64 = n_tile * 2 + (b & 1);
+      if (t64 * 64 < g.N) p = g.w[b >> 1] + (size_t)t64 * kc * 4096;
+    } else {
+      const int n = n_tile * BG_BN + b * 64;
+      if (n < g.N) {
+        const int s = n >= g.seg_n0[1] ? (n >= g.seg_n0[2] ? 2 : 1) : 0;
+        p = g.w[s] + (size_t)((n - g.seg_n0[s]) >> 6) * kc * 4096;
+      }
+    }
+    bblk[b] = p;
+  }
+  uint4 ra[BG_PIECES], rb[BG_PIECES];
+  auto load = [&](int c) {
+    const int k0 = c * BG_BK;
+#pragma unroll
+    for (int i = 0; i < BG_PIECES; ++i) {
+      const int p = tid + BG_NT * i, row = p >> 3, k = k0 + (p & 7) * 8, m = m0 + row;
+      ra[i] = (m < g.M && k < g.K) ? *reinterpret_cast<const uint4*>(g.a + (size_t)m * g.lda + k)
+                                   : make_uint4(0, 0, 0, 0);
+      const uint16_t* bp = bblk[p >> 9];
+      rb[i] = bp ? *reinterpret_cast<const uint4*>(bp + (size_t)c * 4096 + (size_t)(p & 511) * 8)
+                 : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf) {
+    uint16_t* A = sA + buf * BG_BM * BG_LDK;
+    uint16_t* B = sB + buf * BG_BN * BG_LDK;
+#pragma unroll
+    for (int i = 0; i < BG_PIECES; ++i) {
+      const int p = tid + BG_NT * i, q = p & 511;
+      *reinterpret_cast<uint4*>(A + (p >> 3) * BG_LDK + (p & 7) * 8) = ra[i];
+      const int row = (p >> 9) * 64 + (q >> 7) * 16 + (q & 15), kk = ((q >> 6) & 1) * 32 + ((q >> 4) & 3) * 8;
+      *reinterpret_cast<uint4*>(B + row * BG_LDK + kk) = rb[i];
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+
+  if (nk > 0) {
+    load(0);
+    store(0);
+    lds_barrier();
+    for (int t = 0; t < nk; ++t) {
+      if (t + 1 < nk) load(t + 1);
+      const uint16_t* A = sA + (t & 1) * BG_BM * BG_LDK + (wm * 128 + l32) * BG_LDK + lh * 8;
+      const uint16_t* B = sB + (t & 1) * BG_BN * BG_LDK + (wn * 128 + l32) * BG_LDK + lh * 8;
+#pragma unroll
+      for (int ks = 0; ks < BG_BK / 16; ++ks) {
+        uint4 af[4], bf[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) af[a] = *reinterpret_cast<const uint4*>(A + a * 32 * BG_LDK + ks * 16);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const uint4*>(B + b * 32 * BG_LDK + ks * 16);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(af[a], bf[b], acc[a][b]);
+      }
+      if (t + 1 < nk) store((t + 1) & 1);
+      lds_barrier();
+    }
+  }
+
+  // Epilogue in four passes of 64 rows (the two waves owning them write sC).
+  float* sC = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    if (wm == (pass >> 1)) {
+#pragma unroll
+      for (int ah = 0; ah < 2; ++ah) {
+        const int a = (pass & 1) * 2 + ah;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = ah * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+            sC[row * BG_LDC + wn * 128 + b * 32 + l32] = acc[a][b][i];
+          }
+      }
+    }
+    __syncthreads();
+    epilogue<EPI, BG_BN, BG_NT>(g, sC, BG_LDC, m0 + pass * 64, 64, n_tile);
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -630,11 +770,18 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* tile_bes
   if (lane == 0) tokens[m] = bi == INT_MAX ? -1 : bi;
 }
 
-int gemm_tile_bm(int tile) { return tile == TILE_64x128 ? 64 : 128; }
-int gemm_tile_bn(int) { return 128; }
+int gemm_tile_bm(int tile) { return tile == TILE_64x128 ? 64 : (tile == TILE_256x256 ? 256 : 128); }
+int gemm_tile_bn(int tile) { return tile == TILE_256x256 ? 256 : 128; }
 
-int gemm_n_tiles(int epi, int N, int) {
-  return epi == EPI_SWIGLU ? (N + 63) / 64 : (N + 127) / 128;
+int gemm_n_tiles(int epi, int N, int tile) {
+  const int bn = gemm_tile_bn(tile);
+  return epi == EPI_SWIGLU ? (N + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
+}
+
+template <int EPI>
+static void launch_big(const GemmArgs& g, hipStream_t st) {
+  const int tiles = gemm_n_tiles(EPI, g.N, TILE_256x256) * ((g.M + BG_BM - 1) / BG_BM);
+  hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(tiles), dim3(BG_NT), 0, st, g);
 }
 
 // Large tiles (prefill-sized M) never split K: there are enough output tiles.
@@ -644,7 +791,7 @@ static void launch_t(const GemmArgs& g0, hipStream_t st) {
   g.splits = 1;
   g.k_split = g.K;
   const int n_tiles = EPI == EPI_SWIGLU ? (g.N + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
-  dim3 grid(n_tiles, (g.M + BM - 1) / BM, 1);
+  dim3 grid(n_tiles * ((g.M + BM - 1) / BM), 1, 1);
   hipLaunchKernelGGL((gemm_kernel<BM, BN, AMODE, EPI>), grid, dim3(256), 0, st, g);
 }
 
@@ -692,6 +839,15 @@ void launch_gemm(int amode, int epi, int tile, const GemmArgs& g, hipStream_t st
       case EPI_LOGITS: return launch_skinny<EPI_LOGITS>(g, st);
     }
     return;
+  }
+  if (tile == TILE_256x256) {
+    if (amode != A_BF16) return;
+    switch (epi) {
+      case EPI_QKV: return launch_big<EPI_QKV>(g, st);
+      case EPI_RESID: return launch_big<EPI_RESID>(g, st);
+      case EPI_SWIGLU: return launch_big<EPI_SWIGLU>(g, st);
+      default: return;
+    }
   }
   if (tile == TILE_64x128) launch_tile<64, 128>(amode, epi, g, st);
   else launch_tile<128, 128>(amode, epi, g, st);
