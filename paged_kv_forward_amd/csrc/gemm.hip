@@ -348,13 +348,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
 // ---------------------------------------------------------------------------
 // Large variant for prefill-sized M: a 256 x 256 output tile per workgroup of
-// 4 waves, each wave a 128 x 128 block of 4 x 4 32x32x16 MFMAs (256 fp32
-// accumulators per lane), K in stages of 64 staged through double-buffered
-// LDS.  Per k16 step a wave reads 4 A and 4 B fragments for 16 MFMAs, so LDS
-// traffic is half of what 64 x 64 wave blocks of 16x16 MFMAs need.  The next
-// stage's global loads are in flight while the current stage is computed.
-// The epilogue runs in four passes of 64 rows through LDS.
-constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 64, BG_NT = 256, BG_LDK = BG_BK + 8, BG_LDC = BG_BN + 4;
+// 8 waves (2 along M x 4 along N), each wave a 128 x 64 block of 4 x 2
+// 32x32x16 MFMAs (128 fp32 accumulators per lane), K in stages of 64 staged
+// through double-buffered LDS.  Two waves per SIMD hide each other's load
+// and LDS latency; the next stage's global loads are in flight while the
+// current stage is computed.  The epilogue runs in four passes of 64 rows
+// through LDS.
+constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 64, BG_NT = 512, BG_LDK = BG_BK + 8, BG_LDC = BG_BN + 4;
 constexpr int BG_PIECES = BG_BM * BG_BK / 8 / BG_NT;  // 16-byte pieces per thread per operand per stage (8)
 constexpr int BG_LDS = 2 * (BG_BM + BG_BN) * BG_LDK * 2;
 static_assert(64 * BG_LDC * 4 <= BG_LDS, "epilogue pass fits in the operand buffers");
@@ -365,22 +365,26 @@ __device__ __forceinline__ int big_tiles_n(const GemmArgs& g) {
 }
 
 template <int EPI>
-__global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(GemmArgs g) {
+__global__ __launch_bounds__(BG_NT, 2) void gemm_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[BG_LDS];
   uint16_t* sA = reinterpret_cast<uint16_t*>(smem);
   uint16_t* sB = sA + 2 * BG_BM * BG_LDK;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, lh = lane >> 5;
+  const int wm = wave >> 2, wn = wave & 3, l32 = lane & 31, lh = lane >> 5;
 
+  // XCD-aware raster: workgroup i runs on XCD i % 8 (each XCD has its own
+  // L2).  A window of 256 workgroups covers 16 x 16 tiles, and the 32 that
+  // share an XCD form a 4 x 8 block of it, so each A tile is read by 8 and
+  // each B tile by 4 workgroups of the same XCD.  Windows advance along M
+  // first.  Workgroups of a partial window past the edge exit at once.
   int n_tile, m_tile;
   {
     const int n_tiles = big_tiles_n<EPI>(g), m_tiles = (g.M + BG_BM - 1) / BG_BM;
-    constexpr int GM = 8;
-    const int pid = blockIdx.x, per_group = GM * n_tiles;
-    const int grp = pid / per_group, m0g = grp * GM, gm = min(GM, m_tiles - m0g);
-    const int r = pid - grp * per_group;
-    m_tile = m0g + r % gm;
-    n_tile = r / gm;
+    const int m_win = (m_tiles + 15) / 16;
+    const int pid = blockIdx.x, win = pid >> 8, x = pid & 7, j = (pid & 255) >> 3;
+    m_tile = (win % m_win) * 16 + (x & 3) * 4 + (j & 3);
+    n_tile = (win / m_win) * 16 + (x >> 2) * 8 + (j >> 2);
+    if (m_tile >= m_tiles || n_tile >= n_tiles) return;
   }
   const int m0 = m_tile * BG_BM;
   const int kc = (g.K + 63) / 64;
@@ -428,11 +432,11 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(GemmArgs g) {
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
   if (nk > 0) {
     load(0);
@@ -441,25 +445,25 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(GemmArgs g) {
     for (int t = 0; t < nk; ++t) {
       if (t + 1 < nk) load(t + 1);
       const uint16_t* A = sA + (t & 1) * BG_BM * BG_LDK + (wm * 128 + l32) * BG_LDK + lh * 8;
-      const uint16_t* B = sB + (t & 1) * BG_BN * BG_LDK + (wn * 128 + l32) * BG_LDK + lh * 8;
+      const uint16_t* B = sB + (t & 1) * BG_BN * BG_LDK + (wn * 64 + l32) * BG_LDK + lh * 8;
 #pragma unroll
       for (int ks = 0; ks < BG_BK / 16; ++ks) {
-        uint4 af[4], bf[4];
+        uint4 af[4], bf[2];
 #pragma unroll
         for (int a = 0; a < 4; ++a) af[a] = *reinterpret_cast<const uint4*>(A + a * 32 * BG_LDK + ks * 16);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const uint4*>(B + b * 32 * BG_LDK + ks * 16);
+        for (int b = 0; b < 2; ++b) bf[b] = *reinterpret_cast<const uint4*>(B + b * 32 * BG_LDK + ks * 16);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(af[a], bf[b], acc[a][b]);
+          for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bf[b], acc[a][b]);
       }
       if (t + 1 < nk) store((t + 1) & 1);
       lds_barrier();
     }
   }
 
-  // Epilogue in four passes of 64 rows (the two waves owning them write sC).
+  // Epilogue in four passes of 64 rows (the four waves owning them write sC).
   float* sC = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
@@ -468,11 +472,11 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(GemmArgs g) {
       for (int ah = 0; ah < 2; ++ah) {
         const int a = (pass & 1) * 2 + ah;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int row = ah * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
-            sC[row * BG_LDC + wn * 128 + b * 32 + l32] = acc[a][b][i];
+            sC[row * BG_LDC + wn * 64 + b * 32 + l32] = acc[a][b][i];
           }
       }
     }
@@ -780,8 +784,8 @@ int gemm_n_tiles(int epi, int N, int tile) {
 
 template <int EPI>
 static void launch_big(const GemmArgs& g, hipStream_t st) {
-  const int tiles = gemm_n_tiles(EPI, g.N, TILE_256x256) * ((g.M + BG_BM - 1) / BG_BM);
-  hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(tiles), dim3(BG_NT), 0, st, g);
+  const int m_win = ((g.M + BG_BM - 1) / BG_BM + 15) / 16, n_win = (gemm_n_tiles(EPI, g.N, TILE_256x256) + 15) / 16;
+  hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(m_win * n_win * 256), dim3(BG_NT), 0, st, g);
 }
 
 // Large tiles (prefill-sized M) never split K: there are enough output tiles.
