@@ -42,7 +42,7 @@ struct AttnArgs {
 };
 
 // Rows handled by one prefill workgroup (tokens x query heads of a group).
-constexpr int PREFILL_ROWS = 128;
+constexpr int PREFILL_ROWS = 256;
 
 void launch_attn_decode(const AttnArgs& a, hipStream_t st);
 void launch_attn_combine(const AttnArgs& a, hipStream_t st);

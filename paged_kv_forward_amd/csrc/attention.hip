@@ -254,7 +254,7 @@ __device__ __forceinline__ void load_q(uint4 (&qf)[HD / 32], const uint16_t* qro
   constexpr int STEPS = HD / 32;
 #pragma unroll
   for (int i = 0; i < STEPS; ++i)
-    qf[i] = ok ? *reinterpret_cast<const uint4*>(qrow + (4 * i + g) * 8) : make_uint4(0, 0, 0, CPOL_NT);
+    qf[i] = ok ? *reinterpret_cast<const uint4*>(qrow + (4 * i + g) * 8) : make_uint4(0, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- decode
@@ -368,11 +368,122 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- prefill
 
+// Online-softmax update of RB row blocks with a pair of pages whose K and V
+// sit in LDS in their memory layout.  Unlike compute_pair it finishes S and P
+// for every row block before it reads V, so K and V fragments are never live
+// together.
+template <int HD, bool E4M3, int RB>
+__device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* kb1, const uint8_t* vb0,
+                                             const uint8_t* vb1, int valid0, int valid1, int start0,
+                                             int start1, const uint4 (&qf)[RB][HD / 32],
+                                             f32x4 (&oacc)[RB][HD / 16], float (&m_run)[RB], float (&l_run)[RB],
+                                             const int (&qidx)[RB], float scale_log2, int lane) {
+  constexpr int STEPS = HD / 32, DB = HD / 16, EB = E4M3 ? 1 : 2;
+  const int g = lane >> 4, n = lane & 15;
+  uint4 ph[RB], pl[RB];
+  float alpha[RB];
+  {
+    uint4 kf[2][STEPS];
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+      const int off = ((i * 64 + lane) * 8) * EB;  // the page's own layout
+      if constexpr (E4M3) {
+        kf[0][i] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(kb0 + off));
+        kf[1][i] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(kb1 + off));
+      } else {
+        kf[0][i] = *reinterpret_cast<const uint4*>(kb0 + off);
+        kf[1][i] = *reinterpret_cast<const uint4*>(kb1 + off);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < STEPS; ++i) {
+        s0 = mfma16(kf[0][i], qf[rb][i], s0);
+        s1 = mfma16(kf[1][i], qf[rb][i], s1);
+      }
+      float sc[8];
+      const int qi = qidx[rb];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = 4 * g + j;
+        sc[j] = tok < valid0 && start0 + tok <= qi ? s0[j] * scale_log2 : -INFINITY;
+        sc[4 + j] = tok < valid1 && start1 + tok <= qi ? s1[j] * scale_log2 : -INFINITY;
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[rb], mx);
+      const bool any = m_new != -INFINITY;
+      alpha[rb] = any ? exp2f(m_run[rb] - m_new) : 1.f;
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = any ? exp2f(sc[j] - m_new) : 0.f;
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ps += p[j];
+      l_run[rb] = l_run[rb] * alpha[rb] + ps;
+      m_run[rb] = m_new;
+      ph[rb] = make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]), pack_bf2(p[6], p[7]));
+      const uint32_t hw[4] = {ph[rb].x, ph[rb].y, ph[rb].z, ph[rb].w};
+      float lo[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo[2 * j] = p[2 * j] - bf2f(hw[j] & 0xffffu);
+        lo[2 * j + 1] = p[2 * j + 1] - bf2f(hw[j] >> 16);
+      }
+      pl[rb] = make_uint4(pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(lo[4], lo[5]),
+                          pack_bf2(lo[6], lo[7]));
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    const int off = ((16 * b + n) * PS + 4 * g) * EB;
+    uint2 a0, a1;
+    if constexpr (E4M3) {
+      a0 = v4_bf16<true>(*reinterpret_cast<const uint32_t*>(vb0 + off), valid0 - 4 * g);
+      a1 = v4_bf16<true>(*reinterpret_cast<const uint32_t*>(vb1 + off), valid1 - 4 * g);
+    } else {
+      a0 = v4_bf16<false>(*reinterpret_cast<const uint2*>(vb0 + off), valid0 - 4 * g);
+      a1 = v4_bf16<false>(*reinterpret_cast<const uint2*>(vb1 + off), valid1 - 4 * g);
+    }
+    const uint4 vf = make_uint4(a0.x, a0.y, a1.x, a1.y);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      oacc[rb][b] *= alpha[rb];
+      oacc[rb][b] = mfma16(vf, ph[rb], oacc[rb][b]);
+      oacc[rb][b] = mfma16(vf, pl[rb], oacc[rb][b]);
+    }
+  }
+}
+
+// One workgroup (8 waves, PREFILL_ROWS query rows: PREFILL_ROWS / G tokens x
+// the G query heads of one KV head) per (item, KV head).  The K and V of the
+// sequence pass through LDS four pages (64 tokens) at a time, double
+// buffered, so every page is read from memory once per workgroup and serves
+// all its rows; each wave runs the online softmax over its 32 rows.  Rows see
+// entries up to their own logical index (causal in append order); pages past
+// the workgroup's last row are skipped.
+constexpr int PF_WAVES = 8, PF_NT = 64 * PF_WAVES;
+
 template <int HD, bool E4M3>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
-  constexpr int RB = PREFILL_ROWS / 64;  // row blocks per wave (4 waves)
+__global__ __launch_bounds__(PF_NT, 2) void attn_prefill_kernel(AttnArgs a) {
+  constexpr int RB = PREFILL_ROWS / (16 * PF_WAVES);  // row blocks of 16 per wave
   constexpr int DB = HD / 16, EB = E4M3 ? 1 : 2;
-  const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4;
+  constexpr int PAGE_B = PS * HD * EB;          // bytes of one page's K (or V) for one KV head
+  constexpr int SP = 4;                         // pages per stage
+  constexpr int STAGE_B = SP * 2 * PAGE_B;      // K and V of a stage
+  constexpr int PIECE = PAGE_B / PF_NT >= 4 ? PAGE_B / PF_NT : 4;  // bytes per loading thread
+  constexpr int LOADERS = PAGE_B / PIECE;
+  static_assert(PIECE == 16 || PIECE == 8 || PIECE == 4, "page block split over the loading threads");
+  typedef typename std::conditional<PIECE == 16, uint4,
+                                    typename std::conditional<PIECE == 8, uint2, uint32_t>::type>::type Piece;
+  __shared__ __attribute__((aligned(16))) uint8_t skv[2][STAGE_B];
+  __shared__ int s_valid[2][SP], s_start[2][SP];
+  const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4, tid = threadIdx.x;
   const int4 it = a.items[blockIdx.x];
   const int kvh = blockIdx.y;
   const int s = it.x, tb = it.y, nt = it.z;
@@ -382,7 +493,6 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
 
   uint4 qf[RB][HD / 32];
   int qidx[RB];
-  int last_tok = -1;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = wave * (RB * 16) + rb * 16 + n;
@@ -390,11 +500,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
     const bool ok = tq < nt;
     qidx[rb] = ok ? ctx + tq : -1;
     load_q<HD>(qf[rb], a.q + ((size_t)(row0 + (ok ? tq : 0)) * a.nq + kvh * G + h) * HD, ok, g);
-    const int wave_last = (wave * (RB * 16) + rb * 16 + 15) / G;
-    last_tok = max(last_tok, min(wave_last, nt - 1));
   }
-  if (wave * (RB * 16) / G >= nt) return;  // no rows for this wave
-  const int qmax = ctx + last_tok;
+  const bool wave_live = wave * (RB * 16) / G < nt;
+  const int qmax = ctx + nt - 1;
 
   f32x4 oacc[RB][DB];
   float m_run[RB], l_run[RB];
@@ -409,11 +517,73 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
   const float scale_log2 = a.sm_scale * ks * LOG2E;
   const uint32_t kofs = (uint32_t)(kvh * PS * HD) * EB;
   const uint32_t vofs = (uint32_t)(a.nkv * PS * HD + kvh * HD * PS) * EB;
-  // entries whose first slot is visible to some row of this wave
+  const uint32_t page_bytes = (uint32_t)a.page_stride * EB;
+  const uint8_t* kv = reinterpret_cast<const uint8_t*>(a.kv_layer);
   const int e_begin = a.seq_pg0[s];
   int e_end = a.seq_pg0[s + 1];
   while (e_end > e_begin && a.pg_start[e_end - 1] > qmax) --e_end;
-  attend_range<HD, E4M3, RB>(a, e_begin, e_end, kofs, vofs, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
+  const int n_stages = (e_end - e_begin + SP - 1) / SP;
+  const bool loader = tid < LOADERS;
+
+  // this thread's pieces of a stage: K and V of each of the SP pages
+  Piece pc[SP][2];
+  int pv[SP], ps[SP];
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < SP; ++j) {
+      const int e = e_begin + st * SP + j;
+      const bool live = e < e_end;
+      // the same entry for every lane: keep the page id (and the descriptor) scalar
+      const int pg = __builtin_amdgcn_readfirstlane(live ? a.pg_id[e] : 0);
+      pv[j] = live ? a.pg_valid[e] : 0;
+      ps[j] = live ? a.pg_start[e] : 0;
+      const __amdgpu_buffer_rsrc_t r = page_rsrc(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
+#pragma unroll
+      for (int kvsel = 0; kvsel < 2; ++kvsel) {
+        const uint32_t off = loader ? (kvsel ? vofs : kofs) + (uint32_t)tid * PIECE : 0xFFFFFFF0u;
+        if constexpr (PIECE == 16)
+          pc[j][kvsel] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_NT));
+        else if constexpr (PIECE == 8)
+          pc[j][kvsel] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CPOL_NT));
+        else
+          pc[j][kvsel] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL_NT);
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+    if (loader) {
+#pragma unroll
+      for (int j = 0; j < SP; ++j)
+#pragma unroll
+        for (int kvsel = 0; kvsel < 2; ++kvsel)
+          *reinterpret_cast<Piece*>(&skv[buf][(j * 2 + kvsel) * PAGE_B + tid * PIECE]) = pc[j][kvsel];
+    }
+    if (tid < SP) {
+      s_valid[buf][tid] = pv[tid];
+      s_start[buf][tid] = ps[tid];
+    }
+  };
+
+  if (n_stages > 0) {
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int st = 0; st < n_stages; ++st) {
+      const int buf = st & 1;
+      if (st + 1 < n_stages) load_stage(st + 1);
+      if (wave_live) {
+#pragma unroll
+        for (int j0 = 0; j0 < SP; j0 += 2)
+          prefill_pair<HD, E4M3, RB>(&skv[buf][(j0 * 2) * PAGE_B], &skv[buf][(j0 * 2 + 2) * PAGE_B],
+                                     &skv[buf][(j0 * 2 + 1) * PAGE_B], &skv[buf][(j0 * 2 + 3) * PAGE_B],
+                                     s_valid[buf][j0], s_valid[buf][j0 + 1], s_start[buf][j0],
+                                     s_start[buf][j0 + 1], qf, oacc, m_run, l_run, qidx, scale_log2, lane);
+      }
+      if (st + 1 < n_stages) store_stage(buf ^ 1);  // that buffer was last read in stage st - 1
+      __syncthreads();
+    }
+  }
+
   const float vs = E4M3 ? a.kv_scale[a.nkv + kvh] : 1.f;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -455,11 +625,11 @@ void launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
   if (a.n_items == 0) return;
   dim3 grid(a.n_items, a.nkv);
   if (a.hd == 128) {
-    if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<128, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_prefill_kernel<128, false>), grid, dim3(256), 0, st, a);
+    if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<128, true>), grid, dim3(PF_NT), 0, st, a);
+    else hipLaunchKernelGGL((attn_prefill_kernel<128, false>), grid, dim3(PF_NT), 0, st, a);
   } else {
-    if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<64, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_prefill_kernel<64, false>), grid, dim3(256), 0, st, a);
+    if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<64, true>), grid, dim3(PF_NT), 0, st, a);
+    else hipLaunchKernelGGL((attn_prefill_kernel<64, false>), grid, dim3(PF_NT), 0, st, a);
   }
 }
 

@@ -20,18 +20,25 @@ constexpr int CPOL_NT = 2;
 
 // ---------------------------------------------------------------- formats
 
-// float32 -> bf16 bits, round to nearest even (NaN stays NaN).
+// float32 -> bf16 bits, round to nearest even (NaN stays NaN).  Written as a
+// select, not a branch: it sits in the innermost loops.
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded);
 }
 
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 (a in the low half): one v_cvt_pk_bf16_f32, whose
+// rounding (nearest even, NaN kept) matches f2bf bit for bit (checked on
+// every class of input: ties, denormals, infinities, NaNs).
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // OCP E4M3FN code of x, saturating: clamp to +-448, round to nearest even on

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdlib>
 #include <map>
@@ -331,6 +332,15 @@ void build_work(pie_ctx* c) {
         c->pre.insert(c->pre.end(), {s, tb, std::min(tpw, n_new - tb), 0});
     }
   }
+  // longest first: an item's work grows with its last token's position
+  std::vector<std::array<int, 4>> pre(c->pre.size() / 4);
+  for (size_t i = 0; i < pre.size(); ++i)
+    pre[i] = {c->pre[4 * i], c->pre[4 * i + 1], c->pre[4 * i + 2], c->pre[4 * i + 3]};
+  std::stable_sort(pre.begin(), pre.end(), [&](const std::array<int, 4>& x, const std::array<int, 4>& y) {
+    return p.seq_ctx[x[0]] + x[1] + x[2] > p.seq_ctx[y[0]] + y[1] + y[2];
+  });
+  for (size_t i = 0; i < pre.size(); ++i)
+    for (int k = 0; k < 4; ++k) c->pre[4 * i + k] = pre[i][k];
 }
 
 template <typename T>
