@@ -245,9 +245,10 @@ def main():
     t_prefill = time.perf_counter() - t0
     log("bench: prefill %d x %d tokens in %.2f s" % (N_SEQ, PROMPT, t_prefill))
 
+    ws_arr = np.array(ws, dtype=np.uint64)
+
     def step():
-        toks, _ = rt.forward([Pass(ws[s], [int(nxt[s])], [0], [(0, 1.0, 0)]) for s in range(N_SEQ)])
-        nxt[:] = toks
+        nxt[:] = rt.decode_step(ws_arr, nxt)  # argmax; each sequence feeds back its own token
 
     for _ in range(W):
         step()

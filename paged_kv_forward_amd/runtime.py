@@ -5,6 +5,7 @@ are marshalled into the C structs of include/pie.h.
 from __future__ import annotations
 
 import ctypes
+import itertools
 import os
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence, Tuple
@@ -36,6 +37,20 @@ LAYER_KEYS = ["attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up", "down"]
 
 
 PACKED_KEYS = {"q", "k", "v", "o", "gate", "up", "down"}
+
+
+def _struct_dtype(ctype, formats):
+    """numpy dtype with the field offsets and size of a ctypes Structure."""
+    names = [f for f, _ in ctype._fields_]
+    return np.dtype({"names": names, "formats": [formats[f] for f in names],
+                     "offsets": [getattr(ctype, f).offset for f in names],
+                     "itemsize": ctypes.sizeof(ctype)})
+
+
+PASS_DT = _struct_dtype(N.pie_pass, {"ws": np.uint64, "tokens": np.uint64, "positions": np.uint64,
+                                      "n_tokens": np.int32, "readout": np.uint64, "n_readout": np.int32,
+                                      "epi": np.uint64, "commit": np.int32})
+EPI_DT = _struct_dtype(N.pie_epilogue, {"kind": np.int32, "temperature": np.float32, "seed": np.uint64})
 
 
 def upload_weights(recipe, device="cuda", progress=None) -> Dict:
@@ -92,6 +107,7 @@ class PieRuntime:
         self.desc = model_desc(shape)
         self.limits = N.pie_limits(max_rows, max_seqs, max_readout, max_ctx)
         self._keep = []
+        self._decode_bufs = {}
         L = N.lib()
         self.page_bytes = L.pie_kv_page_bytes(ctypes.byref(self.desc))
         self.ws_bytes = L.pie_workspace_bytes(ctypes.byref(self.desc), ctypes.byref(self.limits))
@@ -162,22 +178,83 @@ class PieRuntime:
 
     # ------------------------------------------------------------ forward
     def _marshal(self, passes: Sequence[Pass]):
-        arr = (N.pie_pass * len(passes))()
-        keep = []
-        for i, p in enumerate(passes):
-            tok = np.ascontiguousarray(p.tokens, dtype=np.int32)
-            ro = np.ascontiguousarray(p.readout, dtype=np.int32)
-            epi = (N.pie_epilogue * max(len(p.readout), 1))()
-            for j, e in enumerate(p.epi):
-                epi[j] = N.pie_epilogue(int(e[0]), float(e[1]), int(e[2]) & 0xFFFFFFFFFFFFFFFF)
-            pos = None if p.positions is None else np.ascontiguousarray(p.positions, dtype=np.int32)
-            keep += [tok, ro, epi, pos]
-            ip = ctypes.POINTER(ctypes.c_int32)
-            arr[i] = N.pie_pass(p.ws, tok.ctypes.data_as(ip),
-                                pos.ctypes.data_as(ip) if pos is not None else None, len(tok),
-                                ro.ctypes.data_as(ip) if len(ro) else None, len(ro),
-                                epi if len(ro) else None, 1 if p.commit else 0)
-        return arr, keep
+        """The pie_pass array of `passes`, built with a few numpy operations: all
+        tokens, positions, readout indices and epilogues of the call sit in one
+        array each, and each pass points into them."""
+        n = len(passes)
+        chain = itertools.chain.from_iterable
+        n_tok = np.fromiter((len(p.tokens) for p in passes), dtype=np.int64, count=n)
+        if n_tok.sum() <= 4096 and not any(isinstance(p.tokens, np.ndarray) for p in passes):
+            tok = np.fromiter(chain(p.tokens for p in passes), dtype=np.int32, count=int(n_tok.sum()))
+        else:
+            tok = np.concatenate([np.asarray(p.tokens, dtype=np.int32).reshape(-1) for p in passes])
+        n_ro = np.fromiter((len(p.readout) for p in passes), dtype=np.int64, count=n)
+        R = int(n_ro.sum())
+        ro = np.fromiter(chain(p.readout for p in passes), dtype=np.int32, count=R) if R else np.zeros(1, np.int32)
+        epi = np.zeros(max(R, 1), dtype=EPI_DT)
+        if R:
+            epis = list(chain(p.epi for p in passes))
+            epi["kind"] = np.fromiter((e[0] for e in epis), dtype=np.int32, count=R)
+            epi["temperature"] = np.fromiter((e[1] for e in epis), dtype=np.float32, count=R)
+            epi["seed"] = np.fromiter((int(e[2]) & 0xFFFFFFFFFFFFFFFF for e in epis), dtype=np.uint64, count=R)
+        has_pos = np.fromiter((p.positions is not None for p in passes), dtype=bool, count=n)
+        pos = None
+        if has_pos.any():
+            pos = np.concatenate([np.asarray(p.positions if p.positions is not None else np.zeros(len(p.tokens)),
+                                             dtype=np.int32).reshape(-1) for p in passes])
+        tok_off = np.zeros(n, dtype=np.uint64)
+        np.cumsum(n_tok[:-1], out=tok_off[1:])
+        ro_off = np.zeros(n, dtype=np.uint64)
+        np.cumsum(n_ro[:-1], out=ro_off[1:])
+        arr = np.zeros(n, dtype=PASS_DT)
+        arr["ws"] = np.fromiter((p.ws for p in passes), dtype=np.uint64, count=n)
+        arr["tokens"] = np.uint64(tok.ctypes.data) + tok_off * np.uint64(4)
+        if pos is not None:
+            arr["positions"] = np.where(has_pos, np.uint64(pos.ctypes.data) + tok_off * np.uint64(4), np.uint64(0))
+        arr["n_tokens"] = n_tok
+        arr["readout"] = np.where(n_ro > 0, np.uint64(ro.ctypes.data) + ro_off * np.uint64(4), np.uint64(0))
+        arr["n_readout"] = n_ro
+        arr["epi"] = np.where(n_ro > 0, np.uint64(epi.ctypes.data) + ro_off * np.uint64(EPI_DT.itemsize),
+                              np.uint64(0))
+        arr["commit"] = np.fromiter((p.commit for p in passes), dtype=np.int32, count=n)
+        return arr, [tok, ro, epi, pos, arr]
+
+    def decode_step(self, ws: np.ndarray, tokens: np.ndarray, kind=0, temperature=1.0, seed=0,
+                    flags: int = 0, logits_out=None) -> np.ndarray:
+        """One decode token for each working set in `ws` (uint64 handles), read
+        out with the given epilogue (scalars or per-row arrays); committed.
+        The same pie_forward call as forward(), with the pass array built by
+        vector operations on buffers reused across calls of the same batch size.
+        Returns the token ids (int32)."""
+        n = len(ws)
+        buf = self._decode_bufs.get(n)
+        if buf is None:
+            arr = np.zeros(n, dtype=PASS_DT)
+            tok = np.zeros(n, dtype=np.int32)
+            ro = np.zeros(n, dtype=np.int32)
+            epi = np.zeros(n, dtype=EPI_DT)
+            out = np.zeros(n, dtype=np.int32)
+            idx = np.arange(n, dtype=np.uint64)
+            arr["tokens"] = np.uint64(tok.ctypes.data) + idx * np.uint64(4)
+            arr["n_tokens"] = 1
+            arr["readout"] = np.uint64(ro.ctypes.data)  # every pass reads out its only row
+            arr["n_readout"] = 1
+            arr["epi"] = np.uint64(epi.ctypes.data) + idx * np.uint64(EPI_DT.itemsize)
+            arr["commit"] = 1
+            buf = self._decode_bufs[n] = (arr, tok, epi, out)
+        arr, tok, epi, out = buf
+        arr["ws"] = ws
+        tok[:] = tokens
+        epi["kind"] = kind
+        epi["temperature"] = temperature
+        epi["seed"] = seed
+        logits_ptr = None
+        if logits_out is not None:
+            logits_ptr = logits_out.data_ptr()
+            flags |= N.PIE_FLAG_LOGITS_DEVICE
+        check(N.lib().pie_forward(self.ctx, arr.ctypes.data_as(ctypes.POINTER(N.pie_pass)), n,
+                                  out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), logits_ptr, flags))
+        return out.copy()
 
     def forward(self, passes: Sequence[Pass], want_logits: bool = False, flags: int = 0,
                 logits_out=None):
@@ -196,7 +273,7 @@ class PieRuntime:
         elif want_logits and R:
             logits = np.empty((R, self.shape.vocab), dtype=np.float32)
             logits_ptr = logits.ctypes.data
-        check(N.lib().pie_forward(self.ctx, arr, len(passes),
+        check(N.lib().pie_forward(self.ctx, arr.ctypes.data_as(ctypes.POINTER(N.pie_pass)), len(passes),
                                   toks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                   logits_ptr, flags))
         del keep
