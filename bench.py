@@ -36,7 +36,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(shape, recipe, n_seq=2, n_layers=2):
+def cpu_baseline(shape, recipe, n_seq=4, n_layers=8):
     """The oracle's decode step on a bounded sample, scaled to a full step:
     `n_seq` decode rows (context 2048, synthetic bf16 K/V) through `n_layers`
     layers plus the head, timed on the host cores."""
@@ -117,8 +117,34 @@ def summarize(out_dir):
              "duration from `c2_kernel_stats.csv`.", "",
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
     for r in stats[:24]:
-        lines.append("| `%s` | %s | %.2f | %.2f | %s |" % (short_name(r["Name"]), r["Calls"],
-                     float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6, r["Percentage"][:5]))
+        lines.append("| `%s` | %s | %.2f | %.2f | %.3f |" % (short_name(r["Name"]), r["Calls"],
+                     float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    # one decode step from the trace: the launches from a 64-row embedding to the next
+    trace = sorted(csv.DictReader(open(glob.glob(os.path.join(out_dir, "trace_c2", "*kernel_trace.csv"))[0])),
+                   key=lambda r: int(r["Start_Timestamp"]))
+    steps, cur = [], None
+    for r in trace:
+        if "embed_kernel" in r["Kernel_Name"]:
+            cur = [] if int(r["Grid_Size_X"]) == N_SEQ * 256 else None
+            if cur is not None:
+                steps.append(cur)
+        if cur is not None:
+            cur.append(r)
+    if len(steps) > 2:
+        st = steps[len(steps) // 2]
+        span = (int(st[-1]["End_Timestamp"]) - int(st[0]["Start_Timestamp"])) / 1e3
+        agg = {}
+        for r in st:
+            k = short_name(r["Kernel_Name"])
+            a = agg.setdefault(k, [0, 0.0])
+            a[0] += 1
+            a[1] += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        busy = sum(v[1] for v in agg.values())
+        lines += ["", "One decode step (the middle one of the run): %d launches, %.1f us from the first "
+                  "kernel's start to the last one's end, %.1f us of it inside kernels." % (len(st), span, busy),
+                  "", "| kernel | launches per step | us per step |", "|---|---|---|"]
+        for k, (n, d) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+            lines.append("| `%s` | %d | %.1f |" % (k, n, d))
     with open(os.path.join(prof, "decode_llama8b_b64_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
