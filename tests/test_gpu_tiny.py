@@ -278,3 +278,49 @@ def test_pack_weight_layout(torch_cuda, n, k):
     np.testing.assert_array_equal(got, packed_reference(w))
     # overlapping buffers are refused
     assert N.lib().pie_pack_weight(dst.data_ptr(), dst.data_ptr(), n, k, None) == N.PIE_EINVAL
+
+
+def test_tiny_readout_lanes_positions_and_rollback(torch_cuda):
+    """Several readout rows per pass (Gumbel lanes 0..2, unordered), explicit
+    RoPE positions with a gap, a single-token first pass, and a writable
+    buffer rolled back with pie_truncate before new tokens are appended."""
+    from paged_kv_forward_amd.runtime import Pass
+    recipe = RECIPES["gains_spread"]
+    shape = recipe.shape
+    w = SynthWeights(recipe, cache_layers=True)
+    num = default_numerics(shape)
+    rt = make_runtime(shape, recipe, torch_cuda)
+    rep = Report()
+    a, b = rt.alloc(), rt.alloc()
+    toks_a = synth.prompt_tokens(1, 70, 20, shape.vocab)
+    pos_a = list(range(5, 15)) + list(range(115, 125))        # a gap of 100 positions
+    ro_a = [19, 3, 10]
+    epi_a = [(1, 0.7, 777), (1, 0.7, 777), (1, 0.7, 777)]     # lanes 0, 1, 2 of one seed
+    tok_b = [int(synth.prompt_tokens(1, 71, 1, shape.vocab)[0])]  # a first pass of one token
+    toks, lg = rt.forward([Pass(a, toks_a, ro_a, epi_a, positions=pos_a),
+                           Pass(b, tok_b, [0], [(0, 1.0, 0)])], want_logits=True)
+    sa, sb = Session(w, num), Session(w, num)
+    ref_a = sa.step(toks_a, positions=pos_a, readout=ro_a)
+    ref_b = sb.step(tok_b)
+    for j in range(3):
+        t, m = apply(ref_a[j], 1, 0.7, 777, j)
+        rep.add(toks[j], t, m, tau_for(1, 0.7), lg[j], ref_a[j], ("lane", j))
+    t, m = apply(ref_b[0], 0)
+    rep.add(toks[3], t, m, tau_for(0, 1.0), lg[3], ref_b[0], ("single", 0))
+    # uncommitted draft of 6 tokens, read out, then rolled back
+    draft = synth.prompt_tokens(1, 72, 6, shape.vocab)
+    rt.forward([Pass(a, draft, [5], [(0, 1.0, 0)], positions=list(range(125, 131)), commit=False)])
+    info = rt.ws_info(a)
+    assert info["len"] == 26 and info["frozen_len"] == 20
+    rt.truncate(a, 20)
+    assert rt.ws_info(a)["len"] == 20
+    new = synth.prompt_tokens(1, 73, 3, shape.vocab)
+    toks, lg = rt.forward([Pass(a, new, [0, 2], [(0, 1.0, 0), (1, 1.0, 5)], positions=[125, 126, 127])],
+                          want_logits=True)
+    ref = sa.step(new, positions=[125, 126, 127], readout=[0, 2])
+    t, m = apply(ref[0], 0)
+    rep.add(toks[0], t, m, tau_for(0, 1.0), lg[0], ref[0], ("after rollback", 0))
+    t, m = apply(ref[1], 1, 1.0, 5, 1)
+    rep.add(toks[1], t, m, tau_for(1, 1.0), lg[1], ref[1], ("after rollback", 2))
+    rep.check()
+    rt.close()
