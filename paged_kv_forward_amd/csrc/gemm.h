@@ -92,8 +92,11 @@ struct GemmArgs {
 // Tile configurations.  TILE_SKINNY: M <= 64 with a bf16 A operand, 128 output
 // columns per workgroup, weights streamed through registers (decode).
 // TILE_256x256: prefill-sized M with a bf16 A operand and EPI_QKV, EPI_RESID
-// or EPI_SWIGLU (for EPI_QKV the q and k/v widths must be multiples of 256).
-enum GemmTile { TILE_64x128 = 0, TILE_128x128 = 1, TILE_SKINNY = 2, TILE_256x256 = 3 };
+// or EPI_SWIGLU (for EPI_QKV the q and k/v widths must be multiples of 256);
+// operands are loaded straight into LDS when K is a multiple of 32 and A rows
+// are 16-byte aligned, else staged through registers.  TILE_256x256_STAGED
+// always stages through registers (same results, bit for bit).
+enum GemmTile { TILE_64x128 = 0, TILE_128x128 = 1, TILE_SKINNY = 2, TILE_256x256 = 3, TILE_256x256_STAGED = 4 };
 
 // Most K splits of one skinny GEMM.
 constexpr int SK_MAX_SPLITS = 16;

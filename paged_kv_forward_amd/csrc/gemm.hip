@@ -11,6 +11,7 @@
 // in-kernel device-scope fence would write back and invalidate the whole L2
 // of the XCD for every workgroup.
 #include <climits>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm.h"
@@ -41,36 +42,59 @@ struct Cfg {
 };
 
 // Epilogue over rows [m0, m0 + rows) of output tile n_tile, whose fp32 values
-// are in sC (row stride ldc).  Called by all 256 threads of a workgroup.
-template <int EPI, int BN, int NTH = 256>
+// are in sC (row stride ldc).  Called by all NTH threads of a workgroup.
+// Global loads are issued B units at a time before any of their
+// results is used, so a wave waits for memory once per batch rather than
+// once per row (tiles run one workgroup, one wave per SIMD, per CU, so
+// nothing else hides that latency).
+template <int EPI, int BN, int NTH = 256, int B = 8>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int ldc, int m0, int rows,
                                          int n_tile) {
   constexpr int NW = NTH / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if constexpr (EPI == EPI_RESID) {
-    // y += C; per-64-column sums of squares of the new y for the next RMSNorm
-    const int n0 = n_tile * BN;
-    constexpr int CH = BN / 64;
-    for (int p = wave; p < rows * CH; p += NW) {
-      int row = p / CH, ch = p % CH, m = m0 + row;
-      if (m >= g.M) continue;
-      const int col = ch * 64 + lane;
-      const size_t off = (size_t)m * g.ldy + n0 + col;
-      const float v = g.y_out[off] + sC[row * ldc + col];
-      g.y_out[off] = v;
-      const float s = wave_sum(v * v);
-      if (lane == 0) g.ss_out[(size_t)m * g.n_ss + n0 / 64 + ch] = s;
+    // y += C, and the per-64-column sums of squares of the new y for the
+    // next RMSNorm.  A wave step covers RPI rows x BN columns, a float4 per
+    // lane; the 16 lanes of a 64-column chunk reduce its sum of squares.
+    constexpr int F4 = BN / 4, RPI = 64 / F4;
+    const int n0 = n_tile * BN, c4 = lane % F4, rs = lane / F4, col = c4 * 4;
+    const bool col_ok = n0 + col < g.N;  // N is a multiple of 64
+    const int steps = (rows + RPI - 1) / RPI;
+    for (int s0 = wave; s0 < steps; s0 += NW * B) {
+      float4 v[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int row = (s0 + u * NW) * RPI + rs, m = m0 + row;
+        const bool ok = s0 + u * NW < steps && row < rows && m < g.M && col_ok;
+        v[u] = ok ? *reinterpret_cast<const float4*>(g.y_out + (size_t)m * g.ldy + n0 + col)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int row = (s0 + u * NW) * RPI + rs, m = m0 + row;
+        const bool ok = s0 + u * NW < steps && row < rows && m < g.M && col_ok;
+        float4 c = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ok) c = *reinterpret_cast<const float4*>(sC + row * ldc + col);
+        const float4 nv = make_float4(v[u].x + c.x, v[u].y + c.y, v[u].z + c.z, v[u].w + c.w);
+        if (ok) *reinterpret_cast<float4*>(g.y_out + (size_t)m * g.ldy + n0 + col) = nv;
+        float sq = nv.x * nv.x + nv.y * nv.y + nv.z * nv.z + nv.w * nv.w;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+        if (ok && (lane & 15) == 0) g.ss_out[(size_t)m * g.n_ss + (n0 + col) / 64] = sq;
+      }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    constexpr int HALF = BN / 2;
+    // h = bf16(silu(gate) * up), four columns per thread (N is a multiple of 8)
+    constexpr int HALF = BN / 2, F4 = HALF / 4;
     const int j0 = n_tile * HALF;
-    for (int idx = tid; idx < rows * HALF; idx += NTH) {
-      int row = idx / HALF, j = idx % HALF, m = m0 + row, n = j0 + j;
-      if (m < g.M && n < g.N) {
-        float gt = sC[row * ldc + j], up = sC[row * ldc + HALF + j];
-        float h = gt / (1.0f + expf(-gt)) * up;
-        g.h_out[(size_t)m * g.N + n] = f2bf(h);
-      }
+    for (int idx = tid; idx < rows * F4; idx += NTH) {
+      const int row = idx / F4, j = (idx % F4) * 4, m = m0 + row, n = j0 + j;
+      if (m >= g.M || n >= g.N) continue;
+      const float4 gt = *reinterpret_cast<const float4*>(sC + row * ldc + j);
+      const float4 up = *reinterpret_cast<const float4*>(sC + row * ldc + HALF + j);
+      const float h0 = gt.x / (1.0f + expf(-gt.x)) * up.x, h1 = gt.y / (1.0f + expf(-gt.y)) * up.y;
+      const float h2 = gt.z / (1.0f + expf(-gt.z)) * up.z, h3 = gt.w / (1.0f + expf(-gt.w)) * up.w;
+      *reinterpret_cast<uint2*>(g.h_out + (size_t)m * g.N + n) = make_uint2(pack_bf2(h0, h1), pack_bf2(h2, h3));
     }
   } else if constexpr (EPI == EPI_QKV) {
     const int n0 = n_tile * BN;
@@ -78,81 +102,128 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int
     const int qw = g.nq * hd, kw = g.nkv * hd;
     const int kind = n0 < qw ? 0 : (n0 < qw + kw ? 1 : 2);
     if (kind < 2) {
-      for (int idx = tid; idx < rows * (BN / 2); idx += NTH) {
-        int row = idx / (BN / 2), pr = idx % (BN / 2), m = m0 + row;
-        if (m >= g.M) continue;
-        int hl = pr / hd2, dd = pr % hd2;
-        int c1 = hl * hd + dd, c2 = c1 + hd2;
-        float cs = g.rope_cs[((size_t)m * hd2 + dd) * 2], sn = g.rope_cs[((size_t)m * hd2 + dd) * 2 + 1];
-        float x1 = sC[row * ldc + c1], x2 = sC[row * ldc + c2];
-        float o1 = x1 * cs - x2 * sn, o2 = x2 * cs + x1 * sn;
-        if (kind == 0) {
-          int head = (n0 + c1) / hd;
-          uint16_t* q = g.q_out + (size_t)m * qw + head * hd;
-          q[dd] = f2bf(o1);
-          q[dd + hd2] = f2bf(o2);
-        } else {
-          int kvh = (n0 - qw + c1) / hd;
-          int sl = g.slot[m], page = sl / P, off = sl % P;
-          // K page layout [kv head][hd / 8][token][8]
-          size_t base = (size_t)page * g.page_stride + (size_t)kvh * P * hd + (size_t)off * 8;
-          const size_t i1 = base + (size_t)(dd >> 3) * P * 8 + (dd & 7);
-          const size_t i2 = base + (size_t)((dd + hd2) >> 3) * P * 8 + ((dd + hd2) & 7);
-          if (g.kv_e4m3) {
-            float s = g.kv_scale[kvh];
-            uint8_t* kv = reinterpret_cast<uint8_t*>(g.kv_layer);
-            kv[i1] = f2e4m3(o1 / s);
-            kv[i2] = f2e4m3(o2 / s);
+      // RoPE on q or k: a wave step is one row's 64 consecutive rotation
+      // pairs (a tile row holds BN / 2 pairs, hd / 2 per head).
+      constexpr int UPR = BN / 2 / 64;
+      const int steps = rows * UPR;
+      for (int s0 = wave; s0 < steps; s0 += NW * B) {
+        float2 cs[B];
+        int sl[B];
+        float sc[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          const int st = s0 + u * NW, row = st / UPR, pr = (st % UPR) * 64 + lane, m = m0 + row;
+          const bool ok = st < steps && m < g.M;
+          const int dd = pr % hd2, kvh = (n0 - qw + pr / hd2 * hd) / hd;
+          cs[u] = ok ? *reinterpret_cast<const float2*>(g.rope_cs + ((size_t)m * hd2 + dd) * 2) : make_float2(1.f, 0.f);
+          sl[u] = ok && kind == 1 ? g.slot[m] : 0;
+          sc[u] = ok && kind == 1 && g.kv_e4m3 ? g.kv_scale[kvh] : 1.f;
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          const int st = s0 + u * NW, row = st / UPR, pr = (st % UPR) * 64 + lane, m = m0 + row;
+          if (st >= steps || m >= g.M) continue;
+          const int hl = pr / hd2, dd = pr % hd2;
+          const int c1 = hl * hd + dd, c2 = c1 + hd2;
+          const float x1 = sC[row * ldc + c1], x2 = sC[row * ldc + c2];
+          const float o1 = x1 * cs[u].x - x2 * cs[u].y, o2 = x2 * cs[u].x + x1 * cs[u].y;
+          if (kind == 0) {
+            const int head = (n0 + c1) / hd;
+            uint16_t* q = g.q_out + (size_t)m * qw + head * hd;
+            q[dd] = f2bf(o1);
+            q[dd + hd2] = f2bf(o2);
           } else {
-            uint16_t* kv = reinterpret_cast<uint16_t*>(g.kv_layer);
-            kv[i1] = f2bf(o1);
-            kv[i2] = f2bf(o2);
+            const int kvh = (n0 - qw + c1) / hd;
+            const int page = sl[u] / P, off = sl[u] % P;
+            // K page layout [kv head][hd / 8][token][8]
+            const size_t base = (size_t)page * g.page_stride + (size_t)kvh * P * hd + (size_t)off * 8;
+            const size_t i1 = base + (size_t)(dd >> 3) * P * 8 + (dd & 7);
+            const size_t i2 = base + (size_t)((dd + hd2) >> 3) * P * 8 + ((dd + hd2) & 7);
+            if (g.kv_e4m3) {
+              uint8_t* kv = reinterpret_cast<uint8_t*>(g.kv_layer);
+              kv[i1] = f2e4m3(o1 / sc[u]);
+              kv[i2] = f2e4m3(o2 / sc[u]);
+            } else {
+              uint16_t* kv = reinterpret_cast<uint16_t*>(g.kv_layer);
+              kv[i1] = f2bf(o1);
+              kv[i2] = f2bf(o2);
+            }
           }
         }
       }
     } else {
-      for (int idx = tid; idx < rows * BN; idx += NTH) {
-        int row = idx / BN, c = idx % BN, m = m0 + row;
-        if (m >= g.M) continue;
-        int vc = n0 - qw - kw + c, kvh = vc / hd, dd = vc % hd;
-        int sl = g.slot[m], page = sl / P, off = sl % P;
-        size_t idx_v = (size_t)page * g.page_stride + (size_t)g.nkv * P * hd + (size_t)kvh * hd * P +
-                       (size_t)dd * P + off;
-        float x = sC[row * ldc + c];
-        if (g.kv_e4m3) {
-          reinterpret_cast<uint8_t*>(g.kv_layer)[idx_v] = f2e4m3(x / g.kv_scale[g.nkv + kvh]);
-        } else {
-          reinterpret_cast<uint16_t*>(g.kv_layer)[idx_v] = f2bf(x);
+      // v: a wave step is one row's 64 consecutive columns; V page layout [kv head][hd][token]
+      constexpr int UPR = BN / 64;
+      const int steps = rows * UPR;
+      for (int s0 = wave; s0 < steps; s0 += NW * B) {
+        int sl[B];
+        float sc[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          const int st = s0 + u * NW, row = st / UPR, c = (st % UPR) * 64 + lane, m = m0 + row;
+          const bool ok = st < steps && m < g.M;
+          const int kvh = (n0 - qw - kw + c) / hd;
+          sl[u] = ok ? g.slot[m] : 0;
+          sc[u] = ok && g.kv_e4m3 ? g.kv_scale[g.nkv + kvh] : 1.f;
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          const int st = s0 + u * NW, row = st / UPR, c = (st % UPR) * 64 + lane, m = m0 + row;
+          if (st >= steps || m >= g.M) continue;
+          const int vc = n0 - qw - kw + c, kvh = vc / hd, dd = vc % hd;
+          const int page = sl[u] / P, off = sl[u] % P;
+          const size_t idx_v = (size_t)page * g.page_stride + (size_t)g.nkv * P * hd + (size_t)kvh * hd * P +
+                               (size_t)dd * P + off;
+          const float x = sC[row * ldc + c];
+          if (g.kv_e4m3) {
+            reinterpret_cast<uint8_t*>(g.kv_layer)[idx_v] = f2e4m3(x / sc[u]);
+          } else {
+            reinterpret_cast<uint16_t*>(g.kv_layer)[idx_v] = f2bf(x);
+          }
         }
       }
     }
   } else if constexpr (EPI == EPI_LOGITS) {
+    // one wave per row; the row's readout parameters are loaded a batch of rows at a time
     const int n0 = n_tile * BN;
-    for (int row = wave; row < rows; row += NW) {
-      int m = m0 + row;
-      if (m >= g.M) continue;
-      const int kind = g.ro_kind[m];
-      const float T = g.ro_temp[m];
-      const uint32_t lo = g.ro_seed_lo[m], hi = g.ro_seed_hi[m], ln = (uint32_t)g.ro_lane[m];
-      float best = -INFINITY;
-      int bi = INT_MAX;
-      for (int c = lane; c < BN; c += 64) {
-        int v = n0 + c;
-        if (v >= g.N) break;
-        float l = sC[row * ldc + c];
-        if (g.logits) g.logits[(size_t)m * g.N + v] = l;
-        float s = kind == 0 ? l : l / T + gumbel((uint32_t)v, ln, lo, hi);
-        if (s > best) { best = s; bi = v; }
+    for (int r0 = wave; r0 < rows; r0 += NW * B) {
+      int kd[B], ln[B];
+      float tp[B];
+      uint32_t lo[B], hi[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int row = r0 + u * NW, m = m0 + row;
+        const bool ok = row < rows && m < g.M;
+        kd[u] = ok ? g.ro_kind[m] : 0;
+        tp[u] = ok ? g.ro_temp[m] : 1.f;
+        lo[u] = ok ? g.ro_seed_lo[m] : 0u;
+        hi[u] = ok ? g.ro_seed_hi[m] : 0u;
+        ln[u] = ok ? g.ro_lane[m] : 0;
       }
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        float ob = __shfl_xor(best, o, 64);
-        int oi = __shfl_xor(bi, o, 64);
-        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-      }
-      if (lane == 0) {
-        g.tile_best[(size_t)n_tile * g.M + m] = best;
-        g.tile_idx[(size_t)n_tile * g.M + m] = bi;
+      for (int u = 0; u < B; ++u) {
+        const int row = r0 + u * NW, m = m0 + row;
+        if (row >= rows || m >= g.M) continue;
+        float best = -INFINITY;
+        int bi = INT_MAX;
+        for (int c = lane; c < BN; c += 64) {
+          const int v = n0 + c;
+          if (v >= g.N) break;
+          const float l = sC[row * ldc + c];
+          if (g.logits) g.logits[(size_t)m * g.N + v] = l;
+          const float sv = kd[u] == 0 ? l : l / tp[u] + gumbel((uint32_t)v, (uint32_t)ln[u], lo[u], hi[u]);
+          if (sv > best) { best = sv; bi = v; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const float ob = __shfl_xor(best, o, 64);
+          const int oi = __shfl_xor(bi, o, 64);
+          if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+        }
+        if (lane == 0) {
+          g.tile_best[(size_t)n_tile * g.M + m] = best;
+          g.tile_idx[(size_t)n_tile * g.M + m] = bi;
+        }
       }
     }
   }
@@ -481,7 +552,215 @@ __global__ __launch_bounds__(BG_NT, 2) void gemm_big_kernel(GemmArgs g) {
       }
     }
     __syncthreads();
-    epilogue<EPI, BG_BN, BG_NT>(g, sC, BG_LDC, m0 + pass * 64, 64, n_tile);
+    epilogue<EPI, BG_BN, BG_NT, 2>(g, sC, BG_LDC, m0 + pass * 64, 64, n_tile);
+    __syncthreads();
+  }
+}
+
+// Raw buffer descriptor over [base, base + bytes); loads past the end read zeros.
+constexpr uint32_t OOB = 0xFFFFFFF0u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS form of the 256 x 256 tile (K a multiple of 64, A rows
+// 16-byte aligned).  Operands go from memory straight into LDS with 16-byte
+// buffer loads that write LDS (lane l of a load writes bytes [16l, 16l + 16)
+// of a 1 KiB block at a wave-uniform address): staging costs no VGPRs and no
+// LDS store instructions.  Four waves, one per SIMD, each own a 128 x 128
+// block (4 x 4 32x32x16 MFMAs, 256 fp32 accumulators); K advances in stages
+// of 64 through two LDS buffers.
+//  - A stage: 256 rows of 128 bytes.  Row r's eight 16-byte chunks sit at
+//    slots chunk ^ swz(r), so the MFMA operand reads (32 rows at one chunk)
+//    hit every bank once both in 8-lane and in 16-lane LDS phases.  One load
+//    covers 8 whole rows (whole 128-byte lines); each lane fetches the chunk
+//    that belongs in its slot.
+//  - B stage: the four 64-row blocks of the tiled weight layout, 8 KiB each,
+//    copied as they are; the operand reads are contiguous 256-byte runs.
+// The loop is software-pipelined and its order pinned by scheduling
+// barriers, because with one wave per SIMD the wave itself must keep the
+// matrix core busy: each k-step's 16 MFMAs run while the next k-step's
+// operands are read from LDS.  One barrier per stage, between k-steps 2 and
+// 3: by then every wave has read all of stage t (k-step 3's operands were
+// read during k-step 2) and waited for its own loads of stage t + 1, so
+// after it stage t + 1 may be read and stage t + 2 loaded into t's buffer.
+constexpr int DG_BK = 64, DG_NT = 256;
+constexpr int DG_STAGE = (BG_BM + BG_BN) * DG_BK * 2;  // 64 KiB
+constexpr int DG_LDS = 2 * DG_STAGE;                    // 128 KiB
+static_assert(64 * BG_LDC * 4 <= DG_LDS, "epilogue pass fits in the stage buffers");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor words over [base, base + bytes) (raw, no stride).
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// 16-byte buffer load into LDS: lane l's bytes [voff + soff, + 16) of the
+// buffer go to LDS bytes [16l, 16l + 16) past `lds` (wave-uniform).  Written
+// as inline assembly so that the compiler does not track it: it would
+// otherwise make every LDS read wait for all such loads in flight.  The
+// caller waits for them with s_waitcnt vmcnt.  M0 carries the LDS address;
+// the nop covers the M0-write hazard of these loads.
+__device__ __forceinline__ void dma16(i32x4_t r, const void* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m = (uint32_t)(size_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+
+__device__ __forceinline__ int dg_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// s_waitcnt: vector-memory counter at most n and every LDS access of the wave
+// complete (expcnt left at its maximum).
+#define DG_WAIT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x70)
+
+// Barrier without a memory fence: a workgroup-scope fence would also wait for
+// every LDS-writing load in flight, which is what the pipeline keeps in
+// flight.  The memory clobber keeps the compiler from moving LDS accesses
+// across it; the loads a wave depends on are waited for before it.
+__device__ __forceinline__ void dg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int EPI>
+__global__ __launch_bounds__(DG_NT, 1) void gemm_dma_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DG_LDS];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, lh = lane >> 5;
+
+  int n_tile, m_tile;
+  {
+    const int n_tiles = big_tiles_n<EPI>(g), m_tiles = (g.M + BG_BM - 1) / BG_BM;
+    const int m_win = (m_tiles + 15) / 16;
+    const int pid = blockIdx.x, win = pid >> 8, x = pid & 7, j = (pid & 255) >> 3;
+    m_tile = (win % m_win) * 16 + (x & 3) * 4 + (j & 3);
+    n_tile = (win / m_win) * 16 + (x >> 2) * 8 + (j >> 2);
+    if (m_tile >= m_tiles || n_tile >= n_tiles) return;
+  }
+  const int m0 = m_tile * BG_BM;
+  const int nk = g.K / DG_BK;  // = 64-column blocks of the packed weights
+
+  // A: this wave loads rows 64 * wave .. + 63 of every stage (eight 8-row
+  // loads).  Rows past M read row M - 1 (their outputs are never stored).
+  const i32x4_t ra = rsrc_words(g.a, (uint32_t)((size_t)g.M * g.lda * 2));
+  uint32_t a_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = wave * 64 + i * 8 + (lane >> 3);
+    const int m = min(m0 + r, g.M - 1);
+    a_off[i] = (uint32_t)(((size_t)m * g.lda + (((lane & 7) ^ dg_swz(r)) * 8)) * 2);
+  }
+  // B: this wave loads the tile's 64-row block `wave` (8 KiB per stage).
+  // Blocks past N read the last one (their outputs are never stored).
+  i32x4_t rb;
+  {
+    const uint16_t* base;
+    if (EPI == EPI_SWIGLU) {
+      const int t64 = min(n_tile * 2 + (wave & 1), (g.N - 1) >> 6);
+      base = g.w[wave >> 1] + (size_t)t64 * nk * 4096;
+    } else {
+      const int n = min(n_tile * BG_BN + wave * 64, g.N - 1);
+      const int s = n >= g.seg_n0[1] ? (n >= g.seg_n0[2] ? 2 : 1) : 0;
+      base = g.w[s] + (size_t)((n - g.seg_n0[s]) >> 6) * nk * 4096;
+    }
+    rb = rsrc_words(base, (uint32_t)nk * 8192u);
+  }
+  // Load i (0..15) of stage t.  Every iteration issues them, also for t >=
+  // nk, so that the loop body is one branch-free block: past the end, A
+  // lanes use an offset beyond the buffer and B offsets run past the matrix
+  // row, both of which read zeros without touching memory, into the buffer
+  // of a stage that is no longer read.
+  auto issue_one = [&](int t, int i) {
+    uint8_t* st = smem + (t & 1) * DG_STAGE;
+    if (i < 8) {
+      const bool live = t < nk;
+      dma16(ra, st + (wave * 8 + i) * 1024, live ? a_off[i] : OOB, live ? (uint32_t)t * (DG_BK * 2) : 0u);
+    } else {
+      dma16(rb, st + BG_BM * 128 + wave * 8192 + (i - 8) * 1024, (uint32_t)lane * 16u,
+            (uint32_t)t * 8192u + (uint32_t)(i - 8) * 1024u);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+
+  // Operand fragment f of k-step ks of stage t: f < 4 the A rows of block f,
+  // f >= 4 the B columns of block f - 4.
+  const int a_rd = (wm * 128 + l32) * 128;
+  const int a_sw = dg_swz(l32);  // swz depends on the row mod 16 only
+  const int b_rd = BG_BM * 128 + wn * 2 * 8192 + (l32 >> 4) * 2048 + lh * 256 + (l32 & 15) * 16;
+  auto frag = [&](int t, int ks, int f) -> uint4 {
+    const uint8_t* st = smem + (t & 1) * DG_STAGE;
+    if (f < 4) return *reinterpret_cast<const uint4*>(st + a_rd + f * 4096 + (((ks * 2 + lh) ^ a_sw) * 16));
+    const int b = f - 4;  // column block b: 64-row block (wn * 128 + b * 32) / 64, panel offset
+    return *reinterpret_cast<const uint4*>(st + b_rd + (b >> 1) * 8192 + (b & 1) * 4096 + (ks >> 1) * 1024 +
+                                           (ks & 1) * 512);
+  };
+
+  uint4 FA[8], FB[8];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) issue_one(0, i);
+  __builtin_amdgcn_s_waitcnt(DG_WAIT(0));
+  dg_barrier();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) issue_one(1, i);
+#pragma unroll
+  for (int f = 0; f < 8; ++f) FA[f] = frag(0, 0, f);
+
+  for (int t = 0; t < nk; ++t) {
+    // k-steps 0..2: MFMAs on one fragment set while the next is read
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      uint4 (&cur)[8] = (ks & 1) ? FB : FA;
+      uint4 (&nxt)[8] = (ks & 1) ? FA : FB;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int a = q >> 2, b = q & 3;
+        acc[a][b] = mfma32(cur[a], cur[4 + b], acc[a][b]);
+        if (q < 8) nxt[q] = frag(t, ks + 1, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // stage t + 1 landed everywhere; all of stage t has been read
+    __builtin_amdgcn_s_waitcnt(DG_WAIT(0));
+    dg_barrier();
+    // k-step 3 (FB) while reading k-step 0 of stage t + 1 (FA; unused past
+    // the last stage) and loading stage t + 2 into stage t's buffer
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int a = q >> 2, b = q & 3;
+      acc[a][b] = mfma32(FB[a], FB[4 + b], acc[a][b]);
+      if (q < 8) FA[q] = frag(t + 1, 0, q);
+      issue_one(t + 2, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(DG_WAIT(0));
+  __syncthreads();
+
+  float* sC = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    if (wm == (pass >> 1)) {
+#pragma unroll
+      for (int ah = 0; ah < 2; ++ah) {
+        const int a = (pass & 1) * 2 + ah;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = ah * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+            sC[row * BG_LDC + wn * 128 + b * 32 + l32] = acc[a][b][i];
+          }
+      }
+    }
+    __syncthreads();
+    epilogue<EPI, BG_BN, DG_NT>(g, sC, BG_LDC, m0 + pass * 64, 64, n_tile);
     __syncthreads();
   }
 }
@@ -510,11 +789,6 @@ constexpr int SK_GK = SK_KC * SK_DEPTH;          // K of one activation group (5
 constexpr int SK_LDX = SK_GK + 8;                // bf16 per LDS row (16-byte pad)
 constexpr int SK_XP = 64 * SK_GK / 8 / SK_NT;    // 16-byte activation pieces per thread per group (8)
 constexpr int SK_LDS = 2 * 64 * SK_LDX * 2 > 64 * SK_LDC * 4 ? 2 * 64 * SK_LDX * 2 : 64 * SK_LDC * 4;
-constexpr uint32_t OOB = 0xFFFFFFF0u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 template <int CPOL = 0>
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
@@ -774,18 +1048,19 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* tile_bes
   if (lane == 0) tokens[m] = bi == INT_MAX ? -1 : bi;
 }
 
-int gemm_tile_bm(int tile) { return tile == TILE_64x128 ? 64 : (tile == TILE_256x256 ? 256 : 128); }
-int gemm_tile_bn(int tile) { return tile == TILE_256x256 ? 256 : 128; }
+int gemm_tile_bm(int tile) { return tile == TILE_64x128 ? 64 : (tile >= TILE_256x256 ? 256 : 128); }
+int gemm_tile_bn(int tile) { return tile >= TILE_256x256 ? 256 : 128; }
 
 int gemm_n_tiles(int epi, int N, int tile) {
   const int bn = gemm_tile_bn(tile);
   return epi == EPI_SWIGLU ? (N + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
 }
 
-template <int EPI>
+template <int EPI, bool DMA>
 static void launch_big(const GemmArgs& g, hipStream_t st) {
   const int m_win = ((g.M + BG_BM - 1) / BG_BM + 15) / 16, n_win = (gemm_n_tiles(EPI, g.N, TILE_256x256) + 15) / 16;
-  hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(m_win * n_win * 256), dim3(BG_NT), 0, st, g);
+  if (DMA) hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3(m_win * n_win * 256), dim3(DG_NT), 0, st, g);
+  else hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(m_win * n_win * 256), dim3(BG_NT), 0, st, g);
 }
 
 // Large tiles (prefill-sized M) never split K: there are enough output tiles.
@@ -844,12 +1119,14 @@ void launch_gemm(int amode, int epi, int tile, const GemmArgs& g, hipStream_t st
     }
     return;
   }
-  if (tile == TILE_256x256) {
+  if (tile == TILE_256x256 || tile == TILE_256x256_STAGED) {
     if (amode != A_BF16) return;
+    const bool dma = tile == TILE_256x256 && g.K % DG_BK == 0 && g.lda % 8 == 0 &&
+                     ((uintptr_t)g.a & 15) == 0 && (size_t)g.M * g.lda * 2 < ((size_t)1 << 32);
     switch (epi) {
-      case EPI_QKV: return launch_big<EPI_QKV>(g, st);
-      case EPI_RESID: return launch_big<EPI_RESID>(g, st);
-      case EPI_SWIGLU: return launch_big<EPI_SWIGLU>(g, st);
+      case EPI_QKV: return dma ? launch_big<EPI_QKV, true>(g, st) : launch_big<EPI_QKV, false>(g, st);
+      case EPI_RESID: return dma ? launch_big<EPI_RESID, true>(g, st) : launch_big<EPI_RESID, false>(g, st);
+      case EPI_SWIGLU: return dma ? launch_big<EPI_SWIGLU, true>(g, st) : launch_big<EPI_SWIGLU, false>(g, st);
       default: return;
     }
   }
