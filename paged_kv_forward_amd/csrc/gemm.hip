@@ -47,6 +47,127 @@ struct Cfg {
 // results is used, so a wave waits for memory once per batch rather than
 // once per row (tiles run one workgroup, one wave per SIMD, per CU, so
 // nothing else hides that latency).
+// EPI_QKV part of the epilogue: RoPE on q and k, q to its bf16 buffer, k and
+// v to their KV page slots.  Head size HD (64 or 128) and the 16-token page
+// are compile-time, so every index is shifts and masks.
+constexpr int KV_PAGE = 16;  // tokens per KV page (the only page size the engine accepts)
+
+template <int HD, int BN, int NTH, int B>
+__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const float* sC, int ldc, int m0, int rows,
+                                             int n_tile) {
+  constexpr int NW = NTH / 64, HD2 = HD / 2, P = KV_PAGE;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = n_tile * BN;
+  const int qw = g.nq * HD, kw = g.nkv * HD;
+  const int kind = n0 < qw ? 0 : (n0 < qw + kw ? 1 : 2);
+  if (kind == 0) {
+    // q: a wave step is one row's 64 consecutive rotation pairs (a tile row
+    // holds BN / 2 pairs, HD / 2 per head); stores run along the row
+    constexpr int UPR = BN / 2 / 64;
+    const int steps = rows * UPR;
+    const int head0 = n0 / HD;
+    for (int s0 = wave; s0 < steps; s0 += NW * B) {
+      float2 cs[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int st = s0 + u * NW, row = st / UPR, pr = (st % UPR) * 64 + lane, m = m0 + row;
+        const bool ok = st < steps && m < g.M;
+        cs[u] = ok ? *reinterpret_cast<const float2*>(g.rope_cs + ((size_t)m * HD2 + pr % HD2) * 2)
+                   : make_float2(1.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int st = s0 + u * NW, row = st / UPR, pr = (st % UPR) * 64 + lane, m = m0 + row;
+        if (st >= steps || m >= g.M) continue;
+        const int hl = pr / HD2, dd = pr % HD2;
+        const int c1 = hl * HD + dd, c2 = c1 + HD2;
+        const float x1 = sC[row * ldc + c1], x2 = sC[row * ldc + c2];
+        uint16_t* q = g.q_out + (size_t)m * qw + (head0 + hl) * HD;
+        q[dd] = f2bf(x1 * cs[u].x - x2 * cs[u].y);
+        q[dd + HD2] = f2bf(x2 * cs[u].x + x1 * cs[u].y);
+      }
+    }
+  } else if (kind == 1) {
+    // k: a wave step is 8 rows x 8 consecutive rotation pairs, so that the
+    // stores of consecutive tokens of a page, whose 8-element groups are
+    // adjacent in the K page layout [kv head][HD / 8][token][8], merge
+    constexpr int PG = BN / 2 / 8;  // groups of 8 pairs in a tile row
+    const int rb_n = (rows + 7) / 8, steps = rb_n * PG;
+    const int head0 = (n0 - qw) / HD;
+    const int tok = lane >> 3, d8 = lane & 7;
+    for (int s0 = wave; s0 < steps; s0 += NW * B) {
+      float2 cs[B];
+      int sl[B];
+      float sc[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int st = s0 + u * NW, row = (st % rb_n) * 8 + tok, pr = (st / rb_n) * 8 + d8, m = m0 + row;
+        const bool ok = st < steps && row < rows && m < g.M;
+        cs[u] = ok ? *reinterpret_cast<const float2*>(g.rope_cs + ((size_t)m * HD2 + pr % HD2) * 2)
+                   : make_float2(1.f, 0.f);
+        sl[u] = ok ? g.slot[m] : 0;
+        sc[u] = ok && g.kv_e4m3 ? g.kv_scale[head0 + pr / HD2] : 1.f;
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int st = s0 + u * NW, row = (st % rb_n) * 8 + tok, pr = (st / rb_n) * 8 + d8, m = m0 + row;
+        if (st >= steps || row >= rows || m >= g.M) continue;
+        const int hl = pr / HD2, dd = pr % HD2;
+        const int c1 = hl * HD + dd, c2 = c1 + HD2;
+        const float x1 = sC[row * ldc + c1], x2 = sC[row * ldc + c2];
+        const float o1 = x1 * cs[u].x - x2 * cs[u].y, o2 = x2 * cs[u].x + x1 * cs[u].y;
+        const int page = sl[u] / P, off = sl[u] % P;
+        const size_t base = (size_t)page * g.page_stride + (size_t)(head0 + hl) * P * HD + (size_t)off * 8;
+        const size_t i1 = base + (size_t)(dd >> 3) * P * 8 + (dd & 7);
+        const size_t i2 = base + (size_t)((dd + HD2) >> 3) * P * 8 + ((dd + HD2) & 7);
+        if (g.kv_e4m3) {
+          uint8_t* kv = reinterpret_cast<uint8_t*>(g.kv_layer);
+          kv[i1] = f2e4m3(o1 / sc[u]);
+          kv[i2] = f2e4m3(o2 / sc[u]);
+        } else {
+          uint16_t* kv = reinterpret_cast<uint16_t*>(g.kv_layer);
+          kv[i1] = f2bf(o1);
+          kv[i2] = f2bf(o2);
+        }
+      }
+    }
+  } else {
+    // v: a wave step is 16 rows x 4 columns, so that the stores of the
+    // consecutive tokens of a page, adjacent in the V page layout
+    // [kv head][HD][token], merge
+    constexpr int CG = BN / 4;  // groups of 4 columns in a tile row
+    const int rb_n = (rows + 15) / 16, steps = rb_n * CG;
+    const int v0 = n0 - qw - kw;
+    const int tok = lane & 15, c4 = lane >> 4;
+    for (int s0 = wave; s0 < steps; s0 += NW * B) {
+      int sl[B];
+      float sc[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int st = s0 + u * NW, row = (st % rb_n) * 16 + tok, c = (st / rb_n) * 4 + c4, m = m0 + row;
+        const bool ok = st < steps && row < rows && m < g.M;
+        sl[u] = ok ? g.slot[m] : 0;
+        sc[u] = ok && g.kv_e4m3 ? g.kv_scale[g.nkv + (v0 + c) / HD] : 1.f;
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int st = s0 + u * NW, row = (st % rb_n) * 16 + tok, c = (st / rb_n) * 4 + c4, m = m0 + row;
+        if (st >= steps || row >= rows || m >= g.M) continue;
+        const int vc = v0 + c, kvh = vc / HD, dd = vc % HD;
+        const int page = sl[u] / P, off = sl[u] % P;
+        const size_t idx_v = (size_t)page * g.page_stride + (size_t)g.nkv * P * HD + (size_t)kvh * HD * P +
+                             (size_t)dd * P + off;
+        const float x = sC[row * ldc + c];
+        if (g.kv_e4m3) {
+          reinterpret_cast<uint8_t*>(g.kv_layer)[idx_v] = f2e4m3(x / sc[u]);
+        } else {
+          reinterpret_cast<uint16_t*>(g.kv_layer)[idx_v] = f2bf(x);
+        }
+      }
+    }
+  }
+}
+
 template <int EPI, int BN, int NTH = 256, int B = 8>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int ldc, int m0, int rows,
                                          int n_tile) {
@@ -97,92 +218,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int
       *reinterpret_cast<uint2*>(g.h_out + (size_t)m * g.N + n) = make_uint2(pack_bf2(h0, h1), pack_bf2(h2, h3));
     }
   } else if constexpr (EPI == EPI_QKV) {
-    const int n0 = n_tile * BN;
-    const int hd = g.hd, hd2 = hd >> 1, P = g.page_size;
-    const int qw = g.nq * hd, kw = g.nkv * hd;
-    const int kind = n0 < qw ? 0 : (n0 < qw + kw ? 1 : 2);
-    if (kind < 2) {
-      // RoPE on q or k: a wave step is one row's 64 consecutive rotation
-      // pairs (a tile row holds BN / 2 pairs, hd / 2 per head).
-      constexpr int UPR = BN / 2 / 64;
-      const int steps = rows * UPR;
-      for (int s0 = wave; s0 < steps; s0 += NW * B) {
-        float2 cs[B];
-        int sl[B];
-        float sc[B];
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          const int st = s0 + u * NW, row = st / UPR, pr = (st % UPR) * 64 + lane, m = m0 + row;
-          const bool ok = st < steps && m < g.M;
-          const int dd = pr % hd2, kvh = (n0 - qw + pr / hd2 * hd) / hd;
-          cs[u] = ok ? *reinterpret_cast<const float2*>(g.rope_cs + ((size_t)m * hd2 + dd) * 2) : make_float2(1.f, 0.f);
-          sl[u] = ok && kind == 1 ? g.slot[m] : 0;
-          sc[u] = ok && kind == 1 && g.kv_e4m3 ? g.kv_scale[kvh] : 1.f;
-        }
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          const int st = s0 + u * NW, row = st / UPR, pr = (st % UPR) * 64 + lane, m = m0 + row;
-          if (st >= steps || m >= g.M) continue;
-          const int hl = pr / hd2, dd = pr % hd2;
-          const int c1 = hl * hd + dd, c2 = c1 + hd2;
-          const float x1 = sC[row * ldc + c1], x2 = sC[row * ldc + c2];
-          const float o1 = x1 * cs[u].x - x2 * cs[u].y, o2 = x2 * cs[u].x + x1 * cs[u].y;
-          if (kind == 0) {
-            const int head = (n0 + c1) / hd;
-            uint16_t* q = g.q_out + (size_t)m * qw + head * hd;
-            q[dd] = f2bf(o1);
-            q[dd + hd2] = f2bf(o2);
-          } else {
-            const int kvh = (n0 - qw + c1) / hd;
-            const int page = sl[u] / P, off = sl[u] % P;
-            // K page layout [kv head][hd / 8][token][8]
-            const size_t base = (size_t)page * g.page_stride + (size_t)kvh * P * hd + (size_t)off * 8;
-            const size_t i1 = base + (size_t)(dd >> 3) * P * 8 + (dd & 7);
-            const size_t i2 = base + (size_t)((dd + hd2) >> 3) * P * 8 + ((dd + hd2) & 7);
-            if (g.kv_e4m3) {
-              uint8_t* kv = reinterpret_cast<uint8_t*>(g.kv_layer);
-              kv[i1] = f2e4m3(o1 / sc[u]);
-              kv[i2] = f2e4m3(o2 / sc[u]);
-            } else {
-              uint16_t* kv = reinterpret_cast<uint16_t*>(g.kv_layer);
-              kv[i1] = f2bf(o1);
-              kv[i2] = f2bf(o2);
-            }
-          }
-        }
-      }
-    } else {
-      // v: a wave step is one row's 64 consecutive columns; V page layout [kv head][hd][token]
-      constexpr int UPR = BN / 64;
-      const int steps = rows * UPR;
-      for (int s0 = wave; s0 < steps; s0 += NW * B) {
-        int sl[B];
-        float sc[B];
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          const int st = s0 + u * NW, row = st / UPR, c = (st % UPR) * 64 + lane, m = m0 + row;
-          const bool ok = st < steps && m < g.M;
-          const int kvh = (n0 - qw - kw + c) / hd;
-          sl[u] = ok ? g.slot[m] : 0;
-          sc[u] = ok && g.kv_e4m3 ? g.kv_scale[g.nkv + kvh] : 1.f;
-        }
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          const int st = s0 + u * NW, row = st / UPR, c = (st % UPR) * 64 + lane, m = m0 + row;
-          if (st >= steps || m >= g.M) continue;
-          const int vc = n0 - qw - kw + c, kvh = vc / hd, dd = vc % hd;
-          const int page = sl[u] / P, off = sl[u] % P;
-          const size_t idx_v = (size_t)page * g.page_stride + (size_t)g.nkv * P * hd + (size_t)kvh * hd * P +
-                               (size_t)dd * P + off;
-          const float x = sC[row * ldc + c];
-          if (g.kv_e4m3) {
-            reinterpret_cast<uint8_t*>(g.kv_layer)[idx_v] = f2e4m3(x / sc[u]);
-          } else {
-            reinterpret_cast<uint16_t*>(g.kv_layer)[idx_v] = f2bf(x);
-          }
-        }
-      }
-    }
+    if (g.hd == 128) qkv_epilogue<128, BN, NTH, B>(g, sC, ldc, m0, rows, n_tile);
+    else qkv_epilogue<64, BN, NTH, B>(g, sC, ldc, m0, rows, n_tile);
   } else if constexpr (EPI == EPI_LOGITS) {
     // one wave per row; the row's readout parameters are loaded a batch of rows at a time
     const int n0 = n_tile * BN;
@@ -708,10 +745,14 @@ __global__ __launch_bounds__(DG_NT, 1) void gemm_dma_kernel(GemmArgs g) {
   __builtin_amdgcn_s_waitcnt(DG_WAIT(0));
   dg_barrier();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) issue_one(1, i);
+  for (int i = 0; i < 8; ++i) issue_one(1, i);
 #pragma unroll
   for (int f = 0; f < 8; ++f) FA[f] = frag(0, 0, f);
 
+  // A stage's 16 loads are issued half in k-step 3 of the iteration two
+  // before it (right after the barrier that frees its buffer) and half in
+  // k-step 0 of the next one, so that the loads of a workgroup spread over
+  // two k-steps of MFMAs rather than queueing behind one.
   for (int t = 0; t < nk; ++t) {
     // k-steps 0..2: MFMAs on one fragment set while the next is read
 #pragma unroll
@@ -723,6 +764,7 @@ __global__ __launch_bounds__(DG_NT, 1) void gemm_dma_kernel(GemmArgs g) {
         const int a = q >> 2, b = q & 3;
         acc[a][b] = mfma32(cur[a], cur[4 + b], acc[a][b]);
         if (q < 8) nxt[q] = frag(t, ks + 1, q);
+        if (ks == 0 && (q & 1)) issue_one(t + 1, 8 + (q >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -730,13 +772,13 @@ __global__ __launch_bounds__(DG_NT, 1) void gemm_dma_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(DG_WAIT(0));
     dg_barrier();
     // k-step 3 (FB) while reading k-step 0 of stage t + 1 (FA; unused past
-    // the last stage) and loading stage t + 2 into stage t's buffer
+    // the last stage) and loading half of stage t + 2 into stage t's buffer
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int a = q >> 2, b = q & 3;
       acc[a][b] = mfma32(FB[a], FB[4 + b], acc[a][b]);
       if (q < 8) FA[q] = frag(t + 1, 0, q);
-      issue_one(t + 2, q);
+      if (q & 1) issue_one(t + 2, q >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
