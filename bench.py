@@ -27,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PREFILL_TIMED_LAUNCHES = 4
 N_SEQ = 64
 PROMPT = 2048
 PREFILL_SEQS_PER_LAUNCH = 4
@@ -101,6 +103,60 @@ def short_name(name):
     return name.split("(")[0].replace("void ", "").strip()
 
 
+def summarize_prefill(trace, prof):
+    """Per-projection durations of the prefill GEMMs (8192 rows per launch)
+    and of prefill attention, from the same kernel trace."""
+    from synth import workload
+    shape = workload(2).shape
+    T = PREFILL_SEQS_PER_LAUNCH * PROMPT
+    d, f_, hq, hk = shape.d_model, shape.d_ffn, shape.n_q_heads * shape.head_dim, shape.n_kv_heads * shape.head_dim
+    nk = {"qkv": (hq + 2 * hk, d), "o": (d, hq), "gate_up": (2 * f_, d), "down": (d, f_)}
+    dur = {k: [] for k in nk}
+    attn = []
+    prev = None
+    for r in trace:
+        k = short_name(r["Kernel_Name"])
+        if "embed_kernel" in k and int(r["Grid_Size_X"]) == N_SEQ * 256:
+            break  # decode starts
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if k.startswith("pie::gemm_dma_kernel") or k.startswith("pie::gemm_big_kernel"):
+            epi = k.split("<")[1].rstrip(">")
+            proj = {"0": "qkv", "2": "gate_up"}.get(epi)
+            if epi == "1":
+                proj = "down" if prev == "gate_up" else "o"
+            dur[proj].append(us)
+            prev = proj
+        elif k.startswith("pie::attn_prefill_kernel"):
+            attn.append(us)
+            prev = "attn"
+    rows = ["# Prefill kernels of the benchmark run (Llama-3.1-8B shape, 8192 rows per launch)", "",
+            "Same run as `decode_llama8b_b64_kernel_trace.md`:", "", "    " + TRACE_CMD, "",
+            "The prefill is 16 launches of 4 sequences x 2048 tokens (T = 8192 rows).  Each projection",
+            "GEMM runs once per layer; flops = 2 T N K.  Peak: %.0f TFLOP/s (dense bf16 MFMA)." % PEAK_BF16_TFLOPS, "",
+            "| kernel | projection (N x K) | launches | avg us | TFLOP/s | fraction of peak |",
+            "|---|---|---|---|---|---|"]
+    tot_f, tot_t = 0.0, 0.0
+    for proj, (n, k) in nk.items():
+        if not dur[proj]:
+            continue
+        avg = sum(dur[proj]) / len(dur[proj])
+        tf = 2.0 * T * n * k / (avg * 1e-6) / 1e12
+        tot_f += 2.0 * T * n * k * len(dur[proj])
+        tot_t += sum(dur[proj]) * 1e-6
+        kern = "gemm_dma_kernel<%s>" % {"qkv": 0, "o": 1, "gate_up": 2, "down": 1}[proj]
+        rows.append("| `%s` | %s (%d x %d) | %d | %.1f | %.0f | %.3f |"
+                    % (kern, proj, n, k, len(dur[proj]), avg, tf, tf / PEAK_BF16_TFLOPS))
+    if tot_t:
+        rows.append("| all four | | | | %.0f | %.3f |" % (tot_f / tot_t / 1e12, tot_f / tot_t / 1e12 / PEAK_BF16_TFLOPS))
+    if attn:
+        avg = sum(attn) / len(attn)
+        fl = 4.0 * shape.n_q_heads * shape.head_dim * (PROMPT * (PROMPT + 1) / 2) * PREFILL_SEQS_PER_LAUNCH
+        rows += ["", "Prefill attention (causal, 4 sequences of 2048 per launch): %d launches, avg %.1f us, "
+                 "%.0f TFLOP/s." % (len(attn), avg, fl / (avg * 1e-6) / 1e12)]
+    with open(os.path.join(prof, "prefill_llama8b_t8192_kernel_trace.md"), "w") as f:
+        f.write("\n".join(rows) + "\n")
+
+
 def summarize(out_dir):
     """Write the committed summaries under profiles/ from a rocprofv3 kernel
     trace (out_dir/trace_c2) and the FETCH_SIZE / WRITE_SIZE counter runs
@@ -147,6 +203,7 @@ def summarize(out_dir):
             lines.append("| `%s` | %d | %.1f |" % (k, n, d))
     with open(os.path.join(prof, "decode_llama8b_b64_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    summarize_prefill(trace, prof)
 
     def per_kernel(csv_path):
         agg = {}
@@ -263,13 +320,40 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     nxt = np.zeros(N_SEQ, dtype=np.int32)
+    gemm_classes = ["gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down"]
+    n_launch = N_SEQ // PREFILL_SEQS_PER_LAUNCH
     for b in range(0, N_SEQ, PREFILL_SEQS_PER_LAUNCH):
+        if b // PREFILL_SEQS_PER_LAUNCH == n_launch - PREFILL_TIMED_LAUNCHES:
+            # the last launches run with HIP events around every GEMM launch
+            rt.profile_enable(gemm_classes + ["attn_prefill"])
         ss = range(b, b + PREFILL_SEQS_PER_LAUNCH)
         toks, _ = rt.forward([Pass(ws[s], prompts[s], [PROMPT - 1], [(0, 1.0, 0)]) for s in ss])
         nxt[b:b + PREFILL_SEQS_PER_LAUNCH] = toks
     torch.cuda.synchronize()
     t_prefill = time.perf_counter() - t0
+    pf = rt.profile_read()
+    rt.profile_enable([])
     log("bench: prefill %d x %d tokens in %.2f s" % (N_SEQ, PROMPT, t_prefill))
+    # prefill GEMM flops per launch (T rows x 2 N K per projection, every layer)
+    T_pf = PREFILL_SEQS_PER_LAUNCH * PROMPT
+    d, f_, hq, hk = shape.d_model, shape.d_ffn, shape.n_q_heads * shape.head_dim, shape.n_kv_heads * shape.head_dim
+    nk_pairs = {"gemm_qkv": (hq + 2 * hk, d), "gemm_o": (d, hq), "gemm_gateup": (2 * f_, d), "gemm_down": (d, f_)}
+    gemm_flop = {c: 2.0 * T_pf * n * k * shape.n_layers for c, (n, k) in nk_pairs.items()}
+    gemm_ms = {c: pf[c][0] / PREFILL_TIMED_LAUNCHES for c in gemm_classes}
+    tot_ms = sum(gemm_ms.values())
+    tot_flop = sum(gemm_flop.values())
+    prefill_gemm = {
+        "bound": "mfma", "achieved": round(tot_flop / (tot_ms * 1e-3) / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(tot_flop / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "flops_per_launch": tot_flop, "gemm_ms_per_launch": round(tot_ms, 3),
+        "by_projection_tflops": {c[5:]: round(gemm_flop[c] / (gemm_ms[c] * 1e-3) / 1e12, 1) for c in gemm_classes},
+        "attn_prefill_ms_per_launch": round(pf["attn_prefill"][0] / PREFILL_TIMED_LAUNCHES, 3),
+        # causal attention: scores and P.V, 2 x 2 flops per (query, key <= query) pair per head dim
+        "attn_prefill_tflops": round(4.0 * shape.n_q_heads * shape.head_dim * (PROMPT * (PROMPT + 1) / 2)
+                                     * PREFILL_SEQS_PER_LAUNCH * shape.n_layers
+                                     / (pf["attn_prefill"][0] / PREFILL_TIMED_LAUNCHES * 1e-3) / 1e12, 1),
+        "timed_over": "the last %d prefill launches (%d rows each), HIP events around every GEMM launch"
+                      % (PREFILL_TIMED_LAUNCHES, T_pf)}
 
     ws_arr = np.array(ws, dtype=np.uint64)
 
@@ -353,6 +437,7 @@ def main():
                      "achieved_gbs": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "prefill_tokens_per_s": round(N_SEQ * PROMPT / t_prefill, 1),
+        "prefill_gemm": prefill_gemm,
     }
     if breakdown:
         out["ms_per_step_by_kernel"] = breakdown
