@@ -52,9 +52,18 @@ struct Cfg {
 // are compile-time, so every index is shifts and masks.
 constexpr int KV_PAGE = 16;  // tokens per KV page (the only page size the engine accepts)
 
+// Optional LDS copies of what the epilogue would otherwise load per row:
+// rope = the rows' RoPE table ([rows][HD / 2] (cos, sin)), slot = their KV
+// slots, scale = the layer's e4m3 scales ([2][nkv]).
+struct QkvStaged {
+  const float2* rope;
+  const int* slot;
+  const float* scale;
+};
+
 template <int HD, int BN, int NTH, int B>
 __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const float* sC, int ldc, int m0, int rows,
-                                             int n_tile) {
+                                             int n_tile, QkvStaged sg) {
   constexpr int NW = NTH / 64, HD2 = HD / 2, P = KV_PAGE;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = n_tile * BN;
@@ -72,8 +81,9 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const float* sC,
       for (int u = 0; u < B; ++u) {
         const int st = s0 + u * NW, row = st / UPR, pr = (st % UPR) * 64 + lane, m = m0 + row;
         const bool ok = st < steps && m < g.M;
-        cs[u] = ok ? *reinterpret_cast<const float2*>(g.rope_cs + ((size_t)m * HD2 + pr % HD2) * 2)
-                   : make_float2(1.f, 0.f);
+        cs[u] = !ok ? make_float2(1.f, 0.f)
+                    : sg.rope ? sg.rope[row * HD2 + pr % HD2]
+                              : *reinterpret_cast<const float2*>(g.rope_cs + ((size_t)m * HD2 + pr % HD2) * 2);
       }
 #pragma unroll
       for (int u = 0; u < B; ++u) {
@@ -103,10 +113,11 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const float* sC,
       for (int u = 0; u < B; ++u) {
         const int st = s0 + u * NW, row = (st % rb_n) * 8 + tok, pr = (st / rb_n) * 8 + d8, m = m0 + row;
         const bool ok = st < steps && row < rows && m < g.M;
-        cs[u] = ok ? *reinterpret_cast<const float2*>(g.rope_cs + ((size_t)m * HD2 + pr % HD2) * 2)
-                   : make_float2(1.f, 0.f);
-        sl[u] = ok ? g.slot[m] : 0;
-        sc[u] = ok && g.kv_e4m3 ? g.kv_scale[head0 + pr / HD2] : 1.f;
+        cs[u] = !ok ? make_float2(1.f, 0.f)
+                    : sg.rope ? sg.rope[row * HD2 + pr % HD2]
+                              : *reinterpret_cast<const float2*>(g.rope_cs + ((size_t)m * HD2 + pr % HD2) * 2);
+        sl[u] = !ok ? 0 : sg.slot ? sg.slot[row] : g.slot[m];
+        sc[u] = !(ok && g.kv_e4m3) ? 1.f : sg.scale ? sg.scale[head0 + pr / HD2] : g.kv_scale[head0 + pr / HD2];
       }
 #pragma unroll
       for (int u = 0; u < B; ++u) {
@@ -146,8 +157,9 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const float* sC,
       for (int u = 0; u < B; ++u) {
         const int st = s0 + u * NW, row = (st % rb_n) * 16 + tok, c = (st / rb_n) * 4 + c4, m = m0 + row;
         const bool ok = st < steps && row < rows && m < g.M;
-        sl[u] = ok ? g.slot[m] : 0;
-        sc[u] = ok && g.kv_e4m3 ? g.kv_scale[g.nkv + (v0 + c) / HD] : 1.f;
+        sl[u] = !ok ? 0 : sg.slot ? sg.slot[row] : g.slot[m];
+        const int si = g.nkv + (v0 + c) / HD;
+        sc[u] = !(ok && g.kv_e4m3) ? 1.f : sg.scale ? sg.scale[si] : g.kv_scale[si];
       }
 #pragma unroll
       for (int u = 0; u < B; ++u) {
@@ -170,7 +182,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const float* sC,
 
 template <int EPI, int BN, int NTH = 256, int B = 8>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int ldc, int m0, int rows,
-                                         int n_tile) {
+                                         int n_tile, QkvStaged sg = QkvStaged{nullptr, nullptr, nullptr}) {
   constexpr int NW = NTH / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if constexpr (EPI == EPI_RESID) {
@@ -218,8 +230,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int
       *reinterpret_cast<uint2*>(g.h_out + (size_t)m * g.N + n) = make_uint2(pack_bf2(h0, h1), pack_bf2(h2, h3));
     }
   } else if constexpr (EPI == EPI_QKV) {
-    if (g.hd == 128) qkv_epilogue<128, BN, NTH, B>(g, sC, ldc, m0, rows, n_tile);
-    else qkv_epilogue<64, BN, NTH, B>(g, sC, ldc, m0, rows, n_tile);
+    if (g.hd == 128) qkv_epilogue<128, BN, NTH, B>(g, sC, ldc, m0, rows, n_tile, sg);
+    else qkv_epilogue<64, BN, NTH, B>(g, sC, ldc, m0, rows, n_tile, sg);
   } else if constexpr (EPI == EPI_LOGITS) {
     // one wave per row; the row's readout parameters are loaded a batch of rows at a time
     const int n0 = n_tile * BN;
@@ -472,6 +484,25 @@ __device__ __forceinline__ int big_tiles_n(const GemmArgs& g) {
   return EPI == EPI_SWIGLU ? (g.N + BG_BN / 2 - 1) / (BG_BN / 2) : (g.N + BG_BN - 1) / BG_BN;
 }
 
+// XCD-aware raster of the 256 x 256 tiles, one workgroup per tile.
+// Workgroup i runs on XCD i % 8 (each XCD has its own L2).  The tiles, in
+// bands of 4 tile rows walked along N, are cut into 8 contiguous ranges, one
+// per XCD, of the sizes that the round-robin hands each XCD, so every XCD
+// gets the same share (to one tile) whatever the grid, and the 32 tiles an
+// XCD runs at a time form a 4 x 8 block: each A tile is read by 8 and each
+// B tile by 4 of them through the same L2.
+constexpr int BIG_BAND = 4;
+
+__device__ __forceinline__ void big_tile_of(int pid, int m_tiles, int n_tiles, int& m_tile, int& n_tile) {
+  const int T = m_tiles * n_tiles, q = T >> 3, r = T & 7;
+  const int x = pid & 7, j = pid >> 3;
+  const int t = x * q + min(x, r) + j;  // XCD x's range starts after the q (+1) tiles of each XCD before it
+  const int per_band = BIG_BAND * n_tiles, band = t / per_band;
+  const int mb = band * BIG_BAND, bm = min(BIG_BAND, m_tiles - mb), u = t - band * per_band;
+  m_tile = mb + u % bm;
+  n_tile = u / bm;
+}
+
 template <int EPI>
 __global__ __launch_bounds__(BG_NT, 2) void gemm_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[BG_LDS];
@@ -480,20 +511,8 @@ __global__ __launch_bounds__(BG_NT, 2) void gemm_big_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave >> 2, wn = wave & 3, l32 = lane & 31, lh = lane >> 5;
 
-  // XCD-aware raster: workgroup i runs on XCD i % 8 (each XCD has its own
-  // L2).  A window of 256 workgroups covers 16 x 16 tiles, and the 32 that
-  // share an XCD form a 4 x 8 block of it, so each A tile is read by 8 and
-  // each B tile by 4 workgroups of the same XCD.  Windows advance along M
-  // first.  Workgroups of a partial window past the edge exit at once.
   int n_tile, m_tile;
-  {
-    const int n_tiles = big_tiles_n<EPI>(g), m_tiles = (g.M + BG_BM - 1) / BG_BM;
-    const int m_win = (m_tiles + 15) / 16;
-    const int pid = blockIdx.x, win = pid >> 8, x = pid & 7, j = (pid & 255) >> 3;
-    m_tile = (win % m_win) * 16 + (x & 3) * 4 + (j & 3);
-    n_tile = (win / m_win) * 16 + (x >> 2) * 8 + (j >> 2);
-    if (m_tile >= m_tiles || n_tile >= n_tiles) return;
-  }
+  big_tile_of(blockIdx.x, (g.M + BG_BM - 1) / BG_BM, big_tiles_n<EPI>(g), m_tile, n_tile);
   const int m0 = m_tile * BG_BM;
   const int kc = (g.K + 63) / 64;
   const int nk = kc;
@@ -626,7 +645,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 constexpr int DG_BK = 64, DG_NT = 256;
 constexpr int DG_STAGE = (BG_BM + BG_BN) * DG_BK * 2;  // 64 KiB
 constexpr int DG_LDS = 2 * DG_STAGE;                    // 128 KiB
-static_assert(64 * BG_LDC * 4 <= DG_LDS, "epilogue pass fits in the stage buffers");
+// Epilogue LDS: one 64-row pass of fp32 results, then (QKV) 64 RoPE rows of
+// up to 64 (cos, sin) pairs, 64 slots and up to 2 x 128 e4m3 scales.
+constexpr int DG_EPI_C = (64 * BG_LDC * 4 + 1023) / 1024 * 1024, DG_EPI_ROPE = 64 * 64 * 8;
+static_assert(DG_EPI_C + DG_EPI_ROPE + 256 + 2 * 128 * 4 <= DG_LDS, "epilogue pass fits in the stage buffers");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -668,14 +690,7 @@ __global__ __launch_bounds__(DG_NT, 1) void gemm_dma_kernel(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, lh = lane >> 5;
 
   int n_tile, m_tile;
-  {
-    const int n_tiles = big_tiles_n<EPI>(g), m_tiles = (g.M + BG_BM - 1) / BG_BM;
-    const int m_win = (m_tiles + 15) / 16;
-    const int pid = blockIdx.x, win = pid >> 8, x = pid & 7, j = (pid & 255) >> 3;
-    m_tile = (win % m_win) * 16 + (x & 3) * 4 + (j & 3);
-    n_tile = (win / m_win) * 16 + (x >> 2) * 8 + (j >> 2);
-    if (m_tile >= m_tiles || n_tile >= n_tiles) return;
-  }
+  big_tile_of(blockIdx.x, (g.M + BG_BM - 1) / BG_BM, big_tiles_n<EPI>(g), m_tile, n_tile);
   const int m0 = m_tile * BG_BM;
   const int nk = g.K / DG_BK;  // = 64-column blocks of the packed weights
 
@@ -786,6 +801,10 @@ __global__ __launch_bounds__(DG_NT, 1) void gemm_dma_kernel(GemmArgs g) {
   __syncthreads();
 
   float* sC = reinterpret_cast<float*>(smem);
+  // QKV epilogue staging, past the 64-row pass of sC
+  uint8_t* s_rope = smem + DG_EPI_C;
+  int* s_slot = reinterpret_cast<int*>(smem + DG_EPI_C + DG_EPI_ROPE);
+  float* s_scale = reinterpret_cast<float*>(smem + DG_EPI_C + DG_EPI_ROPE + 256);
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     if (wm == (pass >> 1)) {
@@ -801,8 +820,25 @@ __global__ __launch_bounds__(DG_NT, 1) void gemm_dma_kernel(GemmArgs g) {
           }
       }
     }
+    QkvStaged sg{nullptr, nullptr, nullptr};
+    if constexpr (EPI == EPI_QKV) {
+      // The pass's 64 RoPE rows (contiguous in the table) go to LDS with the
+      // same LDS-writing loads, its slots and the e4m3 scales with plain
+      // loads, so the epilogue itself makes no global loads.
+      const int hd2 = g.hd >> 1, rb = 64 * hd2 * 8;  // bytes of 64 RoPE rows
+      const int r0 = m0 + pass * 64;
+      const i32x4_t rr = rsrc_words(g.rope_cs, (uint32_t)((size_t)g.M * hd2 * 8));
+      for (int i = wave; i < rb / 1024; i += DG_NT / 64)
+        dma16(rr, s_rope + i * 1024, (uint32_t)lane * 16u, (uint32_t)((size_t)r0 * hd2 * 8 + i * 1024));
+      if (threadIdx.x < 64) s_slot[threadIdx.x] = g.slot[min(r0 + (int)threadIdx.x, g.M - 1)];
+      const bool stage_scale = g.kv_e4m3 && g.nkv <= 128;
+      if (stage_scale && pass == 0)
+        for (int i = threadIdx.x; i < 2 * g.nkv; i += DG_NT) s_scale[i] = g.kv_scale[i];
+      __builtin_amdgcn_s_waitcnt(DG_WAIT(0));
+      sg = QkvStaged{reinterpret_cast<const float2*>(s_rope), s_slot, stage_scale ? s_scale : nullptr};
+    }
     __syncthreads();
-    epilogue<EPI, BG_BN, DG_NT>(g, sC, BG_LDC, m0 + pass * 64, 64, n_tile);
+    epilogue<EPI, BG_BN, DG_NT, EPI == EPI_QKV ? 2 : 8>(g, sC, BG_LDC, m0 + pass * 64, 64, n_tile, sg);
     __syncthreads();
   }
 }
@@ -1100,9 +1136,9 @@ int gemm_n_tiles(int epi, int N, int tile) {
 
 template <int EPI, bool DMA>
 static void launch_big(const GemmArgs& g, hipStream_t st) {
-  const int m_win = ((g.M + BG_BM - 1) / BG_BM + 15) / 16, n_win = (gemm_n_tiles(EPI, g.N, TILE_256x256) + 15) / 16;
-  if (DMA) hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3(m_win * n_win * 256), dim3(DG_NT), 0, st, g);
-  else hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(m_win * n_win * 256), dim3(BG_NT), 0, st, g);
+  const int tiles = ((g.M + BG_BM - 1) / BG_BM) * gemm_n_tiles(EPI, g.N, TILE_256x256);
+  if (DMA) hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3(tiles), dim3(DG_NT), 0, st, g);
+  else hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(tiles), dim3(BG_NT), 0, st, g);
 }
 
 // Large tiles (prefill-sized M) never split K: there are enough output tiles.
