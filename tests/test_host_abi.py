@@ -306,6 +306,25 @@ def test_noise_bounds_rule(tmp_path):
     assert noise_bounds([str(b)]) == (2e-2, 2e-2)
 
 
+def test_noise_mean_bound_rule(tmp_path):
+    """The mean |dlogit| bound is twice the largest twin mean of the files."""
+    import json
+    from tests.parity import Report, noise_mean_bound
+    a, b = tmp_path / "a.json", tmp_path / "b.json"
+    a.write_text(json.dumps({"max_abs_dlogit": 1.3, "mean_abs_dlogit": 0.21}))
+    b.write_text(json.dumps({"max_abs_dlogit": 0.1, "mean_abs_dlogit": 0.02}))
+    assert abs(noise_mean_bound([str(a), str(b)]) - 0.42) < 1e-12
+    rep = Report()
+    rep.add(1, 1, 0.5, 2.0)  # excluded: margin below tau
+    rep.sum_err = 0.5
+    rep.max_err = 0.5
+    rep.check(tol=1.0, max_excluded_frac=1.0, mean_tol=0.6)
+    with pytest.raises(AssertionError):
+        rep.check(tol=1.0, max_excluded_frac=1.0, mean_tol=0.4)
+    with pytest.raises(AssertionError):
+        rep.check(tol=1.0, max_excluded_frac=0.6, mean_tol=0.6)
+
+
 def test_stored_conditioning_files_are_complete():
     import glob
     import json
