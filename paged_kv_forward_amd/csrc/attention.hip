@@ -37,6 +37,10 @@ constexpr int PS = 16;  // page size
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+// 2^x for the softmax (x <= 0 or -inf): the hardware exp2.  Results below
+// 2^-126 flush to zero, which no row sum (at least 1) can register.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -372,16 +376,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 // sit in LDS in their memory layout.  Unlike compute_pair it finishes S and P
 // for every row block before it reads V, so K and V fragments are never live
 // together.
-template <int HD, bool E4M3, int RB>
+// Byte offset of a bf16 V page block in LDS: the two 16-byte halves of every
+// 32-byte row (16 tokens of one head-dim index) trade places in rows whose
+// bit 3 is set, so the MFMA operand reads (16 rows x 8 bytes per lane group)
+// hit every bank once instead of twice.  e4m3 rows are 16 bytes and need none.
+__device__ __forceinline__ int vswz(int o) { return o ^ (((o >> 8) & 1) << 4); }
+
+template <int HD, bool E4M3, int RB, bool FULL>
 __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* kb1, const uint8_t* vb0,
                                              const uint8_t* vb1, int valid0, int valid1, int start0,
                                              int start1, const uint4 (&qf)[RB][HD / 32],
                                              f32x4 (&oacc)[RB][HD / 16], float (&m_run)[RB], float (&l_run)[RB],
                                              const int (&qidx)[RB], float scale_log2, int lane) {
+  // FULL: both pages hold 16 tokens and every one of them is visible to every
+  // row of the wave, so no score or V slot needs masking.
   constexpr int STEPS = HD / 32, DB = HD / 16, EB = E4M3 ? 1 : 2;
   const int g = lane >> 4, n = lane & 15;
   uint4 ph[RB], pl[RB];
   float alpha[RB];
+  bool rescale[RB];
   {
     uint4 kf[2][STEPS];
 #pragma unroll
@@ -407,24 +420,35 @@ __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* 
       const int qi = qidx[rb];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int tok = 4 * g + j;
-        sc[j] = tok < valid0 && start0 + tok <= qi ? s0[j] * scale_log2 : -INFINITY;
-        sc[4 + j] = tok < valid1 && start1 + tok <= qi ? s1[j] * scale_log2 : -INFINITY;
+        if constexpr (FULL) {
+          sc[j] = s0[j] * scale_log2;
+          sc[4 + j] = s1[j] * scale_log2;
+        } else {
+          const int tok = 4 * g + j;
+          sc[j] = tok < valid0 && start0 + tok <= qi ? s0[j] * scale_log2 : -INFINITY;
+          sc[4 + j] = tok < valid1 && start1 + tok <= qi ? s1[j] * scale_log2 : -INFINITY;
+        }
       }
-      float mx = sc[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
+      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run[rb], mx);
-      const bool any = m_new != -INFINITY;
-      alpha[rb] = any ? exp2f(m_run[rb] - m_new) : 1.f;
       float p[8];
+      if constexpr (FULL) {
+        // m_new is finite: these rows see every key of the pair
+        alpha[rb] = exp2_fast(m_run[rb] - m_new);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = any ? exp2f(sc[j] - m_new) : 0.f;
-      float ps = 0.f;
+        for (int j = 0; j < 8; ++j) p[j] = exp2_fast(sc[j] - m_new);
+      } else {
+        const bool any = m_new != -INFINITY;
+        alpha[rb] = any ? exp2_fast(m_run[rb] - m_new) : 1.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ps += p[j];
+        for (int j = 0; j < 8; ++j) p[j] = any ? exp2_fast(sc[j] - m_new) : 0.f;
+      }
+      // O is rescaled only when some row's running max moved (alpha != 1);
+      // multiplying by 1 changes nothing, so skipping it is exact
+      rescale[rb] = __builtin_amdgcn_ballot_w64(alpha[rb] != 1.f) != 0;
+      const float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       l_run[rb] = l_run[rb] * alpha[rb] + ps;
       m_run[rb] = m_new;
       ph[rb] = make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]), pack_bf2(p[6], p[7]));
@@ -444,16 +468,19 @@ __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* 
     const int off = ((16 * b + n) * PS + 4 * g) * EB;
     uint2 a0, a1;
     if constexpr (E4M3) {
-      a0 = v4_bf16<true>(*reinterpret_cast<const uint32_t*>(vb0 + off), valid0 - 4 * g);
-      a1 = v4_bf16<true>(*reinterpret_cast<const uint32_t*>(vb1 + off), valid1 - 4 * g);
+      a0 = v4_bf16<true>(*reinterpret_cast<const uint32_t*>(vb0 + off), FULL ? 4 : valid0 - 4 * g);
+      a1 = v4_bf16<true>(*reinterpret_cast<const uint32_t*>(vb1 + off), FULL ? 4 : valid1 - 4 * g);
+    } else if constexpr (FULL) {
+      a0 = *reinterpret_cast<const uint2*>(vb0 + vswz(off));
+      a1 = *reinterpret_cast<const uint2*>(vb1 + vswz(off));
     } else {
-      a0 = v4_bf16<false>(*reinterpret_cast<const uint2*>(vb0 + off), valid0 - 4 * g);
-      a1 = v4_bf16<false>(*reinterpret_cast<const uint2*>(vb1 + off), valid1 - 4 * g);
+      a0 = v4_bf16<false>(*reinterpret_cast<const uint2*>(vb0 + vswz(off)), valid0 - 4 * g);
+      a1 = v4_bf16<false>(*reinterpret_cast<const uint2*>(vb1 + vswz(off)), valid1 - 4 * g);
     }
     const uint4 vf = make_uint4(a0.x, a0.y, a1.x, a1.y);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      oacc[rb][b] *= alpha[rb];
+      if (rescale[rb]) oacc[rb][b] *= alpha[rb];
       oacc[rb][b] = mfma16(vf, ph[rb], oacc[rb][b]);
       oacc[rb][b] = mfma16(vf, pl[rb], oacc[rb][b]);
     }
@@ -469,21 +496,44 @@ __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* 
 // the workgroup's last row are skipped.
 constexpr int PF_WAVES = 8, PF_NT = 64 * PF_WAVES;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte buffer load into LDS (lane l's 16 bytes at voff + soff go to LDS
+// bytes [16l, 16l + 16) past `lds`, a wave-uniform address).  Inline
+// assembly keeps the compiler from tracking it (it would make every LDS read
+// wait for all such loads); the caller waits with s_waitcnt vmcnt.  M0 holds
+// the LDS address; the nop covers the M0-write hazard of these loads.
+__device__ __forceinline__ void dma16(i32x4_t r, const void* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m = (uint32_t)(size_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+
+__device__ __forceinline__ i32x4_t page_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return i32x4_t{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// s_waitcnt: vector-memory counter at most n, every LDS access and scalar
+// load of the wave complete.
+#define PF_WAIT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x70)
+
 template <int HD, bool E4M3>
-__global__ __launch_bounds__(PF_NT, 2) void attn_prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(AttnArgs a) {
   constexpr int RB = PREFILL_ROWS / (16 * PF_WAVES);  // row blocks of 16 per wave
   constexpr int DB = HD / 16, EB = E4M3 ? 1 : 2;
   constexpr int PAGE_B = PS * HD * EB;          // bytes of one page's K (or V) for one KV head
   constexpr int SP = 4;                         // pages per stage
   constexpr int STAGE_B = SP * 2 * PAGE_B;      // K and V of a stage
-  constexpr int PIECE = PAGE_B / PF_NT >= 4 ? PAGE_B / PF_NT : 4;  // bytes per loading thread
-  constexpr int LOADERS = PAGE_B / PIECE;
-  static_assert(PIECE == 16 || PIECE == 8 || PIECE == 4, "page block split over the loading threads");
-  typedef typename std::conditional<PIECE == 16, uint4,
-                                    typename std::conditional<PIECE == 8, uint2, uint32_t>::type>::type Piece;
-  __shared__ __attribute__((aligned(16))) uint8_t skv[2][STAGE_B];
-  __shared__ int s_valid[2][SP], s_start[2][SP];
-  const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4, tid = threadIdx.x;
+  constexpr int NS = 3;                         // stages in the LDS ring
+  constexpr int PB_L = PAGE_B / 1024;           // 1 KiB loads per page block
+  constexpr int LPW = STAGE_B / 1024 / PF_WAVES;  // loads per wave per stage
+  static_assert(PAGE_B % 1024 == 0 && LPW >= 1 && (STAGE_B / 1024) % PF_WAVES == 0, "stage split over the waves");
+  static_assert(LPW <= PB_L * 2 && (PB_L % LPW == 0 || LPW % PB_L == 0), "a wave's loads of a stage stay in one page");
+  __shared__ __attribute__((aligned(1024))) uint8_t skv[NS][STAGE_B];
+  const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4;
   const int4 it = a.items[blockIdx.x];
   const int kvh = blockIdx.y;
   const int s = it.x, tb = it.y, nt = it.z;
@@ -502,6 +552,9 @@ __global__ __launch_bounds__(PF_NT, 2) void attn_prefill_kernel(AttnArgs a) {
     load_q<HD>(qf[rb], a.q + ((size_t)(row0 + (ok ? tq : 0)) * a.nq + kvh * G + h) * HD, ok, g);
   }
   const bool wave_live = wave * (RB * 16) / G < nt;
+  // logical index of the wave's first (lowest) query token: a page whose
+  // last token is at or before it is visible to every row of the wave
+  const int q_first = ctx + wave * (RB * 16) / G;
   const int qmax = ctx + nt - 1;
 
   f32x4 oacc[RB][DB];
@@ -519,69 +572,70 @@ __global__ __launch_bounds__(PF_NT, 2) void attn_prefill_kernel(AttnArgs a) {
   const uint32_t vofs = (uint32_t)(a.nkv * PS * HD + kvh * HD * PS) * EB;
   const uint32_t page_bytes = (uint32_t)a.page_stride * EB;
   const uint8_t* kv = reinterpret_cast<const uint8_t*>(a.kv_layer);
+  // the page table is read with scalar loads (wave-uniform entries), which
+  // the vector-memory counter the ring waits on does not count
+  const_i32_t* pg_id = (const_i32_t*)a.pg_id;
+  const_i32_t* pg_valid = (const_i32_t*)a.pg_valid;
+  const_i32_t* pg_start = (const_i32_t*)a.pg_start;
   const int e_begin = a.seq_pg0[s];
   int e_end = a.seq_pg0[s + 1];
   while (e_end > e_begin && a.pg_start[e_end - 1] > qmax) --e_end;
   const int n_stages = (e_end - e_begin + SP - 1) / SP;
-  const bool loader = tid < LOADERS;
+  // everything loaded above has landed before the ring's loads are counted
+  __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
 
-  // this thread's pieces of a stage: K and V of each of the SP pages
-  Piece pc[SP][2];
-  int pv[SP], ps[SP];
-  auto load_stage = [&](int st) {
+  // This wave's loads of a stage: byte range [wave * LPW KiB, + LPW KiB) of
+  // the stage, all within one page's K or V block.  Stages past the end use a
+  // zero-size descriptor (zeros, no memory access), so every iteration issues
+  // the same number of loads and waits on a fixed count.
+  const int l0 = wave * LPW, pj = l0 / (2 * PB_L), kvsel = (l0 / PB_L) & 1, part0 = l0 % PB_L;
+  auto issue = [&](int st) {
+    const int e = e_begin + st * SP + pj;
+    const bool live = st < n_stages && e < e_end;
+    const int pg = live ? pg_id[e] : 0;
+    const i32x4_t r = page_words(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
+    uint8_t* dst = &skv[st % NS][(pj * 2 + kvsel) * PAGE_B];
 #pragma unroll
-    for (int j = 0; j < SP; ++j) {
-      const int e = e_begin + st * SP + j;
-      const bool live = e < e_end;
-      // the same entry for every lane: keep the page id (and the descriptor) scalar
-      const int pg = __builtin_amdgcn_readfirstlane(live ? a.pg_id[e] : 0);
-      pv[j] = live ? a.pg_valid[e] : 0;
-      ps[j] = live ? a.pg_start[e] : 0;
-      const __amdgpu_buffer_rsrc_t r = page_rsrc(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
-#pragma unroll
-      for (int kvsel = 0; kvsel < 2; ++kvsel) {
-        const uint32_t off = loader ? (kvsel ? vofs : kofs) + (uint32_t)tid * PIECE : 0xFFFFFFF0u;
-        if constexpr (PIECE == 16)
-          pc[j][kvsel] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_NT));
-        else if constexpr (PIECE == 8)
-          pc[j][kvsel] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CPOL_NT));
-        else
-          pc[j][kvsel] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL_NT);
-      }
-    }
-  };
-  auto store_stage = [&](int buf) {
-    if (loader) {
-#pragma unroll
-      for (int j = 0; j < SP; ++j)
-#pragma unroll
-        for (int kvsel = 0; kvsel < 2; ++kvsel)
-          *reinterpret_cast<Piece*>(&skv[buf][(j * 2 + kvsel) * PAGE_B + tid * PIECE]) = pc[j][kvsel];
-    }
-    if (tid < SP) {
-      s_valid[buf][tid] = pv[tid];
-      s_start[buf][tid] = ps[tid];
+    for (int k = 0; k < LPW; ++k) {
+      const int d = (part0 + k) * 1024 + lane * 16;  // destination byte in the block
+      // V rows are stored with their 16-byte halves swizzled (vswz, an involution)
+      const int src = kvsel && !E4M3 ? vswz(d) : d;
+      dma16(r, dst + (part0 + k) * 1024, (uint32_t)src + (kvsel ? vofs : kofs), 0u);
     }
   };
 
   if (n_stages > 0) {
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
+    issue(0);
+    issue(1);
     for (int st = 0; st < n_stages; ++st) {
-      const int buf = st & 1;
-      if (st + 1 < n_stages) load_stage(st + 1);
+      // stage st landed here (only stage st + 1 may be in flight) and
+      // everywhere after the barrier, which also frees stage st - 1's slot
+      __builtin_amdgcn_s_waitcnt(PF_WAIT(LPW));
+      // a plain barrier: a workgroup fence would also wait for the ring's
+      // loads in flight; the memory clobber keeps LDS accesses on their side
+      asm volatile("s_barrier" ::: "memory");
+      issue(st + 2);
       if (wave_live) {
+        const int eb = e_begin + st * SP;
+        const uint8_t* sb = skv[st % NS];
 #pragma unroll
-        for (int j0 = 0; j0 < SP; j0 += 2)
-          prefill_pair<HD, E4M3, RB>(&skv[buf][(j0 * 2) * PAGE_B], &skv[buf][(j0 * 2 + 2) * PAGE_B],
-                                     &skv[buf][(j0 * 2 + 1) * PAGE_B], &skv[buf][(j0 * 2 + 3) * PAGE_B],
-                                     s_valid[buf][j0], s_valid[buf][j0 + 1], s_start[buf][j0],
-                                     s_start[buf][j0 + 1], qf, oacc, m_run, l_run, qidx, scale_log2, lane);
+        for (int j0 = 0; j0 < SP; j0 += 2) {
+          const int e0 = eb + j0, e1 = eb + j0 + 1;
+          const int v0 = e0 < e_end ? pg_valid[e0] : 0, v1 = e1 < e_end ? pg_valid[e1] : 0;
+          const int st0 = e0 < e_end ? pg_start[e0] : 0, st1 = e1 < e_end ? pg_start[e1] : 0;
+          const uint8_t *k0 = sb + (j0 * 2) * PAGE_B, *k1 = sb + (j0 * 2 + 2) * PAGE_B;
+          const uint8_t *vv0 = sb + (j0 * 2 + 1) * PAGE_B, *vv1 = sb + (j0 * 2 + 3) * PAGE_B;
+          if (v0 == PS && v1 == PS && max(st0, st1) + PS - 1 <= q_first)
+            prefill_pair<HD, E4M3, RB, true>(k0, k1, vv0, vv1, v0, v1, st0, st1, qf, oacc, m_run, l_run, qidx,
+                                             scale_log2, lane);
+          else
+            prefill_pair<HD, E4M3, RB, false>(k0, k1, vv0, vv1, v0, v1, st0, st1, qf, oacc, m_run, l_run, qidx,
+                                              scale_log2, lane);
+        }
       }
-      if (st + 1 < n_stages) store_stage(buf ^ 1);  // that buffer was last read in stage st - 1
-      __syncthreads();
     }
+    // no load into this workgroup's LDS may still be in flight when it ends
+    __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
   }
 
   const float vs = E4M3 ? a.kv_scale[a.nkv + kvh] : 1.f;
