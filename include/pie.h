@@ -228,6 +228,34 @@ typedef struct pie_pass {
 int pie_forward(pie_ctx* ctx, const pie_pass* passes, int32_t n_passes, int32_t* out_tokens,
                 float* out_logits, int32_t flags);
 
+/* Loop-carried decode, enqueued without waiting ("How Pie thinks", section 3
+ * Forward passes: submitting a pass to a Pipeline returns at once and queued
+ * passes run in order, so later passes can be submitted before earlier
+ * results are back; section 5 Epilogues: only the chosen token leaves the GPU).
+ * Here the token does not even leave it: each step's output feeds the next.
+ * One committed pass of one token per working set ws[0..n), read out at that
+ * token with epi[i] (host [n]), at position = the working set's length.
+ *  tokens_in:  DEVICE int32 [n]; pass i's token is tokens_in[i] as the step
+ *              reads it on the GPU, so it may be the output of a step still
+ *              in flight (tokens_in == tokens_out is allowed).
+ *  tokens_out: DEVICE int32 [n]; receives the chosen tokens.
+ *  logits_dev: NULL, or DEVICE float32 [n][vocab] for the step's logits.
+ * Nothing is copied to the host and the call returns once the step is
+ * enqueued on the context's stream; steps run in the order enqueued.  The
+ * host bookkeeping (working-set lengths, page reservation) advances at
+ * enqueue, with the same validation and all-or-nothing rule as pie_forward
+ * (token values are not checked: they are on the device).  At most 4 calls
+ * are staged ahead of the GPU; a further call waits for the oldest staging
+ * copy to run.  The device arrays must stay valid until the step has run
+ * (pie_sync).  Kernel timing (pie_profile_enable) must be off: PIE_EINVAL.
+ * Errors: as pie_forward; a HIP error of a step may surface at pie_sync. */
+int pie_decode_async(pie_ctx* ctx, const pie_ws* ws, int32_t n, const int32_t* tokens_in, int32_t* tokens_out,
+                     const pie_epilogue* epi, float* logits_dev);
+
+/* Wait until every enqueued step has run; PIE_EHIP (and a poisoned context)
+ * if one of them failed. */
+int pie_sync(pie_ctx* ctx);
+
 const char* pie_last_error(void);
 
 /* ---------------------------------------------------------------------------

@@ -191,6 +191,9 @@ struct GraphEntry {
 
 }  // namespace
 
+// Pinned metadata staging slots: how many calls may be enqueued ahead of the GPU.
+constexpr int PIE_STAGING_SLOTS = 4;
+
 struct pie_ctx {
   pie_model_desc d{};
   pie_limits lim{};
@@ -206,7 +209,18 @@ struct pie_ctx {
   hipStream_t stream = nullptr;
   pie::KVStore store{16};
   pie::Plan plan;
+  // Pinned metadata staging: a ring of slots, each reused only after the
+  // copy out of it (recorded by its event) has run, so calls may be
+  // enqueued ahead of the GPU.  `pinned` is the slot of the current call.
   int32_t* pinned = nullptr;
+  std::vector<int32_t*> pin_ring;
+  std::vector<hipEvent_t> pin_ev;
+  int pin_next = 0;
+  // loop-carried decode: device token arrays of the call being enqueued
+  const int32_t* dev_tok_in = nullptr;
+  int32_t* dev_tok_out = nullptr;
+  std::vector<pie_pass> async_pass;
+  std::vector<int32_t> async_zero;
   std::vector<int32_t> dec, comb, pre;  // int4 items, flattened
   int n_parts = 0;
   // profiling: events bracketing timed launches, recorded into a sink
@@ -366,10 +380,23 @@ int stage(pie_ctx* c) {
   return PIE_OK;
 }
 
-// Metadata upload (pinned staging -> device), on the caller's stream.
+// Take the next staging slot, once the copy last made out of it has run.
+int acquire_staging(pie_ctx* c) {
+  if (c->pin_ring.empty()) return PIE_OK;  // host-only context: one host buffer
+  c->pinned = c->pin_ring[c->pin_next];
+  HIP_TRY(c, hipEventSynchronize(c->pin_ev[c->pin_next]));
+  return PIE_OK;
+}
+
+// Metadata upload (pinned staging -> device), on the caller's stream; the
+// slot's event marks when the slot may be packed again.
 int upload_meta(pie_ctx* c) {
   int32_t* dmeta = reinterpret_cast<int32_t*>(c->ws + c->lay.meta);
   HIP_TRY(c, hipMemcpyAsync(dmeta, c->pinned, c->lay.tokens_out * 4, hipMemcpyHostToDevice, c->stream));
+  if (!c->pin_ring.empty()) {
+    HIP_TRY(c, hipEventRecord(c->pin_ev[c->pin_next], c->stream));
+    c->pin_next = (c->pin_next + 1) % (int)c->pin_ring.size();
+  }
   return PIE_OK;
 }
 
@@ -409,7 +436,7 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
   if ((rc = check_launch(c, flags, "rope table"))) return rc;
   {
     Timed tm(c, PIE_K_EMBED);
-    pie::launch_embed(c->embed, M32(L.tok), T, d.d_model, y, ss, st);
+    pie::launch_embed(c->embed, c->dev_tok_in ? c->dev_tok_in : M32(L.tok), T, d.d_model, y, ss, st);
   }
   if ((rc = check_launch(c, flags, "embed"))) return rc;
 
@@ -567,7 +594,7 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
     if ((rc = check_launch(c, flags, "down gemm"))) return rc;
   }
 
-  int32_t* dtok = M32(L.tokens_out);
+  int32_t* dtok = c->dev_tok_out ? c->dev_tok_out : M32(L.tokens_out);
   if (R > 0) {
     float* logits = nullptr;
     if (out_logits) logits = (flags & PIE_FLAG_LOGITS_DEVICE) ? out_logits : reinterpret_cast<float*>(c->ws + L.logits);
@@ -613,7 +640,9 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
 // time its launch shape comes up) a graph of the whole launch sequence.
 // Graphs are captured on an internal stream and launched on the caller's.
 int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
-  int rc = stage(c);
+  int rc = acquire_staging(c);
+  if (rc) return rc;
+  rc = stage(c);
   if (rc) return rc;
   const pie::Plan& p = c->plan;
   const bool host_logits = out_logits && !(flags & PIE_FLAG_LOGITS_DEVICE);
@@ -665,6 +694,24 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
   if (c->prof_mask) collect_profile(c, c->sink);
   if (p.n_readout > 0) std::memcpy(out_tokens, c->pinned + c->lay.tokens_out, (size_t)p.n_readout * 4);
   return PIE_OK;
+}
+
+// Enqueue one loop-carried decode step: tokens come from and go to device
+// arrays, nothing is copied back and nothing waits for the GPU.
+int run_decode_async(pie_ctx* c, const int32_t* tokens_in, int32_t* tokens_out, float* logits_dev) {
+  int rc = acquire_staging(c);
+  if (rc) return rc;
+  if ((rc = stage(c))) return rc;
+  if ((rc = upload_meta(c))) return rc;
+  c->cur = c->stream;
+  c->sink.used = 0;
+  c->sink.marks.clear();
+  c->dev_tok_in = tokens_in;
+  c->dev_tok_out = tokens_out;
+  rc = enqueue(c, logits_dev, logits_dev ? PIE_FLAG_LOGITS_DEVICE : 0);
+  c->dev_tok_in = nullptr;
+  c->dev_tok_out = nullptr;
+  return rc;
 }
 
 }  // namespace
@@ -753,8 +800,21 @@ int pie_init(const pie_model_desc* desc, const pie_weights* w, void* kv_arena, s
     delete c;
     return set_err(PIE_ESTATE, std::string("pie_init: kernels are built for gfx950, device is ") + prop.gcnArchName);
   }
-  e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned), c->lay.meta_ints * 4, hipHostMallocDefault);
-  if (e != hipSuccess) { delete c; return set_err(PIE_EHIP, std::string("pie_init: hipHostMalloc: ") + hipGetErrorString(e)); }
+  for (int i = 0; i < PIE_STAGING_SLOTS; ++i) {
+    int32_t* buf = nullptr;
+    hipEvent_t ev = nullptr;
+    e = hipHostMalloc(reinterpret_cast<void**>(&buf), c->lay.meta_ints * 4, hipHostMallocDefault);
+    if (e == hipSuccess) c->pin_ring.push_back(buf);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e == hipSuccess) c->pin_ev.push_back(ev);
+    if (e != hipSuccess) {
+      for (auto b : c->pin_ring) (void)hipHostFree(b);
+      for (auto v : c->pin_ev) (void)hipEventDestroy(v);
+      delete c;
+      return set_err(PIE_EHIP, std::string("pie_init: staging buffers: ") + hipGetErrorString(e));
+    }
+  }
+  c->pinned = c->pin_ring[0];
   // a default-priority stream of our own, used only to capture launch graphs
   if (hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess) c->cap_stream = nullptr;
   // Graph replay is opt-in: on the measured ROCm stack a replay of the
@@ -774,7 +834,8 @@ int pie_destroy(pie_ctx* c) {
     (void)hipStreamSynchronize(c->stream);
     release_graphs(c);
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
-    if (c->pinned) (void)hipHostFree(c->pinned);
+    for (auto b : c->pin_ring) (void)hipHostFree(b);
+    for (auto v : c->pin_ev) (void)hipEventDestroy(v);
     for (auto e : c->sink.ev) (void)hipEventDestroy(e);
   }
   delete c;
@@ -858,6 +919,46 @@ int pie_forward(pie_ctx* c, const pie_pass* passes, int32_t n_passes, int32_t* o
     return PIE_OK;
   }
   return run_forward(c, out_tokens, out_logits, flags);
+}
+
+int pie_decode_async(pie_ctx* c, const pie_ws* ws, int32_t n, const int32_t* tokens_in, int32_t* tokens_out,
+                     const pie_epilogue* epi, float* logits_dev) {
+  CTX_OK(c);
+  if (c->host_only) return set_err(PIE_ESTATE, "pie_decode_async: host-only context");
+  if (!ws || n < 1 || !tokens_in || !tokens_out || !epi)
+    return set_err(PIE_EINVAL, "pie_decode_async: null argument or n < 1");
+  if (c->prof_mask) return set_err(PIE_EINVAL, "pie_decode_async: kernel timing needs synchronous calls");
+  // one committed pass of one token per working set, read out at its row;
+  // the host token is a placeholder (the embedding reads tokens_in)
+  if ((int)c->async_zero.size() < n) c->async_zero.assign(n, 0);
+  c->async_pass.resize(n);
+  static const int32_t zero_row = 0;
+  for (int i = 0; i < n; ++i) {
+    pie_pass& q = c->async_pass[i];
+    q = pie_pass{};
+    q.ws = ws[i];
+    q.tokens = &c->async_zero[i];
+    q.n_tokens = 1;
+    q.positions = nullptr;
+    q.readout = &zero_row;
+    q.n_readout = 1;
+    q.epi = &epi[i];
+    q.commit = 1;
+  }
+  pie::PackLimits pl{c->lim.max_rows, c->lim.max_seqs, c->lim.max_readout, c->lim.max_ctx,
+                     c->lay.max_pe, c->d.vocab};
+  std::string err;
+  int rc = pie::pack_batch(c->store, c->async_pass.data(), n, pl, &c->plan, &err);
+  if (rc) return set_err(rc, err);
+  return run_decode_async(c, tokens_in, tokens_out, logits_dev);
+}
+
+int pie_sync(pie_ctx* c) {
+  CTX_OK(c);
+  if (c->host_only) return PIE_OK;
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  HIP_TRY(c, hipGetLastError());
+  return PIE_OK;
 }
 
 const char* pie_last_error(void) { return g_err.c_str(); }

@@ -97,6 +97,11 @@ def upload_weights(recipe, device="cuda", progress=None) -> Dict:
     return w
 
 
+def torch_int32():
+    import torch
+    return torch.int32
+
+
 class PieRuntime:
     """One context over torch-owned device memory (or a host-only context when
     weights is None: working sets and packing without the GPU)."""
@@ -241,8 +246,9 @@ class PieRuntime:
             arr["n_readout"] = 1
             arr["epi"] = np.uint64(epi.ctypes.data) + idx * np.uint64(EPI_DT.itemsize)
             arr["commit"] = 1
-            buf = self._decode_bufs[n] = (arr, tok, epi, out)
-        arr, tok, epi, out = buf
+            # every array the pass records point into is kept alive with them
+            buf = self._decode_bufs[n] = (arr, tok, epi, out, ro)
+        arr, tok, epi, out, _ = buf
         arr["ws"] = ws
         tok[:] = tokens
         epi["kind"] = kind
@@ -255,6 +261,35 @@ class PieRuntime:
         check(N.lib().pie_forward(self.ctx, arr.ctypes.data_as(ctypes.POINTER(N.pie_pass)), n,
                                   out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), logits_ptr, flags))
         return out.copy()
+
+    def decode_async(self, ws: np.ndarray, tokens_in, tokens_out, kind=0, temperature=1.0, seed=0,
+                     logits_out=None) -> None:
+        """Enqueue one loop-carried decode step (pie_decode_async): one token per
+        working set in `ws` (uint64 handles), read from the device int32 tensor
+        `tokens_in`, the chosen tokens written to the device int32 tensor
+        `tokens_out` (which may be `tokens_in`); returns without waiting.
+        Epilogue parameters are scalars or per-row arrays."""
+        n = len(ws)
+        for t in (tokens_in, tokens_out):
+            if t.dtype != torch_int32() or not t.is_cuda or t.numel() < n or not t.is_contiguous():
+                raise ValueError("tokens_in / tokens_out: contiguous int32 device tensors of >= %d elements" % n)
+        key = ("async", n)
+        buf = self._decode_bufs.get(key)
+        if buf is None:
+            buf = self._decode_bufs[key] = (np.zeros(n, dtype=np.uint64), np.zeros(n, dtype=EPI_DT))
+        wsa, epi = buf
+        wsa[:] = ws
+        epi["kind"] = kind
+        epi["temperature"] = temperature
+        epi["seed"] = seed
+        check(N.lib().pie_decode_async(
+            self.ctx, wsa.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), n, tokens_in.data_ptr(),
+            tokens_out.data_ptr(), epi.ctypes.data_as(ctypes.POINTER(N.pie_epilogue)),
+            logits_out.data_ptr() if logits_out is not None else None))
+
+    def sync(self) -> None:
+        """Wait for every enqueued step (pie_sync)."""
+        check(N.lib().pie_sync(self.ctx))
 
     def forward(self, passes: Sequence[Pass], want_logits: bool = False, flags: int = 0,
                 logits_out=None):

@@ -324,3 +324,92 @@ def test_tiny_readout_lanes_positions_and_rollback(torch_cuda):
     rep.add(toks[1], t, m, tau_for(1, 1.0), lg[1], ref[1], ("after rollback", 2))
     rep.check()
     rt.close()
+
+
+def test_tiny_async_loop_carried_decode(torch_cuda):
+    """pie_decode_async: each step reads its tokens from the previous step's
+    device output, nothing returns to the host until the end.  Every step's
+    tokens and logits equal the synchronous pie_forward loop's, bit for bit,
+    for argmax and for Gumbel-max with a fresh seed per step; the greedy
+    trajectory agrees with the oracle's free-running loop up to a near-tie."""
+    torch = torch_cuda
+    recipe = RECIPES["gains1"]
+    shape = recipe.shape
+    prompts = [synth.prompt_tokens(1, s, PROMPT, shape.vocab) for s in range(N_SEQ)]
+    ref = oracle_greedy(recipe, prompts, STEPS, [0] * N_SEQ, [1.0] * N_SEQ, lambda s, k: 0)
+    rt = make_runtime(shape, recipe, torch_cuda)
+    for kind, temp in [(0, 1.0), (1, 0.7)]:
+        seeds = lambda k: np.array([synth.epilogue_seed(0x5EED0000 + s, k) for s in range(N_SEQ)], dtype=np.uint64)
+        ws_sync = np.array([rt.alloc() for _ in range(N_SEQ)], dtype=np.uint64)
+        ws_async = np.array([rt.alloc() for _ in range(N_SEQ)], dtype=np.uint64)
+        first = None
+        for ws in (ws_sync, ws_async):
+            from paged_kv_forward_amd.runtime import Pass
+            toks, _ = rt.forward([Pass(int(ws[s]), prompts[s], [PROMPT - 1], [(0, 1.0, 0)]) for s in range(N_SEQ)])
+            first = toks if first is None else first
+            assert list(toks) == list(first)
+        # synchronous loop
+        sync_toks, sync_lg = [], []
+        cur = np.array(first, dtype=np.int32)
+        lg = torch.empty((N_SEQ, shape.vocab), dtype=torch.float32, device="cuda")
+        for k in range(STEPS):
+            cur = rt.decode_step(ws_sync, cur, kind=kind, temperature=temp, seed=seeds(k), logits_out=lg)
+            sync_toks.append(cur.copy())
+            sync_lg.append(lg.cpu().numpy())
+        # loop-carried: one device buffer is both input and output of every step
+        tok_dev = torch.tensor(np.array(first, dtype=np.int32), device="cuda")
+        hist = torch.empty((STEPS, N_SEQ), dtype=torch.int32, device="cuda")
+        lgs = torch.empty((STEPS, N_SEQ, shape.vocab), dtype=torch.float32, device="cuda")
+        for k in range(STEPS):
+            rt.decode_async(ws_async, tok_dev, tok_dev, kind=kind, temperature=temp, seed=seeds(k),
+                            logits_out=lgs[k])
+            hist[k].copy_(tok_dev)  # same stream as the library: runs after the step
+            rt.sync()
+        a_toks = hist.cpu().numpy()
+        for k in range(STEPS):
+            np.testing.assert_array_equal(a_toks[k], sync_toks[k])
+            np.testing.assert_array_equal(lgs[k].cpu().numpy(), sync_lg[k])
+        for s in range(N_SEQ):
+            assert rt.ws_info(int(ws_async[s]))["len"] == PROMPT + STEPS
+        if kind == 0:
+            gen = np.concatenate([np.array(first)[None, :], a_toks], axis=0)
+            for s in range(N_SEQ):
+                for k in range(STEPS + 1):
+                    t, m, _ = ref[s][k]
+                    if gen[k][s] != t:
+                        assert m < 2e-2, (s, k, gen[k][s], t, m)
+                        break
+    rt.close()
+
+
+def test_tiny_async_steps_enqueued_back_to_back(torch_cuda):
+    """Steps enqueued without any host wait in between (more than the staging
+    ring holds) give the synchronous loop's tokens; the only wait is at the end."""
+    torch = torch_cuda
+    recipe = RECIPES["gains_spread"]
+    shape = recipe.shape
+    from paged_kv_forward_amd.runtime import Pass
+    prompts = [synth.prompt_tokens(1, 20 + s, PROMPT + s, shape.vocab) for s in range(N_SEQ)]
+    rt = make_runtime(shape, recipe, torch_cuda)
+    steps = 12
+    ws_a = np.array([rt.alloc() for _ in range(N_SEQ)], dtype=np.uint64)
+    ws_b = np.array([rt.alloc() for _ in range(N_SEQ)], dtype=np.uint64)
+    firsts = []
+    for ws in (ws_a, ws_b):
+        toks, _ = rt.forward([Pass(int(ws[s]), prompts[s], [len(prompts[s]) - 1], [(0, 1.0, 0)])
+                              for s in range(N_SEQ)])
+        firsts.append(np.array(toks, dtype=np.int32))
+    cur = firsts[0]
+    sync_toks = []
+    for k in range(steps):
+        cur = rt.decode_step(ws_a, cur)
+        sync_toks.append(cur.copy())
+    bufs = torch.empty((steps + 1, N_SEQ), dtype=torch.int32, device="cuda")
+    bufs[0].copy_(torch.tensor(firsts[1], device="cuda"))
+    torch.cuda.synchronize()
+    for k in range(steps):
+        rt.decode_async(ws_b, bufs[k], bufs[k + 1])
+    rt.sync()
+    got = bufs.cpu().numpy()[1:]
+    np.testing.assert_array_equal(got, np.stack(sync_toks))
+    rt.close()

@@ -202,6 +202,23 @@ def test_host_only_context_refuses_launch():
     rt.close()
 
 
+def test_async_decode_refused_without_a_gpu_context():
+    """pie_decode_async needs a context with device state; pie_sync of a
+    host-only context has nothing to wait for; a null context is refused."""
+    import ctypes
+    rt = host_rt()
+    a = rt.alloc()
+    ws = (ctypes.c_uint64 * 1)(a)
+    epi = (N.pie_epilogue * 1)()
+    rc = N.lib().pie_decode_async(rt.ctx, ws, 1, ctypes.c_void_p(16), ctypes.c_void_p(16), epi, None)
+    assert rc == N.PIE_ESTATE
+    assert rt.ws_info(a)["len"] == 0
+    assert N.lib().pie_sync(rt.ctx) == N.PIE_OK
+    assert N.lib().pie_decode_async(None, ws, 1, ctypes.c_void_p(16), ctypes.c_void_p(16), epi, None) == N.PIE_EINVAL
+    assert N.lib().pie_sync(None) == N.PIE_EINVAL
+    rt.close()
+
+
 def test_plan_layout_of_a_mixed_batch():
     """Packed rows, slots and page tables of a batch that mixes a prefill chunk,
     a decode row, a forked branch and explicit positions."""
