@@ -256,6 +256,22 @@ int pie_decode_async(pie_ctx* ctx, const pie_ws* ws, int32_t n, const int32_t* t
  * if one of them failed. */
 int pie_sync(pie_ctx* ctx);
 
+/* Prefix sharing across requests ("How Pie thinks", section 4 Working sets:
+ * a fork shares the frozen prefix and copies nothing; this extends that to
+ * working sets with no common parent).  Every whole page of a committed
+ * prefix whose token ids were given on the host (pie_forward, not
+ * pie_decode_async) at the default positions 0, 1, 2, ... is remembered
+ * under its token prefix.  This call returns in *out a new working set
+ * holding the longest remembered prefix of tokens (host [n]) in whole pages,
+ * at most n - 1 tokens, shared with the working sets that computed it
+ * (reference counts +1, no KV byte copied or recomputed); *n_shared is its
+ * length, 0 when nothing matched (a plain empty working set).  The caller then
+ * runs tokens[*n_shared, n) as the set's first pass.  A page is forgotten when
+ * its last holder frees it.  Matching compares the page's own token ids and
+ * two independent chain hashes of everything before it.
+ * Errors: PIE_EINVAL (null argument, n < 1, token id out of range). */
+int pie_prefix_lookup(pie_ctx* ctx, const int32_t* tokens, int32_t n, pie_ws* out, int32_t* n_shared);
+
 const char* pie_last_error(void);
 
 /* ---------------------------------------------------------------------------

@@ -24,7 +24,7 @@ EXPORTS = ["pie_kv_page_bytes", "pie_workspace_bytes", "pie_init", "pie_destroy"
            "pie_alloc_working_set", "pie_fork", "pie_free_working_set", "pie_truncate",
            "pie_ws_info", "pie_pool_stats_get", "pie_forward", "pie_last_error",
            "pie_profile_enable", "pie_profile_read", "pie_debug_plan", "pie_debug_philox",
-           "pie_packed_weight_bytes", "pie_pack_weight", "pie_decode_async", "pie_sync"]
+           "pie_packed_weight_bytes", "pie_pack_weight", "pie_decode_async", "pie_sync", "pie_prefix_lookup"]
 
 
 class pie_model_desc(Structure):
@@ -110,6 +110,7 @@ def lib():
         "pie_decode_async": (c_int, [c_void_p, P(c_uint64), c_int32, c_void_p, c_void_p, P(pie_epilogue),
                                      c_void_p]),
         "pie_sync": (c_int, [c_void_p]),
+        "pie_prefix_lookup": (c_int, [c_void_p, P(c_int32), c_int32, P(c_uint64), P(c_int32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

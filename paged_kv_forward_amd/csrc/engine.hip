@@ -948,9 +948,20 @@ int pie_decode_async(pie_ctx* c, const pie_ws* ws, int32_t n, const int32_t* tok
   pie::PackLimits pl{c->lim.max_rows, c->lim.max_seqs, c->lim.max_readout, c->lim.max_ctx,
                      c->lay.max_pe, c->d.vocab};
   std::string err;
-  int rc = pie::pack_batch(c->store, c->async_pass.data(), n, pl, &c->plan, &err);
+  int rc = pie::pack_batch(c->store, c->async_pass.data(), n, pl, &c->plan, &err, /*host_tokens=*/false);
   if (rc) return set_err(rc, err);
   return run_decode_async(c, tokens_in, tokens_out, logits_dev);
+}
+
+int pie_prefix_lookup(pie_ctx* c, const int32_t* tokens, int32_t n, pie_ws* out, int32_t* n_shared) {
+  CTX_OK(c);
+  if (tokens && n > 0)
+    for (int32_t i = 0; i < n; ++i)
+      if (tokens[i] < 0 || tokens[i] >= c->d.vocab)
+        return set_err(PIE_EINVAL, "pie_prefix_lookup: token id out of range");
+  std::string err;
+  int rc = c->store.lookup(tokens, n, out, n_shared, &err);
+  return rc ? set_err(rc, err) : PIE_OK;
 }
 
 int pie_sync(pie_ctx* c) {

@@ -10,11 +10,23 @@
 // is held once and has room, otherwise to fresh pages.  So a partly filled page
 // shared by a fork stays partly filled, and its unused slots are skipped.
 //
+// Frozen prefixes are also shared across requests ("How Pie thinks", section 4:
+// fork shares a prefix without copying it; here the same holds between working
+// sets that never forked from each other).  Every full page of a frozen
+// prefix whose tokens the host knows, at positions 0, 1, 2, ..., is entered in
+// a registry under a chained hash of all tokens up to the page's end;
+// lookup() walks a new request's tokens page by page and hands back a
+// working set that shares the longest registered prefix (reference counts +1,
+// nothing is copied or recomputed).  An entry also keeps the page's own tokens
+// and a second, independently seeded chain hash, and a match needs all three.
+// A page leaves the registry when its last holder lets go of it.
+//
 // Host-only code: no HIP here.
 #pragma once
 
 #include <cstdint>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 namespace pie {
@@ -47,6 +59,12 @@ struct WorkingSet {
   int32_t len = 0;
   int32_t frozen_len = 0;
   std::vector<PageEntry> pages;
+  // prefix registry bookkeeping: the tokens in append order while the host
+  // knows them and every position equals the token's index (else hist_ok is
+  // false for good), and the two chain hashes after each registered page
+  bool hist_ok = true;
+  std::vector<int32_t> toks;
+  std::vector<uint64_t> chain, chain2;
 };
 
 // What appending n tokens to a working set needs and where they go.
@@ -58,7 +76,13 @@ struct AppendPlan {
 class KVStore {
  public:
   explicit KVStore(int32_t page_size = 16) : P_(page_size) {}
-  void reset(int64_t n_pages) { pool_.reset(n_pages); sets_.clear(); free_slots_.clear(); }
+  void reset(int64_t n_pages) {
+    pool_.reset(n_pages);
+    sets_.clear();
+    free_slots_.clear();
+    prefix_.clear();
+    page_key_.assign((size_t)n_pages, 0);
+  }
 
   int32_t page_size() const { return P_; }
   const PagePool& pool() const { return pool_; }
@@ -75,15 +99,38 @@ class KVStore {
   // Append n tokens (the pool must hold plan.fresh_pages free pages).  slot_out[i]
   // receives page * page_size + offset of token i.
   void append(WorkingSet& ws, int32_t n, int32_t* slot_out);
-  void commit(WorkingSet& ws) { ws.frozen_len = ws.len; }
+  // Freeze everything appended so far and enter its new full pages in the
+  // prefix registry.
+  void commit(WorkingSet& ws);
+  // Record the n tokens about to be appended (tokens: host ids, or nullptr
+  // when only the device knows them; positions: nullptr for len + i).
+  void note_tokens(WorkingSet& ws, const int32_t* tokens, const int32_t* positions, int32_t n);
+
+  // A new working set sharing the longest registered prefix of tokens[0, n),
+  // whole pages only, at most n - 1 tokens (so that a pass remains to read
+  // out the last one).  *n_shared = its length (0: a plain empty set).
+  int lookup(const int32_t* tokens, int32_t n, uint64_t* out, int32_t* n_shared, std::string* err);
+  size_t registered_pages() const { return prefix_.size(); }
 
   size_t live_sets() const;
 
  private:
+  struct PrefixEntry {
+    int32_t page;
+    uint64_t h2;
+    std::vector<int32_t> toks;
+  };
+  void unref_page(int32_t page);  // pool unref; a freed page leaves the registry
+
   int32_t P_;
   PagePool pool_;
   std::vector<WorkingSet> sets_;
   std::vector<uint32_t> free_slots_;
+  std::unordered_map<uint64_t, PrefixEntry> prefix_;  // chain hash -> page
+  std::vector<uint64_t> page_key_;                     // page -> its registry key, 0 if none
 };
+
+// Chain hash of a page of tokens after the hash `prev` of everything before it.
+uint64_t prefix_hash(uint64_t prev, const int32_t* toks, int32_t n, uint64_t seed);
 
 }  // namespace pie

@@ -15,7 +15,7 @@ static int fail(std::string* err, int code, const char* fmt, long a = 0, long b 
 }
 
 int pack_batch(KVStore& store, const pie_pass* passes, int32_t n_passes, const PackLimits& lim,
-               Plan* plan, std::string* err) {
+               Plan* plan, std::string* err, bool host_tokens) {
   if (n_passes < 1) return fail(err, PIE_EINVAL, "pie_forward: need at least one pass");
   if (!passes) return fail(err, PIE_EINVAL, "pie_forward: null passes");
   if (n_passes > lim.max_seqs)
@@ -111,6 +111,7 @@ int pack_batch(KVStore& store, const pie_pass* passes, int32_t n_passes, const P
       pl.pos[row + i] = p.positions ? p.positions[i] : ws->len + i;
       pl.row_seq[row + i] = s;
     }
+    store.note_tokens(*ws, host_tokens ? p.tokens : nullptr, p.positions, p.n_tokens);
     store.append(*ws, p.n_tokens, &pl.slot[row]);
     if (p.commit) store.commit(*ws);
     pl.seq_len[s] = ws->len;

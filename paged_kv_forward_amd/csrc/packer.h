@@ -42,7 +42,10 @@ struct PackLimits {
 
 // Validate, reserve and apply.  With apply == false only validation and the
 // reservation check run (nothing changes).  Returns a pie_status.
+// host_tokens: false when the passes' token arrays are placeholders and the
+// real ids exist only on the device (loop-carried decode); such tokens are
+// kept out of the prefix registry.
 int pack_batch(KVStore& store, const pie_pass* passes, int32_t n_passes, const PackLimits& lim,
-               Plan* plan, std::string* err);
+               Plan* plan, std::string* err, bool host_tokens = true);
 
 }  // namespace pie

@@ -287,6 +287,16 @@ class PieRuntime:
             tokens_out.data_ptr(), epi.ctypes.data_as(ctypes.POINTER(N.pie_epilogue)),
             logits_out.data_ptr() if logits_out is not None else None))
 
+    def prefix_lookup(self, tokens) -> Tuple[int, int]:
+        """(working set, shared length): a new working set holding the longest
+        remembered page-aligned prefix of `tokens` (pie_prefix_lookup)."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        h = ctypes.c_uint64()
+        k = ctypes.c_int32()
+        check(N.lib().pie_prefix_lookup(self.ctx, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(t),
+                                        ctypes.byref(h), ctypes.byref(k)))
+        return h.value, k.value
+
     def sync(self) -> None:
         """Wait for every enqueued step (pie_sync)."""
         check(N.lib().pie_sync(self.ctx))

@@ -413,3 +413,36 @@ def test_tiny_async_steps_enqueued_back_to_back(torch_cuda):
     got = bufs.cpu().numpy()[1:]
     np.testing.assert_array_equal(got, np.stack(sync_toks))
     rt.close()
+
+
+def test_tiny_prefix_lookup_reuses_pages_exactly(torch_cuda):
+    """A request that starts with another request's committed prefix gets the
+    prefix's pages through pie_prefix_lookup and runs only its own tokens: its
+    readout equals a from-scratch run of the whole sequence (same kernels on
+    the same values) and the oracle's, and no page is allocated for the
+    shared part."""
+    from paged_kv_forward_amd.runtime import Pass
+    recipe = RECIPES["gains_spread"]
+    shape = recipe.shape
+    rt = make_runtime(shape, recipe, torch_cuda)
+    pre = synth.prompt_tokens(1, 40, 40, shape.vocab)
+    tail = synth.prompt_tokens(1, 41, 10, shape.vocab)
+    full = np.concatenate([pre[:32], tail])
+    a = rt.alloc()
+    rt.forward([Pass(a, pre, [39], [(0, 1.0, 0)])])
+    st0 = rt.pool_stats()
+    b, k = rt.prefix_lookup(full)
+    assert k == 32
+    assert list(rt.ws_info(b)["pages"]) == list(rt.ws_info(a)["pages"][:2])
+    tb, lb = rt.forward([Pass(b, full[32:], [9], [(0, 1.0, 0)])], want_logits=True)
+    assert rt.pool_stats()["pages_ever_allocated"] == st0["pages_ever_allocated"] + 1  # b's own tail page
+    c = rt.alloc()
+    tc, lc = rt.forward([Pass(c, full, [41], [(0, 1.0, 0)])], want_logits=True)
+    assert int(tb[0]) == int(tc[0])
+    np.testing.assert_allclose(lb, lc, rtol=0, atol=1e-5)
+    w = SynthWeights(recipe, cache_layers=True)
+    ref = Session(w, default_numerics(shape)).step(list(full))[0]
+    err = float(np.max(np.abs(lb[0] - ref)))
+    say("prefix reuse: max|dlogit| vs oracle %.4f" % err)
+    assert err <= 2e-2
+    rt.close()

@@ -352,3 +352,83 @@ def test_stored_conditioning_files_are_complete():
         # the float32 noise floor grows with depth (80 layers of the 70B shape
         # reach about 1.3) but stays below the spread of the logits themselves
         assert 0 < d["mean_abs_dlogit"] <= d["max_abs_dlogit"] < d["logit_std"]
+
+
+def test_prefix_lookup_shares_whole_committed_pages():
+    """pie_prefix_lookup: a request whose tokens start with a committed
+    prefix gets that prefix's whole pages (no new page, no copy), at most
+    n - 1 tokens; a different token anywhere in a page stops the match there."""
+    rt = host_rt(pages=32)
+    a = rt.alloc()
+    pre = toks(40, 7)
+    fwd(rt, [Pass(a, pre)])                      # committed: pages 0, 1 full, page 2 holds 8
+    pages_a = list(rt.ws_info(a)["pages"])
+    st0 = rt.pool_stats()
+    b, k = rt.prefix_lookup(pre[:32] + toks(5, 900))
+    assert k == 32
+    ib = rt.ws_info(b)
+    assert ib["len"] == ib["frozen_len"] == 32 and list(ib["pages"]) == pages_a[:2]
+    assert rt.pool_stats()["pages_ever_allocated"] == st0["pages_ever_allocated"]
+    assert rt.pool_stats()["kv_bytes_copied"] == 0
+    # continue the shared prefix: new tokens go to a fresh page of b's own
+    fwd(rt, [Pass(b, toks(5, 900), [4], [(0, 1.0, 0)])])
+    assert list(rt.ws_info(b)["pages"][:2]) == pages_a[:2] and rt.ws_info(b)["pages"][2] not in pages_a
+    # the whole input matches: at most n - 1 tokens are shared
+    c, k = rt.prefix_lookup(pre[:32])
+    assert k == 16
+    # a changed token in page 1 stops the match after page 0
+    alt = list(pre[:40])
+    alt[20] = (alt[20] + 1) % synth.TINY.vocab
+    d, k = rt.prefix_lookup(alt)
+    assert k == 16 and list(rt.ws_info(d)["pages"]) == pages_a[:1]
+    # nothing in common
+    e, k = rt.prefix_lookup(toks(40, 3000))
+    assert k == 0 and rt.ws_info(e)["len"] == 0
+    rt.close()
+
+
+def test_prefix_registry_rules():
+    """Only host-known tokens at default positions are remembered; the
+    writable buffer is not; a page is forgotten when its last holder frees it."""
+    rt = host_rt(pages=32)
+    a = rt.alloc()
+    fwd(rt, [Pass(a, toks(20, 11), commit=0)])   # not committed: nothing to share
+    _, k = rt.prefix_lookup(toks(30, 11))
+    assert k == 0
+    fwd(rt, [Pass(a, toks(20, 31), commit=1)])   # commits all 40
+    _, k = rt.prefix_lookup(toks(20, 11) + toks(20, 31))
+    assert k == 32
+    # explicit positions that differ from the index: never remembered
+    p = rt.alloc()
+    fwd(rt, [Pass(p, toks(33, 500), positions=list(range(100, 133)))])
+    _, k = rt.prefix_lookup(toks(33, 500))
+    assert k == 0
+    # pages freed by every holder are forgotten
+    q = rt.alloc()
+    fwd(rt, [Pass(q, toks(17, 700))])
+    h, k = rt.prefix_lookup(toks(17, 700))
+    assert k == 16
+    rt.free(q)
+    h2, k = rt.prefix_lookup(toks(17, 700))
+    assert k == 16                               # h still holds the page
+    rt.free(h)
+    rt.free(h2)                                  # (every lookup result holds it too)
+    _, k = rt.prefix_lookup(toks(17, 700))
+    assert k == 0
+    # a fork of a page-aligned prefix inherits it and extends it
+    g = rt.alloc()
+    fwd(rt, [Pass(g, toks(48, 200))])
+    f = rt.fork(g)
+    fwd(rt, [Pass(f, toks(20, 60))])
+    _, k = rt.prefix_lookup(toks(48, 200) + toks(20, 60))
+    assert k == 64
+    # behind a partly filled page shared by a fork, token blocks no longer
+    # line up with pages: the match stops there
+    f2 = rt.fork(a)                              # a's third page holds 8 tokens
+    fwd(rt, [Pass(f2, toks(30, 60))])
+    _, k = rt.prefix_lookup(toks(20, 11) + toks(20, 31) + toks(30, 60))
+    assert k == 32
+    with pytest.raises(N.PieError) as e:
+        rt.prefix_lookup([synth.TINY.vocab])
+    assert e.value.code == N.PIE_EINVAL
+    rt.close()
