@@ -446,3 +446,29 @@ def test_tiny_prefix_lookup_reuses_pages_exactly(torch_cuda):
     say("prefix reuse: max|dlogit| vs oracle %.4f" % err)
     assert err <= 2e-2
     rt.close()
+
+
+@pytest.mark.parametrize("lens", [(150, 150), (600,), (257, 64)])
+def test_tiny_large_prefill_tiles_with_ragged_edges(torch_cuda, lens):
+    """Prefill launches of 256 rows or more use the 256 x 256 GEMM tiles: at the
+    tiny shape their row and column edges are ragged (300, 600 and 321 rows;
+    gate/up width 688 = 5 x 128 + 48), the down projection's K (688) is not a
+    multiple of 64 (register-staged tile) and the others' K (256) is (tiles
+    loaded straight into LDS).  Last-row logits of every sequence against the
+    oracle."""
+    from paged_kv_forward_amd.runtime import Pass
+    recipe = RECIPES["gains_spread"]
+    shape = recipe.shape
+    rt = make_runtime(shape, recipe, torch_cuda, max_rows=1024)
+    prompts = [synth.prompt_tokens(1, 60 + i, n, shape.vocab) for i, n in enumerate(lens)]
+    ws = [rt.alloc() for _ in prompts]
+    toks, lg = rt.forward([Pass(ws[i], prompts[i], [len(prompts[i]) - 1], [(0, 1.0, 0)])
+                           for i in range(len(prompts))], want_logits=True)
+    w = SynthWeights(recipe, cache_layers=True)
+    rep = Report()
+    for i, pr in enumerate(prompts):
+        ref = Session(w, default_numerics(shape)).step(list(pr))[0]
+        tok, margin = apply(ref, 0, 1.0, 0, 0)
+        rep.add(toks[i], tok, margin, tau_for(0, 1.0), lg[i], ref, tag=("prefill", len(pr)))
+    rep.check(max_excluded_frac=1.0)  # one or two rows: the logits carry the check
+    rt.close()
