@@ -270,7 +270,7 @@ def main():
     ap.add_argument("--steps", type=int, default=125)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true", help="time every kernel class (extra pass)")
+    ap.add_argument("--breakdown", action="store_true", help="(always on; kept for old command lines)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write profiles/ summaries from the rocprofv3 outputs under DIR and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -410,14 +410,26 @@ def main():
     step_bytes = weight_bytes + (ctx_sum / K) * kv_tok * shape.n_layers
     ms_step = t_dec / K * 1e3
 
-    breakdown = None
-    if args.breakdown:
-        rt.profile_enable(N.KERNEL_CLASSES)
-        for _ in range(3):
-            step()
-        pb = rt.profile_read()
-        rt.profile_enable([])
-        breakdown = {k: round(v[0] / 3, 4) for k, v in pb.items() if v[1]}
+    # every kernel class of 3 more steps with HIP events: time per step, and
+    # for the HBM-bound classes their algorithmic bytes per step / that time
+    ctx_bd = rt.ws_info(ws[0])["len"] + 1
+    rt.profile_enable(N.KERNEL_CLASSES)
+    for _ in range(3):
+        step()
+    pb = rt.profile_read()
+    rt.profile_enable([])
+    breakdown = {k: round(v[0] / 3, 4) for k, v in pb.items() if v[1]}
+    d, L_ = shape.d_model, shape.n_layers
+    wbytes = {"gemm_qkv": 2 * L_ * d * (shape.q_width + 2 * shape.kv_width),
+              "gemm_o": 2 * L_ * shape.q_width * d, "gemm_gateup": 2 * L_ * d * 2 * shape.d_ffn,
+              "gemm_down": 2 * L_ * shape.d_ffn * d, "lm_head": 2 * shape.vocab * d,
+              "attn_decode": L_ * (sum(N_SEQ * (ctx_bd + i) for i in range(3)) / 3 * kv_tok + qo)}
+    decode_kernels = {}
+    for k, b in wbytes.items():
+        if k in breakdown and breakdown[k] > 0:
+            gbs = b / (breakdown[k] * 1e-3) / 1e9
+            decode_kernels[k] = {"ms_per_step": breakdown[k], "bytes_per_step": int(b),
+                                 "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
     traffic = measured_traffic()
     out = {
@@ -454,8 +466,8 @@ def main():
         "prefill_tokens_per_s": round(N_SEQ * PROMPT / t_prefill, 1),
         "prefill_gemm": prefill_gemm,
     }
-    if breakdown:
-        out["ms_per_step_by_kernel"] = breakdown
+    out["ms_per_step_by_kernel"] = breakdown
+    out["decode_kernels_hbm"] = decode_kernels
     rt.close()
     del weights
     torch.cuda.empty_cache()

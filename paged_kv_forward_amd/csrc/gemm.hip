@@ -938,11 +938,13 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   if (nc > 0) {
     // Whole groups of SK_DEPTH chunks, with no branches inside a group:
     // chunks past nc load zeros (out-of-range offsets) and add nothing.
+    // the first activation group is needed before any MFMA, so its loads
+    // (L2 hits) go ahead of the weight stream's in the memory pipeline
+    uint4 xv[SK_XP];
+    load_x(xv, 0);
     WSlot ring[SK_DEPTH];
 #pragma unroll
     for (int j = 0; j < SK_DEPTH; ++j) load_w(ring[j], j);
-    uint4 xv[SK_XP];
-    load_x(xv, 0);
     store_x(xv, 0);
     lds_barrier();
     const int ngroups = (nc + SK_DEPTH - 1) / SK_DEPTH;
