@@ -149,7 +149,7 @@ Layout make_layout(const pie_model_desc& d, const pie_limits& l) {
   struct G { int n_tiles, K; } gs[4] = {
       {(int)((qw + 2 * kvw + GEMM_BN - 1) / GEMM_BN), d.d_model},
       {(d.d_model + GEMM_BN - 1) / GEMM_BN, (int)qw},
-      {(d.d_ffn + GEMM_BN / 2 - 1) / (GEMM_BN / 2), d.d_model},
+      {pie::gemm_n_tiles(pie::EPI_SWIGLU, d.d_ffn, pie::TILE_SKINNY), d.d_model},
       {(d.d_model + GEMM_BN - 1) / GEMM_BN, d.d_ffn}};
   size_t worst = 0;
   for (auto& g : gs) {

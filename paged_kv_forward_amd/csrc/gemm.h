@@ -70,6 +70,7 @@ struct GemmArgs {
   uint16_t* x_out;
   // EPI_SWIGLU
   uint16_t* h_out;  // [M][N] bf16
+  int cw;           // TILE_SKINNY: gate (and up) columns per tile, a multiple of 8 (0: BN / 2)
   // EPI_QKV
   uint16_t* q_out;  // [M][nq*hd] bf16
   const float* rope_cs;  // [M][hd/2][2] (cos, sin)
@@ -97,6 +98,15 @@ struct GemmArgs {
 // are 16-byte aligned, else staged through registers.  TILE_256x256_STAGED
 // always stages through registers (same results, bit for bit).
 enum GemmTile { TILE_64x128 = 0, TILE_128x128 = 1, TILE_SKINNY = 2, TILE_256x256 = 3, TILE_256x256_STAGED = 4 };
+
+// Gate/up columns per TILE_SKINNY EPI_SWIGLU tile: the gated width is cut into
+// whole rounds of 256 tiles (one per compute unit of the MI355X) of at most 64
+// columns each, in units of 8 columns, so every unit streams about the same
+// number of weight bytes (d_ffn 14336: 256 tiles of 56).
+inline int skinny_swiglu_cols(int N) {
+  const int units = (N + 7) / 8, tiles = 256 * ((N + 64 * 256 - 1) / (64 * 256));
+  return 8 * ((units + tiles - 1) / tiles);
+}
 
 // Most K splits of one skinny GEMM.
 constexpr int SK_MAX_SPLITS = 16;

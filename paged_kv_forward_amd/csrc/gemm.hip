@@ -219,10 +219,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int
   } else if constexpr (EPI == EPI_SWIGLU) {
     // h = bf16(silu(gate) * up), four columns per thread (N is a multiple of 8)
     constexpr int HALF = BN / 2, F4 = HALF / 4;
-    const int j0 = n_tile * HALF;
+    const int cw = g.cw ? g.cw : HALF, j0 = n_tile * cw;
     for (int idx = tid; idx < rows * F4; idx += NTH) {
       const int row = idx / F4, j = (idx % F4) * 4, m = m0 + row, n = j0 + j;
-      if (m >= g.M || n >= g.N) continue;
+      if (m >= g.M || n >= g.N || j >= cw) continue;
       const float4 gt = *reinterpret_cast<const float4*>(sC + row * ldc + j);
       const float4 up = *reinterpret_cast<const float4*>(sC + row * ldc + HALF + j);
       const float h0 = gt.x / (1.0f + expf(-gt.x)) * up.x, h1 = gt.y / (1.0f + expf(-gt.y)) * up.y;
@@ -872,7 +872,7 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
 }
 
-template <int EPI>
+template <int EPI, int WPOL>
 __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   // activation groups (two buffers), later reused for the output tile
   __shared__ __attribute__((aligned(16))) uint8_t smem[SK_LDS];
@@ -884,26 +884,36 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   const int ke = g.splits > 1 ? min(g.K, kb + g.k_split) : g.K;
   const int nc = ke > kb ? (ke - kb + SK_KC - 1) / SK_KC : 0;
 
-  // The wave's packed weight tensor, its 64-row block and 16-row panel.
+  // The wave's packed weight tensor and the element of this lane's piece in
+  // half 0 of K chunk 0 (half 1 is 512 further): B row r16 of the wave's 16
+  // output columns, k group gq.
+  const int kc = (g.K + 63) / 64;
   const uint16_t* wt;
-  int wblk, wrows;
+  int wrows;
+  uint32_t wbase;
+  bool wok = true;
   if (EPI == EPI_SWIGLU) {
+    // tile t: gated columns [t * cw, t * cw + cw), gate in waves 0-3, up in
+    // waves 4-7, 16 columns per wave.  cw is a multiple of 8, so a wave's
+    // columns may straddle two 16-row panels: each lane addresses its own row
+    // (8 consecutive rows of a k group stay one 128-byte run).
     const bool up = wave >= 4;
     wt = up ? g.w[1] : g.w[0];
-    wblk = t;
     wrows = g.N;
+    const int j = (wave & 3) * 16 + r16, c = t * g.cw + j;
+    wok = j < g.cw && c < g.N;
+    wbase = (uint32_t)(c >> 6) * (uint32_t)kc * 4096u + (uint32_t)((c >> 4) & 3) * 1024u + (uint32_t)gq * 128u +
+            (uint32_t)(c & 15) * 8u;
   } else {
     const int n0 = t * SK_BN;  // whole tiles lie in one segment
     const int sg = n0 >= g.seg_n0[1] ? (n0 >= g.seg_n0[2] ? 2 : 1) : 0;
     wt = g.w[sg];
-    wblk = (n0 - g.seg_n0[sg]) / 64 + (wave >> 2);
+    const int wblk = (n0 - g.seg_n0[sg]) / 64 + (wave >> 2);
     wrows = min(g.N, g.seg_n0[sg + 1]) - g.seg_n0[sg];
+    wbase = (uint32_t)wblk * (uint32_t)kc * 4096u + (uint32_t)(wave & 3) * 1024u + (uint32_t)lane * 8u;
   }
-  const int kc = (g.K + 63) / 64;
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wt, (uint32_t)(packed_elems(wrows, g.K) * 2));
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(g.a, (uint32_t)((size_t)g.M * g.lda * 2));
-  // element of this lane's piece in half 0 of K chunk 0 (half 1 is 512 further)
-  const uint32_t wbase = (uint32_t)wblk * (uint32_t)kc * 4096u + (uint32_t)(wave & 3) * 1024u + (uint32_t)lane * 8u;
   const int c0 = kb / SK_KC;
   // this thread's activation pieces of a group: rows xr0 + 8i, columns xk .. xk + 7
   const int xr0 = tid / (SK_GK / 8), xk = (tid % (SK_GK / 8)) * 8;
@@ -914,8 +924,8 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   auto load_w = [&](WSlot& sl, int j) {
     // chunks past nc (this split's end) read zeros; a chunk's padding past K is stored as zeros
     const uint32_t e = wbase + (uint32_t)(c0 + j) * 4096u;
-    sl.w0 = bload16<CPOL_NT>(wrs, j < nc ? e * 2u : OOB);
-    sl.w1 = bload16<CPOL_NT>(wrs, j < nc ? (e + 512u) * 2u : OOB);
+    sl.w0 = bload16<WPOL>(wrs, j < nc && wok ? e * 2u : OOB);
+    sl.w1 = bload16<WPOL>(wrs, j < nc && wok ? (e + 512u) * 2u : OOB);
   };
   auto load_x = [&](uint4 (&xv)[SK_XP], int gi) {
     const int kx = kb + gi * SK_GK + xk;
@@ -1132,6 +1142,10 @@ int gemm_tile_bm(int tile) { return tile == TILE_64x128 ? 64 : (tile >= TILE_256
 int gemm_tile_bn(int tile) { return tile >= TILE_256x256 ? 256 : 128; }
 
 int gemm_n_tiles(int epi, int N, int tile) {
+  if (epi == EPI_SWIGLU && tile == TILE_SKINNY) {
+    const int cw = skinny_swiglu_cols(N);
+    return (N + cw - 1) / cw;
+  }
   const int bn = gemm_tile_bn(tile);
   return epi == EPI_SWIGLU ? (N + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
 }
@@ -1154,11 +1168,16 @@ static void launch_t(const GemmArgs& g0, hipStream_t st) {
   hipLaunchKernelGGL((gemm_kernel<BM, BN, AMODE, EPI>), grid, dim3(256), 0, st, g);
 }
 
+// Weights stream with non-temporal loads, except the QKV projection's: at its
+// size (50 MB at the 8B shape) plain loads measured slightly faster.
 template <int EPI>
-static void launch_skinny(const GemmArgs& g, hipStream_t st) {
+static void launch_skinny(const GemmArgs& g0, hipStream_t st) {
+  GemmArgs g = g0;
+  if (EPI == EPI_SWIGLU) g.cw = skinny_swiglu_cols(g.N);
   const int n_tiles = gemm_n_tiles(EPI, g.N, TILE_SKINNY);
-  hipLaunchKernelGGL((gemm_skinny_kernel<EPI>), dim3(n_tiles, g.splits > 1 ? g.splits : 1), dim3(SK_NT), 0,
-                     st, g);
+  const dim3 grid(n_tiles, g.splits > 1 ? g.splits : 1);
+  if (EPI == EPI_QKV) hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 0>), grid, dim3(SK_NT), 0, st, g);
+  else hipLaunchKernelGGL((gemm_skinny_kernel<EPI, CPOL_NT>), grid, dim3(SK_NT), 0, st, g);
   const bool norm = EPI == EPI_RESID && g.x_out;
   if (g.splits > 1 && norm) {
     const size_t lds = ((size_t)g.N + g.N / 64) * 4;
