@@ -244,7 +244,9 @@ int pie_forward(pie_ctx* ctx, const pie_pass* passes, int32_t n_passes, int32_t*
  * enqueued on the context's stream; steps run in the order enqueued.  The
  * host bookkeeping (working-set lengths, page reservation) advances at
  * enqueue, with the same validation and all-or-nothing rule as pie_forward
- * (token values are not checked: they are on the device).  At most 4 calls
+ * (token values are not checked: they are on the device; an id outside
+ * [0, vocab), such as the -1 an all-NaN logits row yields, embeds as a zero
+ * row rather than reading outside the table).  At most 4 calls
  * are staged ahead of the GPU; a further call waits for the oldest staging
  * copy to run.  The device arrays must stay valid until the step has run
  * (pie_sync).  Kernel timing (pie_profile_enable) must be off: PIE_EINVAL.

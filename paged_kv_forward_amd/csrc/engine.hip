@@ -436,7 +436,7 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
   if ((rc = check_launch(c, flags, "rope table"))) return rc;
   {
     Timed tm(c, PIE_K_EMBED);
-    pie::launch_embed(c->embed, c->dev_tok_in ? c->dev_tok_in : M32(L.tok), T, d.d_model, y, ss, st);
+    pie::launch_embed(c->embed, c->dev_tok_in ? c->dev_tok_in : M32(L.tok), T, d.d_model, d.vocab, y, ss, st);
   }
   if ((rc = check_launch(c, flags, "embed"))) return rc;
 

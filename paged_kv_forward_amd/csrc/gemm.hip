@@ -958,8 +958,13 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
     store_x(xv, 0);
     lds_barrier();
     const int ngroups = (nc + SK_DEPTH - 1) / SK_DEPTH;
+    // The scheduling barriers pin the issue order: the next group's activation
+    // loads first, then each chunk's refill right after the MFMAs that free its
+    // ring slot.  Left alone, the compiler sinks all refills to the end of the
+    // group, so the ring drains to empty once per group.
     for (int gi = 0; gi < ngroups; ++gi) {
       load_x(xv, gi + 1);  // the next group, in flight during this one
+      __builtin_amdgcn_sched_barrier(0);
       const uint16_t* X = sX + (gi & 1) * 64 * SK_LDX;
 #pragma unroll
       for (int j = 0; j < SK_DEPTH; ++j) {
@@ -974,6 +979,7 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
           for (int a = 0; a < 4; ++a) acc[a] = mfma16(af[ks][a], ks ? ring[j].w1 : ring[j].w0, acc[a]);
         load_w(ring[j], (gi + 1) * SK_DEPTH + j);
+        __builtin_amdgcn_sched_barrier(0);
       }
       store_x(xv, (gi + 1) & 1);  // that buffer was last read in group gi - 1
       lds_barrier();

@@ -6,7 +6,7 @@
 
 namespace pie {
 
-void launch_embed(const uint16_t* E, const int32_t* tok, int n_rows, int d, float* y, float* ss,
+void launch_embed(const uint16_t* E, const int32_t* tok, int n_rows, int d, int vocab, float* y, float* ss,
                   hipStream_t st);
 void launch_rope_table(const int32_t* pos, int n_rows, int hd, double theta, float* cs,
                        hipStream_t st);

@@ -7,17 +7,22 @@
 namespace pie {
 
 // y[t, :] = float(E[tok[t], :]); ss[t, c] = sum of y[t, 64c : 64c + 64]^2.
-// One workgroup (4 waves) per row; each wave takes 64-column chunks.
+// One workgroup (4 waves) per row; each wave takes 64-column chunks.  Token
+// ids that only exist on the device (loop-carried decode) are not validated
+// by the host: an id outside [0, vocab) embeds as a zero row instead of
+// reading outside the table.
 __global__ __launch_bounds__(256) void embed_kernel(const uint16_t* __restrict__ E,
-                                                    const int32_t* __restrict__ tok, int d,
+                                                    const int32_t* __restrict__ tok, int d, int vocab,
                                                     float* __restrict__ y, float* __restrict__ ss,
                                                     int n_ss) {
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint16_t* src = E + (size_t)tok[t] * d;
+  const int id = tok[t];
+  const bool ok = id >= 0 && id < vocab;
+  const uint16_t* src = E + (size_t)(ok ? id : 0) * d;
   float* dst = y + (size_t)t * d;
   for (int c = wave; c < n_ss; c += 4) {
     const int k = c * 64 + lane;
-    const float a = bf2f(src[k]);
+    const float a = ok ? bf2f(src[k]) : 0.f;
     dst[k] = a;
     const float s = wave_sum(a * a);
     if (lane == 0) ss[(size_t)t * n_ss + c] = s;
@@ -48,10 +53,10 @@ __global__ void philox_kernel(uint32_t seed_lo, uint32_t seed_hi, uint32_t lane,
   if (i < n) out[i] = philox_w0(v0 + (uint32_t)i, lane, seed_lo, seed_hi);
 }
 
-void launch_embed(const uint16_t* E, const int32_t* tok, int n_rows, int d, float* y, float* ss,
+void launch_embed(const uint16_t* E, const int32_t* tok, int n_rows, int d, int vocab, float* y, float* ss,
                   hipStream_t st) {
   if (n_rows <= 0) return;
-  hipLaunchKernelGGL(embed_kernel, dim3(n_rows), dim3(256), 0, st, E, tok, d, y, ss, d / 64);
+  hipLaunchKernelGGL(embed_kernel, dim3(n_rows), dim3(256), 0, st, E, tok, d, vocab, y, ss, d / 64);
 }
 
 void launch_rope_table(const int32_t* pos, int n_rows, int hd, double theta, float* cs,

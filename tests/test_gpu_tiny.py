@@ -415,6 +415,32 @@ def test_tiny_async_steps_enqueued_back_to_back(torch_cuda):
     rt.close()
 
 
+def test_tiny_async_out_of_range_device_token(torch_cuda):
+    """Loop-carried token ids are never checked on the host.  An id outside
+    [0, vocab) (the -1 of an all-NaN logits row, or any stray value) embeds as
+    a zero row: two working sets with the same prompt fed -1 and vocab + 7 give
+    bit-identical logits and a valid token, and a third fed a real id differs."""
+    torch = torch_cuda
+    recipe = RECIPES["gains1"]
+    shape = recipe.shape
+    from paged_kv_forward_amd.runtime import Pass
+    prompt = synth.prompt_tokens(1, 40, PROMPT, shape.vocab)
+    rt = make_runtime(shape, recipe, torch_cuda)
+    ws = np.array([rt.alloc() for _ in range(3)], dtype=np.uint64)
+    toks, _ = rt.forward([Pass(int(w), prompt, [PROMPT - 1], [(0, 1.0, 0)]) for w in ws])
+    tok_in = torch.tensor([-1, shape.vocab + 7, int(toks[0])], dtype=torch.int32, device="cuda")
+    tok_out = torch.empty(3, dtype=torch.int32, device="cuda")
+    lg = torch.empty((3, shape.vocab), dtype=torch.float32, device="cuda")
+    rt.decode_async(ws, tok_in, tok_out, logits_out=lg)
+    rt.sync()
+    out, lgs = tok_out.cpu().numpy(), lg.cpu().numpy()
+    assert np.all(np.isfinite(lgs))
+    np.testing.assert_array_equal(lgs[0], lgs[1])
+    assert out[0] == out[1] and 0 <= out[0] < shape.vocab
+    assert not np.array_equal(lgs[0], lgs[2])
+    rt.close()
+
+
 def test_tiny_prefix_lookup_reuses_pages_exactly(torch_cuda):
     """A request that starts with another request's committed prefix gets the
     prefix's pages through pie_prefix_lookup and runs only its own tokens: its
