@@ -64,117 +64,118 @@ struct QkvStaged {
 template <int HD, int BN, int NTH, int B>
 __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const float* sC, int ldc, int m0, int rows,
                                              int n_tile, QkvStaged sg) {
-  constexpr int NW = NTH / 64, HD2 = HD / 2, P = KV_PAGE;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // q and k: a unit is one row's group of 8 consecutive rotation pairs
+  // (d0 .. d0 + 7 with their partners d0 + HD/2 ..), so each half goes out
+  // as one 16-byte store (8 bf16; 8 bytes for e4m3 K).  v: a unit is one
+  // column over 8 consecutive rows; when their slots are 8 consecutive
+  // slots of one page (the usual prefill case) they go out as one store,
+  // else one element at a time.
+  constexpr int HD2 = HD / 2, P = KV_PAGE, GPR = BN / 16, GPH = HD2 / 8;
+  const int tid = threadIdx.x;
   const int n0 = n_tile * BN;
   const int qw = g.nq * HD, kw = g.nkv * HD;
   const int kind = n0 < qw ? 0 : (n0 < qw + kw ? 1 : 2);
-  if (kind == 0) {
-    // q: a wave step is one row's 64 consecutive rotation pairs (a tile row
-    // holds BN / 2 pairs, HD / 2 per head); stores run along the row
-    constexpr int UPR = BN / 2 / 64;
-    const int steps = rows * UPR;
-    const int head0 = n0 / HD;
-    for (int s0 = wave; s0 < steps; s0 += NW * B) {
-      float2 cs[B];
+  auto slot_of = [&](int row, int m) { return sg.slot ? sg.slot[row] : g.slot[m]; };
+  if (kind <= 1) {
+    const int head0 = kind == 0 ? n0 / HD : (n0 - qw) / HD;
+    // k units run along 16 consecutive rows first, so that the stores of
+    // consecutive tokens of a page ([kv head][HD / 8][token][8]) are adjacent
+    const int units = kind == 0 ? rows * GPR : (rows + 15) / 16 * 16 * GPR;
+    for (int u = tid; u < units; u += NTH) {
+      const int row = kind == 0 ? u / GPR : (u / (16 * GPR)) * 16 + u % 16;
+      const int grp = kind == 0 ? u % GPR : (u / 16) % GPR;
+      const int m = m0 + row;
+      if (row >= rows || m >= g.M) continue;
+      const int hl = grp / GPH, d0 = (grp % GPH) * 8;
+      const float* xr = sC + row * ldc + hl * HD + d0;
+      const float4* cs4 = reinterpret_cast<const float4*>(
+          sg.rope ? sg.rope + row * HD2 + d0 : reinterpret_cast<const float2*>(g.rope_cs) + (size_t)m * HD2 + d0);
+      float4 c4[4];
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        const int st = s0 + u * NW, row = st / UPR, pr = (st % UPR) * 64 + lane, m = m0 + row;
-        const bool ok = st < steps && m < g.M;
-        cs[u] = !ok ? make_float2(1.f, 0.f)
-                    : sg.rope ? sg.rope[row * HD2 + pr % HD2]
-                              : *reinterpret_cast<const float2*>(g.rope_cs + ((size_t)m * HD2 + pr % HD2) * 2);
+      for (int i = 0; i < 4; ++i) c4[i] = cs4[i];  // (cos, sin) of pairs 2i, 2i + 1
+      const float4 a0 = *reinterpret_cast<const float4*>(xr), a1 = *reinterpret_cast<const float4*>(xr + 4);
+      const float4 b0 = *reinterpret_cast<const float4*>(xr + HD2), b1 = *reinterpret_cast<const float4*>(xr + HD2 + 4);
+      const float x1[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float x2[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float o1[8], o2[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float c = (i & 1) ? c4[i >> 1].z : c4[i >> 1].x, sn = (i & 1) ? c4[i >> 1].w : c4[i >> 1].y;
+        o1[i] = x1[i] * c - x2[i] * sn;
+        o2[i] = x2[i] * c + x1[i] * sn;
       }
-#pragma unroll
-      for (int u = 0; u < B; ++u) {
-        const int st = s0 + u * NW, row = st / UPR, pr = (st % UPR) * 64 + lane, m = m0 + row;
-        if (st >= steps || m >= g.M) continue;
-        const int hl = pr / HD2, dd = pr % HD2;
-        const int c1 = hl * HD + dd, c2 = c1 + HD2;
-        const float x1 = sC[row * ldc + c1], x2 = sC[row * ldc + c2];
-        uint16_t* q = g.q_out + (size_t)m * qw + (head0 + hl) * HD;
-        q[dd] = f2bf(x1 * cs[u].x - x2 * cs[u].y);
-        q[dd + HD2] = f2bf(x2 * cs[u].x + x1 * cs[u].y);
+      if (kind == 0) {
+        uint16_t* q = g.q_out + (size_t)m * qw + (head0 + hl) * HD + d0;
+        *reinterpret_cast<uint4*>(q) = make_uint4(pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3]),
+                                                  pack_bf2(o1[4], o1[5]), pack_bf2(o1[6], o1[7]));
+        *reinterpret_cast<uint4*>(q + HD2) = make_uint4(pack_bf2(o2[0], o2[1]), pack_bf2(o2[2], o2[3]),
+                                                        pack_bf2(o2[4], o2[5]), pack_bf2(o2[6], o2[7]));
+        continue;
       }
-    }
-  } else if (kind == 1) {
-    // k: a wave step is 8 rows x 8 consecutive rotation pairs, so that the
-    // stores of consecutive tokens of a page, whose 8-element groups are
-    // adjacent in the K page layout [kv head][HD / 8][token][8], merge
-    constexpr int PG = BN / 2 / 8;  // groups of 8 pairs in a tile row
-    const int rb_n = (rows + 7) / 8, steps = rb_n * PG;
-    const int head0 = (n0 - qw) / HD;
-    const int tok = lane >> 3, d8 = lane & 7;
-    for (int s0 = wave; s0 < steps; s0 += NW * B) {
-      float2 cs[B];
-      int sl[B];
-      float sc[B];
+      const int sl = slot_of(row, m), page = sl / P, off = sl % P;
+      const size_t base = (size_t)page * g.page_stride + (size_t)(head0 + hl) * P * HD + (size_t)off * 8;
+      const size_t i1 = base + (size_t)(d0 >> 3) * P * 8, i2 = base + (size_t)((d0 + HD2) >> 3) * P * 8;
+      if (g.kv_e4m3) {
+        const float sc = sg.scale ? sg.scale[head0 + hl] : g.kv_scale[head0 + hl];
+        uint32_t w1[2] = {0u, 0u}, w2[2] = {0u, 0u};
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        const int st = s0 + u * NW, row = (st % rb_n) * 8 + tok, pr = (st / rb_n) * 8 + d8, m = m0 + row;
-        const bool ok = st < steps && row < rows && m < g.M;
-        cs[u] = !ok ? make_float2(1.f, 0.f)
-                    : sg.rope ? sg.rope[row * HD2 + pr % HD2]
-                              : *reinterpret_cast<const float2*>(g.rope_cs + ((size_t)m * HD2 + pr % HD2) * 2);
-        sl[u] = !ok ? 0 : sg.slot ? sg.slot[row] : g.slot[m];
-        sc[u] = !(ok && g.kv_e4m3) ? 1.f : sg.scale ? sg.scale[head0 + pr / HD2] : g.kv_scale[head0 + pr / HD2];
-      }
-#pragma unroll
-      for (int u = 0; u < B; ++u) {
-        const int st = s0 + u * NW, row = (st % rb_n) * 8 + tok, pr = (st / rb_n) * 8 + d8, m = m0 + row;
-        if (st >= steps || row >= rows || m >= g.M) continue;
-        const int hl = pr / HD2, dd = pr % HD2;
-        const int c1 = hl * HD + dd, c2 = c1 + HD2;
-        const float x1 = sC[row * ldc + c1], x2 = sC[row * ldc + c2];
-        const float o1 = x1 * cs[u].x - x2 * cs[u].y, o2 = x2 * cs[u].x + x1 * cs[u].y;
-        const int page = sl[u] / P, off = sl[u] % P;
-        const size_t base = (size_t)page * g.page_stride + (size_t)(head0 + hl) * P * HD + (size_t)off * 8;
-        const size_t i1 = base + (size_t)(dd >> 3) * P * 8 + (dd & 7);
-        const size_t i2 = base + (size_t)((dd + HD2) >> 3) * P * 8 + ((dd + HD2) & 7);
-        if (g.kv_e4m3) {
-          uint8_t* kv = reinterpret_cast<uint8_t*>(g.kv_layer);
-          kv[i1] = f2e4m3(o1 / sc[u]);
-          kv[i2] = f2e4m3(o2 / sc[u]);
-        } else {
-          uint16_t* kv = reinterpret_cast<uint16_t*>(g.kv_layer);
-          kv[i1] = f2bf(o1);
-          kv[i2] = f2bf(o2);
+        for (int i = 0; i < 8; ++i) {
+          w1[i >> 2] |= (uint32_t)f2e4m3(o1[i] / sc) << (8 * (i & 3));
+          w2[i >> 2] |= (uint32_t)f2e4m3(o2[i] / sc) << (8 * (i & 3));
         }
+        uint8_t* kv = reinterpret_cast<uint8_t*>(g.kv_layer);
+        *reinterpret_cast<uint2*>(kv + i1) = make_uint2(w1[0], w1[1]);
+        *reinterpret_cast<uint2*>(kv + i2) = make_uint2(w2[0], w2[1]);
+      } else {
+        uint16_t* kv = reinterpret_cast<uint16_t*>(g.kv_layer);
+        *reinterpret_cast<uint4*>(kv + i1) = make_uint4(pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3]),
+                                                        pack_bf2(o1[4], o1[5]), pack_bf2(o1[6], o1[7]));
+        *reinterpret_cast<uint4*>(kv + i2) = make_uint4(pack_bf2(o2[0], o2[1]), pack_bf2(o2[2], o2[3]),
+                                                        pack_bf2(o2[4], o2[5]), pack_bf2(o2[6], o2[7]));
       }
     }
   } else {
-    // v: a wave step is 16 rows x 4 columns, so that the stores of the
-    // consecutive tokens of a page, adjacent in the V page layout
-    // [kv head][HD][token], merge
-    constexpr int CG = BN / 4;  // groups of 4 columns in a tile row
-    const int rb_n = (rows + 15) / 16, steps = rb_n * CG;
+    // v: layout [kv head][HD][token]; consecutive threads take consecutive
+    // columns (conflict-free reads of sC)
     const int v0 = n0 - qw - kw;
-    const int tok = lane & 15, c4 = lane >> 4;
-    for (int s0 = wave; s0 < steps; s0 += NW * B) {
-      int sl[B];
-      float sc[B];
+    const int units = (rows + 7) / 8 * BN;
+    for (int u = tid; u < units; u += NTH) {
+      const int c = u % BN, r0 = (u / BN) * 8;
+      const int vc = v0 + c, kvh = vc / HD, dd = vc % HD;
+      const size_t col = (size_t)g.nkv * P * HD + (size_t)kvh * HD * P + (size_t)dd * P;
+      const float sc = !g.kv_e4m3 ? 1.f : sg.scale ? sg.scale[g.nkv + kvh] : g.kv_scale[g.nkv + kvh];
+      int sl[8];
+      float x[8];
+      bool whole = true;
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        const int st = s0 + u * NW, row = (st % rb_n) * 16 + tok, c = (st / rb_n) * 4 + c4, m = m0 + row;
-        const bool ok = st < steps && row < rows && m < g.M;
-        sl[u] = !ok ? 0 : sg.slot ? sg.slot[row] : g.slot[m];
-        const int si = g.nkv + (v0 + c) / HD;
-        sc[u] = !(ok && g.kv_e4m3) ? 1.f : sg.scale ? sg.scale[si] : g.kv_scale[si];
+      for (int i = 0; i < 8; ++i) {
+        const int row = r0 + i, m = m0 + row;
+        const bool ok = row < rows && m < g.M;
+        sl[i] = ok ? slot_of(row, m) : -1;
+        x[i] = ok ? sC[row * ldc + c] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        const int st = s0 + u * NW, row = (st % rb_n) * 16 + tok, c = (st / rb_n) * 4 + c4, m = m0 + row;
-        if (st >= steps || row >= rows || m >= g.M) continue;
-        const int vc = v0 + c, kvh = vc / HD, dd = vc % HD;
-        const int page = sl[u] / P, off = sl[u] % P;
-        const size_t idx_v = (size_t)page * g.page_stride + (size_t)g.nkv * P * HD + (size_t)kvh * HD * P +
-                             (size_t)dd * P + off;
-        const float x = sC[row * ldc + c];
+      for (int i = 0; i < 8; ++i) whole = whole && sl[i] == sl[0] + i;
+      whole = whole && sl[0] >= 0 && (sl[0] & 7) == 0;  // 8 slots inside one page
+      if (whole) {
+        const size_t idx = (size_t)(sl[0] / P) * g.page_stride + col + (sl[0] % P);
         if (g.kv_e4m3) {
-          reinterpret_cast<uint8_t*>(g.kv_layer)[idx_v] = f2e4m3(x / sc[u]);
+          uint32_t w[2] = {0u, 0u};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)f2e4m3(x[i] / sc) << (8 * (i & 3));
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(g.kv_layer) + idx) = make_uint2(w[0], w[1]);
         } else {
-          reinterpret_cast<uint16_t*>(g.kv_layer)[idx_v] = f2bf(x);
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.kv_layer) + idx) =
+              make_uint4(pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7]));
         }
+        continue;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (sl[i] < 0) continue;
+        const size_t idx = (size_t)(sl[i] / P) * g.page_stride + col + (sl[i] % P);
+        if (g.kv_e4m3) reinterpret_cast<uint8_t*>(g.kv_layer)[idx] = f2e4m3(x[i] / sc);
+        else reinterpret_cast<uint16_t*>(g.kv_layer)[idx] = f2bf(x[i]);
       }
     }
   }
