@@ -839,7 +839,9 @@ __global__ __launch_bounds__(DG_NT, 1) void gemm_dma_kernel(GemmArgs g) {
       sg = QkvStaged{reinterpret_cast<const float2*>(s_rope), s_slot, stage_scale ? s_scale : nullptr};
     }
     __syncthreads();
-    epilogue<EPI, BG_BN, DG_NT, EPI == EPI_QKV ? 2 : 8>(g, sC, BG_LDC, m0 + pass * 64, 64, n_tile, sg);
+    // EPI_RESID: all 16 of a thread's residual loads of the pass in one batch
+    epilogue<EPI, BG_BN, DG_NT, EPI == EPI_QKV ? 2 : (EPI == EPI_RESID ? 16 : 8)>(g, sC, BG_LDC, m0 + pass * 64, 64,
+                                                                                n_tile, sg);
     __syncthreads();
   }
 }
