@@ -534,8 +534,11 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(AttnArgs a) {
   static_assert(LPW <= PB_L * 2 && (PB_L % LPW == 0 || LPW % PB_L == 0), "a wave's loads of a stage stay in one page");
   __shared__ __attribute__((aligned(1024))) uint8_t skv[NS][STAGE_B];
   const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4;
-  const int4 it = a.items[blockIdx.x];
-  const int kvh = blockIdx.y;
+  // grid (KV head, item): workgroups are dispatched in flat order, so every
+  // head of the longest item (items are sorted longest first) starts before
+  // any shorter item, and the last round holds only the shortest
+  const int4 it = a.items[blockIdx.y];
+  const int kvh = blockIdx.x;
   const int s = it.x, tb = it.y, nt = it.z;
   const int G = a.nq / a.nkv;
   const int row0 = a.seq_row0[s] + tb;
@@ -677,7 +680,7 @@ void launch_attn_combine(const AttnArgs& a, hipStream_t st) {
 
 void launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
   if (a.n_items == 0) return;
-  dim3 grid(a.n_items, a.nkv);
+  dim3 grid(a.nkv, a.n_items);
   if (a.hd == 128) {
     if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<128, true>), grid, dim3(PF_NT), 0, st, a);
     else hipLaunchKernelGGL((attn_prefill_kernel<128, false>), grid, dim3(PF_NT), 0, st, a);
