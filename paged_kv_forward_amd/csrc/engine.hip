@@ -346,6 +346,16 @@ void build_work(pie_ctx* c) {
         c->pre.insert(c->pre.end(), {s, tb, std::min(tpw, n_new - tb), 0});
     }
   }
+  // decode items longest first (more entries, more bytes); stable, so equal
+  // lengths keep sequence order
+  std::vector<std::array<int, 4>> dec(c->dec.size() / 4);
+  for (size_t i = 0; i < dec.size(); ++i)
+    dec[i] = {c->dec[4 * i], c->dec[4 * i + 1], c->dec[4 * i + 2], c->dec[4 * i + 3]};
+  std::stable_sort(dec.begin(), dec.end(), [](const std::array<int, 4>& x, const std::array<int, 4>& y) {
+    return x[2] - x[1] > y[2] - y[1];
+  });
+  for (size_t i = 0; i < dec.size(); ++i)
+    for (int k = 0; k < 4; ++k) c->dec[4 * i + k] = dec[i][k];
   // longest first: an item's work grows with its last token's position
   std::vector<std::array<int, 4>> pre(c->pre.size() / 4);
   for (size_t i = 0; i < pre.size(); ++i)
