@@ -1038,24 +1038,31 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, int n_ti
 }
 
 // Split-K reduce of an EPI_RESID skinny GEMM fused with the RMSNorm that
-// follows it: one workgroup per row holds the whole new row of y.  It adds
-// the partials in split order, writes y and the per-64-column sums of
-// squares exactly as the EPI_RESID epilogue does, sums those partials in
-// column order as rmsnorm_kernel does, and writes the normed bf16 row.
-constexpr int RN_NT = 1024;
+// follows it: one workgroup per row holds the whole new row of y, four
+// columns per thread, in registers.  It adds the partials in split order,
+// writes y and the per-64-column sums of squares exactly as the EPI_RESID
+// epilogue does (four squares per lane, then the 16 lanes of a 64-column
+// chunk), sums those partials in column order as rmsnorm_kernel does, and
+// writes the normed bf16 row.  N <= RN_NT * 4 * RN_MAXC.
+constexpr int RN_NT = 1024, RN_MAXC = 2;
 __global__ __launch_bounds__(RN_NT) void skinny_reduce_norm_kernel(GemmArgs g, int n_tiles) {
-  extern __shared__ __attribute__((aligned(16))) float s_row[];  // [N] new y, then [N / 64] sums
+  __shared__ float s_ssq[RN_NT * 4 * RN_MAXC / 64];
   __shared__ float s_r;
-  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int N = g.N, n_grp = N / 64;
-  float* s_ssq = s_row + N;
   const size_t ld = (size_t)n_tiles * SK_BN, zs = 64 * ld;
-  for (int c = tid * 4; c < N; c += RN_NT * 4) {
-    const float* p = g.partial + (size_t)m * ld + c;
+  float4 yn[RN_MAXC];
+#pragma unroll
+  for (int c = 0; c < RN_MAXC; ++c) {
+    const int col = (tid + c * RN_NT) * 4;
+    const bool ok = col < N;
+    const float* p = g.partial + (size_t)m * ld + col;
     float4 x[SK_MAX_SPLITS];
 #pragma unroll
     for (int z = 0; z < SK_MAX_SPLITS; ++z)
-      x[z] = z < g.splits ? *reinterpret_cast<const float4*>(p + z * zs) : make_float4(0.f, 0.f, 0.f, 0.f);
+      x[z] = ok && z < g.splits ? *reinterpret_cast<const float4*>(p + z * zs) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4* yp = reinterpret_cast<float4*>(g.y_out + (size_t)m * g.ldy + (ok ? col : 0));
+    const float4 yo = ok ? *yp : make_float4(0.f, 0.f, 0.f, 0.f);
     float4 v = x[0];
 #pragma unroll
     for (int z = 1; z < SK_MAX_SPLITS; ++z) {
@@ -1064,19 +1071,14 @@ __global__ __launch_bounds__(RN_NT) void skinny_reduce_norm_kernel(GemmArgs g, i
       v.z += x[z].z;
       v.w += x[z].w;
     }
-    float4* yp = reinterpret_cast<float4*>(g.y_out + (size_t)m * g.ldy + c);
-    const float4 yo = *yp;
-    const float4 yn = make_float4(yo.x + v.x, yo.y + v.y, yo.z + v.z, yo.w + v.w);
-    *yp = yn;
-    *reinterpret_cast<float4*>(&s_row[c]) = yn;
-  }
-  __syncthreads();
-  for (int grp = wave; grp < n_grp; grp += RN_NT / 64) {
-    const float v = s_row[grp * 64 + lane];
-    const float sq = wave_sum(v * v);
-    if (lane == 0) {
-      g.ss_out[(size_t)m * g.n_ss + grp] = sq;
-      s_ssq[grp] = sq;
+    yn[c] = make_float4(yo.x + v.x, yo.y + v.y, yo.z + v.z, yo.w + v.w);
+    if (ok) *yp = yn[c];
+    float sq = yn[c].x * yn[c].x + yn[c].y * yn[c].y + yn[c].z * yn[c].z + yn[c].w * yn[c].w;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+    if (ok && (lane & 15) == 0) {
+      g.ss_out[(size_t)m * g.n_ss + col / 64] = sq;
+      s_ssq[col / 64] = sq;
     }
   }
   __syncthreads();
@@ -1087,16 +1089,15 @@ __global__ __launch_bounds__(RN_NT) void skinny_reduce_norm_kernel(GemmArgs g, i
   }
   __syncthreads();
   const float r = s_r;
-  for (int k = tid * 8; k < N; k += RN_NT * 8) {
-    const float4 a = *reinterpret_cast<const float4*>(&s_row[k]);
-    const float4 b = *reinterpret_cast<const float4*>(&s_row[k + 4]);
-    const uint4 gw = *reinterpret_cast<const uint4*>(g.next_gain + k);
-    uint4 o;
-    o.x = pack_bf2(a.x * r * bf2f(gw.x & 0xffffu), a.y * r * bf2f(gw.x >> 16));
-    o.y = pack_bf2(a.z * r * bf2f(gw.y & 0xffffu), a.w * r * bf2f(gw.y >> 16));
-    o.z = pack_bf2(b.x * r * bf2f(gw.z & 0xffffu), b.y * r * bf2f(gw.z >> 16));
-    o.w = pack_bf2(b.z * r * bf2f(gw.w & 0xffffu), b.w * r * bf2f(gw.w >> 16));
-    *reinterpret_cast<uint4*>(g.x_out + (size_t)m * g.N + k) = o;
+#pragma unroll
+  for (int c = 0; c < RN_MAXC; ++c) {
+    const int col = (tid + c * RN_NT) * 4;
+    if (col >= N) continue;
+    const uint2 gw = *reinterpret_cast<const uint2*>(g.next_gain + col);
+    const float4 a = yn[c];
+    *reinterpret_cast<uint2*>(g.x_out + (size_t)m * g.N + col) =
+        make_uint2(pack_bf2(a.x * r * bf2f(gw.x & 0xffffu), a.y * r * bf2f(gw.x >> 16)),
+                   pack_bf2(a.z * r * bf2f(gw.y & 0xffffu), a.w * r * bf2f(gw.y >> 16)));
   }
 }
 
@@ -1188,14 +1189,14 @@ static void launch_skinny(const GemmArgs& g0, hipStream_t st) {
   if (EPI == EPI_QKV) hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 0>), grid, dim3(SK_NT), 0, st, g);
   else hipLaunchKernelGGL((gemm_skinny_kernel<EPI, CPOL_NT>), grid, dim3(SK_NT), 0, st, g);
   const bool norm = EPI == EPI_RESID && g.x_out;
-  if (g.splits > 1 && norm) {
-    const size_t lds = ((size_t)g.N + g.N / 64) * 4;
-    hipLaunchKernelGGL(skinny_reduce_norm_kernel, dim3(g.M), dim3(RN_NT), lds, st, g, n_tiles);
+  const bool fused_norm = g.splits > 1 && norm && g.N <= RN_NT * 4 * RN_MAXC;
+  if (fused_norm) {
+    hipLaunchKernelGGL(skinny_reduce_norm_kernel, dim3(g.M), dim3(RN_NT), 0, st, g, n_tiles);
   } else if (g.splits > 1) {
     hipLaunchKernelGGL((skinny_reduce_kernel<EPI>), dim3(n_tiles, (g.M + SK_RED_ROWS - 1) / SK_RED_ROWS),
                        dim3(256), 0, st, g, n_tiles);
   }
-  if (g.splits <= 1 && norm)
+  if (norm && !fused_norm)
     launch_rmsnorm(g.y_out, g.ss_out, g.n_ss, g.next_gain, g.M, g.N, g.eps, nullptr, g.x_out, st);
 }
 
