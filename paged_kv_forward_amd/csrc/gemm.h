@@ -86,8 +86,8 @@ struct GemmArgs {
   const uint32_t* ro_seed_lo;
   const uint32_t* ro_seed_hi;
   const int32_t* ro_lane;
-  float* tile_best;      // [n_tiles][M] decision value
-  int32_t* tile_idx;     // [n_tiles][M] its index
+  float* tile_best;      // [M][n_tiles] decision value (a row's tiles contiguous for the final reduce)
+  int32_t* tile_idx;     // [M][n_tiles] its index
 };
 
 // Tile configurations.  TILE_SKINNY: M <= 64 with a bf16 A operand, 128 output

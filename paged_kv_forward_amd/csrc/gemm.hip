@@ -271,8 +271,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const float* sC, int
           if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
         }
         if (lane == 0) {
-          g.tile_best[(size_t)n_tile * g.M + m] = best;
-          g.tile_idx[(size_t)n_tile * g.M + m] = bi;
+          const int n_tiles = (g.N + BN - 1) / BN;
+          g.tile_best[(size_t)m * n_tiles + n_tile] = best;
+          g.tile_idx[(size_t)m * n_tiles + n_tile] = bi;
         }
       }
     }
@@ -1135,8 +1136,8 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* tile_bes
   float best = -INFINITY;
   int bi = INT_MAX;
   for (int t = lane; t < n_tiles; t += 64) {
-    float s = tile_best[(size_t)t * M + m];
-    int i = tile_idx[(size_t)t * M + m];
+    float s = tile_best[(size_t)m * n_tiles + t];
+    int i = tile_idx[(size_t)m * n_tiles + t];
     if (s > best || (s == best && i < bi)) { best = s; bi = i; }
   }
 #pragma unroll
