@@ -273,6 +273,9 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="(always on; kept for old command lines)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write profiles/ summaries from the rocprofv3 outputs under DIR and exit")
+    ap.add_argument("--fp8-weights", action="store_true",
+                    help="the FP8 variant: layer projections are block-scaled FP8 (e4m3 codes, one "
+                         "power-of-two scale per 128 x 128 block) and decode streams the FP8 copies")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the known-size "
                          "kernel that scales HBM byte counters) and exit")
@@ -301,11 +304,14 @@ def main():
 
     torch.cuda.set_device(0)
     shape = synth.LLAMA_8B
-    recipe = synth.WeightRecipe(shape)
+    fp8 = args.fp8_weights
+    recipe = synth.WeightRecipe(shape, fp8_blocks=fp8)
     wl = synth.workload(2)
     t0 = time.perf_counter()
-    log("bench: drawing and uploading %.2f B seeded weights" % (shape.n_params() / 1e9))
-    weights = upload_weights(recipe, "cuda:0", progress=lambda l: (l % 8 == 7) and log("  layer", l + 1))
+    log("bench: drawing and uploading %.2f B seeded weights%s" % (shape.n_params() / 1e9,
+                                                                  " (FP8 projections)" if fp8 else ""))
+    weights = upload_weights(recipe, "cuda:0", progress=lambda l: (l % 8 == 7) and log("  layer", l + 1),
+                             fp8=fp8)
     log("bench: weights ready in %.1f s" % (time.perf_counter() - t0))
     K, W = args.steps, args.warmup
     max_ctx = PROMPT + W + 3 * K + 3 + 8
@@ -407,6 +413,9 @@ def main():
     attn_gbs = attn_bytes / (attn_ms / 1e3) / 1e9 if attn_ms > 0 else 0.0
     per_launch = attn_bytes / max(attn_n, 1)
     weight_bytes = 2 * (shape.n_params() - shape.vocab * shape.d_model)  # all but the embedding table
+    proj_params = shape.n_layers * shape.d_model * (2 * shape.q_width + 2 * shape.kv_width + 3 * shape.d_ffn)
+    if fp8:  # projections at one byte per weight plus one fp32 scale per 128 x 128 block
+        weight_bytes -= proj_params - 4 * proj_params // (128 * 128)
     step_bytes = weight_bytes + (ctx_sum / K) * kv_tok * shape.n_layers
     ms_step = t_dec / K * 1e3
 
@@ -420,9 +429,10 @@ def main():
     rt.profile_enable([])
     breakdown = {k: round(v[0] / 3, 4) for k, v in pb.items() if v[1]}
     d, L_ = shape.d_model, shape.n_layers
-    wbytes = {"gemm_qkv": 2 * L_ * d * (shape.q_width + 2 * shape.kv_width),
-              "gemm_o": 2 * L_ * shape.q_width * d, "gemm_gateup": 2 * L_ * d * 2 * shape.d_ffn,
-              "gemm_down": 2 * L_ * shape.d_ffn * d, "lm_head": 2 * shape.vocab * d,
+    wb = 1 if fp8 else 2  # bytes per projection weight streamed by decode
+    wbytes = {"gemm_qkv": wb * L_ * d * (shape.q_width + 2 * shape.kv_width),
+              "gemm_o": wb * L_ * shape.q_width * d, "gemm_gateup": wb * L_ * d * 2 * shape.d_ffn,
+              "gemm_down": wb * L_ * shape.d_ffn * d, "lm_head": 2 * shape.vocab * d,
               "attn_decode": L_ * (sum(N_SEQ * (ctx_bd + i) for i in range(3)) / 3 * kv_tok + qo)}
     decode_kernels = {}
     for k, b in wbytes.items():
@@ -443,10 +453,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) bf16 weights, uniform random tokens)",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, uniform random tokens)" + (
+            "; layer projections rounded to block-scaled FP8 (e4m3, power-of-two scale per 128x128 block)"
+            if fp8 else ""),
         "config": {"workload": "llama31-8b decode: batch 64, context %d..%d, bf16 paged KV (page 16), "
-                               "argmax epilogue, loop-carried steps (pie_decode_async)"
-                               % (ctx_first, ctx_first + K - 1),
+                               "argmax epilogue, loop-carried steps (pie_decode_async)%s"
+                               % (ctx_first, ctx_first + K - 1,
+                                  ", FP8 block-scaled projection weights streamed by decode" if fp8 else ""),
                    "global_batch": N_SEQ, "seq_len": PROMPT, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "paged decode attention (split-KV + combine)",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -129,6 +129,42 @@ size_t pie_packed_weight_bytes(int32_t n, int32_t k);
  * synchronises it.  Needs no context.  Errors: PIE_EINVAL, PIE_EHIP. */
 int pie_pack_weight(const void* src, void* dst, int32_t n, int32_t k, void* hip_stream);
 
+/* Block-scaled FP8 copies of the layer projections for the decode GEMMs
+ * ("Write a model in Poem", section 2: weights in dtype.e4m3tile128a8,
+ * block-scaled FP8; the pages do not define the blocking).  Reading taken:
+ * OCP e4m3 codes with one power-of-two scale per 128 x 128 block of the
+ * [out][in] matrix, 2^e with e the least integer for which the block's
+ * largest |w| is at most 448 * 2^e.  A code times its scale is exactly a
+ * bf16 value, so a bf16 matrix whose every block is e4m3 times its scale
+ * converts losslessly; other values are rounded to the nearest code (ties
+ * to even, saturating).  Decode-sized calls (at most 64 rows) then stream
+ * half the weight bytes and compute exactly what the bf16 weights give;
+ * larger calls keep using the bf16 weights of pie_init.
+ * pie_packed_weight_fp8_bytes: bytes of the codes of an [n][k] matrix (a
+ * tiled layout of 4 KiB blocks of 64 x 64, see gemm.h); pie_fp8_scale_count:
+ * floats of its scales, [ceil(n / 128)][ceil(k / 128)]. */
+size_t pie_packed_weight_fp8_bytes(int32_t n, int32_t k);
+size_t pie_fp8_scale_count(int32_t n, int32_t k);
+
+/* src: DEVICE bf16 [n][k] row-major; codes: DEVICE memory of
+ * pie_packed_weight_fp8_bytes(n, k) bytes (cleared here); scales: DEVICE
+ * float32 [pie_fp8_scale_count(n, k)].  Runs on hip_stream and synchronises
+ * it.  Needs no context.  Errors: PIE_EINVAL, PIE_EHIP. */
+int pie_pack_weight_fp8(const void* src, void* codes, float* scales, int32_t n, int32_t k, void* hip_stream);
+
+/* Per-layer HOST arrays of n_layers DEVICE pointers: codes and scales of each
+ * projection, made by pie_pack_weight_fp8 from the same matrices pie_init
+ * was given.  The caller keeps them alive until pie_destroy. */
+typedef struct pie_fp8_weights {
+  const void* const *wq, *const *wk, *const *wv, *const *wo, *const *w_gate, *const *w_up, *const *w_down;
+  const float* const *sq, *const *sk, *const *sv, *const *so, *const *s_gate, *const *s_up, *const *s_down;
+} pie_fp8_weights;
+
+/* From the next call on, decode-sized calls stream these FP8 copies instead
+ * of the bf16 projections.  Errors: PIE_EINVAL (null array or pointer),
+ * PIE_ESTATE (poisoned context). */
+int pie_attach_fp8_weights(pie_ctx* ctx, const pie_fp8_weights* w);
+
 /* Bytes of one KV page over all layers (K and V, every KV head, page_size tokens). */
 size_t pie_kv_page_bytes(const pie_model_desc* desc);
 

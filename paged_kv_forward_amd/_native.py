@@ -24,7 +24,8 @@ EXPORTS = ["pie_kv_page_bytes", "pie_workspace_bytes", "pie_init", "pie_destroy"
            "pie_alloc_working_set", "pie_fork", "pie_free_working_set", "pie_truncate",
            "pie_ws_info", "pie_pool_stats_get", "pie_forward", "pie_last_error",
            "pie_profile_enable", "pie_profile_read", "pie_debug_plan", "pie_debug_philox",
-           "pie_packed_weight_bytes", "pie_pack_weight", "pie_decode_async", "pie_sync", "pie_prefix_lookup"]
+           "pie_packed_weight_bytes", "pie_pack_weight", "pie_decode_async", "pie_sync", "pie_prefix_lookup",
+           "pie_packed_weight_fp8_bytes", "pie_fp8_scale_count", "pie_pack_weight_fp8", "pie_attach_fp8_weights"]
 
 
 class pie_model_desc(Structure):
@@ -41,6 +42,11 @@ class pie_weights(Structure):
                 ("mlp_norm", POINTER(c_void_p)), ("w_gate", POINTER(c_void_p)),
                 ("w_up", POINTER(c_void_p)), ("w_down", POINTER(c_void_p)),
                 ("kv_scale", c_void_p)]
+
+
+class pie_fp8_weights(Structure):
+    _fields_ = [(nm, POINTER(c_void_p)) for nm in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
+                                                  "sq", "sk", "sv", "so", "s_gate", "s_up", "s_down")]
 
 
 class pie_limits(Structure):
@@ -111,6 +117,10 @@ def lib():
                                      c_void_p]),
         "pie_sync": (c_int, [c_void_p]),
         "pie_prefix_lookup": (c_int, [c_void_p, P(c_int32), c_int32, P(c_uint64), P(c_int32)]),
+        "pie_packed_weight_fp8_bytes": (c_size_t, [c_int32, c_int32]),
+        "pie_fp8_scale_count": (c_size_t, [c_int32, c_int32]),
+        "pie_pack_weight_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
+        "pie_attach_fp8_weights": (c_int, [c_void_p, P(pie_fp8_weights)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

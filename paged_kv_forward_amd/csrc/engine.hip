@@ -200,6 +200,11 @@ struct pie_ctx {
   bool host_only = false, poisoned = false;
   const uint16_t *embed = nullptr, *final_norm = nullptr, *lm_head = nullptr;
   std::vector<const uint16_t*> attn_norm, wq, wk, wv, wo, mlp_norm, wg, wu, wd;
+  // block-scaled FP8 copies of the projections for the decode GEMMs
+  // (pie_attach_fp8_weights), in the order q, k, v, o, gate, up, down
+  bool f8 = false;
+  std::vector<const uint8_t*> f8w[7];
+  std::vector<const float*> f8s[7];
   const float* kv_scale = nullptr;
   uint8_t* kv = nullptr;
   int64_t n_pages = 0;
@@ -506,6 +511,10 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       g.gain = c->attn_norm[l];
       g.w[0] = c->wq[l]; g.w[1] = c->wk[l]; g.w[2] = c->wv[l];
       g.seg_n0[0] = 0; g.seg_n0[1] = qw; g.seg_n0[2] = qw + kvw; g.seg_n0[3] = qw + 2 * kvw;
+      if (small && c->f8) {
+        for (int i = 0; i < 3; ++i) { g.w8[i] = c->f8w[i][l]; g.s8[i] = c->f8s[i][l]; }
+        g.f8 = 1;
+      }
       g.q_out = q;
       g.rope_cs = rope;
       g.slot = M32(L.slot);
@@ -558,6 +567,10 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       g.lda = qw;
       g.w[0] = g.w[1] = g.w[2] = c->wo[l];
       g.seg_n0[0] = 0; g.seg_n0[1] = g.seg_n0[2] = g.seg_n0[3] = d.d_model;
+      if (small && c->f8) {
+        g.w8[0] = c->f8w[3][l]; g.s8[0] = c->f8s[3][l];
+        g.f8 = 1;
+      }
       set_split(g, pie::gemm_n_tiles(pie::EPI_RESID, g.N, tile));
       if (small) {  // and the MLP RMSNorm of the new rows
         g.next_gain = c->mlp_norm[l];
@@ -574,6 +587,11 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       g.K = d.d_model;
       g.gain = c->mlp_norm[l];
       g.w[0] = c->wg[l]; g.w[1] = c->wu[l]; g.w[2] = c->wu[l];
+      if (small && c->f8) {
+        g.w8[0] = c->f8w[4][l]; g.s8[0] = c->f8s[4][l];
+        g.w8[1] = c->f8w[5][l]; g.s8[1] = c->f8s[5][l];
+        g.f8 = 1;
+      }
       g.h_out = hb;
       set_split(g, pie::gemm_n_tiles(pie::EPI_SWIGLU, g.N, tile));
       Timed tm(c, PIE_K_GEMM_GATEUP);
@@ -593,6 +611,10 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       g.lda = d.d_ffn;
       g.w[0] = g.w[1] = g.w[2] = c->wd[l];
       g.seg_n0[0] = 0; g.seg_n0[1] = g.seg_n0[2] = g.seg_n0[3] = d.d_model;
+      if (small && c->f8) {
+        g.w8[0] = c->f8w[6][l]; g.s8[0] = c->f8s[6][l];
+        g.f8 = 1;
+      }
       set_split(g, pie::gemm_n_tiles(pie::EPI_RESID, g.N, tile));
       if (small && l + 1 < d.n_layers) {  // and the next layer's attention RMSNorm
         g.next_gain = c->attn_norm[l + 1];
@@ -1026,6 +1048,53 @@ int pie_debug_philox(pie_ctx* c, uint64_t seed, uint32_t lane, uint32_t v0, int3
   pie::launch_philox(seed, lane, v0, n, out, c->stream);
   HIP_TRY(c, hipGetLastError());
   HIP_TRY(c, hipStreamSynchronize(c->stream));
+  return PIE_OK;
+}
+
+size_t pie_packed_weight_fp8_bytes(int32_t n, int32_t k) {
+  if (n <= 0 || k <= 0) return 0;
+  return pie::packed_elems(n, k);
+}
+
+size_t pie_fp8_scale_count(int32_t n, int32_t k) {
+  if (n <= 0 || k <= 0) return 0;
+  return (size_t)pie::fp8_scale_blocks(n) * pie::fp8_scale_blocks(k);
+}
+
+int pie_pack_weight_fp8(const void* src, void* codes, float* scales, int32_t n, int32_t k, void* hip_stream) {
+  if (!src || !codes || !scales || n <= 0 || k <= 0) return set_err(PIE_EINVAL, "pie_pack_weight_fp8: bad arguments");
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  hipError_t e = hipMemsetAsync(codes, 0, pie::packed_elems(n, k), st);
+  if (e == hipSuccess) {
+    pie::launch_pack_weight_fp8(static_cast<const uint16_t*>(src), static_cast<uint8_t*>(codes), scales, n, k, st);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return set_err(PIE_EHIP, std::string("pie_pack_weight_fp8: ") + hipGetErrorString(e));
+  return PIE_OK;
+}
+
+int pie_attach_fp8_weights(pie_ctx* c, const pie_fp8_weights* w) {
+  CTX_OK(c);
+  if (!w) return set_err(PIE_EINVAL, "pie_attach_fp8_weights: null weights");
+  const int L = c->d.n_layers;
+  const void* const* codes[7] = {w->wq, w->wk, w->wv, w->wo, w->w_gate, w->w_up, w->w_down};
+  const float* const* sc[7] = {w->sq, w->sk, w->sv, w->so, w->s_gate, w->s_up, w->s_down};
+  for (int i = 0; i < 7; ++i) {
+    if (!codes[i] || !sc[i]) return set_err(PIE_EINVAL, "pie_attach_fp8_weights: null array");
+    for (int l = 0; l < L; ++l)
+      if (!codes[i][l] || !sc[i][l]) return set_err(PIE_EINVAL, "pie_attach_fp8_weights: null pointer");
+  }
+  for (int i = 0; i < 7; ++i) {
+    c->f8w[i].assign(L, nullptr);
+    c->f8s[i].assign(L, nullptr);
+    for (int l = 0; l < L; ++l) {
+      c->f8w[i][l] = static_cast<const uint8_t*>(codes[i][l]);
+      c->f8s[i][l] = sc[i][l];
+    }
+  }
+  c->f8 = true;
+  release_graphs(c);  // captured launches name the bf16 weights
   return PIE_OK;
 }
 

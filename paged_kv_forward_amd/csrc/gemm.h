@@ -37,6 +37,27 @@ __host__ __device__ inline size_t packed_elems(int N, int K) { return (size_t)((
 
 // dst (packed, packed_elems(N, K) bf16) <- src ([N][K] row-major bf16).
 void launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t stream);
+
+// Block-scaled FP8 copy of a projection for the decode GEMMs: OCP e4m3 codes
+// with one power-of-two scale per 128 x 128 block, scale = 2^e with e the
+// least integer for which the block's largest |w| is at most 448 * 2^e.  A
+// code times its scale is exactly a bf16 value, so when every block of the
+// bf16 matrix is already e4m3 times its scale the copy is lossless (else each
+// value is rounded to the nearest e4m3 code, ties to even, saturating).
+// Codes use the tiled layout with 1-byte elements: 4 KiB blocks of 64 x 64
+// at the same block index as packed_index, each [4 panels of 16 rows][64
+// lanes][16 bytes], lane = group * 16 + row of a 16-row panel, its 16 bytes
+// = the 8 k of that group in the block's first 32 columns, then the 8 in the
+// last 32: one 16-byte load is a lane's MFMA B operands of a 64-wide chunk.
+__host__ __device__ inline size_t packed_index_fp8(int n, int k, int kc) {
+  const int r = n & 63, kk = k & 63;
+  return ((size_t)(n >> 6) * kc + (k >> 6)) * 4096 + (size_t)(r >> 4) * 1024 +
+         (size_t)(((kk & 31) >> 3) * 16 + (r & 15)) * 16 + (size_t)(kk >> 5) * 8 + (kk & 7);
+}
+__host__ __device__ inline int fp8_scale_blocks(int n) { return (n + 127) / 128; }
+// codes (packed_elems(N, K) bytes, zero-initialised by the caller),
+// scales ([ceil(N/128)][ceil(K/128)] fp32) <- src ([N][K] row-major bf16).
+void launch_pack_weight_fp8(const uint16_t* src, uint8_t* codes, float* scales, int N, int K, hipStream_t stream);
 enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
 struct GemmArgs {
@@ -56,6 +77,12 @@ struct GemmArgs {
   // are multiples of 64.  EPI_SWIGLU: w[0] = gate, w[1] = up, both [N][K].
   const uint16_t* w[3];
   int seg_n0[4];
+  // TILE_SKINNY only: when f8 is set the weights stream as block-scaled FP8
+  // (w8[s] codes in the FP8 tiled layout, s8[s] the [ceil(rows/128)][ceil(K/128)]
+  // scales of segment s) instead of w[s]
+  const uint8_t* w8[3];
+  const float* s8[3];
+  int f8;
   // split-K (splits > 1): K range of split z is [z*k_split, min(K, (z+1)*k_split));
   // split partials go to partial[split][BM][n_tiles * BN] and a reduce kernel
   // runs the epilogue (only with a single M tile).

@@ -876,7 +876,15 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
 }
 
-template <int EPI, int WPOL>
+// Four e4m3 codes (one 32-bit word) times a power-of-two scale -> four bf16
+// (exact: a code has at most 4 significant bits).
+__device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t w, float s) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return make_uint2(pack_bf2(a.x * s, a.y * s), pack_bf2(b.x * s, b.y * s));
+}
+
+template <int EPI, int WPOL, bool F8>
 __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   // activation groups (two buffers), later reused for the output tile
   __shared__ __attribute__((aligned(16))) uint8_t smem[SK_LDS];
@@ -893,43 +901,70 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   // output columns, k group gq.
   const int kc = (g.K + 63) / 64;
   const uint16_t* wt;
-  int wrows;
-  uint32_t wbase;
+  const uint8_t* wt8;
+  const float* st8;
+  int wrows, wrow;  // rows of the wave's weight matrix; this lane's row in it
+  uint32_t wbase, wbase8;
   bool wok = true;
   if (EPI == EPI_SWIGLU) {
     // tile t: gated columns [t * cw, t * cw + cw), gate in waves 0-3, up in
     // waves 4-7, 16 columns per wave.  cw is a multiple of 8, so a wave's
     // columns may straddle two 16-row panels: each lane addresses its own row
     // (8 consecutive rows of a k group stay one 128-byte run).
-    const bool up = wave >= 4;
-    wt = up ? g.w[1] : g.w[0];
+    const int u = wave >= 4 ? 1 : 0;
+    wt = g.w[u];
+    wt8 = g.w8[u];
+    st8 = g.s8[u];
     wrows = g.N;
     const int j = (wave & 3) * 16 + r16, c = t * g.cw + j;
     wok = j < g.cw && c < g.N;
+    wrow = c;
     wbase = (uint32_t)(c >> 6) * (uint32_t)kc * 4096u + (uint32_t)((c >> 4) & 3) * 1024u + (uint32_t)gq * 128u +
             (uint32_t)(c & 15) * 8u;
   } else {
     const int n0 = t * SK_BN;  // whole tiles lie in one segment
     const int sg = n0 >= g.seg_n0[1] ? (n0 >= g.seg_n0[2] ? 2 : 1) : 0;
     wt = g.w[sg];
+    wt8 = g.w8[sg];
+    st8 = g.s8[sg];
     const int wblk = (n0 - g.seg_n0[sg]) / 64 + (wave >> 2);
     wrows = min(g.N, g.seg_n0[sg + 1]) - g.seg_n0[sg];
+    wrow = wblk * 64 + (wave & 3) * 16 + r16;
     wbase = (uint32_t)wblk * (uint32_t)kc * 4096u + (uint32_t)(wave & 3) * 1024u + (uint32_t)lane * 8u;
   }
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wt, (uint32_t)(packed_elems(wrows, g.K) * 2));
+  // FP8: the same 4 KiB block of 64 x 64 codes, panel, and the lane of row
+  // wrow (16 bytes: both k halves of its group)
+  wbase8 = (uint32_t)(wrow >> 6) * (uint32_t)kc * 4096u + (uint32_t)((wrow >> 4) & 3) * 1024u +
+           (uint32_t)(gq * 16 + (wrow & 15)) * 16u;
+  const int kb8 = fp8_scale_blocks(g.K);
+  const uint32_t srow8 = (uint32_t)(wrow >> 7) * (uint32_t)kb8;
+  const __amdgpu_buffer_rsrc_t wrs = F8 ? make_rsrc(wt8, (uint32_t)packed_elems(wrows, g.K))
+                                        : make_rsrc(wt, (uint32_t)(packed_elems(wrows, g.K) * 2));
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(F8 ? st8 : nullptr, F8 ? (uint32_t)(fp8_scale_blocks(wrows) * kb8 * 4) : 0u);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(g.a, (uint32_t)((size_t)g.M * g.lda * 2));
   const int c0 = kb / SK_KC;
   // this thread's activation pieces of a group: rows xr0 + 8i, columns xk .. xk + 7
   const int xr0 = tid / (SK_GK / 8), xk = (tid % (SK_GK / 8)) * 8;
 
+  // bf16: the two k halves of the chunk as loaded; FP8: w0 holds the 16 codes
+  // and s the block's scale (converted to bf16 when the chunk is consumed)
   struct WSlot {
     uint4 w0, w1;
+    float s;
   };
   auto load_w = [&](WSlot& sl, int j) {
     // chunks past nc (this split's end) read zeros; a chunk's padding past K is stored as zeros
-    const uint32_t e = wbase + (uint32_t)(c0 + j) * 4096u;
-    sl.w0 = bload16<WPOL>(wrs, j < nc && wok ? e * 2u : OOB);
-    sl.w1 = bload16<WPOL>(wrs, j < nc && wok ? (e + 512u) * 2u : OOB);
+    if constexpr (F8) {
+      const uint32_t e = wbase8 + (uint32_t)(c0 + j) * 4096u;
+      sl.w0 = bload16<WPOL>(wrs, j < nc && wok ? e : OOB);
+      sl.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           srs, j < nc && wok ? (srow8 + (uint32_t)(c0 + j) / 2u) * 4u : OOB, 0, 0));
+    } else {
+      const uint32_t e = wbase + (uint32_t)(c0 + j) * 4096u;
+      sl.w0 = bload16<WPOL>(wrs, j < nc && wok ? e * 2u : OOB);
+      sl.w1 = bload16<WPOL>(wrs, j < nc && wok ? (e + 512u) * 2u : OOB);
+    }
   };
   auto load_x = [&](uint4 (&xv)[SK_XP], int gi) {
     const int kx = kb + gi * SK_GK + xk;
@@ -978,10 +1013,17 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
           for (int a = 0; a < 4; ++a)
             af[ks][a] = *reinterpret_cast<const uint4*>(&X[(a * 16 + r16) * SK_LDX + j * SK_KC + ks * 32 + gq * 8]);
+        uint4 b0 = ring[j].w0, b1 = ring[j].w1;
+        if constexpr (F8) {
+          const uint2 p0 = fp8x4_to_bf16(b0.x, ring[j].s), p1 = fp8x4_to_bf16(b0.y, ring[j].s);
+          const uint2 p2 = fp8x4_to_bf16(b0.z, ring[j].s), p3 = fp8x4_to_bf16(b0.w, ring[j].s);
+          b0 = make_uint4(p0.x, p0.y, p1.x, p1.y);
+          b1 = make_uint4(p2.x, p2.y, p3.x, p3.y);
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int a = 0; a < 4; ++a) acc[a] = mfma16(af[ks][a], ks ? ring[j].w1 : ring[j].w0, acc[a]);
+          for (int a = 0; a < 4; ++a) acc[a] = mfma16(af[ks][a], ks ? b1 : b0, acc[a]);
         load_w(ring[j], (gi + 1) * SK_DEPTH + j);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1187,8 +1229,13 @@ static void launch_skinny(const GemmArgs& g0, hipStream_t st) {
   if (EPI == EPI_SWIGLU) g.cw = skinny_swiglu_cols(g.N);
   const int n_tiles = gemm_n_tiles(EPI, g.N, TILE_SKINNY);
   const dim3 grid(n_tiles, g.splits > 1 ? g.splits : 1);
-  if (EPI == EPI_QKV) hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 0>), grid, dim3(SK_NT), 0, st, g);
-  else hipLaunchKernelGGL((gemm_skinny_kernel<EPI, CPOL_NT>), grid, dim3(SK_NT), 0, st, g);
+  if (g.f8) {
+    if (EPI == EPI_QKV) hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 0, true>), grid, dim3(SK_NT), 0, st, g);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<EPI, CPOL_NT, true>), grid, dim3(SK_NT), 0, st, g);
+  } else {
+    if (EPI == EPI_QKV) hipLaunchKernelGGL((gemm_skinny_kernel<EPI, 0, false>), grid, dim3(SK_NT), 0, st, g);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<EPI, CPOL_NT, false>), grid, dim3(SK_NT), 0, st, g);
+  }
   const bool norm = EPI == EPI_RESID && g.x_out;
   const bool fused_norm = g.splits > 1 && norm && g.N <= RN_NT * 4 * RN_MAXC;
   if (fused_norm) {
@@ -1270,6 +1317,47 @@ void launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, hipStr
   if (pieces == 0) return;
   hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st, src, dst, N, K,
                      pieces);
+}
+
+// One workgroup per 128 x 128 block: the block's largest |w|, its power-of-two
+// scale, then every code at its place in the FP8 tiled layout.
+__global__ __launch_bounds__(256) void pack_weight_fp8_kernel(const uint16_t* __restrict__ src,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ scales, int N, int K) {
+  __shared__ float s_max[4];
+  const int bk = blockIdx.x, bn = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kc = (K + 63) / 64;
+  float amax = 0.f;
+  for (int i = tid; i < 128 * 128; i += 256) {
+    const int n = bn * 128 + i / 128, k = bk * 128 + i % 128;
+    if (n < N && k < K) amax = fmaxf(amax, fabsf(bf2f(src[(size_t)n * K + k])));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (lane == 0) s_max[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  // least e with amax <= 448 * 2^e (products with powers of two are exact)
+  int e = 0;
+  if (amax > 0.f) {
+    int x;
+    frexpf(amax / 448.f, &x);
+    e = x;
+    while (e > -126 && amax <= 448.f * ldexpf(1.f, e - 1)) --e;
+    while (amax > 448.f * ldexpf(1.f, e)) ++e;
+  }
+  const float inv = ldexpf(1.f, -e);
+  if (tid == 0) scales[(size_t)bn * ((K + 127) / 128) + bk] = ldexpf(1.f, e);
+  for (int i = tid; i < 128 * 128; i += 256) {
+    const int n = bn * 128 + i / 128, k = bk * 128 + i % 128;
+    if (n < N && k < K) codes[packed_index_fp8(n, k, kc)] = f2e4m3(bf2f(src[(size_t)n * K + k]) * inv);
+  }
+}
+
+void launch_pack_weight_fp8(const uint16_t* src, uint8_t* codes, float* scales, int N, int K, hipStream_t st) {
+  if (N <= 0 || K <= 0) return;
+  hipLaunchKernelGGL(pack_weight_fp8_kernel, dim3(fp8_scale_blocks(K), fp8_scale_blocks(N)), dim3(256), 0, st, src,
+                     codes, scales, N, K);
 }
 
 void launch_rmsnorm(const float* y, const float* ss, int n_ss, const uint16_t* gain, int M, int d,

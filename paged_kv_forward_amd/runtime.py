@@ -53,12 +53,15 @@ PASS_DT = _struct_dtype(N.pie_pass, {"ws": np.uint64, "tokens": np.uint64, "posi
 EPI_DT = _struct_dtype(N.pie_epilogue, {"kind": np.int32, "temperature": np.float32, "seed": np.uint64})
 
 
-def upload_weights(recipe, device="cuda", progress=None) -> Dict:
+def upload_weights(recipe, device="cuda", progress=None, fp8=False) -> Dict:
     """Draw the seeded bf16 weights of `recipe` (a synth.WeightRecipe) on the
     host and copy them to `device`, one tensor at a time through pinned
     memory.  Projections and lm_head are converted on the device to the
     library's tiled layout (pie_pack_weight) through one staging buffer, so
-    the checkpoint-layout copy never exists for more than one tensor."""
+    the checkpoint-layout copy never exists for more than one tensor.
+    fp8: also the block-scaled FP8 copy of every layer projection
+    (pie_pack_weight_fp8), under layers[l]["fp8"][name] = (codes, scales),
+    which PieRuntime attaches for the decode GEMMs."""
     import torch
     import synth
     shape = recipe.shape
@@ -79,16 +82,24 @@ def upload_weights(recipe, device="cuda", progress=None) -> Dict:
         rows, cols = shp
         dev_stage[:n].copy_(stage[:n], non_blocking=False)
         t = torch.empty(L.pie_packed_weight_bytes(rows, cols) // 2, dtype=torch.bfloat16, device=device)
-        check(L.pie_pack_weight(dev_stage.data_ptr(), t.data_ptr(), rows, cols,
-                                torch.cuda.current_stream(device).cuda_stream))
+        st = torch.cuda.current_stream(device).cuda_stream
+        check(L.pie_pack_weight(dev_stage.data_ptr(), t.data_ptr(), rows, cols, st))
+        if fp8 and name.startswith("layers."):
+            codes = torch.empty(L.pie_packed_weight_fp8_bytes(rows, cols), dtype=torch.uint8, device=device)
+            scales = torch.empty(L.pie_fp8_scale_count(rows, cols), dtype=torch.float32, device=device)
+            check(L.pie_pack_weight_fp8(dev_stage.data_ptr(), codes.data_ptr(), scales.data_ptr(), rows, cols, st))
+            f8[name.split(".")[-1]] = (codes, scales)
         return t
 
     w = {"embed": one("embed", (shape.vocab, shape.d_model)),
          "final_norm": one("final_norm", (shape.d_model,)),
          "lm_head": one("head", (shape.vocab, shape.d_model), packed=True), "layers": []}
     for l in range(shape.n_layers):
+        f8 = {}
         w["layers"].append({k: one("layers.%d.%s" % (l, k), s, packed=k in PACKED_KEYS)
                             for k, s in synth.layer_tensor_shapes(shape)})
+        if fp8:
+            w["layers"][-1]["fp8"] = f8
         if progress:
             progress(l)
     del dev_stage
@@ -136,7 +147,18 @@ class PieRuntime:
                              kv_bytes, self.workspace.data_ptr(), self.ws_bytes,
                              ctypes.byref(self.limits), ctypes.c_void_p(self.stream.cuda_stream),
                              ctypes.byref(ctx)))
+            if "fp8" in weights["layers"][0]:
+                check(L.pie_attach_fp8_weights(ctx, ctypes.byref(self._fp8_struct(weights))))
         self.ctx = ctx
+
+    def _fp8_struct(self, w):
+        L = self.shape.n_layers
+        fields = []
+        for i in (0, 1):  # codes, then scales
+            for k in ("q", "k", "v", "o", "gate", "up", "down"):
+                fields.append((ctypes.c_void_p * L)(*[w["layers"][l]["fp8"][k][i].data_ptr() for l in range(L)]))
+        self._keep.append(fields)
+        return N.pie_fp8_weights(*fields)
 
     def _weights_struct(self, w):
         L = self.shape.n_layers

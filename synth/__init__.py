@@ -161,6 +161,34 @@ def first_layers(shape: ModelShape, n_layers: int) -> ModelShape:
     return replace(shape, name="%s-first%d" % (shape.name, n_layers), n_layers=n_layers)
 
 
+FP8_BLOCK = 128
+E4M3_MAX = 448.0
+
+
+def fp8_block_bits(bits: np.ndarray) -> np.ndarray:
+    """A weight matrix drawn for a block-scaled FP8 model: each 128 x 128 block
+    of the [out][in] bf16 matrix `bits` becomes the nearest OCP e4m3 values
+    (ties to even, saturating at 448) times the block's power-of-two scale
+    2^e, e the least integer with max |w| <= 448 * 2^e.  The result holds bf16
+    bits; every value is exactly representable (at most 4 significant bits).
+    This shapes an input; the forward pass only ever sees the values."""
+    import torch
+    rows, cols = bits.shape
+    pr, pc = -(-rows // FP8_BLOCK) * FP8_BLOCK, -(-cols // FP8_BLOCK) * FP8_BLOCK
+    w = torch.zeros((pr, pc), dtype=torch.float32)
+    w[:rows, :cols] = (torch.from_numpy(bits.astype(np.int32)) << 16).view(torch.float32)
+    blk = w.view(pr // FP8_BLOCK, FP8_BLOCK, pc // FP8_BLOCK, FP8_BLOCK)
+    amax = blk.abs().amax(dim=(1, 3)).double()
+    e = torch.where(amax > 0, torch.ceil(torch.log2(torch.where(amax > 0, amax, 1.0) / E4M3_MAX)), 0.0)
+    # exact adjustment: least e with amax <= 448 * 2^e
+    e = torch.where(amax > E4M3_MAX * torch.exp2(e), e + 1, e)
+    e = torch.where((amax > 0) & (amax <= E4M3_MAX * torch.exp2(e - 1)), e - 1, e)
+    scale = torch.exp2(e).float()[:, None, :, None]
+    q = torch.clamp(blk / scale, -E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).float()
+    out = (q * scale).reshape(pr, pc)[:rows, :cols].contiguous()
+    return (out.view(torch.int32) >> 16).to(torch.int32).numpy().astype(np.uint16)
+
+
 def layer_tensor_shapes(m: ModelShape) -> List[Tuple[str, Tuple[int, ...]]]:
     """Per-layer weights, row-major [out][in] for matrices (the checkpoint layout)."""
     d, f = m.d_model, m.d_ffn
@@ -171,11 +199,14 @@ def layer_tensor_shapes(m: ModelShape) -> List[Tuple[str, Tuple[int, ...]]]:
 
 @dataclass(frozen=True)
 class WeightRecipe:
-    """How the seeded weights of one model are drawn."""
+    """How the seeded weights of one model are drawn.  fp8_blocks: every layer
+    projection is a block-scaled FP8 matrix (see fp8_block_bits); its bf16
+    values are exactly the codes times their block scales."""
     shape: ModelShape
     weight_seed: int = 1234
     std: float = 0.02
     gain_std: float = 0.0  # 0 -> gains are exactly 1.0
+    fp8_blocks: bool = False
 
     def key(self, name: str) -> int:
         return key_of("%d/%s" % (self.weight_seed, name))
@@ -189,7 +220,10 @@ class WeightRecipe:
                 bits.reshape(-1)[:] = 0x3F80  # bf16(1.0)
                 return bits.reshape(shape)
             return normal_bf16(n, self.key(name), 1.0, self.gain_std, out=out).reshape(shape)
-        return normal_bf16(n, self.key(name), 0.0, self.std, out=out).reshape(shape)
+        bits = normal_bf16(n, self.key(name), 0.0, self.std, out=out).reshape(shape)
+        if self.fp8_blocks and name.startswith("layers."):
+            bits[...] = fp8_block_bits(bits)
+        return bits
 
     def embed_bits(self) -> np.ndarray:
         m = self.shape

@@ -28,9 +28,9 @@ def torch_cuda():
 
 
 def make_runtime(shape, recipe, torch_cuda, max_rows=512, max_seqs=16, max_readout=64, max_ctx=1024,
-                 pages=2048):
+                 pages=2048, fp8=False):
     from paged_kv_forward_amd.runtime import PieRuntime, upload_weights
-    w = upload_weights(recipe)
+    w = upload_weights(recipe, fp8=fp8)
     page_bytes = shape.n_layers * 2 * shape.n_kv_heads * 16 * shape.head_dim * (
         1 if shape.kv_dtype == synth.KV_E4M3 else 2)
     return PieRuntime(shape, w, page_bytes * pages, max_rows, max_seqs, max_readout, max_ctx)
