@@ -264,6 +264,66 @@ def measured_traffic():
 
 
 
+def fp8_decode_summary(shape, K, W):
+    """The FP8 variant measured beside the headline: the same decode workload
+    (64 sequences of 2048 prompt tokens, argmax, loop-carried steps) with every
+    layer projection block-scaled FP8 and decode streaming the FP8 copies."""
+    import torch
+    import synth
+    from paged_kv_forward_amd import _native as N
+    from paged_kv_forward_amd.runtime import Pass, PieRuntime, upload_weights
+    recipe = synth.WeightRecipe(shape, fp8_blocks=True)
+    wl = synth.workload(2)
+    log("bench: FP8 variant: drawing and uploading weights")
+    weights = upload_weights(recipe, "cuda:0", fp8=True)
+    max_ctx = PROMPT + W + K + 3 + 8
+    pages = N_SEQ * ((max_ctx + 15) // 16 + 1)
+    page_bytes = shape.n_layers * 2 * shape.n_kv_heads * 16 * shape.head_dim * 2
+    rt = PieRuntime(shape, weights, pages * page_bytes, max_rows=PREFILL_SEQS_PER_LAUNCH * PROMPT,
+                    max_seqs=N_SEQ, max_readout=N_SEQ, max_ctx=max_ctx)
+    ws = [rt.alloc() for _ in range(N_SEQ)]
+    nxt = np.zeros(N_SEQ, dtype=np.int32)
+    for b in range(0, N_SEQ, PREFILL_SEQS_PER_LAUNCH):
+        ss = range(b, b + PREFILL_SEQS_PER_LAUNCH)
+        toks, _ = rt.forward([Pass(ws[s], wl.prompt(s), [PROMPT - 1], [(0, 1.0, 0)]) for s in ss])
+        nxt[b:b + PREFILL_SEQS_PER_LAUNCH] = toks
+    ws_arr = np.array(ws, dtype=np.uint64)
+    for _ in range(W):
+        nxt[:] = rt.decode_step(ws_arr, nxt)
+    ctx_first = rt.ws_info(ws[0])["len"] + 1
+    tok_dev = torch.tensor(nxt, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        rt.decode_async(ws_arr, tok_dev, tok_dev)
+    rt.sync()
+    torch.cuda.synchronize()
+    t_dec = time.perf_counter() - t0
+    nxt[:] = tok_dev.cpu().numpy()
+    rt.profile_enable(N.KERNEL_CLASSES)
+    for _ in range(3):
+        nxt[:] = rt.decode_step(ws_arr, nxt)
+    pb = rt.profile_read()
+    rt.profile_enable([])
+    rt.close()
+    del weights
+    torch.cuda.empty_cache()
+    ms = t_dec / K * 1e3
+    kv_tok = shape.n_kv_heads * shape.head_dim * 2 * 2
+    proj = shape.n_layers * shape.d_model * (2 * shape.q_width + 2 * shape.kv_width + 3 * shape.d_ffn)
+    wbytes = proj + 4 * proj // (128 * 128) + 2 * shape.vocab * shape.d_model + 2 * shape.d_model * (
+        2 * shape.n_layers + 1)
+    step_bytes = wbytes + sum(N_SEQ * (ctx_first + i) for i in range(K)) / K * kv_tok * shape.n_layers
+    return {"value": round(N_SEQ * K / t_dec, 2), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+            "steps": K, "warmup": W,
+            "weights": "layer projections block-scaled FP8 (OCP e4m3 codes, one power-of-two scale per "
+                       "128x128 block) streamed by decode; lm_head, embedding and norms bf16",
+            "step_hbm": {"bytes_per_step": int(step_bytes),
+                         "achieved_gbs": round(step_bytes / (ms / 1e3) / 1e9, 1),
+                         "frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "ms_per_step_by_kernel": {k: round(v[0] / 3, 4) for k, v in pb.items() if v[1]}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +333,8 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="(always on; kept for old command lines)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write profiles/ summaries from the rocprofv3 outputs under DIR and exit")
+    ap.add_argument("--no-fp8-variant", action="store_true",
+                    help="skip the FP8-weight decode measured beside the headline")
     ap.add_argument("--fp8-weights", action="store_true",
                     help="the FP8 variant: layer projections are block-scaled FP8 (e4m3 codes, one "
                          "power-of-two scale per 128 x 128 block) and decode streams the FP8 copies")
@@ -484,6 +546,8 @@ def main():
     rt.close()
     del weights
     torch.cuda.empty_cache()
+    if not fp8 and not args.no_fp8_variant:
+        out["fp8_weights_decode"] = fp8_decode_summary(shape, min(K, 60), min(W, 20))
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(shape, recipe)
