@@ -311,13 +311,13 @@ def fp8_decode_summary(shape, K, W):
     ms = t_dec / K * 1e3
     kv_tok = shape.n_kv_heads * shape.head_dim * 2 * 2
     proj = shape.n_layers * shape.d_model * (2 * shape.q_width + 2 * shape.kv_width + 3 * shape.d_ffn)
-    wbytes = proj + 4 * proj // (128 * 128) + 2 * shape.vocab * shape.d_model + 2 * shape.d_model * (
-        2 * shape.n_layers + 1)
+    fp8_params = proj + shape.vocab * shape.d_model  # projections and lm_head at one byte each
+    wbytes = fp8_params + 4 * fp8_params // (128 * 128) + 2 * shape.d_model * (2 * shape.n_layers + 1)
     step_bytes = wbytes + sum(N_SEQ * (ctx_first + i) for i in range(K)) / K * kv_tok * shape.n_layers
     return {"value": round(N_SEQ * K / t_dec, 2), "unit": "tokens/s", "ms_per_step": round(ms, 4),
             "steps": K, "warmup": W,
-            "weights": "layer projections block-scaled FP8 (OCP e4m3 codes, one power-of-two scale per "
-                       "128x128 block) streamed by decode; lm_head, embedding and norms bf16",
+            "weights": "layer projections and lm_head block-scaled FP8 (OCP e4m3 codes, one power-of-two "
+                       "scale per 128x128 block) streamed by decode; embedding and norms bf16",
             "step_hbm": {"bytes_per_step": int(step_bytes),
                          "achieved_gbs": round(step_bytes / (ms / 1e3) / 1e9, 1),
                          "frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -476,8 +476,9 @@ def main():
     per_launch = attn_bytes / max(attn_n, 1)
     weight_bytes = 2 * (shape.n_params() - shape.vocab * shape.d_model)  # all but the embedding table
     proj_params = shape.n_layers * shape.d_model * (2 * shape.q_width + 2 * shape.kv_width + 3 * shape.d_ffn)
-    if fp8:  # projections at one byte per weight plus one fp32 scale per 128 x 128 block
-        weight_bytes -= proj_params - 4 * proj_params // (128 * 128)
+    if fp8:  # projections and lm_head at one byte per weight plus one fp32 scale per 128 x 128 block
+        f8p = proj_params + shape.vocab * shape.d_model
+        weight_bytes -= f8p - 4 * f8p // (128 * 128)
     step_bytes = weight_bytes + (ctx_sum / K) * kv_tok * shape.n_layers
     ms_step = t_dec / K * 1e3
 
@@ -494,7 +495,7 @@ def main():
     wb = 1 if fp8 else 2  # bytes per projection weight streamed by decode
     wbytes = {"gemm_qkv": wb * L_ * d * (shape.q_width + 2 * shape.kv_width),
               "gemm_o": wb * L_ * shape.q_width * d, "gemm_gateup": wb * L_ * d * 2 * shape.d_ffn,
-              "gemm_down": wb * L_ * shape.d_ffn * d, "lm_head": 2 * shape.vocab * d,
+              "gemm_down": wb * L_ * shape.d_ffn * d, "lm_head": wb * shape.vocab * d,
               "attn_decode": L_ * (sum(N_SEQ * (ctx_bd + i) for i in range(3)) / 3 * kv_tok + qo)}
     decode_kernels = {}
     for k, b in wbytes.items():

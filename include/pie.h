@@ -158,10 +158,13 @@ int pie_pack_weight_fp8(const void* src, void* codes, float* scales, int32_t n, 
 typedef struct pie_fp8_weights {
   const void* const *wq, *const *wk, *const *wv, *const *wo, *const *w_gate, *const *w_up, *const *w_down;
   const float* const *sq, *const *sk, *const *sv, *const *so, *const *s_gate, *const *s_up, *const *s_down;
+  const void* lm_head;    /* DEVICE codes of [vocab][d_model], or NULL: the head stays bf16 */
+  const float* s_lm_head; /* its scales (NULL with lm_head NULL) */
 } pie_fp8_weights;
 
 /* From the next call on, decode-sized calls stream these FP8 copies instead
- * of the bf16 projections.  Errors: PIE_EINVAL (null array or pointer),
+ * of the bf16 projections (and of the bf16 lm_head when given, for calls of
+ * at most 64 readout rows).  Errors: PIE_EINVAL (null array or pointer),
  * PIE_ESTATE (poisoned context). */
 int pie_attach_fp8_weights(pie_ctx* ctx, const pie_fp8_weights* w);
 

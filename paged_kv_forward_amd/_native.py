@@ -46,7 +46,8 @@ class pie_weights(Structure):
 
 class pie_fp8_weights(Structure):
     _fields_ = [(nm, POINTER(c_void_p)) for nm in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
-                                                  "sq", "sk", "sv", "so", "s_gate", "s_up", "s_down")]
+                                                  "sq", "sk", "sv", "so", "s_gate", "s_up", "s_down")] + [
+        ("lm_head", c_void_p), ("s_lm_head", c_void_p)]
 
 
 class pie_limits(Structure):

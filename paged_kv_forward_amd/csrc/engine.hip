@@ -205,6 +205,8 @@ struct pie_ctx {
   bool f8 = false;
   std::vector<const uint8_t*> f8w[7];
   std::vector<const float*> f8s[7];
+  const uint8_t* f8_head = nullptr;
+  const float* f8_head_s = nullptr;
   const float* kv_scale = nullptr;
   uint8_t* kv = nullptr;
   int64_t n_pages = 0;
@@ -655,6 +657,11 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
         pie::launch_rmsnorm(y, ss, n_ss, c->final_norm, R, d.d_model, d.rms_eps, g.a_rows, xb, st);
         g.a = xb;
         g.lda = d.d_model;
+        if (c->f8 && c->f8_head) {
+          g.w8[0] = c->f8_head;
+          g.s8[0] = c->f8_head_s;
+          g.f8 = 1;
+        }
         pie::launch_gemm(pie::A_BF16, pie::EPI_LOGITS, pie::TILE_SKINNY, g, st);
       } else {
         pie::launch_gemm(pie::A_NORM, pie::EPI_LOGITS, pie::TILE_128x128, g, st);
@@ -1093,8 +1100,13 @@ int pie_attach_fp8_weights(pie_ctx* c, const pie_fp8_weights* w) {
       c->f8s[i][l] = sc[i][l];
     }
   }
+  if (!w->lm_head != !w->s_lm_head) return set_err(PIE_EINVAL, "pie_attach_fp8_weights: lm_head without scales");
+  c->f8_head = static_cast<const uint8_t*>(w->lm_head);
+  c->f8_head_s = w->s_lm_head;
+  // captured launches name the bf16 weights: drop them once nothing runs
+  if (!c->host_only) HIP_TRY(c, hipStreamSynchronize(c->stream));
   c->f8 = true;
-  release_graphs(c);  // captured launches name the bf16 weights
+  release_graphs(c);
   return PIE_OK;
 }
 

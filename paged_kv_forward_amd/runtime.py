@@ -84,16 +84,19 @@ def upload_weights(recipe, device="cuda", progress=None, fp8=False) -> Dict:
         t = torch.empty(L.pie_packed_weight_bytes(rows, cols) // 2, dtype=torch.bfloat16, device=device)
         st = torch.cuda.current_stream(device).cuda_stream
         check(L.pie_pack_weight(dev_stage.data_ptr(), t.data_ptr(), rows, cols, st))
-        if fp8 and name.startswith("layers."):
+        if fp8:
             codes = torch.empty(L.pie_packed_weight_fp8_bytes(rows, cols), dtype=torch.uint8, device=device)
             scales = torch.empty(L.pie_fp8_scale_count(rows, cols), dtype=torch.float32, device=device)
             check(L.pie_pack_weight_fp8(dev_stage.data_ptr(), codes.data_ptr(), scales.data_ptr(), rows, cols, st))
             f8[name.split(".")[-1]] = (codes, scales)
         return t
 
+    f8 = {}
     w = {"embed": one("embed", (shape.vocab, shape.d_model)),
          "final_norm": one("final_norm", (shape.d_model,)),
          "lm_head": one("head", (shape.vocab, shape.d_model), packed=True), "layers": []}
+    if fp8:
+        w["lm_head_fp8"] = f8["head"]
     for l in range(shape.n_layers):
         f8 = {}
         w["layers"].append({k: one("layers.%d.%s" % (l, k), s, packed=k in PACKED_KEYS)
@@ -158,7 +161,9 @@ class PieRuntime:
             for k in ("q", "k", "v", "o", "gate", "up", "down"):
                 fields.append((ctypes.c_void_p * L)(*[w["layers"][l]["fp8"][k][i].data_ptr() for l in range(L)]))
         self._keep.append(fields)
-        return N.pie_fp8_weights(*fields)
+        head = w.get("lm_head_fp8")
+        return N.pie_fp8_weights(*fields, head[0].data_ptr() if head else None,
+                                 head[1].data_ptr() if head else None)
 
     def _weights_struct(self, w):
         L = self.shape.n_layers

@@ -200,8 +200,9 @@ def layer_tensor_shapes(m: ModelShape) -> List[Tuple[str, Tuple[int, ...]]]:
 @dataclass(frozen=True)
 class WeightRecipe:
     """How the seeded weights of one model are drawn.  fp8_blocks: every layer
-    projection is a block-scaled FP8 matrix (see fp8_block_bits); its bf16
-    values are exactly the codes times their block scales."""
+    projection and the lm_head are block-scaled FP8 matrices (see
+    fp8_block_bits); their bf16 values are exactly the codes times their block
+    scales.  The embedding and the norm gains stay as drawn."""
     shape: ModelShape
     weight_seed: int = 1234
     std: float = 0.02
@@ -221,7 +222,7 @@ class WeightRecipe:
                 return bits.reshape(shape)
             return normal_bf16(n, self.key(name), 1.0, self.gain_std, out=out).reshape(shape)
         bits = normal_bf16(n, self.key(name), 0.0, self.std, out=out).reshape(shape)
-        if self.fp8_blocks and name.startswith("layers."):
+        if self.fp8_blocks and (name.startswith("layers.") or name == "head"):
             bits[...] = fp8_block_bits(bits)
         return bits
 
