@@ -168,9 +168,10 @@ def summarize(out_dir):
     stats = list(csv.DictReader(open(glob.glob(os.path.join(out_dir, "trace_c2", "*kernel_stats.csv"))[0])))
     lines = ["# Kernel trace of the decode benchmark (Llama-3.1-8B shape, batch 64)", "",
              "Command (on one MI355X, from the repository root):", "", "    " + TRACE_CMD, "",
-             "The run includes the 64 x 2048-token prefill (16 launches of 4 sequences) and 45 decode",
-             "steps (5 warm-up + 20 timed + 20 with HIP events).  Per kernel: calls, average and total",
-             "duration from `c2_kernel_stats.csv`.", "",
+             "The run includes the 64 x 2048-token prefill (16 launches of 4 sequences) and 68 decode",
+             "steps (5 warm-up + 20 timed + 20 host-loop + 20 with HIP events + 3 per-class), then the",
+             "FP8-weight variant (its own prefill and 28 decode steps; kernels `<..., true>`).  Per kernel:",
+             "calls, average and total duration from `c2_kernel_stats.csv`.", "",
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
     for r in stats[:24]:
         lines.append("| `%s` | %s | %.2f | %.2f | %.3f |" % (short_name(r["Name"]), r["Calls"],
@@ -186,8 +187,14 @@ def summarize(out_dir):
                 steps.append(cur)
         if cur is not None:
             cur.append(r)
-    if len(steps) > 2:
-        st = steps[len(steps) // 2]
+    # decode steps with bf16 weights, then those of the FP8-weight variant
+    # (their skinny GEMM launches are the FP8 instantiations)
+    is_f8 = lambda st: any("gemm_skinny_kernel" in r["Kernel_Name"] and "true" in r["Kernel_Name"] for r in st)
+    for label, group in (("bf16 weights", [st for st in steps if not is_f8(st)]),
+                         ("FP8 projection and lm_head weights", [st for st in steps if is_f8(st)])):
+        if len(group) < 3:
+            continue
+        st = group[len(group) // 2]
         span = (int(st[-1]["End_Timestamp"]) - int(st[0]["Start_Timestamp"])) / 1e3
         agg = {}
         for r in st:
@@ -196,8 +203,9 @@ def summarize(out_dir):
             a[0] += 1
             a[1] += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         busy = sum(v[1] for v in agg.values())
-        lines += ["", "One decode step (the middle one of the run): %d launches, %.1f us from the first "
-                  "kernel's start to the last one's end, %.1f us of it inside kernels." % (len(st), span, busy),
+        lines += ["", "One decode step with %s (the middle one of those in the run): %d launches, %.1f us from "
+                  "the first kernel's start to the last one's end, %.1f us of it inside kernels."
+                  % (label, len(st), span, busy),
                   "", "| kernel | launches per step | us per step |", "|---|---|---|"]
         for k, (n, d) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
             lines.append("| `%s` | %d | %.1f |" % (k, n, d))
