@@ -102,3 +102,22 @@ def test_fp8_weights_8b_two_layers_decode_batch64_equals_bf16(torch_cuda):
     got = run_decode(rt_fp8, prompts, teach, steps)
     rt_fp8.close()
     np.testing.assert_array_equal(got, ref)
+
+
+def test_fp8_weights_70b_two_layers_e4m3_kv_decode_equals_bf16(torch_cuda):
+    """The 70B shape cut to 2 layers (d_model 8192, GQA group 8, d_ffn 28672,
+    e4m3 KV), batch 32: FP8 weights bit for bit against the bf16 weights."""
+    shape = dataclasses.replace(synth.LLAMA_70B, n_layers=2)
+    recipe = synth.WeightRecipe(shape, fp8_blocks=True)
+    n, plen, steps = 32, 40, 2
+    prompts = [synth.prompt_tokens(5, s, plen, shape.vocab) for s in range(n)]
+    teach = [synth.prompt_tokens(6, s, steps, shape.vocab) for s in range(n)]
+    kw = dict(max_rows=n * plen, max_seqs=n, max_readout=n, max_ctx=plen + steps + 8, pages=n * 5)
+    rt_bf16 = make_runtime(shape, recipe, torch_cuda, **kw)
+    ref = run_decode(rt_bf16, prompts, teach, steps)
+    rt_bf16.close()
+    rt_fp8 = make_runtime(shape, recipe, torch_cuda, fp8=True, **kw)
+    got = run_decode(rt_fp8, prompts, teach, steps)
+    rt_fp8.close()
+    np.testing.assert_array_equal(got, ref)
+
