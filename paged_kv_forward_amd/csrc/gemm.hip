@@ -995,14 +995,21 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < SK_DEPTH; ++j) load_w(ring[j], j);
     store_x(xv, 0);
-    lds_barrier();
     const int ngroups = (nc + SK_DEPTH - 1) / SK_DEPTH;
+    // a K range of at most two groups is staged whole, into both buffers, so
+    // the loop needs no activation loads and no barriers
+    const bool whole = ngroups <= 2;
+    if (whole && ngroups == 2) {
+      load_x(xv, 1);
+      store_x(xv, 1);
+    }
+    lds_barrier();
     // The scheduling barriers pin the issue order: the next group's activation
     // loads first, then each chunk's refill right after the MFMAs that free its
     // ring slot.  Left alone, the compiler sinks all refills to the end of the
     // group, so the ring drains to empty once per group.
     for (int gi = 0; gi < ngroups; ++gi) {
-      load_x(xv, gi + 1);  // the next group, in flight during this one
+      if (!whole) load_x(xv, gi + 1);  // the next group, in flight during this one
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t* X = sX + (gi & 1) * 64 * SK_LDX;
 #pragma unroll
@@ -1027,9 +1034,12 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
         load_w(ring[j], (gi + 1) * SK_DEPTH + j);
         __builtin_amdgcn_sched_barrier(0);
       }
-      store_x(xv, (gi + 1) & 1);  // that buffer was last read in group gi - 1
-      lds_barrier();
+      if (!whole) {
+        store_x(xv, (gi + 1) & 1);  // that buffer was last read in group gi - 1
+        lds_barrier();
+      }
     }
+    if (whole) lds_barrier();  // every wave is done with the activations before sC reuses them
   }
 
   // the loop ended with a barrier: the activation buffers are free for sC
