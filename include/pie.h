@@ -148,8 +148,9 @@ size_t pie_fp8_scale_count(int32_t n, int32_t k);
 
 /* src: DEVICE bf16 [n][k] row-major; codes: DEVICE memory of
  * pie_packed_weight_fp8_bytes(n, k) bytes (cleared here); scales: DEVICE
- * float32 [pie_fp8_scale_count(n, k)].  Runs on hip_stream and synchronises
- * it.  Needs no context.  Errors: PIE_EINVAL, PIE_EHIP. */
+ * float32 [pie_fp8_scale_count(n, k)]; the three must not overlap.  Runs on
+ * hip_stream and synchronises it.  Needs no context.  Errors: PIE_EINVAL
+ * (null pointer, n or k <= 0, overlap), PIE_EHIP. */
 int pie_pack_weight_fp8(const void* src, void* codes, float* scales, int32_t n, int32_t k, void* hip_stream);
 
 /* Per-layer HOST arrays of n_layers DEVICE pointers: codes and scales of each

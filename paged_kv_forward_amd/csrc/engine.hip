@@ -1070,6 +1070,13 @@ size_t pie_fp8_scale_count(int32_t n, int32_t k) {
 
 int pie_pack_weight_fp8(const void* src, void* codes, float* scales, int32_t n, int32_t k, void* hip_stream) {
   if (!src || !codes || !scales || n <= 0 || k <= 0) return set_err(PIE_EINVAL, "pie_pack_weight_fp8: bad arguments");
+  const size_t src_bytes = (size_t)n * k * 2, code_bytes = pie::packed_elems(n, k),
+               scale_bytes = (size_t)pie::fp8_scale_blocks(n) * pie::fp8_scale_blocks(k) * 4;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(codes),
+                  c8 = reinterpret_cast<uintptr_t>(scales);
+  if ((a < b + code_bytes && b < a + src_bytes) || (a < c8 + scale_bytes && c8 < a + src_bytes) ||
+      (b < c8 + scale_bytes && c8 < b + code_bytes))
+    return set_err(PIE_EINVAL, "pie_pack_weight_fp8: src, codes and scales overlap");
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   hipError_t e = hipMemsetAsync(codes, 0, pie::packed_elems(n, k), st);
   if (e == hipSuccess) {

@@ -70,6 +70,31 @@ def snapshot(rt, handles):
              for h in handles], rt.pool_stats())
 
 
+def test_fp8_weight_sizes_and_argument_checks():
+    """Sizes of the block-scaled FP8 copies (tiled codes padded to 64 x 64
+    blocks, one scale per 128 x 128 block) and the calls' argument checks,
+    none of which needs a GPU."""
+    L = N.lib()
+    assert L.pie_packed_weight_fp8_bytes(100, 70) == 128 * 128
+    assert L.pie_packed_weight_fp8_bytes(4096, 4096) == 4096 * 4096
+    assert L.pie_packed_weight_fp8_bytes(0, 64) == 0
+    assert L.pie_fp8_scale_count(300, 200) == 3 * 2
+    assert L.pie_fp8_scale_count(128, 128) == 1
+    assert L.pie_fp8_scale_count(-1, 128) == 0
+    assert L.pie_pack_weight_fp8(None, ctypes.c_void_p(16), ctypes.c_void_p(16), 64, 64, None) == N.PIE_EINVAL
+    assert L.pie_pack_weight_fp8(ctypes.c_void_p(16), ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21),
+                                 0, 64, None) == N.PIE_EINVAL
+    # codes overlapping the source
+    assert L.pie_pack_weight_fp8(ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 64),
+                                 ctypes.c_void_p(1 << 24), 64, 64, None) == N.PIE_EINVAL
+    rt = PieRuntime(synth.TINY, None, 64 * 1024 * 1024, 128, 4, 8, 256)
+    assert L.pie_attach_fp8_weights(rt.ctx, None) == N.PIE_EINVAL
+    empty = N.pie_fp8_weights()  # null arrays
+    assert L.pie_attach_fp8_weights(rt.ctx, ctypes.byref(empty)) == N.PIE_EINVAL
+    assert L.pie_attach_fp8_weights(None, ctypes.byref(empty)) == N.PIE_EINVAL
+    rt.close()
+
+
 def test_fork_shares_frozen_pages_and_never_writes_them():
     rt = host_rt(pages=32)
     a = rt.alloc()
