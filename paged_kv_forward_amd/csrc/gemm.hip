@@ -1020,12 +1020,16 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
           for (int a = 0; a < 4; ++a)
             af[ks][a] = *reinterpret_cast<const uint4*>(&X[(a * 16 + r16) * SK_LDX + j * SK_KC + ks * 32 + gq * 8]);
-        uint4 b0 = ring[j].w0, b1 = ring[j].w1;
+        uint4 b0, b1;
         if constexpr (F8) {
-          const uint2 p0 = fp8x4_to_bf16(b0.x, ring[j].s), p1 = fp8x4_to_bf16(b0.y, ring[j].s);
-          const uint2 p2 = fp8x4_to_bf16(b0.z, ring[j].s), p3 = fp8x4_to_bf16(b0.w, ring[j].s);
+          const uint4 c = ring[j].w0;
+          const uint2 p0 = fp8x4_to_bf16(c.x, ring[j].s), p1 = fp8x4_to_bf16(c.y, ring[j].s);
+          const uint2 p2 = fp8x4_to_bf16(c.z, ring[j].s), p3 = fp8x4_to_bf16(c.w, ring[j].s);
           b0 = make_uint4(p0.x, p0.y, p1.x, p1.y);
           b1 = make_uint4(p2.x, p2.y, p3.x, p3.y);
+        } else {
+          b0 = ring[j].w0;
+          b1 = ring[j].w1;
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
