@@ -332,6 +332,88 @@ def fp8_decode_summary(shape, K, W):
             "ms_per_step_by_kernel": {k: round(v[0] / 3, 4) for k, v in pb.items() if v[1]}}
 
 
+def bench_70b(steps, warmup):
+    """Decode at the Llama-3.3-70B shape (workload 5: 32 sequences of 4096
+    prompt tokens, e4m3 KV with per-head scales, argmax, loop-carried steps),
+    once with the bf16 weights and once with their block-scaled FP8 copies
+    attached.  The FP8 copies are made on the device by pie_pack_weight_fp8,
+    which rounds each weight to its block's nearest code (drawing an exactly
+    FP8-representable 70B model on the host would take minutes), so the two
+    runs time the same shapes on slightly different weights.  Prints one
+    JSON line."""
+    import torch
+    import synth
+    from paged_kv_forward_amd.runtime import Pass, PieRuntime, upload_weights
+    torch.cuda.set_device(0)
+    shape = synth.LLAMA_70B
+    wl = synth.workload(5)
+    recipe = synth.WeightRecipe(shape)
+    t0 = time.perf_counter()
+    log("bench 70b: drawing and uploading %.1f B weights with FP8 copies" % (shape.n_params() / 1e9))
+    weights = upload_weights(recipe, "cuda:0", progress=lambda l: (l % 16 == 15) and log("  layer", l + 1),
+                             fp8=True)
+    log("bench 70b: weights ready in %.1f s" % (time.perf_counter() - t0))
+    n, plen = wl.n_seqs, wl.prompt_len[0]
+    K, W = steps, warmup
+    max_ctx = plen + W + K + 8
+    pages = n * ((max_ctx + 15) // 16 + 1)
+    page_bytes = shape.n_layers * 2 * shape.n_kv_heads * 16 * shape.head_dim  # e4m3: one byte
+    per_launch = 2
+    kv_tok = shape.n_kv_heads * shape.head_dim * 2 * shape.n_layers  # e4m3 K and V of one token
+    proj = shape.n_layers * shape.d_model * (2 * shape.q_width + 2 * shape.kv_width + 3 * shape.d_ffn)
+    head = shape.vocab * shape.d_model
+    norms = 2 * shape.d_model * (2 * shape.n_layers + 1)
+    out = {"metric": "decode tokens/s, Llama-3.3-70B shape, batch 32, context 4096, e4m3 KV, 1 GPU",
+           "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W, "higher_is_better": True,
+           "data": "synthetic (seeded N(0,0.02) bf16 weights; FP8 run: their block-scaled FP8 rounding made on "
+                   "the device; uniform random tokens)",
+           "config": {"workload": wl.name, "global_batch": n, "seq_len": plen}}
+    for mode in ("bf16", "fp8"):
+        w = dict(weights)
+        if mode == "bf16":
+            w["layers"] = [{k: v for k, v in lw.items() if k != "fp8"} for lw in weights["layers"]]
+            w.pop("lm_head_fp8", None)
+        rt = PieRuntime(shape, w, pages * page_bytes, max_rows=per_launch * plen, max_seqs=n, max_readout=n,
+                        max_ctx=max_ctx)
+        ws = [rt.alloc() for _ in range(n)]
+        nxt = np.zeros(n, dtype=np.int32)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for b in range(0, n, per_launch):
+            ss = range(b, b + per_launch)
+            toks, _ = rt.forward([Pass(ws[s], wl.prompt(s), [plen - 1], [(0, 1.0, 0)]) for s in ss])
+            nxt[b:b + per_launch] = toks
+        torch.cuda.synchronize()
+        t_pf = time.perf_counter() - t0
+        ws_arr = np.array(ws, dtype=np.uint64)
+        for _ in range(W):
+            nxt[:] = rt.decode_step(ws_arr, nxt)
+        ctx_first = rt.ws_info(ws[0])["len"] + 1
+        tok_dev = torch.tensor(nxt, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            rt.decode_async(ws_arr, tok_dev, tok_dev)
+        rt.sync()
+        torch.cuda.synchronize()
+        t_dec = time.perf_counter() - t0
+        rt.close()
+        ms = t_dec / K * 1e3
+        wbytes = (proj + head) * (1 if mode == "fp8" else 2) + norms
+        if mode == "fp8":
+            wbytes += 4 * (proj + head) // (128 * 128)
+        step_bytes = wbytes + sum(n * (ctx_first + i) for i in range(K)) / K * kv_tok
+        out[mode] = {"value": round(n * K / t_dec, 2), "ms_per_step": round(ms, 3),
+                     "context": [ctx_first, ctx_first + K - 1],
+                     "step_hbm": {"bytes_per_step": int(step_bytes),
+                                  "achieved_gbs": round(step_bytes / (ms / 1e3) / 1e9, 1),
+                                  "frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+                     "prefill_tokens_per_s": round(n * plen / t_pf, 1)}
+        log("bench 70b: %s decode %.2f ms per step, prefill %.0f tokens/s" % (mode, ms, n * plen / t_pf))
+    out["value"] = out["bf16"]["value"]
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -341,6 +423,8 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="(always on; kept for old command lines)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write profiles/ summaries from the rocprofv3 outputs under DIR and exit")
+    ap.add_argument("--model", default="llama31-8b", choices=["llama31-8b", "llama33-70b"],
+                    help="llama33-70b: decode at the 70B shape (workload 5) with bf16 and FP8 weights")
     ap.add_argument("--no-fp8-variant", action="store_true",
                     help="skip the FP8-weight decode measured beside the headline")
     ap.add_argument("--fp8-weights", action="store_true",
@@ -367,6 +451,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+        return
+    if args.model == "llama33-70b":
+        bench_70b(min(args.steps, 32), min(args.warmup, 3))
         return
     import synth
     from paged_kv_forward_amd import _native as N
