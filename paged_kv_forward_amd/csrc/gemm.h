@@ -134,6 +134,13 @@ inline int skinny_swiglu_cols(int N) {
   const int units = (N + 7) / 8, tiles = 256 * ((N + 64 * 256 - 1) / (64 * 256));
   return 8 * ((units + tiles - 1) / tiles);
 }
+// The same for the FP8 tiles whose waves own two 16-row panels (at most 128
+// gate + 128 up columns): used when it gives more than 64 columns a tile
+// (d_ffn 28672: 256 tiles of 112).
+inline int skinny_swiglu_cols_wide(int N) {
+  const int units = (N + 7) / 8, tiles = 256 * ((N + 128 * 256 - 1) / (128 * 256));
+  return 8 * ((units + tiles - 1) / tiles);
+}
 
 // Most K splits of one skinny GEMM.
 constexpr int SK_MAX_SPLITS = 16;

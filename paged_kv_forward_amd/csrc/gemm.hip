@@ -884,8 +884,14 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t w, float s) {
   return make_uint2(pack_bf2(a.x * s, a.y * s), pack_bf2(b.x * s, b.y * s));
 }
 
-template <int EPI, int WPOL, bool F8>
+// W2 (FP8 gate/up only, no split-K): each wave owns two 16-row panels, so a
+// tile holds up to 128 gate + 128 up columns and every activation fragment
+// read from LDS feeds both.
+constexpr int SK_LDC_W = 2 * SK_BN + 4;
+static_assert(64 * SK_LDC_W * 4 <= SK_LDS, "the wide output tile fits in the activation buffers");
+template <int EPI, int WPOL, bool F8, bool W2 = false>
 __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
+  static_assert(!W2 || (F8 && EPI == EPI_SWIGLU), "two panels per wave: FP8 gate/up only");
   // activation groups (two buffers), later reused for the output tile
   __shared__ __attribute__((aligned(16))) uint8_t smem[SK_LDS];
   uint16_t* sX = reinterpret_cast<uint16_t*>(smem);
@@ -942,6 +948,19 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
                                         : make_rsrc(wt, (uint32_t)(packed_elems(wrows, g.K) * 2));
   const __amdgpu_buffer_rsrc_t srs =
       make_rsrc(F8 ? st8 : nullptr, F8 ? (uint32_t)(fp8_scale_blocks(wrows) * kb8 * 4) : 0u);
+  // W2: this lane's rows in the wave's two panels (columns 32 (wave & 3) + 16 p + r16 of the tile's half)
+  uint32_t wb2[2] = {0u, 0u}, sr2[2] = {0u, 0u};
+  bool ok2[2] = {false, false};
+  if constexpr (W2) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int j = (wave & 3) * 32 + p * 16 + r16, c = t * g.cw + j;
+      ok2[p] = j < g.cw && c < g.N;
+      wb2[p] = (uint32_t)(c >> 6) * (uint32_t)kc * 4096u + (uint32_t)((c >> 4) & 3) * 1024u +
+               (uint32_t)(gq * 16 + (c & 15)) * 16u;
+      sr2[p] = (uint32_t)(c >> 7) * (uint32_t)kb8;
+    }
+  }
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(g.a, (uint32_t)((size_t)g.M * g.lda * 2));
   const int c0 = kb / SK_KC;
   // this thread's activation pieces of a group: rows xr0 + 8i, columns xk .. xk + 7
@@ -951,11 +970,19 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   // and s the block's scale (converted to bf16 when the chunk is consumed)
   struct WSlot {
     uint4 w0, w1;
-    float s;
+    float s, s1;
   };
   auto load_w = [&](WSlot& sl, int j) {
     // chunks past nc (this split's end) read zeros; a chunk's padding past K is stored as zeros
-    if constexpr (F8) {
+    if constexpr (W2) {
+      const uint32_t kk = (uint32_t)(c0 + j);
+      sl.w0 = bload16<WPOL>(wrs, j < nc && ok2[0] ? wb2[0] + kk * 4096u : OOB);
+      sl.w1 = bload16<WPOL>(wrs, j < nc && ok2[1] ? wb2[1] + kk * 4096u : OOB);
+      sl.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           srs, j < nc && ok2[0] ? (sr2[0] + kk / 2u) * 4u : OOB, 0, 0));
+      sl.s1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            srs, j < nc && ok2[1] ? (sr2[1] + kk / 2u) * 4u : OOB, 0, 0));
+    } else if constexpr (F8) {
       const uint32_t e = wbase8 + (uint32_t)(c0 + j) * 4096u;
       sl.w0 = bload16<WPOL>(wrs, j < nc && wok ? e : OOB);
       sl.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -980,9 +1007,9 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
     for (int i = 0; i < SK_XP; ++i) *reinterpret_cast<uint4*>(&X[(xr0 + 8 * i) * SK_LDX + xk]) = xv[i];
   };
 
-  f32x4 acc[4];
+  f32x4 acc[4], acc2[4];  // acc2: the second panel (W2)
 #pragma unroll
-  for (int a = 0; a < 4; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < 4; ++a) acc[a] = acc2[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nc > 0) {
     // Whole groups of SK_DEPTH chunks, with no branches inside a group:
@@ -1021,6 +1048,16 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
           for (int a = 0; a < 4; ++a)
             af[ks][a] = *reinterpret_cast<const uint4*>(&X[(a * 16 + r16) * SK_LDX + j * SK_KC + ks * 32 + gq * 8]);
         uint4 b0, b1;
+        if constexpr (W2) {
+          const uint4 c = ring[j].w1;  // second panel: converted and multiplied here
+          const uint2 p0 = fp8x4_to_bf16(c.x, ring[j].s1), p1 = fp8x4_to_bf16(c.y, ring[j].s1);
+          const uint2 p2 = fp8x4_to_bf16(c.z, ring[j].s1), p3 = fp8x4_to_bf16(c.w, ring[j].s1);
+          const uint4 e0 = make_uint4(p0.x, p0.y, p1.x, p1.y), e1 = make_uint4(p2.x, p2.y, p3.x, p3.y);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) acc2[a] = mfma16(af[ks][a], ks ? e1 : e0, acc2[a]);
+        }
         if constexpr (F8) {
           const uint4 c = ring[j].w0;
           const uint2 p0 = fp8x4_to_bf16(c.x, ring[j].s), p1 = fp8x4_to_bf16(c.y, ring[j].s);
@@ -1047,6 +1084,19 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
   }
 
   // the loop ended with a barrier: the activation buffers are free for sC
+  if constexpr (W2) {
+    // gate panels in columns 0..127, up panels in 128..255
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sC[(a * 16 + 4 * gq + i) * SK_LDC_W + wave * 32 + r16] = acc[a][i];
+        sC[(a * 16 + 4 * gq + i) * SK_LDC_W + wave * 32 + 16 + r16] = acc2[a][i];
+      }
+    __syncthreads();
+    epilogue<EPI, 2 * SK_BN, SK_NT>(g, sC, SK_LDC_W, 0, 64, t);
+    return;
+  }
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -1240,6 +1290,12 @@ static void launch_t(const GemmArgs& g0, hipStream_t st) {
 template <int EPI>
 static void launch_skinny(const GemmArgs& g0, hipStream_t st) {
   GemmArgs g = g0;
+  if (EPI == EPI_SWIGLU && g.f8 && g.splits <= 1 && skinny_swiglu_cols_wide(g.N) > 64) {
+    g.cw = skinny_swiglu_cols_wide(g.N);
+    const dim3 gw((g.N + g.cw - 1) / g.cw);
+    hipLaunchKernelGGL((gemm_skinny_kernel<EPI_SWIGLU, CPOL_NT, true, true>), gw, dim3(SK_NT), 0, st, g);
+    return;
+  }
   if (EPI == EPI_SWIGLU) g.cw = skinny_swiglu_cols(g.N);
   const int n_tiles = gemm_n_tiles(EPI, g.N, TILE_SKINNY);
   const dim3 grid(n_tiles, g.splits > 1 ? g.splits : 1);
