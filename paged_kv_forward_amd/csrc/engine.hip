@@ -494,7 +494,10 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
 
   auto set_split = [&](pie::GemmArgs& g, int n_tiles) {
     SplitK sk = choose_split(T, n_tiles, g.K);
-    if ((size_t)n_tiles * sk.splits * 64 * GEMM_BN > L.gpart_floats) sk = {1, g.K};
+    // the reduce kernels address the partials with 32-bit byte offsets
+    if ((size_t)n_tiles * sk.splits * 64 * GEMM_BN > L.gpart_floats ||
+        (size_t)n_tiles * sk.splits * 64 * GEMM_BN * 4 >= ((size_t)1 << 31))
+      sk = {1, g.K};
     g.splits = sk.splits;
     g.k_split = sk.k_split;
   };

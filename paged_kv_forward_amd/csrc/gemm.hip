@@ -1120,17 +1120,51 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs g) {
 // of every split before it adds them, in split order; then the epilogue on
 // those rows.
 constexpr int SK_RED_ROWS = 8;
+
+// Loads the split-K partials of four consecutive columns: split z from byte
+// offset off0 + z * zstride of the partial buffer r (which spans less than
+// 2^31 bytes).  Splits past n, and every split of a lane whose ok is false,
+// read zeros.  The loads carry no branch, so all of them are in flight
+// before the first is used (per-lane conditional loads made the compiler
+// wait on the first two before issuing the rest).
+__device__ __forceinline__ void load_partials(__amdgpu_buffer_rsrc_t r, bool ok, uint32_t off0, uint32_t zstride,
+                                              int n, float4 (&x)[SK_MAX_SPLITS]) {
+#pragma unroll
+  for (int z = 0; z < SK_MAX_SPLITS; ++z) {
+    const uint32_t off = ok && z < n ? off0 + (uint32_t)z * zstride : OOB;
+    x[z] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+}
+
+// Byte size of the split-K partial region of a skinny GEMM with n_tiles
+// tiles (rows of 64, SK_BN columns per tile).
+__host__ __device__ inline size_t skinny_partial_bytes(int splits, int n_tiles) {
+  return (size_t)splits * 64 * n_tiles * SK_BN * 4;
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, int n_tiles) {
   __shared__ __attribute__((aligned(16))) float sC[SK_RED_ROWS * SK_LDC];
-  const int t = blockIdx.x, r0 = blockIdx.y * SK_RED_ROWS;
-  const int row = threadIdx.x / (SK_BN / 4), col = (threadIdx.x % (SK_BN / 4)) * 4;
-  const size_t ld = (size_t)n_tiles * SK_BN, zs = 64 * ld;
-  const float* base = g.partial + (size_t)(r0 + row) * ld + (size_t)t * SK_BN + col;
+  // EPI_QKV: the rows' RoPE table and KV slots, loaded with the partials
+  __shared__ __attribute__((aligned(16))) float2 s_rope[EPI == EPI_QKV ? SK_RED_ROWS * 64 : 1];
+  __shared__ int s_slot[SK_RED_ROWS];
+  const int t = blockIdx.x, r0 = blockIdx.y * SK_RED_ROWS, tid = threadIdx.x;
+  const int row = tid / (SK_BN / 4), col = (tid % (SK_BN / 4)) * 4;
+  const uint32_t ld = (uint32_t)n_tiles * SK_BN;
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.partial, (uint32_t)skinny_partial_bytes(g.splits, n_tiles));
   float4 x[SK_MAX_SPLITS];
-#pragma unroll
-  for (int z = 0; z < SK_MAX_SPLITS; ++z)
-    x[z] = z < g.splits ? *reinterpret_cast<const float4*>(base + z * zs) : make_float4(0.f, 0.f, 0.f, 0.f);
+  load_partials(pr, true, ((uint32_t)(r0 + row) * ld + (uint32_t)t * SK_BN + col) * 4, 64 * ld * 4, g.splits, x);
+  float4 cs = make_float4(0.f, 0.f, 0.f, 0.f);
+  int sl = 0;
+  const int hd2 = g.hd / 2, rope_f4 = SK_RED_ROWS * hd2 / 2;
+  if constexpr (EPI == EPI_QKV) {
+    // rows past M take row M - 1's values, which no store uses
+    if (tid < rope_f4) {
+      const int m = min(r0 + tid / (hd2 / 2), g.M - 1);
+      cs = reinterpret_cast<const float4*>(g.rope_cs)[(size_t)m * (hd2 / 2) + tid % (hd2 / 2)];
+    }
+    if (tid < SK_RED_ROWS) sl = g.slot[min(r0 + tid, g.M - 1)];
+  }
   float4 v = x[0];
 #pragma unroll
   for (int z = 1; z < SK_MAX_SPLITS; ++z) {
@@ -1140,8 +1174,15 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, int n_ti
     v.w += x[z].w;
   }
   *reinterpret_cast<float4*>(&sC[row * SK_LDC + col]) = v;
+  if constexpr (EPI == EPI_QKV) {
+    if (tid < rope_f4) reinterpret_cast<float4*>(s_rope)[tid] = cs;
+    if (tid < SK_RED_ROWS) s_slot[tid] = sl;
+  }
   __syncthreads();
-  epilogue<EPI, SK_BN, 256>(g, sC, SK_LDC, r0, SK_RED_ROWS, t);
+  if constexpr (EPI == EPI_QKV)
+    epilogue<EPI, SK_BN, 256>(g, sC, SK_LDC, r0, SK_RED_ROWS, t, QkvStaged{s_rope, s_slot, nullptr});
+  else
+    epilogue<EPI, SK_BN, 256>(g, sC, SK_LDC, r0, SK_RED_ROWS, t);
 }
 
 // Split-K reduce of an EPI_RESID skinny GEMM fused with the RMSNorm that
@@ -1153,23 +1194,31 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, int n_ti
 // writes the normed bf16 row.  N <= RN_NT * 4 * RN_MAXC.
 constexpr int RN_NT = 1024, RN_MAXC = 2;
 __global__ __launch_bounds__(RN_NT) void skinny_reduce_norm_kernel(GemmArgs g, int n_tiles) {
-  __shared__ float s_ssq[RN_NT * 4 * RN_MAXC / 64];
+  __shared__ __attribute__((aligned(16))) float s_ssq[RN_NT * 4 * RN_MAXC / 64];
   __shared__ float s_r;
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int N = g.N, n_grp = N / 64;
-  const size_t ld = (size_t)n_tiles * SK_BN, zs = 64 * ld;
+  const uint32_t ld = (uint32_t)n_tiles * SK_BN;
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.partial, (uint32_t)skinny_partial_bytes(g.splits, n_tiles));
+  // y and the gain of this thread's columns, before the partials, from
+  // addresses kept inside the row (columns past N are not used)
+  float4 yo[RN_MAXC];
+  uint2 gw[RN_MAXC];
+#pragma unroll
+  for (int c = 0; c < RN_MAXC; ++c) {
+    const int col = (tid + c * RN_NT) * 4, cc = col < N ? col : 0;
+    yo[c] = *reinterpret_cast<const float4*>(g.y_out + (size_t)m * g.ldy + cc);
+    gw[c] = *reinterpret_cast<const uint2*>(g.next_gain + cc);
+  }
   float4 yn[RN_MAXC];
 #pragma unroll
   for (int c = 0; c < RN_MAXC; ++c) {
+    yn[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c * RN_NT * 4 >= N) continue;  // uniform
     const int col = (tid + c * RN_NT) * 4;
     const bool ok = col < N;
-    const float* p = g.partial + (size_t)m * ld + col;
     float4 x[SK_MAX_SPLITS];
-#pragma unroll
-    for (int z = 0; z < SK_MAX_SPLITS; ++z)
-      x[z] = ok && z < g.splits ? *reinterpret_cast<const float4*>(p + z * zs) : make_float4(0.f, 0.f, 0.f, 0.f);
-    float4* yp = reinterpret_cast<float4*>(g.y_out + (size_t)m * g.ldy + (ok ? col : 0));
-    const float4 yo = ok ? *yp : make_float4(0.f, 0.f, 0.f, 0.f);
+    load_partials(pr, ok, ((uint32_t)m * ld + col) * 4, 64 * ld * 4, g.splits, x);
     float4 v = x[0];
 #pragma unroll
     for (int z = 1; z < SK_MAX_SPLITS; ++z) {
@@ -1178,8 +1227,8 @@ __global__ __launch_bounds__(RN_NT) void skinny_reduce_norm_kernel(GemmArgs g, i
       v.z += x[z].z;
       v.w += x[z].w;
     }
-    yn[c] = make_float4(yo.x + v.x, yo.y + v.y, yo.z + v.z, yo.w + v.w);
-    if (ok) *yp = yn[c];
+    yn[c] = make_float4(yo[c].x + v.x, yo[c].y + v.y, yo[c].z + v.z, yo[c].w + v.w);
+    if (ok) *reinterpret_cast<float4*>(g.y_out + (size_t)m * g.ldy + col) = yn[c];
     float sq = yn[c].x * yn[c].x + yn[c].y * yn[c].y + yn[c].z * yn[c].z + yn[c].w * yn[c].w;
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
@@ -1190,8 +1239,18 @@ __global__ __launch_bounds__(RN_NT) void skinny_reduce_norm_kernel(GemmArgs g, i
   }
   __syncthreads();
   if (tid == 0) {
+    // column order, four LDS values per read
     float sum = 0.f;
-    for (int c = 0; c < n_grp; ++c) sum += s_ssq[c];
+    int c = 0;
+#pragma unroll 4
+    for (; c + 4 <= n_grp; c += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(&s_ssq[c]);
+      sum += q.x;
+      sum += q.y;
+      sum += q.z;
+      sum += q.w;
+    }
+    for (; c < n_grp; ++c) sum += s_ssq[c];
     s_r = 1.0f / sqrtf(sum / (float)N + g.eps);
   }
   __syncthreads();
@@ -1200,11 +1259,10 @@ __global__ __launch_bounds__(RN_NT) void skinny_reduce_norm_kernel(GemmArgs g, i
   for (int c = 0; c < RN_MAXC; ++c) {
     const int col = (tid + c * RN_NT) * 4;
     if (col >= N) continue;
-    const uint2 gw = *reinterpret_cast<const uint2*>(g.next_gain + col);
     const float4 a = yn[c];
     *reinterpret_cast<uint2*>(g.x_out + (size_t)m * g.N + col) =
-        make_uint2(pack_bf2(a.x * r * bf2f(gw.x & 0xffffu), a.y * r * bf2f(gw.x >> 16)),
-                   pack_bf2(a.z * r * bf2f(gw.y & 0xffffu), a.w * r * bf2f(gw.y >> 16)));
+        make_uint2(pack_bf2(a.x * r * bf2f(gw[c].x & 0xffffu), a.y * r * bf2f(gw[c].x >> 16)),
+                   pack_bf2(a.z * r * bf2f(gw[c].y & 0xffffu), a.w * r * bf2f(gw[c].y >> 16)));
   }
 }
 
