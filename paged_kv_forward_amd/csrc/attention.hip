@@ -228,28 +228,43 @@ __device__ __forceinline__ void compute_pair(const PairRaw<HD, E4M3>& f, const u
   }
 }
 
-// Entries [e_begin, e_end) of sequence s, two at a time through a two-slot ring.
+// Entries [sb, se) (at most 64, page-table slice sl loaded), two at a time
+// through a two-slot ring.
 template <int HD, bool E4M3, int RB>
-__device__ __forceinline__ void attend_range(const AttnArgs& a, int e_begin, int e_end, uint32_t kofs,
+__device__ __forceinline__ void attend_slice(const AttnArgs& a, const PtSlice& sl, int sb, int se, uint32_t kofs,
                                              uint32_t vofs, const uint4 (&qf)[RB][HD / 32],
                                              f32x4 (&oacc)[RB][HD / 16], float (&m_run)[RB],
                                              float (&l_run)[RB], const int (&qidx)[RB], float scale_log2,
                                              int lane) {
-  for (int sb = e_begin; sb < e_end; sb += 64) {
-    const int se = min(e_end, sb + 64);
+  const int n_pairs = (se - sb + 1) / 2;
+  PairRaw<HD, E4M3> s0, s1;
+  load_pair<HD, E4M3>(s0, a, sl, sb, se, kofs, vofs, lane);
+  load_pair<HD, E4M3>(s1, a, sl, sb + 2, se, kofs, vofs, lane);
+  // straight-line pairs of slots; pairs past n_pairs are absent (all masked)
+  for (int pp = 0; pp < n_pairs; pp += 2) {
+    compute_pair<HD, E4M3, RB>(s0, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
+    load_pair<HD, E4M3>(s0, a, sl, sb + 2 * (pp + 2), se, kofs, vofs, lane);
+    compute_pair<HD, E4M3, RB>(s1, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
+    load_pair<HD, E4M3>(s1, a, sl, sb + 2 * (pp + 3), se, kofs, vofs, lane);
+  }
+}
+
+// Entries [e_begin, e_end) of sequence s.  sl0 is the page-table slice of
+// the first 64 entries, which the caller loads ahead of its other loads.
+template <int HD, bool E4M3, int RB>
+__device__ __forceinline__ void attend_range(const AttnArgs& a, const PtSlice& sl0, int e_begin, int e_end,
+                                             uint32_t kofs, uint32_t vofs, const uint4 (&qf)[RB][HD / 32],
+                                             f32x4 (&oacc)[RB][HD / 16], float (&m_run)[RB],
+                                             float (&l_run)[RB], const int (&qidx)[RB], float scale_log2,
+                                             int lane) {
+  if (e_begin < e_end)
+    attend_slice<HD, E4M3, RB>(a, sl0, e_begin, min(e_end, e_begin + 64), kofs, vofs, qf, oacc, m_run, l_run, qidx,
+                               scale_log2, lane);
+  for (int sb = e_begin + 64; sb < e_end; sb += 64) {
     PtSlice sl;
-    load_slice(sl, a, sb, se, lane);
-    const int n_pairs = (se - sb + 1) / 2;
-    PairRaw<HD, E4M3> s0, s1;
-    load_pair<HD, E4M3>(s0, a, sl, sb, se, kofs, vofs, lane);
-    load_pair<HD, E4M3>(s1, a, sl, sb + 2, se, kofs, vofs, lane);
-    // straight-line pairs of slots; pairs past n_pairs are absent (all masked)
-    for (int pp = 0; pp < n_pairs; pp += 2) {
-      compute_pair<HD, E4M3, RB>(s0, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
-      load_pair<HD, E4M3>(s0, a, sl, sb + 2 * (pp + 2), se, kofs, vofs, lane);
-      compute_pair<HD, E4M3, RB>(s1, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
-      load_pair<HD, E4M3>(s1, a, sl, sb + 2 * (pp + 3), se, kofs, vofs, lane);
-    }
+    load_slice(sl, a, sb, min(e_end, sb + 64), lane);
+    attend_slice<HD, E4M3, RB>(a, sl, sb, min(e_end, sb + 64), kofs, vofs, qf, oacc, m_run, l_run, qidx, scale_log2,
+                               lane);
   }
 }
 
@@ -259,6 +274,19 @@ __device__ __forceinline__ void load_q(uint4 (&qf)[HD / 32], const uint16_t* qro
 #pragma unroll
   for (int i = 0; i < STEPS; ++i)
     qf[i] = ok ? *reinterpret_cast<const uint4*>(qrow + (4 * i + g) * 8) : make_uint4(0, 0, 0, 0);
+}
+
+// The same through a buffer descriptor r over one token's q row: a lane
+// whose ok is false reads zeros from an out-of-range offset.  The loads carry
+// no branch, so the page loads after them need not wait for them.
+template <int HD>
+__device__ __forceinline__ void load_q_row(uint4 (&qf)[HD / 32], __amdgpu_buffer_rsrc_t r, uint32_t head_off,
+                                           bool ok, int g) {
+  constexpr int STEPS = HD / 32;
+#pragma unroll
+  for (int i = 0; i < STEPS; ++i)
+    qf[i] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(r, ok ? head_off + (uint32_t)(4 * i + g) * 16 : 0xFFFFFFF0u, 0, 0));
 }
 
 // ---------------------------------------------------------------- decode
@@ -280,11 +308,21 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
   const int4 it = a.items[blockIdx.x];
   const int kvh = blockIdx.y;
   const int s = it.x, e_begin = it.y, e_end = it.z, part = it.w;
+  // this wave's run of entry pairs and the page-table slice it starts with,
+  // loaded before the sequence's row (which q's address needs): the two
+  // lookups overlap instead of following each other
+  const int n_pairs = (e_end - e_begin + 1) / 2;
+  const int ppw = (n_pairs + 3) / 4;
+  const int wb = e_begin + 2 * min(n_pairs, wave * ppw);
+  const int we = min(e_end, e_begin + 2 * min(n_pairs, (wave + 1) * ppw));
+  PtSlice sl0;
+  load_slice(sl0, a, wb, min(we, wb + 64), lane);
   const int G = a.nq / a.nkv;
   const int row = a.seq_row0[s];
 
   uint4 qf[1][HD / 32];
-  load_q<HD>(qf[0], a.q + ((size_t)row * a.nq + kvh * G + n) * HD, n < G, g);
+  load_q_row<HD>(qf[0], page_rsrc(a.q + (size_t)row * a.nq * HD, (uint32_t)(a.nq * HD * 2)),
+                 (uint32_t)((kvh * G + n) * HD * 2), n < G, g);
   const int qidx[1] = {INT_MAX};
   f32x4 oacc[1][DB];
 #pragma unroll
@@ -295,11 +333,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
   const uint32_t kofs = (uint32_t)(kvh * PS * HD) * EB;
   const uint32_t vofs = (uint32_t)(a.nkv * PS * HD + kvh * HD * PS) * EB;
 
-  const int n_pairs = (e_end - e_begin + 1) / 2;
-  const int ppw = (n_pairs + 3) / 4;
-  const int wb = e_begin + 2 * min(n_pairs, wave * ppw);
-  const int we = min(e_end, e_begin + 2 * min(n_pairs, (wave + 1) * ppw));
-  attend_range<HD, E4M3, 1>(a, wb, we, kofs, vofs, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
+  attend_range<HD, E4M3, 1>(a, sl0, wb, we, kofs, vofs, qf, oacc, m_run, l_run, qidx, scale_log2, lane);
 
   float l = l_run[0];
   l += __shfl_xor(l, 16, 64);
