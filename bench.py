@@ -77,6 +77,8 @@ def cpu_baseline(shape, recipe, n_seq=4, n_layers=8):
 ATTN_SOURCES = ["paged_kv_forward_amd/csrc/attention.hip", "paged_kv_forward_amd/csrc/attention.h",
                 "paged_kv_forward_amd/csrc/common.h"]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attn_decode_hbm_counters.json")
+# back-to-back runs of each decode-attention launch in the roofline's timed pass
+ATTN_REPS = 8
 TRACE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace_c2 -o c2 -- "
              "python3 <repo>/bench.py --steps 20 --warmup 5 --no-cpu-baseline")
 PMC_CMDS = [
@@ -169,7 +171,8 @@ def summarize(out_dir):
     lines = ["# Kernel trace of the decode benchmark (Llama-3.1-8B shape, batch 64)", "",
              "Command (on one MI355X, from the repository root):", "", "    " + TRACE_CMD, "",
              "The run includes the 64 x 2048-token prefill (16 launches of 4 sequences) and 68 decode",
-             "steps (5 warm-up + 20 timed + 20 host-loop + 20 with HIP events + 3 per-class), then the",
+             "steps (5 warm-up + 20 timed + 20 host-loop + 20 with HIP events, each decode-attention launch",
+             "run %d times back to back there, + 3 per-class), then the" % ATTN_REPS,
              "FP8-weight variant (its own prefill and 28 decode steps; kernels `<..., true>`).  Per kernel:",
              "calls, average and total duration from `c2_kernel_stats.csv`.", "",
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
@@ -209,6 +212,22 @@ def summarize(out_dir):
                   "", "| kernel | launches per step | us per step |", "|---|---|---|"]
         for k, (n, d) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
             lines.append("| `%s` | %d | %.1f |" % (k, n, d))
+    # the roofline's timed pass of the traced run: bf16 decode steps 46-65
+    # (5 warm-up, 20 timed, 20 host-loop steps before it)
+    bf = [st for st in steps if not is_f8(st)]
+    att = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+           for st in bf[45:65] for r in st if "attn_decode_kernel" in r["Kernel_Name"]]
+    if att:
+        lines += ["", "Decode attention in the pass that `bench.py` times its roofline over (bf16 decode steps "
+                  "46-65 of this run): %d launches, average %.2f us in this trace." % (len(att), sum(att) / len(att))]
+        # the traced run's own JSON line, when its output was kept as out_dir/trace.log
+        log_path = os.path.join(out_dir, "trace.log")
+        js = [l for l in open(log_path).read().splitlines() if l.startswith('{"metric"')] \
+            if os.path.exists(log_path) else []
+        if js:
+            rf = json.loads(js[-1])["roofline"]
+            lines.append("The same run's JSON line: `avg_launch_ms` %.5f (%.2f us), %s."
+                         % (rf["avg_launch_ms"], rf["avg_launch_ms"] * 1e3, rf["timed_over"]))
     with open(os.path.join(prof, "decode_llama8b_b64_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     summarize_prefill(trace, prof)
@@ -547,9 +566,12 @@ def main():
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t0
     log("bench: %d host-loop decode steps in %.3f s" % (K, t_host))
-    # second timed pass of K steps with HIP events around every decode-attention
-    # launch on the library's stream (timed calls launch kernels directly)
+    # third timed pass of K steps: HIP events on the library's stream around
+    # every decode-attention launch, which runs ATTN_REPS times back to back
+    # there (same inputs and outputs), so that the events' own cost (several
+    # microseconds of idle GPU per interval) is shared by ATTN_REPS launches
     ctx_prof = rt.ws_info(ws[0])["len"] + 1
+    rt.profile_repeat(ATTN_REPS)
     rt.profile_enable(["attn_decode"])
     t0 = time.perf_counter()
     for _ in range(K):
@@ -558,6 +580,7 @@ def main():
     t_prof = time.perf_counter() - t0
     prof = rt.profile_read()
     rt.profile_enable([])
+    rt.profile_repeat(1)
 
     # algorithmic bytes of decode attention: every K and V element of every
     # sequence's context once, plus q in and o out
@@ -565,7 +588,8 @@ def main():
     qo = N_SEQ * shape.q_width * 2 * 2
     ctx_sum = sum(N_SEQ * (ctx_first + i) for i in range(K))
     ctx_sum_prof = sum(N_SEQ * (ctx_prof + i) for i in range(K))
-    attn_bytes = (ctx_sum_prof * kv_tok + K * qo) * shape.n_layers
+    # over the timed pass, where each launch ran ATTN_REPS times
+    attn_bytes = (ctx_sum_prof * kv_tok + K * qo) * shape.n_layers * ATTN_REPS
     attn_ms, attn_n = prof["attn_decode"]
     attn_gbs = attn_bytes / (attn_ms / 1e3) / 1e9 if attn_ms > 0 else 0.0
     per_launch = attn_bytes / max(attn_n, 1)
@@ -628,8 +652,9 @@ def main():
                                       if traffic else "counters not taken for this kernel's sources"),
                      "bytes_per_launch": int(per_launch),
                      "avg_launch_ms": round(attn_ms / max(attn_n, 1), 5),
-                     "timed_over": "a third pass of %d decode steps (context %d..%d) with HIP events "
-                                   "around each launch" % (K, ctx_prof, ctx_prof + K - 1),
+                     "timed_over": "a third pass of %d decode steps (context %d..%d): HIP events around "
+                                   "each launch, which runs %d times back to back between them"
+                                   % (K, ctx_prof, ctx_prof + K - 1, ATTN_REPS),
                      "ms_per_step_events_pass": round(t_prof / K * 1e3, 4)},
         "step_hbm": {"bytes_per_step": int(step_bytes),
                      "achieved_gbs": round(step_bytes / (ms_step / 1e3) / 1e9, 1),

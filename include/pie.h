@@ -337,6 +337,15 @@ enum pie_kernel_class {
  * (0 turns timing off and clears totals). */
 int pie_profile_enable(pie_ctx* ctx, uint32_t class_mask);
 
+/* While decode attention (PIE_K_ATTN_DECODE) is timed, run each of its
+ * launches reps times back to back inside its timed interval (1 <= reps <= 64;
+ * 1 until set).  The repeats read the same q and KV and write the same output,
+ * so results do not change, and the class's launch count advances by reps.
+ * The event records around an interval idle the GPU for several microseconds;
+ * over reps launches that cost is shared, and the average per launch comes
+ * close to the kernel's own duration.  Errors: PIE_EINVAL. */
+int pie_profile_repeat(pie_ctx* ctx, int32_t reps);
+
 /* Per class: total milliseconds and number of launches timed since enabling.
  * Synchronises the stream.  ms and counts are host arrays [PIE_K_NUM_CLASSES]. */
 int pie_profile_read(pie_ctx* ctx, double* ms, int64_t* counts);

@@ -185,7 +185,12 @@ Layout make_layout(const pie_model_desc& d, const pie_limits& l) {
 // Events of the timed launches of one call (timed calls are never captured).
 struct EventSink {
   std::vector<hipEvent_t> ev;
-  std::vector<std::pair<int, size_t>> marks;  // (class, index of the start event)
+  struct Mark {
+    int k;         // class
+    size_t first;  // index of the start event
+    int n;         // launches between the two events
+  };
+  std::vector<Mark> marks;
   size_t used = 0;
 };
 
@@ -248,6 +253,7 @@ struct pie_ctx {
   int n_parts = 0;
   // profiling: events bracketing timed launches, recorded into a sink
   uint32_t prof_mask = 0;
+  int prof_reps = 1;  // back-to-back runs of each timed decode-attention launch
   EventSink sink;
   hipStream_t cur = nullptr;    // stream launches go to while enqueueing
   double prof_ms[PIE_K_NUM_CLASSES] = {0};
@@ -285,15 +291,19 @@ hipEvent_t next_event(EventSink* k) {
 struct Timed {
   pie_ctx* c;
   bool on;
-  size_t first = 0;
+  size_t first = 0, mark = 0;
   Timed(pie_ctx* c_, int k) : c(c_), on(((c_->prof_mask >> k) & 1u) && !c_->capturing) {
     if (on) {
       hipEvent_t a = next_event(&c->sink), b = next_event(&c->sink);
       if (!a || !b) { on = false; return; }
       first = c->sink.used - 2;
-      c->sink.marks.push_back({k, first});
+      c->sink.marks.push_back({k, first, 1});
+      mark = c->sink.marks.size() - 1;
       (void)hipEventRecord(a, c->cur);
     }
+  }
+  void set_launches(int n) {
+    if (on) c->sink.marks[mark].n = n;
   }
   ~Timed() {
     if (on) (void)hipEventRecord(c->sink.ev[first + 1], c->cur);
@@ -303,9 +313,9 @@ struct Timed {
 void collect_profile(pie_ctx* c, EventSink& k) {
   for (auto& m : k.marks) {
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, k.ev[m.second], k.ev[m.second + 1]) == hipSuccess) {
-      c->prof_ms[m.first] += ms;
-      c->prof_n[m.first] += 1;
+    if (hipEventElapsedTime(&ms, k.ev[m.first], k.ev[m.first + 1]) == hipSuccess) {
+      c->prof_ms[m.k] += ms;
+      c->prof_n[m.k] += m.n;
     }
   }
   (void)hipGetLastError();  // a failed timing query must not surface in a later call
@@ -565,8 +575,14 @@ int enqueue(pie_ctx* c, float* out_logits, int flags) {
       at.n_combine = (int)(c->comb.size() / 4);
       {
         Timed tm(c, PIE_K_ATTN_DECODE);
-        pie::launch_attn_decode(at, st);
-        pie::launch_attn_combine(at, st);
+        // when timed, the pair may run several times back to back (same
+        // inputs, same outputs): the events' fixed cost spreads over them
+        const int reps = tm.on ? c->prof_reps : 1;
+        for (int r = 0; r < reps; ++r) {
+          pie::launch_attn_decode(at, st);
+          pie::launch_attn_combine(at, st);
+        }
+        tm.set_launches(reps);
       }
       if ((rc = check_launch(c, flags, "decode attention"))) return rc;
     }
@@ -1039,6 +1055,13 @@ int pie_profile_enable(pie_ctx* c, uint32_t mask) {
     c->prof_ms[k] = 0;
     c->prof_n[k] = 0;
   }
+  return PIE_OK;
+}
+
+int pie_profile_repeat(pie_ctx* c, int32_t reps) {
+  CTX_OK(c);
+  if (reps < 1 || reps > 64) return set_err(PIE_EINVAL, "pie_profile_repeat: reps must be in [1, 64]");
+  c->prof_reps = reps;
   return PIE_OK;
 }
 

@@ -372,6 +372,10 @@ class PieRuntime:
             mask |= 1 << N.KERNEL_CLASSES.index(c)
         check(N.lib().pie_profile_enable(self.ctx, mask))
 
+    def profile_repeat(self, reps: int) -> None:
+        """Timed decode-attention launches run reps times back to back."""
+        check(N.lib().pie_profile_repeat(self.ctx, int(reps)))
+
     def profile_read(self) -> Dict[str, Tuple[float, int]]:
         ms = (ctypes.c_double * N.PIE_K_NUM_CLASSES)()
         cnt = (ctypes.c_int64 * N.PIE_K_NUM_CLASSES)()

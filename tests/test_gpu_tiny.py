@@ -441,6 +441,32 @@ def test_tiny_async_out_of_range_device_token(torch_cuda):
     rt.close()
 
 
+def test_tiny_timed_attention_repeats_change_nothing(torch_cuda):
+    """With decode attention timed and pie_profile_repeat(4), each decode
+    attention launch runs four times back to back: the decode step's logits
+    are bit-identical to an untimed step on an identical working set, and the
+    class counts four launches per layer."""
+    recipe = RECIPES["gains1"]
+    shape = recipe.shape
+    from paged_kv_forward_amd.runtime import Pass
+    prompt = synth.prompt_tokens(2, 40, PROMPT, shape.vocab)
+    rt = make_runtime(shape, recipe, torch_cuda)
+    a, b = rt.alloc(), rt.alloc()
+    toks, _ = rt.forward([Pass(w, prompt, [PROMPT - 1], [(0, 1.0, 0)]) for w in (a, b)])
+    nxt = [int(toks[0])]
+    _, la = rt.forward([Pass(a, nxt, [0], [(0, 1.0, 0)])], want_logits=True)
+    rt.profile_repeat(4)
+    rt.profile_enable(["attn_decode"])
+    _, lb = rt.forward([Pass(b, nxt, [0], [(0, 1.0, 0)])], want_logits=True)
+    prof = rt.profile_read()
+    rt.profile_enable([])
+    rt.profile_repeat(1)
+    np.testing.assert_array_equal(la, lb)
+    ms, n = prof["attn_decode"]
+    assert n == 4 * shape.n_layers and ms > 0
+    rt.close()
+
+
 def test_tiny_prefix_lookup_reuses_pages_exactly(torch_cuda):
     """A request that starts with another request's committed prefix gets the
     prefix's pages through pie_prefix_lookup and runs only its own tokens: its

@@ -95,6 +95,20 @@ def test_fp8_weight_sizes_and_argument_checks():
     rt.close()
 
 
+def test_profile_repeat_argument_checks():
+    """pie_profile_repeat takes 1..64 back-to-back runs; anything else is
+    PIE_EINVAL and leaves the setting as it was."""
+    L = N.lib()
+    rt = PieRuntime(synth.TINY, None, 64 * 1024 * 1024, 128, 4, 8, 256)
+    assert L.pie_profile_repeat(rt.ctx, 0) == N.PIE_EINVAL
+    assert L.pie_profile_repeat(rt.ctx, 65) == N.PIE_EINVAL
+    assert L.pie_profile_repeat(rt.ctx, -3) == N.PIE_EINVAL
+    assert L.pie_profile_repeat(None, 4) == N.PIE_EINVAL
+    assert L.pie_profile_repeat(rt.ctx, 1) == N.PIE_OK
+    assert L.pie_profile_repeat(rt.ctx, 64) == N.PIE_OK
+    rt.close()
+
+
 def test_fork_shares_frozen_pages_and_never_writes_them():
     rt = host_rt(pages=32)
     a = rt.alloc()
