@@ -17,15 +17,33 @@ __global__ __launch_bounds__(256) void embed_kernel(const uint16_t* __restrict__
                                                     int n_ss) {
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int id = tok[t];
-  const bool ok = id >= 0 && id < vocab;
-  const uint16_t* src = E + (size_t)(ok ? id : 0) * d;
   float* dst = y + (size_t)t * d;
-  for (int c = wave; c < n_ss; c += 4) {
-    const int k = c * 64 + lane;
-    const float a = ok ? bf2f(src[k]) : 0.f;
-    dst[k] = a;
-    const float s = wave_sum(a * a);
-    if (lane == 0) ss[(size_t)t * n_ss + c] = s;
+  if (id < 0 || id >= vocab) {  // whole workgroup: a zero row
+    for (int c = wave; c < n_ss; c += 4) {
+      dst[c * 64 + lane] = 0.f;
+      if (lane == 0) ss[(size_t)t * n_ss + c] = 0.f;
+    }
+    return;
+  }
+  const uint16_t* src = E + (size_t)id * d;
+  // the loads of U chunks go out before the first is used (a chunk at a
+  // time made every chunk a full memory round trip)
+  constexpr int U = 8;
+  for (int c0 = wave; c0 < n_ss; c0 += 4 * U) {
+    float a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = min(c0 + 4 * u, n_ss - 1);  // past the row: a valid chunk, not used
+      a[u] = bf2f(src[c * 64 + lane]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 4 * u;
+      if (c >= n_ss) break;
+      dst[c * 64 + lane] = a[u];
+      const float s = wave_sum(a[u] * a[u]);
+      if (lane == 0) ss[(size_t)t * n_ss + c] = s;
+    }
   }
 }
 
