@@ -1273,12 +1273,22 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
                                                       uint16_t* __restrict__ x) {
   const int m = blockIdx.x;
   const int src = rows ? rows[m] : m;
-  __shared__ float s_r;
-  if (threadIdx.x == 0) {
-    float s = 0.f;
-    for (int c = 0; c < n_ss; ++c) s += ss[(size_t)src * n_ss + c];
-    s_r = 1.0f / sqrtf(s / (float)d + eps);
+  __shared__ float s_r, s_part[256];
+  // the per-64-column sums go through LDS 256 at a time (one coalesced load
+  // per thread), then thread 0 adds them in column order; from global memory
+  // one at a time, every add waited for its own load
+  float s = 0.f;
+  for (int c0 = 0; c0 < n_ss; c0 += 256) {
+    if (c0 + (int)threadIdx.x < n_ss) s_part[threadIdx.x] = ss[(size_t)src * n_ss + c0 + threadIdx.x];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int n = min(256, n_ss - c0);
+#pragma unroll 8
+      for (int c = 0; c < n; ++c) s += s_part[c];
+    }
+    __syncthreads();
   }
+  if (threadIdx.x == 0) s_r = 1.0f / sqrtf(s / (float)d + eps);
   __syncthreads();
   const float r = s_r;
   for (int k = threadIdx.x * 8; k < d; k += 256 * 8) {
