@@ -64,7 +64,9 @@ enum pie_epilogue_kind { PIE_EPI_ARGMAX = 0, PIE_EPI_GUMBEL_MAX = 1 };
 /* pie_forward flags */
 enum pie_forward_flags {
   PIE_FLAG_NO_LAUNCH = 1,     /* validate, reserve, pack and update working sets, launch nothing;
-                                 out_tokens are set to -1.  The only mode of a host-only context. */
+                                 out_tokens are set to -1.  The only mode of a host-only context,
+                                 and refused (PIE_EINVAL) on a context with weights, whose
+                                 committed pages must hold computed KV. */
   PIE_FLAG_LOGITS_DEVICE = 2, /* out_logits is a device pointer (default: host pointer)           */
   PIE_FLAG_SYNC_DEBUG = 4     /* synchronise and check for errors after every kernel              */
 };
@@ -123,7 +125,8 @@ typedef struct pie_limits {
  * address order.  Returns the packed size in bytes (0 if n or k <= 0). */
 size_t pie_packed_weight_bytes(int32_t n, int32_t k);
 
-/* Convert one weight matrix to the tiled layout: src is DEVICE bf16 [n][k]
+/* Convert one weight matrix ("Write a model in Poem", section 3 Weights: the
+ * checkpoint's [out][in] tensor) to the tiled layout: src is DEVICE bf16 [n][k]
  * row-major, dst DEVICE memory of pie_packed_weight_bytes(n, k) bytes; they
  * must not overlap.  Runs on hip_stream (NULL = the null stream) and
  * synchronises it.  Needs no context.  Errors: PIE_EINVAL, PIE_EHIP. */
@@ -169,13 +172,19 @@ typedef struct pie_fp8_weights {
  * PIE_ESTATE (poisoned context). */
 int pie_attach_fp8_weights(pie_ctx* ctx, const pie_fp8_weights* w);
 
-/* Bytes of one KV page over all layers (K and V, every KV head, page_size tokens). */
+/* Bytes of one KV page over all layers (K and V, every KV head, page_size
+ * tokens): the per-layer K and V of the caches declaration ("Write a model in
+ * Poem", section 4 State (caches)) for page_size tokens; 0 on a bad desc. */
 size_t pie_kv_page_bytes(const pie_model_desc* desc);
 
-/* Device workspace bytes pie_init needs for these limits (0 on bad input). */
+/* Device workspace bytes pie_init needs for these limits (0 on bad input):
+ * the activations of one batched launch ("How Pie thinks", "Batching is still
+ * the engine's job") plus the attention and GEMM partials. */
 size_t pie_workspace_bytes(const pie_model_desc* desc, const pie_limits* limits);
 
-/* Create a context.
+/* Create a context over one model ("Write a model in Poem", section 1 MODELS
+ * for the shape, section 3 Weights for the tensors, section 4 for the KV
+ * space) on one GPU.
  *  kv_arena/kv_bytes: DEVICE memory for the page pool; pages = kv_bytes / pie_kv_page_bytes.
  *  workspace/ws_bytes: DEVICE scratch of at least pie_workspace_bytes(desc, limits).
  *  hip_stream: the hipStream_t every launch goes to (NULL = the null stream).
@@ -187,7 +196,8 @@ int pie_init(const pie_model_desc* desc, const pie_weights* weights, void* kv_ar
              size_t kv_bytes, void* workspace, size_t ws_bytes, const pie_limits* limits,
              void* hip_stream, pie_ctx** out);
 
-/* Destroy a context; outstanding working sets are released.  NULL is a no-op. */
+/* Destroy a context; outstanding working sets are released.  NULL is a no-op.
+ * Caller-owned memory (weights, arena, workspace, stream) is not freed. */
 int pie_destroy(pie_ctx* ctx);
 
 /* WorkingSet(): a new, empty working set (len = frozen_len = 0). */
@@ -200,11 +210,18 @@ int pie_alloc_working_set(pie_ctx* ctx, pie_ws* out);
  * fresh page, so a partly filled shared page stays partly filled in both. */
 int pie_fork(pie_ctx* ctx, pie_ws parent, pie_ws* child);
 
-/* Release a working set; pages whose reference count drops to 0 return to the pool. */
+/* Release a working set; pages whose reference count drops to 0 return to the
+ * pool.  ("How Pie thinks", section 4 Working sets: a working set is a
+ * sequence's model state, owned by its program until dropped; shared frozen
+ * pages outlive the set as long as a fork still holds them.)  Errors:
+ * PIE_EINVAL (stale or null handle). */
 int pie_free_working_set(pie_ctx* ctx, pie_ws ws);
 
 /* Roll the writable buffer back to new_len tokens (frozen_len <= new_len <= len).
- * Pages left empty return to the pool.  Errors: PIE_EINVAL. */
+ * ("How Pie thinks", section 4 Working sets: the writable buffer holds
+ * uncommitted tokens that may be rolled back, as a speculative draft is;
+ * the frozen prefix never changes.)  Pages left empty return to the pool.
+ * Errors: PIE_EINVAL (stale handle, new_len outside [frozen_len, len]). */
 int pie_truncate(pie_ctx* ctx, pie_ws ws, int32_t new_len);
 
 typedef struct pie_ws_stats {
@@ -213,10 +230,16 @@ typedef struct pie_ws_stats {
   int32_t n_pages;    /* page-table entries                           */
 } pie_ws_stats;
 
-/* Working-set state; page_ids (nullable, host, n_pages entries) receives the
- * page table's page ids in order. */
+/* Working-set state ("How Pie thinks", section 4 Working sets: the committed
+ * prefix length is frozen_len, everything after it is the writable buffer);
+ * page_ids (nullable, host, n_pages entries) receives the page table's page
+ * ids in order, which shows that a fork shares its parent's pages.
+ * Errors: PIE_EINVAL (stale handle or null stats). */
 int pie_ws_info(pie_ctx* ctx, pie_ws ws, pie_ws_stats* stats, int32_t* page_ids);
 
+/* Page-pool counters ("How Pie thinks", section 4 Working sets: a fork shares
+ * the frozen prefix without copying it, so kv_bytes_copied stays 0 and a
+ * fork takes no page from the free list). */
 typedef struct pie_pool_stats {
   int64_t pages_total;
   int64_t pages_free;
@@ -224,6 +247,7 @@ typedef struct pie_pool_stats {
   int64_t kv_bytes_copied;      /* KV bytes ever copied between pages (always 0)  */
 } pie_pool_stats;
 
+/* Errors: PIE_EINVAL (null out). */
 int pie_pool_stats_get(pie_ctx* ctx, pie_pool_stats* out);
 
 /* Epilogue of one readout row.  ARGMAX: the lowest index of the largest logit.
@@ -294,8 +318,9 @@ int pie_forward(pie_ctx* ctx, const pie_pass* passes, int32_t n_passes, int32_t*
 int pie_decode_async(pie_ctx* ctx, const pie_ws* ws, int32_t n, const int32_t* tokens_in, int32_t* tokens_out,
                      const pie_epilogue* epi, float* logits_dev);
 
-/* Wait until every enqueued step has run; PIE_EHIP (and a poisoned context)
- * if one of them failed. */
+/* Wait until every enqueued step has run ("How Pie thinks", section 3: the
+ * awaited result of a submitted pass); PIE_EHIP (and a poisoned context) if
+ * one of them failed. */
 int pie_sync(pie_ctx* ctx);
 
 /* Prefix sharing across requests ("How Pie thinks", section 4 Working sets:
@@ -314,10 +339,13 @@ int pie_sync(pie_ctx* ctx);
  * Errors: PIE_EINVAL (null argument, n < 1, token id out of range). */
 int pie_prefix_lookup(pie_ctx* ctx, const int32_t* tokens, int32_t n, pie_ws* out, int32_t* n_shared);
 
+/* Message of the last failed call on this thread ("" if none). */
 const char* pie_last_error(void);
 
 /* ---------------------------------------------------------------------------
- * Measurement hooks
+ * Measurement hooks.  Not operations of the pages (which publish no
+ * measurement of this path): they time the kernel classes of the forward
+ * pass so its throughput can be set against the HBM and matrix-core peaks.
  * ------------------------------------------------------------------------- */
 
 /* Kernel classes a context can time with HIP events recorded on its stream. */
@@ -351,7 +379,9 @@ int pie_profile_repeat(pie_ctx* ctx, int32_t reps);
 int pie_profile_read(pie_ctx* ctx, double* ms, int64_t* counts);
 
 /* ---------------------------------------------------------------------------
- * Debug views (used by tests)
+ * Debug views (used by tests).  pie_debug_plan exposes the packed batch of
+ * "How Pie thinks" ("Batching is still the engine's job"); pie_debug_philox
+ * the noise of the Gumbel-max epilogue (section 5 Epilogues).
  * ------------------------------------------------------------------------- */
 
 /* The metadata the packer built for the last pie_forward of this context

@@ -10,7 +10,9 @@ from ctypes import (POINTER, Structure, c_char_p, c_double, c_float, c_int, c_in
                     c_size_t, c_uint32, c_uint64, c_void_p)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpie.so")
+# PIE_LIBRARY may name another build of the same library (the sanitized
+# host build of the CPU tests); there is no fallback of any kind.
+LIB_PATH = os.environ.get("PIE_LIBRARY") or os.path.join(HERE, "libpie.so")
 
 PIE_OK, PIE_EINVAL, PIE_ENOMEM, PIE_EHIP, PIE_ESTATE = 0, -1, -2, -3, -4
 PIE_KV_BF16, PIE_KV_E4M3 = 0, 1

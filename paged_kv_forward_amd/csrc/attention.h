@@ -44,6 +44,10 @@ struct AttnArgs {
 // Rows handled by one prefill workgroup (tokens x query heads of a group).
 constexpr int PREFILL_ROWS = 256;
 
+// Most partials one decode sequence may be split into (the combine kernel
+// holds a weight per partial and query head in LDS).
+constexpr int DECODE_MAX_SPLITS = 64;
+
 void launch_attn_decode(const AttnArgs& a, hipStream_t st);
 void launch_attn_combine(const AttnArgs& a, hipStream_t st);
 void launch_attn_prefill(const AttnArgs& a, hipStream_t st);

@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
 
 // Merges the partials of a sequence split over several workgroups.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  constexpr int MAXP = 64;
+  constexpr int MAXP = DECODE_MAX_SPLITS;  // the host never plans more
   __shared__ float s_w[MAXP][16];
   __shared__ float s_den[16];
   const int4 c = a.combine[blockIdx.x];

@@ -45,8 +45,8 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
 // the grid of 3 stored mantissa bits (binades 2^-6 .. 2^8; quantum 2^-9 below 2^-6).
 __device__ __forceinline__ uint8_t f2e4m3(float x) {
   uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  if (!(x == x)) return (uint8_t)(sign | 0x7fu);  // NaN stays NaN (before the clamp, which would drop it)
   float a = fminf(fabsf(x), 448.0f);
-  if (!(a == a)) return 0x7f;  // NaN
   uint32_t code;
   if (a < 0.015625f) {               // below 2^-6: subnormal grid, quantum 2^-9
     code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8 (8 = smallest normal)

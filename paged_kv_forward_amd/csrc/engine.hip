@@ -338,7 +338,7 @@ int check_launch(pie_ctx* c, int flags, const char* what) {
   return PIE_OK;
 }
 
-void build_work(pie_ctx* c) {
+int build_work(pie_ctx* c) {
   const pie::Plan& p = c->plan;
   const int G = c->d.n_q_heads / c->d.n_kv_heads;
   const int tpw = std::max(1, pie::PREFILL_ROWS / G);
@@ -365,12 +365,16 @@ void build_work(pie_ctx* c) {
     const int n_new = p.seq_row0[s + 1] - p.seq_row0[s];
     const int e0 = p.seq_pg0[s], e1 = p.seq_pg0[s + 1];
     if (n_new == 1) {
-      const int ns = std::max(1, (e1 - e0 + pps - 1) / pps);
+      // a long sequence in a batch of short ones takes longer runs, so that
+      // it never has more partials than the combine kernel merges
+      const int cap = ((e1 - e0 + pie::DECODE_MAX_SPLITS - 1) / pie::DECODE_MAX_SPLITS + 1) / 2 * 2;
+      const int pps_s = std::max(pps, cap);
+      const int ns = std::max(1, (e1 - e0 + pps_s - 1) / pps_s);
       if (ns == 1) {
         c->dec.insert(c->dec.end(), {s, e0, e1, -1});
       } else {
         for (int k = 0; k < ns; ++k)
-          c->dec.insert(c->dec.end(), {s, e0 + k * pps, std::min(e1, e0 + (k + 1) * pps), c->n_parts + k});
+          c->dec.insert(c->dec.end(), {s, e0 + k * pps_s, std::min(e1, e0 + (k + 1) * pps_s), c->n_parts + k});
         c->comb.insert(c->comb.end(), {s, c->n_parts, ns, 0});
         c->n_parts += ns;
       }
@@ -398,6 +402,10 @@ void build_work(pie_ctx* c) {
   });
   for (size_t i = 0; i < pre.size(); ++i)
     for (int k = 0; k < 4; ++k) c->pre[4 * i + k] = pre[i][k];
+  for (size_t i = 0; i + 3 < c->comb.size(); i += 4)
+    if (c->comb[i + 2] > pie::DECODE_MAX_SPLITS)
+      return set_err(PIE_EINVAL, "pie_forward: decode split plan exceeds the combine limit");
+  return PIE_OK;
 }
 
 template <typename T>
@@ -409,7 +417,7 @@ void put(int32_t* base, size_t off, const std::vector<T>& v) {
 int stage(pie_ctx* c) {
   const pie::Plan& p = c->plan;
   const Layout& L = c->lay;
-  build_work(c);
+  if (int rc = build_work(c)) return rc;
   if ((int)(c->dec.size() / 4) > L.max_dec_items || (int)(c->pre.size() / 4) > L.max_pre_items)
     return set_err(PIE_ENOMEM, "pie_forward: attention work list exceeds the workspace");
   int32_t* h = c->pinned;
@@ -979,6 +987,10 @@ int pie_forward(pie_ctx* c, const pie_pass* passes, int32_t n_passes, int32_t* o
   CTX_OK(c);
   if (!(flags & PIE_FLAG_NO_LAUNCH) && c->host_only)
     return set_err(PIE_ESTATE, "pie_forward: a host-only context can only plan (PIE_FLAG_NO_LAUNCH)");
+  // planning without computing would commit tokens whose KV no kernel wrote,
+  // and the prefix registry could then hand those pages to another request
+  if ((flags & PIE_FLAG_NO_LAUNCH) && !c->host_only)
+    return set_err(PIE_EINVAL, "pie_forward: PIE_FLAG_NO_LAUNCH is only for host-only contexts");
   pie::PackLimits pl{c->lim.max_rows, c->lim.max_seqs, c->lim.max_readout, c->lim.max_ctx,
                      c->lay.max_pe, c->d.vocab};
   int64_t want_ro = 0;

@@ -1457,8 +1457,13 @@ void launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, hipStr
                      pieces);
 }
 
-// One workgroup per 128 x 128 block: the block's largest |w|, its power-of-two
-// scale, then every code at its place in the FP8 tiled layout.
+// One workgroup per 128 x 128 block: the block's largest finite |w|,
+// its power-of-two scale 2^e -- e the least integer with max |w| <= 448 * 2^e,
+// but at least FP8_MIN_EXP so that every code times the scale is a bf16 value
+// -- then every code at its place in the FP8 tiled layout.  The codes are
+// w * 2^-e rounded to e4m3 (exact scaling by ldexp, so no factor overflows);
+// an infinite w saturates to +-448 and NaN keeps the NaN code.
+constexpr int FP8_MIN_EXP = -124;
 __global__ __launch_bounds__(256) void pack_weight_fp8_kernel(const uint16_t* __restrict__ src,
                                                               uint8_t* __restrict__ codes,
                                                               float* __restrict__ scales, int N, int K) {
@@ -1468,27 +1473,30 @@ __global__ __launch_bounds__(256) void pack_weight_fp8_kernel(const uint16_t* __
   float amax = 0.f;
   for (int i = tid; i < 128 * 128; i += 256) {
     const int n = bn * 128 + i / 128, k = bk * 128 + i % 128;
-    if (n < N && k < K) amax = fmaxf(amax, fabsf(bf2f(src[(size_t)n * K + k])));
+    const float v = n < N && k < K ? fabsf(bf2f(src[(size_t)n * K + k])) : 0.f;
+    if (v < INFINITY) amax = fmaxf(amax, v);  // NaN and infinities left out
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   if (lane == 0) s_max[wave] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-  // least e with amax <= 448 * 2^e (products with powers of two are exact)
-  int e = 0;
+  // least e with amax <= 448 * 2^e: amax / 448 = f * 2^x with 0.5 <= f < 1,
+  // so amax <= 448 * 2^x and, unless f is exactly 0.5, not <= 448 * 2^(x-1).
+  // 448 * 2^k is exact in float, or infinite past its range (which no
+  // finite amax exceeds), so the comparisons are exact.
+  int e = FP8_MIN_EXP;
   if (amax > 0.f) {
     int x;
     frexpf(amax / 448.f, &x);
-    e = x;
-    while (e > -126 && amax <= 448.f * ldexpf(1.f, e - 1)) --e;
-    while (amax > 448.f * ldexpf(1.f, e)) ++e;
+    while (amax > ldexpf(448.f, x)) ++x;
+    while (amax <= ldexpf(448.f, x - 1)) --x;
+    e = max(x, FP8_MIN_EXP);
   }
-  const float inv = ldexpf(1.f, -e);
   if (tid == 0) scales[(size_t)bn * ((K + 127) / 128) + bk] = ldexpf(1.f, e);
   for (int i = tid; i < 128 * 128; i += 256) {
     const int n = bn * 128 + i / 128, k = bk * 128 + i % 128;
-    if (n < N && k < K) codes[packed_index_fp8(n, k, kc)] = f2e4m3(bf2f(src[(size_t)n * K + k]) * inv);
+    if (n < N && k < K) codes[packed_index_fp8(n, k, kc)] = f2e4m3(ldexpf(bf2f(src[(size_t)n * K + k]), -e));
   }
 }
 

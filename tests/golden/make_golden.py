@@ -7,10 +7,19 @@ run it layer-major in one pass (weights drawn once per layer); the GPU test
 feeds the same tokens.  By the incremental-decode invariant of the oracle,
 reading out row i of that chunk equals decoding token by token.
 
-    python tests/golden/make_golden.py c2 [c3 c4 c5] [c2:2 ...]
+    python tests/golden/make_golden.py c2 [c3 c4 c4long c5 c5ctx512] [c2:1 ...]
 
 "cN:L" writes the same case for the model cut to its first L layers
-(<name>_first<L>.npz).  Output: tests/golden/<name>.npz with, per checked readout row, the oracle's
+(<name>_first<L>.npz).  The checked rows follow the sampling plan of the
+parity tests: the 8B decode checks sequences 0, 21, 42 and 63 at every one of
+their 129 readouts; the fork checks the prefix's own readout and branches 0,
+4 and 9 over the suffix and all 64 Gumbel steps; the mix checks prompts 0 and
+7 and the shortest, a middle and the longest decode row; the 70B decode
+checks one sequence at the full 4096-token context and, with the prompt cut
+to 512 tokens, four sequences over 96 steps each (enough rows for some
+oracle margins to clear the 80-layer noise floor).
+
+Output: tests/golden/<name>.npz with, per checked readout row, the oracle's
 token, its top-2 margin, the float32 logits at a fixed seeded subset of
 vocabulary indices, and the full float32 logits for a few rows.
 """
@@ -77,12 +86,13 @@ def finish(name, rows, full_rows, vocab, meta):
           int(np.sum(out["margin"] < 2e-2)), flush=True)
 
 
-def c2(decode_steps=3, seqs=(0, 63)):
-    """Llama-3.1-8B decode: sequences of 2048 prompt tokens + teacher-fed decode steps."""
+def c2(decode_steps=None, seqs=(0, 21, 42, 63)):
+    """Llama-3.1-8B decode: sequences of 2048 prompt tokens + teacher-fed decode steps
+    (all 128 at full depth; 3 when cut to 2 layers, 8 when cut to 1)."""
     wl = synth.workload(2)
     shape = model(wl)
-    if LAYERS is not None:
-        seqs = (0, 21, 42, 63)
+    if decode_steps is None:
+        decode_steps = {None: wl.decode_steps, 2: 3, 1: 8}.get(LAYERS, 8)
     w = SynthWeights(synth.WeightRecipe(shape))
     num = default_numerics(shape)
     chunks = []
@@ -99,20 +109,26 @@ def c2(decode_steps=3, seqs=(0, 63)):
         for k in range(decode_steps + 1):
             rows.append(dict(seq=s, step=k, kind=synth.EPI_ARGMAX, temp=1.0, seed=0, lane=0,
                              logits=logits[ci][k]))
-    full = [0, decode_steps, decode_steps + 1, 2 * decode_steps + 1]
+    per = decode_steps + 1
+    full = sorted({0, decode_steps, per, 2 * per - 1, len(rows) - 1})
     finish("c2_decode_8b", rows, full, shape.vocab,
            dict(seqs=list(seqs), decode_steps=decode_steps))
 
 
-def c3(decode_steps=2, branches=(0, 4, 9)):
-    """Fork at the 8B shape: 8192-token prefix, 256-token suffix per branch, Gumbel T=0.7."""
+def c3(decode_steps=None, branches=(0, 4, 9)):
+    """Fork at the 8B shape: 8192-token prefix (read out at its last token with
+    argmax), 256-token suffix per branch, Gumbel-max at T=0.7 over the suffix's
+    readout and every decode step (64 at full depth; 2 when cut to 2 layers)."""
     wl = synth.workload(3)
     shape = model(wl)
+    if decode_steps is None:
+        decode_steps = 2 if LAYERS == 2 else wl.decode_steps
     w = SynthWeights(synth.WeightRecipe(shape))
     num = default_numerics(shape)
     pre = wl.prefix()
     P = len(pre)
-    chunks = [Chunk(pre, np.arange(P), -1, [])]
+    with_prefix = LAYERS != 2
+    chunks = [Chunk(pre, np.arange(P), -1, [P - 1] if with_prefix else [])]
     for b in branches:
         toks = np.concatenate([wl.prompt(b), teacher_tokens(3, b, decode_steps, shape.vocab)])
         n = len(toks)
@@ -121,27 +137,34 @@ def c3(decode_steps=2, branches=(0, 4, 9)):
     logits = forward_chunks(w, chunks, num)
     print("c3 oracle %.0f s" % (time.time() - t0), flush=True)
     rows = []
+    if with_prefix:
+        # the prefix pass's own readout: sequence -1, step -1, argmax
+        rows.append(dict(seq=-1, step=-1, kind=synth.EPI_ARGMAX, temp=1.0, seed=0, lane=0,
+                         logits=logits[0][0]))
     for ci, b in enumerate(branches):
         for k in range(decode_steps + 1):
             rows.append(dict(seq=b, step=k, kind=synth.EPI_GUMBEL, temp=0.7,
                              seed=synth.epilogue_seed(wl.branch_seed[b], k), lane=0,
                              logits=logits[1 + ci][k]))
-    finish("c3_fork_8b", rows, [0, decode_steps + 1], shape.vocab,
-           dict(branches=list(branches), decode_steps=decode_steps))
+    full = sorted({0, 1, decode_steps + 1, len(rows) - 1})
+    finish("c3_fork_8b", rows, full, shape.vocab,
+           dict(branches=list(branches), decode_steps=decode_steps, prefix_readout=int(with_prefix)))
 
 
-def c4(seqs=None):
+def c4(seqs=None, name="c4_mix_8b"):
     """Mix at the 8B shape: prompts 0 and 7 (4096 tokens, read out at the end of the
-    last 512-chunk), and two decode rows (the shortest context and one other) read out
-    at each of the 8 launches."""
+    last 512-chunk), and decode rows (the shortest context, one other and -- cut to
+    1 layer -- the longest) read out at each of the 8 launches."""
     wl = synth.workload(4)
     shape = model(wl)
     w = SynthWeights(synth.WeightRecipe(shape))
     num = default_numerics(shape)
     dec_ctx = np.array(wl.prompt_len[8:])
     shortest = 8 + int(np.argmin(dec_ctx))
+    longest = 8 + int(np.argmax(dec_ctx))
     other = 8 + 37
-    seqs = seqs or [0, 7, shortest, other]
+    if seqs is None:
+        seqs = [0, 7, shortest, other] + ([longest] if LAYERS == 1 else [])
     chunks, meta_rows = [], []
     for s in seqs:
         if s < 8:
@@ -164,20 +187,34 @@ def c4(seqs=None):
             rows.append(dict(seq=s, step=k, kind=wl.epi_kind[s], temp=1.0,
                              seed=synth.epilogue_seed(wl.branch_seed[s], k), lane=0,
                              logits=logits[ci][j]))
-    finish("c4_mix_8b", rows, [0, 1, 2, len(rows) - 1], shape.vocab, dict(seqs=seqs))
+    finish(name, rows, sorted({0, 1, 2, len(rows) - 1}), shape.vocab, dict(seqs=seqs))
 
 
-def c5(decode_steps=2, seqs=(0,)):
-    """Llama-3.3-70B decode with e4m3 KV: 4096 prompt tokens + teacher-fed decode steps."""
+def c4long():
+    """The mix's longest-context decode row (context 8147), stored apart from the
+    other checked rows of the full-depth mix (c4_mix_8b_long.npz)."""
+    wl = synth.workload(4)
+    longest = 8 + int(np.argmax(np.array(wl.prompt_len[8:])))
+    c4(seqs=[longest], name="c4_mix_8b_long")
+
+
+def c5(decode_steps=None, seqs=None, ctx=None, name="c5_decode_70b"):
+    """Llama-3.3-70B decode with e4m3 KV: the prompt (4096 tokens, or its first
+    `ctx`) + teacher-fed decode steps."""
     wl = synth.workload(5)
     shape = model(wl)
+    if decode_steps is None:
+        decode_steps = 8 if LAYERS == 1 else 2
+    if seqs is None:
+        seqs = (0, 31) if LAYERS == 1 else (0,)
     w = SynthWeights(synth.WeightRecipe(shape))
     num = default_numerics(shape)
+    n_prompt = ctx or wl.prompt_len[0]
     chunks = []
     for s in seqs:
-        toks = np.concatenate([wl.prompt(s), teacher_tokens(5, s, decode_steps, shape.vocab)])
+        toks = np.concatenate([wl.prompt(s)[:n_prompt], teacher_tokens(5, s, decode_steps, shape.vocab)])
         n = len(toks)
-        chunks.append(Chunk(toks, np.arange(n), -1, list(range(wl.prompt_len[s] - 1, n))))
+        chunks.append(Chunk(toks, np.arange(n), -1, list(range(n_prompt - 1, n))))
     t0 = time.time()
     logits = forward_chunks(w, chunks, num)
     print("c5 oracle %.0f s" % (time.time() - t0), flush=True)
@@ -186,8 +223,16 @@ def c5(decode_steps=2, seqs=(0,)):
         for k in range(decode_steps + 1):
             rows.append(dict(seq=s, step=k, kind=synth.EPI_ARGMAX, temp=1.0, seed=0, lane=0,
                              logits=logits[ci][k]))
-    finish("c5_decode_70b", rows, [0, decode_steps], shape.vocab,
-           dict(seqs=list(seqs), decode_steps=decode_steps))
+    meta = dict(seqs=list(seqs), decode_steps=decode_steps)
+    if ctx:
+        meta["ctx"] = ctx
+    finish(name, rows, sorted({0, decode_steps, len(rows) - 1}), shape.vocab, meta)
+
+
+def c5ctx512():
+    """The 70B decode with every prompt cut to its first 512 tokens: four
+    sequences, 96 decode steps each (388 readouts)."""
+    c5(decode_steps=96, seqs=(0, 10, 21, 31), ctx=512, name="c5_decode_70b_ctx512")
 
 
 if __name__ == "__main__":

@@ -31,13 +31,17 @@ NOISE_FACTOR = 2.0
 
 def noise_bounds(conditioning_jsons):
     """(logit tolerance, token margin) from the measured float32-twin noise of
-    the given conditioning files (the largest of them), never below 2e-2."""
+    the given conditioning files (the largest of them).  Where the twin stays
+    below 2e-2 the bounds are 2e-2 itself; above it, twice the twin's largest
+    difference (tolerance) and that difference (margin)."""
     import json
     twin = 0.0
     for path in conditioning_jsons:
         with open(path) as f:
             twin = max(twin, float(json.load(f)["max_abs_dlogit"]))
-    return max(TOL_LOGITS, NOISE_FACTOR * twin), max(TAU_LOGIT, twin)
+    if twin < TOL_LOGITS:
+        return TOL_LOGITS, TAU_LOGIT
+    return NOISE_FACTOR * twin, twin
 
 
 def noise_mean_bound(conditioning_jsons):
@@ -69,21 +73,27 @@ class Report:
     def add(self, gpu_tok, ref_tok, margin, tau, gpu_logits=None, ref_logits=None, tag=""):
         self.rows += 1
         if gpu_logits is not None and ref_logits is not None:
-            self.max_err = max(self.max_err, float(np.max(np.abs(gpu_logits - ref_logits))))
+            err = np.abs(np.asarray(gpu_logits, np.float64) - np.asarray(ref_logits, np.float64))
+            self.max_err = max(self.max_err, float(np.max(err)))
+            self.sum_err += float(np.mean(err))
         if margin < tau:
             self.excluded += 1
             return
         if int(gpu_tok) != int(ref_tok):
             self.mismatched.append((tag, int(gpu_tok), int(ref_tok), float(margin)))
 
-    def check(self, tol=TOL_LOGITS, max_excluded_frac=0.6, mean_tol=None):
+    def check(self, tol=TOL_LOGITS, max_excluded_frac=0.6, mean_tol=None, min_compared=1):
         mean = self.sum_err / max(self.rows, 1)
-        say("parity: rows=%d excluded=%d mismatched=%d max|dlogit|=%.3g mean|dlogit|=%.3g" %
-            (self.rows, self.excluded, len(self.mismatched), self.max_err, mean))
+        compared = self.rows - self.excluded
+        say("parity: rows=%d tokens compared=%d excluded=%d mismatched=%d max|dlogit|=%.3g "
+            "(bound %.3g) mean|dlogit|=%.3g%s" %
+            (self.rows, compared, self.excluded, len(self.mismatched), self.max_err, tol, mean,
+             "" if mean_tol is None else " (bound %.3g)" % mean_tol))
         assert not self.mismatched, self.mismatched[:10]
         assert self.max_err <= tol, self.max_err
         if mean_tol is not None:
             assert mean <= mean_tol, (mean, mean_tol)
+        assert compared >= min_compared, (compared, min_compared)
         assert self.excluded <= max_excluded_frac * max(self.rows, 1)
 
 

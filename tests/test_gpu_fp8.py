@@ -16,6 +16,7 @@ import pytest
 import synth
 from oracle.epilogue import apply
 from oracle.run import Session, SynthWeights, default_numerics
+from tests.parity import say
 from tests.test_gpu_tiny import make_runtime
 
 pytestmark = pytest.mark.gpu
@@ -121,3 +122,71 @@ def test_fp8_weights_70b_two_layers_e4m3_kv_decode_equals_bf16(torch_cuda):
     rt_fp8.close()
     np.testing.assert_array_equal(got, ref)
 
+
+
+def _fp8_layout_index(n, k, kc):
+    """Byte of code (n, k) in the FP8 tiled layout documented in include/pie.h
+    and gemm.h: 4 KiB blocks of 64 x 64 at block (n / 64, k / 64), each
+    [4 panels of 16 rows][64 lanes][16 bytes], lane = (k % 32) / 8 * 16 + n % 16,
+    byte = (k % 64) / 32 * 8 + k % 8."""
+    r, kk = n % 64, k % 64
+    return (((n // 64) * kc + k // 64) * 4096 + (r // 16) * 1024 + (((kk % 32) // 8) * 16 + r % 16) * 16
+            + (kk // 32) * 8 + kk % 8)
+
+
+def _rounding_inputs(n, k, seed):
+    """bf16 [n][k] values the quantiser has to round: normals whose spread
+    changes by row, an all-zero block, a tiny block (exponent floor), ties
+    between neighbouring codes, a block maximum exactly 448 * 2^e, bf16
+    subnormals, negative values that round to zero, NaN and infinities."""
+    from oracle.numerics import round_bf16
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((n, k)) * np.exp(rng.uniform(-6, 6, size=(n, 1)))
+    if n > 128 and k > 128:
+        w[:128, 128:256] = 0.0
+        w[128:256, :128] *= 1e-37
+    # block (0, 0): spread 10, maximum set to 448 * 2^-2 exactly, so its scale is 2^-2
+    w[:128, :128] = rng.standard_normal(w[:128, :128].shape) * 10.0
+    w = round_bf16(w)
+    w[0, 0] = 448.0 * 0.25
+    w[0, 1:5] = np.array([1.0625, 1.1875, -1.1875, 2.0 ** -10]) * 0.25
+    w[0, 5] = 2.0 ** -133          # smallest bf16 subnormal
+    w[0, 6] = -2.0 ** -30           # rounds to a signed zero
+    w[1, :3] = [np.nan, np.inf, -np.inf]
+    assert np.nanmax(np.abs(np.where(np.isinf(w[:128, :128]), 0, w[:128, :128]))) == 112.0
+    return w
+
+
+@pytest.mark.parametrize("n,k", [(300, 260), (128, 128), (64, 1000), (257, 130), (16, 64)])
+def test_pack_weight_fp8_rounds_like_the_oracle(torch_cuda, n, k):
+    """pie_pack_weight_fp8 on matrices it must round: every code byte (in the
+    documented tiled layout) and every block scale equals the oracle's
+    quantiser (oracle/fp8.py), and the padding of partial blocks is zero."""
+    import torch
+    from oracle import fp8
+    from oracle.numerics import bf16_bits
+    from paged_kv_forward_amd import _native as N
+    L = N.lib()
+    w = _rounding_inputs(n, k, seed=n * 1000 + k)
+    bits = bf16_bits(w)
+    nanpos = np.isnan(w)
+    bits[nanpos] = 0x7FC0
+    src = torch.from_numpy(bits.view(np.int16).copy()).to("cuda")
+    codes = torch.empty(L.pie_packed_weight_fp8_bytes(n, k), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(L.pie_fp8_scale_count(n, k), dtype=torch.float32, device="cuda")
+    codes.fill_(0xA5)  # the call clears it
+    st = torch.cuda.current_stream().cuda_stream
+    assert L.pie_pack_weight_fp8(src.data_ptr(), codes.data_ptr(), scales.data_ptr(), n, k, st) == 0
+    got_codes = codes.cpu().numpy()
+    got_scales = scales.cpu().numpy().reshape(-(-n // 128), -(-k // 128))
+    vals, want_bits, want_scales, _ = fp8.quantise(w)
+    np.testing.assert_array_equal(got_scales.view(np.uint32), want_scales.view(np.uint32))
+    kc = -(-k // 64)
+    nn, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    idx = _fp8_layout_index(nn, kk, kc)
+    got = got_codes[idx]
+    np.testing.assert_array_equal(got, want_bits)
+    pad = np.ones(got_codes.size, dtype=bool)
+    pad[idx.reshape(-1)] = False
+    assert not got_codes[pad].any()
+    say("pack fp8 %dx%d: %d codes, %d scales, %d padding bytes match" % (n, k, got.size, got_scales.size, int(pad.sum())))

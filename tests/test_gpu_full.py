@@ -39,6 +39,10 @@ def shape_of(wl, g):
 
 # Which oracle-twin measurements bound which stored case (same model and depth).
 CONDITIONING = {
+    "c2_decode_8b_first1": ["c2_first1"],
+    "c3_fork_8b_first1": ["c3_first1"],
+    "c4_mix_8b_first1": ["c2_first1", "c3_first1"],
+    "c5_decode_70b_first1": ["c5_first1"],
     "c2_decode_8b_first2": ["c2_first2"],
     "c3_fork_8b_first2": ["c3_first2", "c2_first2"],
     "c4_mix_8b_first2": ["c2_first2", "c3_first2"],
@@ -47,25 +51,36 @@ CONDITIONING = {
     "c3_fork_8b": ["c2"],
     "c4_mix_8b": ["c2"],
     "c5_decode_70b": ["c5_ctx512"],
+    "c5_decode_70b_ctx512": ["c5_ctx512"],
 }
+
+# The one case whose stored rows cannot clear its token margin: the 70B shape
+# at full depth and the full 4096-token context stores 3 rows (one sequence;
+# its oracle run takes hours), and at 80 layers the float32 noise floor (1.29)
+# is near the logits' own spread (1.8), so no oracle margin clears it.  It is
+# held by the logit bounds alone; the same model and depth compare tokens in
+# c5_decode_70b_ctx512 (388 rows at a 512-token context).
+LOGITS_ONLY = {"c5_decode_70b"}
+# At 80 layers almost every oracle margin lies below the noise floor, so the
+# token comparison there may exclude nearly all rows (it must still compare
+# some, except in LOGITS_ONLY).
+DEEP_70B = {"c5_decode_70b", "c5_decode_70b_ctx512"}
 
 
 def bounds(name):
-    """(max |dlogit| bound, token margin, mean |dlogit| bound, largest allowed
-    fraction of rows excluded from the token comparison)."""
+    """(max |dlogit| bound, token margin, mean |dlogit| bound, least number of
+    rows whose token is compared, largest fraction of rows excluded)."""
     paths = [os.path.join(GOLDEN, "conditioning_%s.json" % c) for c in CONDITIONING[name]]
     paths = [p for p in paths if os.path.exists(p)]
     if not paths:
         pytest.skip("float32 noise floor for %s not measured" % name)
     tol, tau = noise_bounds(paths)
     mean_tol = noise_mean_bound(paths)
-    # The 70B shape at full depth has a float32 noise floor (about 1.3) near the
-    # logits' own spread (1.8), so few oracle margins clear it and the token
-    # comparison may exclude every row; the mean bound carries that case.
-    max_excl = 1.0 if name == "c5_decode_70b" else 0.6
+    min_compared = 0 if name in LOGITS_ONLY else 1
+    max_excl = 1.0 if name in DEEP_70B else 0.6
     say("%s: bounds |dlogit| <= %.4f, mean |dlogit| <= %.4f, tokens compared at margin >= %.4f"
         % (name, tol, mean_tol, tau))
-    return tol, tau, mean_tol, max_excl
+    return tol, tau, mean_tol, min_compared, max_excl
 
 
 def row_of(g, seq, step):
@@ -91,11 +106,19 @@ def compare(rep, g, row, tok, logits, tag, tau):
     rep.add(tok, g["token"][row], float(g["margin"][row]), tau, tag=tag)
 
 
+_WEIGHTS = {}  # the last uploaded model's device weights, reused by the next case of that model
+
+
 def make_runtime(shape, n_seqs, max_ctx, max_rows, max_readout, pages=None):
     from paged_kv_forward_amd import _native as N
     from paged_kv_forward_amd.runtime import PieRuntime, model_desc, upload_weights
-    say("uploading %s weights (%d layers)" % (shape.name, shape.n_layers))
-    w = upload_weights(synth.WeightRecipe(shape))
+    if shape.name not in _WEIGHTS:
+        _WEIGHTS.clear()
+        import torch
+        torch.cuda.empty_cache()
+        say("uploading %s weights (%d layers)" % (shape.name, shape.n_layers))
+        _WEIGHTS[shape.name] = upload_weights(synth.WeightRecipe(shape))
+    w = _WEIGHTS[shape.name]
     page_bytes = N.lib().pie_kv_page_bytes(ctypes.byref(model_desc(shape)))
     if pages is None:
         pages = n_seqs * ((max_ctx + 15) // 16 + 1)
@@ -112,10 +135,11 @@ def decode_case(name, config_id, per_launch):
     g = golden(name)
     wl = synth.workload(config_id)
     shape = shape_of(wl, g)
-    tol, tau, mean_tol, max_excl = bounds(name)
+    tol, tau, mean_tol, min_cmp, max_excl = bounds(name)
     steps = int(g["meta_decode_steps"])
     checked = [int(s) for s in g["meta_seqs"]]
-    n, ctx = wl.n_seqs, wl.prompt_len[0]
+    n = wl.n_seqs
+    ctx = int(g["meta_ctx"]) if "meta_ctx" in g.files else wl.prompt_len[0]
     rt = make_runtime(shape, n, ctx + steps + 8, per_launch * ctx, n)
     ws = [rt.alloc() for _ in range(n)]
     rep = Report()
@@ -123,7 +147,7 @@ def decode_case(name, config_id, per_launch):
     say("%s: prefill %d x %d in launches of %d" % (name, n, ctx, per_launch))
     for b in range(0, n, per_launch):
         ss = list(range(b, b + per_launch))
-        toks, _ = rt.forward([Pass(ws[s], wl.prompt(s), [ctx - 1], [(0, 1.0, 0)]) for s in ss],
+        toks, _ = rt.forward([Pass(ws[s], wl.prompt(s)[:ctx], [ctx - 1], [(0, 1.0, 0)]) for s in ss],
                              logits_out=logits[:per_launch])
         lg = logits[:per_launch].cpu().numpy()
         for j, s in enumerate(ss):
@@ -138,7 +162,7 @@ def decode_case(name, config_id, per_launch):
         for s in checked:
             compare(rep, g, row_of(g, s, k), toks[s], lg[s], ("decode", k, s), tau)
     rt.close()
-    rep.check(tol=tol, max_excluded_frac=max_excl, mean_tol=mean_tol)
+    rep.check(tol=tol, max_excluded_frac=max_excl, mean_tol=mean_tol, min_compared=min_cmp)
 
 
 def fork_case(name):
@@ -150,7 +174,7 @@ def fork_case(name):
     g = golden(name)
     wl = synth.workload(3)
     shape = shape_of(wl, g)
-    tol, tau, mean_tol, max_excl = bounds(name)
+    tol, tau, mean_tol, min_cmp, max_excl = bounds(name)
     steps = int(g["meta_decode_steps"])
     checked = [int(b) for b in g["meta_branches"]]
     pre = wl.prefix()
@@ -159,14 +183,20 @@ def fork_case(name):
     rt = make_runtime(shape, nb, P + suffix + steps + 8, P, nb)
     root = rt.alloc()
     say("%s: prefix %d" % (name, P))
-    rt.forward([Pass(root, pre)])
+    rep = Report()
+    if "meta_prefix_readout" in g.files and int(g["meta_prefix_readout"]):
+        # the prefix pass reads out its last token with argmax
+        plog = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+        toks, _ = rt.forward([Pass(root, pre, [P - 1], [(0, 1.0, 0)])], logits_out=plog)
+        compare(rep, g, row_of(g, -1, -1), toks[0], plog.cpu().numpy()[0], ("prefix",), tau)
+    else:
+        rt.forward([Pass(root, pre)])
     st0 = rt.pool_stats()
     prefix_pages = list(rt.ws_info(root)["pages"])
     br = [rt.fork(root) for _ in range(nb)]
     assert rt.pool_stats()["pages_free"] == st0["pages_free"]
     for h in br:
         assert list(rt.ws_info(h)["pages"]) == prefix_pages
-    rep = Report()
     logits = torch.empty((nb, shape.vocab), dtype=torch.float32, device="cuda")
     teach = [synth.teacher_tokens(3, b, steps, shape.vocab) for b in range(nb)]
     for k in range(steps + 1):
@@ -190,21 +220,30 @@ def fork_case(name):
     own = (suffix + steps + 15) // 16
     assert st["pages_ever_allocated"] == len(prefix_pages) + nb * own
     rt.close()
-    rep.check(tol=tol, max_excluded_frac=max_excl, mean_tol=mean_tol)
+    rep.check(tol=tol, max_excluded_frac=max_excl, mean_tol=mean_tol, min_compared=min_cmp)
 
 
-def mix_case(name):
+def mix_case(name, extra=()):
     """Continuous batching: 8 prompts of 4096 tokens prefilled in 512-token
     chunks, packed into the same 8 launches as 120 decode rows whose
     contexts (128..8192 tokens) were prefilled beforehand; per-row epilogue
-    argmax or Gumbel-max (T = 1)."""
+    argmax or Gumbel-max (T = 1).  `extra`: further stored files of the same
+    runs (other checked rows), under the same bounds."""
     import torch
     from paged_kv_forward_amd.runtime import Pass
     g = golden(name)
     wl = synth.workload(4)
     shape = shape_of(wl, g)
-    tol, tau, mean_tol, max_excl = bounds(name)
-    checked = sorted(set(int(s) for s in g["row_seq"]))
+    tol, tau, mean_tol, min_cmp, max_excl = bounds(name)
+    gold_of = {int(s): g for s in g["row_seq"]}
+    for x in extra:
+        path = os.path.join(GOLDEN, x + ".npz")
+        if os.path.exists(path):
+            gx = np.load(path, allow_pickle=False)
+            gold_of.update({int(s): gx for s in gx["row_seq"]})
+        else:
+            say("%s: stored rows %s not generated, not checked" % (name, x))
+    checked = sorted(gold_of)
     n, C = wl.n_seqs, wl.chunk
     max_ctx = max(wl.prompt_len) + 8 + 8
     pages = sum((L + 8 + 15) // 16 + 1 for L in wl.prompt_len)
@@ -244,10 +283,27 @@ def mix_case(name):
         lg = logits[:len(ro_seq)].cpu().numpy()
         for i, s in enumerate(ro_seq):
             if s in checked:
-                compare(rep, g, row_of(g, s, k if s >= 8 else n_launch - 1), toks[i], lg[i],
+                gs = gold_of[s]
+                compare(rep, gs, row_of(gs, s, k if s >= 8 else n_launch - 1), toks[i], lg[i],
                         ("mix", s, k), tau)
     rt.close()
-    rep.check(tol=tol, max_excluded_frac=max_excl, mean_tol=mean_tol)
+    rep.check(tol=tol, max_excluded_frac=max_excl, mean_tol=mean_tol, min_compared=min_cmp)
+
+
+def test_c2_first1_llama8b_decode_batch64():
+    decode_case("c2_decode_8b_first1", 2, 4)
+
+
+def test_c3_first1_fork_gumbel():
+    fork_case("c3_fork_8b_first1")
+
+
+def test_c4_first1_mix():
+    mix_case("c4_mix_8b_first1")
+
+
+def test_c5_first1_llama70b_decode_e4m3():
+    decode_case("c5_decode_70b_first1", 5, 2)
 
 
 def test_c2_first2_llama8b_decode_batch64():
@@ -275,8 +331,12 @@ def test_c3_fork_gumbel():
 
 
 def test_c4_mix():
-    mix_case("c4_mix_8b")
+    mix_case("c4_mix_8b", extra=("c4_mix_8b_long",))
 
 
 def test_c5_llama70b_decode_e4m3():
     decode_case("c5_decode_70b", 5, 2)
+
+
+def test_c5_llama70b_decode_e4m3_ctx512():
+    decode_case("c5_decode_70b_ctx512", 5, 8)

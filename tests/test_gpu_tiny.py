@@ -524,3 +524,63 @@ def test_tiny_large_prefill_tiles_with_ragged_edges(torch_cuda, lens):
         rep.add(toks[i], tok, margin, tau_for(0, 1.0), lg[i], ref, tag=("prefill", len(pr)))
     rep.check(max_excluded_frac=1.0)  # one or two rows: the logits carry the check
     rt.close()
+
+
+def test_tiny_long_decode_sequence_and_skewed_batch(torch_cuda):
+    """One decode sequence with 8200 tokens of context, alone and packed with
+    15 short ones: its attention is cut into more pieces than a short batch
+    would take, and every piece must reach the merge (at most 64 per
+    sequence).  Logits and tokens against the oracle."""
+    from paged_kv_forward_amd.runtime import Pass
+    recipe = RECIPES["gains1"]
+    shape = recipe.shape
+    long_len, n_short, short_len = 8200, 15, 16
+    rt = make_runtime(shape, recipe, torch_cuda, max_rows=8300, max_seqs=16, max_readout=16, max_ctx=8300,
+                      pages=1024)
+    w = SynthWeights(recipe, cache_layers=True)
+    num = default_numerics(shape)
+    long_prompt = synth.prompt_tokens(1, 500, long_len, shape.vocab)
+    shorts = [synth.prompt_tokens(1, 501 + s, short_len, shape.vocab) for s in range(n_short)]
+    say("long decode: oracle")
+    sess_long = Session(w, num)
+    sess_long.step(long_prompt, readout=[])
+    sess_short = []
+    for s in range(n_short):
+        ss = Session(w, num)
+        ss.step(shorts[s], readout=[])
+        sess_short.append(ss)
+    feed = synth.prompt_tokens(1, 520, 3, shape.vocab)
+    ref_alone = sess_long.step([int(feed[0])])[0]
+    ref_batch = [sess_long.step([int(feed[1])])[0]] + [sess_short[s].step([int(feed[2])])[0] for s in range(n_short)]
+    say("long decode: gpu")
+    wl = rt.alloc()
+    rt.forward([Pass(wl, long_prompt)])
+    ws = [rt.alloc() for _ in range(n_short)]
+    rt.forward([Pass(ws[s], shorts[s]) for s in range(n_short)])
+    rep = Report()
+    toks, lg = rt.forward([Pass(wl, [int(feed[0])], [0], [(0, 1.0, 0)])], want_logits=True)
+    t, m = apply(ref_alone, 0)
+    rep.add(toks[0], t, m, tau_for(0, 1.0), lg[0], ref_alone, ("alone",))
+    toks, lg = rt.forward([Pass(wl, [int(feed[1])], [0], [(0, 1.0, 0)])] +
+                          [Pass(ws[s], [int(feed[2])], [0], [(0, 1.0, 0)]) for s in range(n_short)],
+                          want_logits=True)
+    for i in range(n_short + 1):
+        t, m = apply(ref_batch[i], 0)
+        rep.add(toks[i], t, m, tau_for(0, 1.0), lg[i], ref_batch[i], ("batch", i))
+    rep.check()
+    rt.close()
+
+
+def test_no_launch_flag_is_refused_on_a_gpu_context(torch_cuda):
+    """Planning without running would commit tokens whose KV was never
+    computed: a context with weights refuses it and changes nothing."""
+    from paged_kv_forward_amd import _native as N
+    from paged_kv_forward_amd.runtime import Pass
+    recipe = RECIPES["gains1"]
+    rt = make_runtime(recipe.shape, recipe, torch_cuda)
+    ws = rt.alloc()
+    before = rt.pool_stats()
+    with pytest.raises(N.PieError):
+        rt.forward([Pass(ws, [1, 2, 3], [2], [(0, 1.0, 0)])], flags=N.PIE_FLAG_NO_LAUNCH)
+    assert rt.ws_info(ws)["len"] == 0 and rt.pool_stats() == before
+    rt.close()

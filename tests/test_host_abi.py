@@ -374,11 +374,38 @@ def test_noise_mean_bound_rule(tmp_path):
     rep.add(1, 1, 0.5, 2.0)  # excluded: margin below tau
     rep.sum_err = 0.5
     rep.max_err = 0.5
-    rep.check(tol=1.0, max_excluded_frac=1.0, mean_tol=0.6)
+    rep.check(tol=1.0, max_excluded_frac=1.0, mean_tol=0.6, min_compared=0)
     with pytest.raises(AssertionError):
-        rep.check(tol=1.0, max_excluded_frac=1.0, mean_tol=0.4)
+        rep.check(tol=1.0, max_excluded_frac=1.0, mean_tol=0.4, min_compared=0)
     with pytest.raises(AssertionError):
-        rep.check(tol=1.0, max_excluded_frac=0.6, mean_tol=0.6)
+        rep.check(tol=1.0, max_excluded_frac=0.6, mean_tol=0.6, min_compared=0)
+    # by default some token must be compared
+    with pytest.raises(AssertionError):
+        rep.check(tol=1.0, max_excluded_frac=1.0, mean_tol=0.6)
+
+
+def test_report_accumulates_the_mean_error_of_rows_given_logits():
+    """Report.add with logits adds the row's mean |dlogit| to the sum the mean
+    bound uses (a row given no logits adds nothing)."""
+    import numpy as np
+    from tests.parity import Report
+    rep = Report()
+    rep.add(3, 3, 1.0, 0.02, np.array([0.0, 1.0, 2.0]), np.array([0.1, 1.0, 1.7]))
+    rep.add(4, 4, 1.0, 0.02)
+    assert abs(rep.sum_err - (0.1 + 0.0 + 0.3) / 3) < 1e-12 and abs(rep.max_err - 0.3) < 1e-12
+    rep.check(tol=0.3 + 1e-9, mean_tol=0.1)
+    with pytest.raises(AssertionError):
+        rep.check(tol=1.0, mean_tol=0.05)
+
+
+def test_noise_bounds_take_2e2_where_the_twin_is_below_it(tmp_path):
+    import json
+    from tests.parity import noise_bounds
+    a, b = tmp_path / "a.json", tmp_path / "b.json"
+    a.write_text(json.dumps({"max_abs_dlogit": 0.019, "mean_abs_dlogit": 0.003}))
+    b.write_text(json.dumps({"max_abs_dlogit": 0.031, "mean_abs_dlogit": 0.005}))
+    assert noise_bounds([str(a)]) == (2e-2, 2e-2)
+    assert noise_bounds([str(a), str(b)]) == (2 * 0.031, 0.031)
 
 
 def test_stored_conditioning_files_are_complete():

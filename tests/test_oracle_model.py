@@ -278,3 +278,103 @@ def test_e4m3_kv_path_runs_and_stays_close_to_bf16():
     e = forward_chunks(w, ch, default_numerics(shape))[0]
     b = forward_chunks(w, ch, Numerics(exact=False, kv_dtype=synth.KV_BF16))[0]
     assert 0 < np.max(np.abs(e - b)) < 0.5
+
+
+# ---------------------------------------------------------------- e4m3 KV scales
+
+def _pow2_scales(L, nkv):
+    """Distinct power-of-two scales per (layer, K|V, head): 2^(5l + 3w + h - 12)."""
+    s = np.empty((L, 2, nkv), dtype=np.float32)
+    for l in range(L):
+        for w in range(2):
+            for h in range(nkv):
+                s[l, w, h] = 2.0 ** (5 * l + 3 * w + h - 12)
+    return s
+
+
+def test_e4m3_kv_applies_the_scale_of_its_layer_kind_and_head():
+    """Values that are exact codes times the right scale store losslessly;
+    a K/V, head or layer mix-up changes the scale by a power of two other than
+    1, which saturates 448 or flushes 2^-9 to zero.  A tie (1.0625 between
+    codes 1 and 1.125) rounds to the even code."""
+    L, nkv, hd = 3, 4, 8
+    scales = _pow2_scales(L, nkv)
+    num = Numerics(exact=False, kv_dtype=synth.KV_E4M3, kv_scales=scales)
+    pattern = np.array([448.0, -448.0, 2.0 ** -9, -2.0 ** -9, 1.125, 0.0, 240.0, 1.0625])
+    for l in range(L):
+        for w in range(2):
+            x = np.empty((5, nkv, hd))
+            for h in range(nkv):
+                x[:, h, :] = float(scales[l, w, h]) * pattern[None, :]
+            got = num.kv(x, l, w)
+            want = x.copy()
+            for h in range(nkv):
+                want[:, h, 7] = float(scales[l, w, h]) * 1.0  # the tie goes to the even code
+            np.testing.assert_array_equal(got, want)
+            # the same values under every other scale do not survive
+            for l2 in range(L):
+                for w2 in range(2):
+                    if (l2, w2) != (l, w):
+                        assert np.any(num.kv(x, l2, w2) != want)
+            rolled = np.roll(x, 1, axis=1)  # heads shifted by one
+            assert np.any(num.kv(rolled, l, w) != np.roll(want, 1, axis=1))
+
+
+def test_e4m3_kv_scales_reach_k_and_v_separately_in_a_layer():
+    """Closed forms of one layer's attention when one of K or V is scaled so
+    far up that it stores as zeros: V = 0 leaves the residual unchanged by
+    attention (o = 0), and K = 0 makes every score 0, so attention averages the
+    visible V rows uniformly."""
+    import dataclasses
+    shape = dataclasses.replace(synth.TINY, kv_dtype=synth.KV_E4M3, n_layers=1)
+    w = SynthWeights(synth.WeightRecipe(shape), cache_layers=True)
+    lw = w.layer(0)
+    n = 6
+    h = w.embed_rows(synth.prompt_tokens(1, 9, n, shape.vocab)).astype(np.float64)
+    empty = np.zeros((0, shape.n_kv_heads, shape.head_dim))
+    huge, ok = np.float32(2.0 ** 40), np.float32(0.05)
+    # V scale huge: every stored V is zero
+    sv = np.array([[[ok] * shape.n_kv_heads, [huge] * shape.n_kv_heads]], dtype=np.float32)
+    num = Numerics(exact=False, kv_dtype=synth.KV_E4M3, kv_scales=sv)
+    _, K, V = layer_forward(lw, h, np.arange(n), empty, empty, shape, num, 0)
+    assert not np.any(V) and np.any(K)
+    # the attention half of the layer adds exactly nothing: compare with a
+    # layer whose o projection is zero
+    lw0 = dict(lw, o=np.zeros_like(lw["o"]))
+    a, _, _ = layer_forward(lw, h, np.arange(n), empty, empty, shape, num, 0)
+    b, _, _ = layer_forward(lw0, h, np.arange(n), empty, empty, shape, num, 0)
+    np.testing.assert_array_equal(a, b)
+    # K scale huge: every stored K is zero, scores are all 0, attention is the
+    # running mean of the stored V rows
+    sk = np.array([[[huge] * shape.n_kv_heads, [ok] * shape.n_kv_heads]], dtype=np.float32)
+    num = Numerics(exact=False, kv_dtype=synth.KV_E4M3, kv_scales=sk)
+    _, K, V = layer_forward(lw, h, np.arange(n), empty, empty, shape, num, 0)
+    assert not np.any(K) and np.any(V)
+    G = shape.n_q_heads // shape.n_kv_heads
+    q = np.zeros((n, shape.n_q_heads, shape.head_dim))
+    o = attention(q, K, V, 0)
+    for i in range(n):
+        for hh in range(shape.n_q_heads):
+            np.testing.assert_allclose(o[i, hh], V[:i + 1, hh // G].mean(axis=0), rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------- top-2 margin
+
+def _brute_margin(v):
+    v = [float(x) for x in v]
+    if len(v) < 2:
+        return math.inf
+    i = max(range(len(v)), key=lambda j: (v[j], -j))
+    rest = v[:i] + v[i + 1:]
+    return v[i] - max(rest)
+
+
+def test_top2_margin_matches_sorted_brute_force_with_ties():
+    from oracle.epilogue import top2_margin
+    rng = np.random.default_rng(4)
+    cases = [rng.standard_normal(50), np.array([1.0, 3.0, 3.0, 2.0]), np.array([5.0]),
+             np.array([-2.0, -1.0]), np.array([0.0, 0.0]), rng.integers(-3, 3, size=40).astype(float),
+             np.array([-np.inf, 1.0, 0.5])]
+    for v in cases:
+        assert top2_margin(v) == _brute_margin(v), v
+    assert top2_margin(np.array([1.0, 3.0, 3.0])) == 0.0
