@@ -52,13 +52,36 @@ teacher_tokens = synth.teacher_tokens
 LAYERS = None  # set by "cN:L" on the command line
 
 
+def matmul_f32(a, w):
+    """The oracle's weight product with float32 inputs and float32 accumulation
+    (the float32 twin of tests/golden/conditioning.py)."""
+    return (np.asarray(a, dtype=np.float32) @ np.asarray(w, dtype=np.float32).T).astype(np.float64)
+
+
+def run(w, chunks, num):
+    """The oracle's logits for the chunks and, for the cut models (cheap), the
+    same run with every weight product in float32: the twin's difference over
+    exactly the stored rows bounds the GPU's (tests/parity.py)."""
+    logits, twin = run(w, chunks, num)
+    if LAYERS is None:
+        return logits, None
+    import oracle.model as om
+    plain = om.matmul_t
+    om.matmul_t = matmul_f32
+    try:
+        twin = forward_chunks(w, chunks, num)
+    finally:
+        om.matmul_t = plain
+    return logits, twin
+
+
 def model(wl):
     """The workload's model, cut to LAYERS layers when asked."""
     return wl.shape if LAYERS is None else synth.first_layers(wl.shape, LAYERS)
 
 
 def finish(name, rows, full_rows, vocab, meta):
-    """rows: list of dicts (seq, step, kind, temp, seed, lane, logits)."""
+    """rows: list of dicts (seq, step, kind, temp, seed, lane, logits[, twin])."""
     if LAYERS is not None:
         name = "%s_first%d" % (name, LAYERS)
         meta = dict(meta, n_layers=LAYERS)
@@ -78,6 +101,11 @@ def finish(name, rows, full_rows, vocab, meta):
     out["row_kind"] = np.array([r["kind"] for r in rows], dtype=np.int32)
     out["full_rows"] = np.array(full_rows, dtype=np.int32)
     out["logits_full"] = np.stack([rows[i]["logits"].astype(np.float32) for i in full_rows])
+    if rows and rows[0].get("twin") is not None:
+        d = np.concatenate([np.abs(r["logits"] - r["twin"]) for r in rows])
+        out["twin_max_abs_dlogit"] = np.asarray(float(d.max()))
+        out["twin_mean_abs_dlogit"] = np.asarray(float(d.mean()))
+        print("%s: float32 twin over the stored rows: max %.4g mean %.4g" % (name, d.max(), d.mean()))
     for k, v in meta.items():
         out["meta_" + k] = np.asarray(v)
     path = os.path.join(HERE, name + ".npz")
@@ -102,13 +130,13 @@ def c2(decode_steps=None, seqs=(0, 21, 42, 63)):
         ro = list(range(wl.prompt_len[s] - 1, n))
         chunks.append(Chunk(toks, np.arange(n), -1, ro))
     t0 = time.time()
-    logits = forward_chunks(w, chunks, num)
+    logits, twin = run(w, chunks, num)
     print("c2 oracle %.0f s" % (time.time() - t0), flush=True)
     rows = []
     for ci, s in enumerate(seqs):
         for k in range(decode_steps + 1):
             rows.append(dict(seq=s, step=k, kind=synth.EPI_ARGMAX, temp=1.0, seed=0, lane=0,
-                             logits=logits[ci][k]))
+                             logits=logits[ci][k], twin=None if twin is None else twin[ci][k]))
     per = decode_steps + 1
     full = sorted({0, decode_steps, per, 2 * per - 1, len(rows) - 1})
     finish("c2_decode_8b", rows, full, shape.vocab,
@@ -134,18 +162,18 @@ def c3(decode_steps=None, branches=(0, 4, 9)):
         n = len(toks)
         chunks.append(Chunk(toks, P + np.arange(n), 0, list(range(wl.prompt_len[b] - 1, n))))
     t0 = time.time()
-    logits = forward_chunks(w, chunks, num)
+    logits, twin = run(w, chunks, num)
     print("c3 oracle %.0f s" % (time.time() - t0), flush=True)
     rows = []
     if with_prefix:
         # the prefix pass's own readout: sequence -1, step -1, argmax
         rows.append(dict(seq=-1, step=-1, kind=synth.EPI_ARGMAX, temp=1.0, seed=0, lane=0,
-                         logits=logits[0][0]))
+                         logits=logits[0][0], twin=None if twin is None else twin[0][0]))
     for ci, b in enumerate(branches):
         for k in range(decode_steps + 1):
             rows.append(dict(seq=b, step=k, kind=synth.EPI_GUMBEL, temp=0.7,
                              seed=synth.epilogue_seed(wl.branch_seed[b], k), lane=0,
-                             logits=logits[1 + ci][k]))
+                             logits=logits[1 + ci][k], twin=None if twin is None else twin[1 + ci][k]))
     full = sorted({0, 1, decode_steps + 1, len(rows) - 1})
     finish("c3_fork_8b", rows, full, shape.vocab,
            dict(branches=list(branches), decode_steps=decode_steps, prefix_readout=int(with_prefix)))
@@ -179,14 +207,14 @@ def c4(seqs=None, name="c4_mix_8b"):
             chunks.append(Chunk(toks, np.arange(n), -1, list(range(len(ctx), n))))
             meta_rows.append([(s, k) for k in range(8)])
     t0 = time.time()
-    logits = forward_chunks(w, chunks, num)
+    logits, twin = run(w, chunks, num)
     print("c4 oracle %.0f s" % (time.time() - t0), flush=True)
     rows = []
     for ci, s in enumerate(seqs):
         for j, (_, k) in enumerate(meta_rows[ci]):
             rows.append(dict(seq=s, step=k, kind=wl.epi_kind[s], temp=1.0,
                              seed=synth.epilogue_seed(wl.branch_seed[s], k), lane=0,
-                             logits=logits[ci][j]))
+                             logits=logits[ci][j], twin=None if twin is None else twin[ci][j]))
     finish(name, rows, sorted({0, 1, 2, len(rows) - 1}), shape.vocab, dict(seqs=seqs))
 
 
@@ -216,13 +244,13 @@ def c5(decode_steps=None, seqs=None, ctx=None, name="c5_decode_70b"):
         n = len(toks)
         chunks.append(Chunk(toks, np.arange(n), -1, list(range(n_prompt - 1, n))))
     t0 = time.time()
-    logits = forward_chunks(w, chunks, num)
+    logits, twin = run(w, chunks, num)
     print("c5 oracle %.0f s" % (time.time() - t0), flush=True)
     rows = []
     for ci, s in enumerate(seqs):
         for k in range(decode_steps + 1):
             rows.append(dict(seq=s, step=k, kind=synth.EPI_ARGMAX, temp=1.0, seed=0, lane=0,
-                             logits=logits[ci][k]))
+                             logits=logits[ci][k], twin=None if twin is None else twin[ci][k]))
     meta = dict(seqs=list(seqs), decode_steps=decode_steps)
     if ctx:
         meta["ctx"] = ctx

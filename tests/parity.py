@@ -44,6 +44,16 @@ def noise_bounds(conditioning_jsons):
     return NOISE_FACTOR * twin, twin
 
 
+def twin_bounds(twin_max, twin_mean):
+    """(logit tolerance, token margin, mean bound) from the float32 twin's
+    difference over the same rows: 2e-2 for both where the twin stays below
+    it, else twice its largest difference and that difference; the mean bound
+    is twice the twin's mean."""
+    if twin_max < TOL_LOGITS:
+        return TOL_LOGITS, TAU_LOGIT, NOISE_FACTOR * twin_mean
+    return NOISE_FACTOR * twin_max, twin_max, NOISE_FACTOR * twin_mean
+
+
 def noise_mean_bound(conditioning_jsons):
     """Bound on the mean |dlogit| over the compared rows: NOISE_FACTOR times the
     twin's largest mean difference.  This is the check that stays sharp where

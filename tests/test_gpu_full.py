@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import synth
-from tests.parity import Report, noise_bounds, noise_mean_bound, say
+from tests.parity import Report, noise_bounds, noise_mean_bound, say, twin_bounds
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -70,12 +70,17 @@ DEEP_70B = {"c5_decode_70b", "c5_decode_70b_ctx512"}
 def bounds(name):
     """(max |dlogit| bound, token margin, mean |dlogit| bound, least number of
     rows whose token is compared, largest fraction of rows excluded)."""
-    paths = [os.path.join(GOLDEN, "conditioning_%s.json" % c) for c in CONDITIONING[name]]
-    paths = [p for p in paths if os.path.exists(p)]
-    if not paths:
-        pytest.skip("float32 noise floor for %s not measured" % name)
-    tol, tau = noise_bounds(paths)
-    mean_tol = noise_mean_bound(paths)
+    g = golden(name)
+    if "twin_max_abs_dlogit" in g.files:
+        # the float32 twin measured over exactly the stored rows
+        tol, tau, mean_tol = twin_bounds(float(g["twin_max_abs_dlogit"]), float(g["twin_mean_abs_dlogit"]))
+    else:
+        paths = [os.path.join(GOLDEN, "conditioning_%s.json" % c) for c in CONDITIONING[name]]
+        paths = [p for p in paths if os.path.exists(p)]
+        if not paths:
+            pytest.skip("float32 noise floor for %s not measured" % name)
+        tol, tau = noise_bounds(paths)
+        mean_tol = noise_mean_bound(paths)
     min_compared = 0 if name in LOGITS_ONLY else 1
     max_excl = 1.0 if name in DEEP_70B else 0.6
     say("%s: bounds |dlogit| <= %.4f, mean |dlogit| <= %.4f, tokens compared at margin >= %.4f"
