@@ -186,7 +186,8 @@ size_t pie_workspace_bytes(const pie_model_desc* desc, const pie_limits* limits)
  * for the shape, section 3 Weights for the tensors, section 4 for the KV
  * space) on one GPU.
  *  kv_arena/kv_bytes: DEVICE memory for the page pool; pages = kv_bytes / pie_kv_page_bytes.
- *  workspace/ws_bytes: DEVICE scratch of at least pie_workspace_bytes(desc, limits).
+ *  workspace/ws_bytes: DEVICE scratch of at least pie_workspace_bytes(desc, limits),
+ *    or NULL and 0 for a context that runs only pie_forward_static.
  *  hip_stream: the hipStream_t every launch goes to (NULL = the null stream).
  * With weights == NULL the context is host-only: it keeps working sets, page
  * pool and batch packing but never touches the GPU (kv_arena and workspace may be
@@ -291,6 +292,33 @@ typedef struct pie_pass {
  * Returns after the stream has finished the call's work. */
 int pie_forward(pie_ctx* ctx, const pie_pass* passes, int32_t n_passes, int32_t* out_tokens,
                 float* out_logits, int32_t flags);
+
+/* Bytes of the library's static device scratch (pie_forward_static), held
+ * by every GPU the library runs on from load to process end. */
+#define PIE_STATIC_SCRATCH_BYTES (96u * 1024u * 1024u)
+
+/* pie_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same passes, validation, all-or-nothing rule, results and errors as
+ * pie_forward, but every buffer the call's kernels use besides the caller's
+ * inputs and outputs (activations, packed metadata, split-K and attention
+ * partials, per-tile maxima of the epilogue) lives in the library's static
+ * device scratch of PIE_STATIC_SCRATCH_BYTES instead of the context's
+ * workspace, and the call allocates nothing (no hipMalloc, hipFree or other
+ * allocating routine; metadata goes through the pinned staging pie_init made).
+ * A context created with workspace == NULL and ws_bytes == 0 serves only
+ * this call (its limits must fit the scratch; pie_forward and
+ * pie_decode_async then return PIE_ESTATE).
+ *  - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *    call's contents; nothing in it needs to start at zero (each kernel
+ *    writes what it later reads within the call).  Calls that overlap on one
+ *    GPU (two contexts on different streams or threads) race: the caller
+ *    serialises them.  The call returns after its stream has finished.
+ *  - Errors: as pie_forward; PIE_ENOMEM (before any state changes) when the
+ *    context's limits need more scratch than PIE_STATIC_SCRATCH_BYTES;
+ *    PIE_EINVAL while kernel timing is on. */
+int pie_forward_static(pie_ctx* ctx, const pie_pass* passes, int32_t n_passes, int32_t* out_tokens,
+                       float* out_logits, int32_t flags);
 
 /* Loop-carried decode, enqueued without waiting ("How Pie thinks", section 3
  * Forward passes: submitting a pass to a Pipeline returns at once and queued

@@ -27,7 +27,9 @@ EXPORTS = ["pie_kv_page_bytes", "pie_workspace_bytes", "pie_init", "pie_destroy"
            "pie_ws_info", "pie_pool_stats_get", "pie_forward", "pie_last_error",
            "pie_profile_enable", "pie_profile_repeat", "pie_profile_read", "pie_debug_plan", "pie_debug_philox",
            "pie_packed_weight_bytes", "pie_pack_weight", "pie_decode_async", "pie_sync", "pie_prefix_lookup",
-           "pie_packed_weight_fp8_bytes", "pie_fp8_scale_count", "pie_pack_weight_fp8", "pie_attach_fp8_weights"]
+           "pie_packed_weight_fp8_bytes", "pie_fp8_scale_count", "pie_pack_weight_fp8", "pie_attach_fp8_weights",
+           "pie_forward_static"]
+PIE_STATIC_SCRATCH_BYTES = 96 * 1024 * 1024
 
 
 class pie_model_desc(Structure):
@@ -109,6 +111,7 @@ def lib():
         "pie_ws_info": (c_int, [c_void_p, c_uint64, P(pie_ws_stats), P(c_int32)]),
         "pie_pool_stats_get": (c_int, [c_void_p, P(pie_pool_stats)]),
         "pie_forward": (c_int, [c_void_p, P(pie_pass), c_int32, P(c_int32), c_void_p, c_int32]),
+        "pie_forward_static": (c_int, [c_void_p, P(pie_pass), c_int32, P(c_int32), c_void_p, c_int32]),
         "pie_last_error": (c_char_p, []),
         "pie_profile_enable": (c_int, [c_void_p, c_uint32]),
         "pie_profile_repeat": (c_int, [c_void_p, c_int32]),

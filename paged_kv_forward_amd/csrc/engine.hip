@@ -18,6 +18,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <map>
+#include <mutex>
 #include <tuple>
 #include <cstdio>
 #include <cstring>
@@ -215,6 +216,35 @@ struct GraphEntry {
 // Pinned metadata staging slots: how many calls may be enqueued ahead of the GPU.
 constexpr int PIE_STAGING_SLOTS = 4;
 
+// Device scratch of pie_forward_static: everything a call's kernels use
+// besides the caller's inputs and outputs (the workspace layout of the
+// context), in a file-scope array that every GPU the library runs on holds
+// from module load to process end.  Host code never uses the array's name as
+// an address: pie_init looks up its device address once per device
+// (hipGetSymbolAddress, with that device current) and keeps it per device.
+static __device__ __align__(256) uint8_t scratch[PIE_STATIC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, uint8_t*> g_scratch_addr;  // device -> address of that device's scratch
+
+// Address of the current device's scratch (looked up once per device).
+hipError_t scratch_address(int dev, uint8_t** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_addr.find(dev);
+  if (it != g_scratch_addr.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+  g_scratch_addr[dev] = static_cast<uint8_t*>(p);
+  *out = static_cast<uint8_t*>(p);
+  return hipSuccess;
+}
+}  // namespace
+
 struct pie_ctx {
   pie_model_desc d{};
   pie_limits lim{};
@@ -263,6 +293,11 @@ struct pie_ctx {
   std::map<GraphKey, GraphEntry> graphs;
   bool use_graphs = false;
   bool capturing = false;
+  // this device's static scratch (pie_forward_static), and whether the
+  // context has a workspace of its own (pie_forward, pie_decode_async)
+  uint8_t* static_ws = nullptr;
+  bool has_workspace = true;
+  bool in_static = false;  // a pie_forward_static call is running
 };
 
 namespace {
@@ -730,7 +765,7 @@ int run_forward(pie_ctx* c, int32_t* out_tokens, float* out_logits, int flags) {
   const bool host_logits = out_logits && !(flags & PIE_FLAG_LOGITS_DEVICE);
   // timed calls launch directly: kernel timing uses events between launches
   const bool graphable = c->use_graphs && c->cap_stream && !host_logits && !c->prof_mask &&
-                         !(flags & PIE_FLAG_SYNC_DEBUG);
+                         !(flags & PIE_FLAG_SYNC_DEBUG) && !c->in_static;
   GraphEntry* ge = nullptr;
   if (graphable) {
     GraphKey key{p.n_rows, p.n_readout, (int)(c->dec.size() / 4), (int)(c->comb.size() / 4),
@@ -848,10 +883,20 @@ int pie_init(const pie_model_desc* desc, const pie_weights* w, void* kv_arena, s
     delete c;
     return set_err(PIE_EINVAL, "pie_init: e4m3 KV needs kv_scale");
   }
-  if (!kv_arena || !workspace || ws_bytes < c->lay.total) {
+  // no workspace at all (NULL, 0): only pie_forward_static can run, in the
+  // library's static scratch, whose size the limits must then fit
+  c->has_workspace = !(workspace == nullptr && ws_bytes == 0);
+  if (!kv_arena || (c->has_workspace && (!workspace || ws_bytes < c->lay.total))) {
     size_t need = c->lay.total;
     delete c;
     return set_err(PIE_EINVAL, "pie_init: workspace too small (need " + std::to_string(need) + " bytes)");
+  }
+  if (!c->has_workspace && c->lay.total > PIE_STATIC_SCRATCH_BYTES) {
+    size_t need = c->lay.total;
+    delete c;
+    return set_err(PIE_ENOMEM, "pie_init: no workspace given and these limits need " + std::to_string(need) +
+                                   " bytes, more than the static scratch's " +
+                                   std::to_string((size_t)PIE_STATIC_SCRATCH_BYTES));
   }
   auto cp = [&](std::vector<const uint16_t*>& dst, const void* const* src, const char* nm) {
     dst.resize(L);
@@ -881,6 +926,17 @@ int pie_init(const pie_model_desc* desc, const pie_weights* w, void* kv_arena, s
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
     delete c;
     return set_err(PIE_ESTATE, std::string("pie_init: kernels are built for gfx950, device is ") + prop.gcnArchName);
+  }
+  // this device's static scratch, for pie_forward_static; without it only a
+  // context that has no workspace of its own cannot run
+  e = scratch_address(dev, &c->static_ws);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // must not surface in a later launch check
+    c->static_ws = nullptr;
+    if (!c->has_workspace) {
+      delete c;
+      return set_err(PIE_EHIP, std::string("pie_init: static scratch address: ") + hipGetErrorString(e));
+    }
   }
   for (int i = 0; i < PIE_STAGING_SLOTS; ++i) {
     int32_t* buf = nullptr;
@@ -991,6 +1047,8 @@ int pie_forward(pie_ctx* c, const pie_pass* passes, int32_t n_passes, int32_t* o
   // and the prefix registry could then hand those pages to another request
   if ((flags & PIE_FLAG_NO_LAUNCH) && !c->host_only)
     return set_err(PIE_EINVAL, "pie_forward: PIE_FLAG_NO_LAUNCH is only for host-only contexts");
+  if (!c->host_only && !c->has_workspace)
+    return set_err(PIE_ESTATE, "pie_forward: the context has no workspace (use pie_forward_static)");
   pie::PackLimits pl{c->lim.max_rows, c->lim.max_seqs, c->lim.max_readout, c->lim.max_ctx,
                      c->lay.max_pe, c->d.vocab};
   int64_t want_ro = 0;
@@ -1007,10 +1065,44 @@ int pie_forward(pie_ctx* c, const pie_pass* passes, int32_t n_passes, int32_t* o
   return run_forward(c, out_tokens, out_logits, flags);
 }
 
+int pie_forward_static(pie_ctx* c, const pie_pass* passes, int32_t n_passes, int32_t* out_tokens,
+                       float* out_logits, int32_t flags) {
+  CTX_OK(c);
+  if (c->host_only) return set_err(PIE_ESTATE, "pie_forward_static: host-only context");
+  if (flags & PIE_FLAG_NO_LAUNCH)
+    return set_err(PIE_EINVAL, "pie_forward_static: PIE_FLAG_NO_LAUNCH is only for host-only contexts");
+  // kernel timing would create events lazily: not in the entry point that allocates nothing
+  if (c->prof_mask) return set_err(PIE_EINVAL, "pie_forward_static: kernel timing must be off");
+  if (c->lay.total > PIE_STATIC_SCRATCH_BYTES)
+    return set_err(PIE_ENOMEM, "pie_forward_static: the context's limits need " + std::to_string(c->lay.total) +
+                                   " bytes of scratch, more than the static scratch's " +
+                                   std::to_string((size_t)PIE_STATIC_SCRATCH_BYTES));
+  if (!c->static_ws) return set_err(PIE_ESTATE, "pie_forward_static: no static scratch on this device");
+  pie::PackLimits pl{c->lim.max_rows, c->lim.max_seqs, c->lim.max_readout, c->lim.max_ctx,
+                     c->lay.max_pe, c->d.vocab};
+  int64_t want_ro = 0;
+  if (passes && n_passes > 0)
+    for (int i = 0; i < n_passes; ++i) want_ro += passes[i].n_readout > 0 ? passes[i].n_readout : 0;
+  if (want_ro > 0 && !out_tokens) return set_err(PIE_EINVAL, "pie_forward_static: null out_tokens");
+  std::string err;
+  int rc = pie::pack_batch(c->store, passes, n_passes, pl, &c->plan, &err);
+  if (rc) return set_err(rc, err);
+  // the same launch sequence over the static scratch instead of the workspace
+  uint8_t* own = c->ws;
+  c->ws = c->static_ws;
+  c->in_static = true;
+  rc = run_forward(c, out_tokens, out_logits, flags);
+  c->in_static = false;
+  c->ws = own;
+  return rc;
+}
+
 int pie_decode_async(pie_ctx* c, const pie_ws* ws, int32_t n, const int32_t* tokens_in, int32_t* tokens_out,
                      const pie_epilogue* epi, float* logits_dev) {
   CTX_OK(c);
   if (c->host_only) return set_err(PIE_ESTATE, "pie_decode_async: host-only context");
+  if (!c->has_workspace)
+    return set_err(PIE_ESTATE, "pie_decode_async: the context has no workspace (use pie_forward_static)");
   if (!ws || n < 1 || !tokens_in || !tokens_out || !epi)
     return set_err(PIE_EINVAL, "pie_decode_async: null argument or n < 1");
   if (c->prof_mask) return set_err(PIE_EINVAL, "pie_decode_async: kernel timing needs synchronous calls");

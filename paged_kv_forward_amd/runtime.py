@@ -121,7 +121,10 @@ class PieRuntime:
     weights is None: working sets and packing without the GPU)."""
 
     def __init__(self, shape, weights: Optional[Dict], kv_bytes: int, max_rows: int,
-                 max_seqs: int, max_readout: int, max_ctx: int, device="cuda", stream=None):
+                 max_seqs: int, max_readout: int, max_ctx: int, device="cuda", stream=None,
+                 workspace: bool = True):
+        """workspace=False: no device workspace (pie_init with NULL, 0); the
+        context then runs only forward_static (the library's static scratch)."""
         self.shape = shape
         self.desc = model_desc(shape)
         self.limits = N.pie_limits(max_rows, max_seqs, max_readout, max_ctx)
@@ -142,12 +145,13 @@ class PieRuntime:
             import torch
             self.device = torch.device(device)
             self.kv = torch.empty(kv_bytes, dtype=torch.uint8, device=self.device)
-            self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+            self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+                              if workspace else None)
             self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
             self.weights = weights
             pw = self._weights_struct(weights)
-            check(L.pie_init(ctypes.byref(self.desc), ctypes.byref(pw), self.kv.data_ptr(),
-                             kv_bytes, self.workspace.data_ptr(), self.ws_bytes,
+            check(L.pie_init(ctypes.byref(self.desc), ctypes.byref(pw), self.kv.data_ptr(), kv_bytes,
+                             self.workspace.data_ptr() if workspace else None, self.ws_bytes if workspace else 0,
                              ctypes.byref(self.limits), ctypes.c_void_p(self.stream.cuda_stream),
                              ctypes.byref(ctx)))
             if "fp8" in weights["layers"][0]:
@@ -328,8 +332,13 @@ class PieRuntime:
         """Wait for every enqueued step (pie_sync)."""
         check(N.lib().pie_sync(self.ctx))
 
+    def forward_static(self, passes: Sequence[Pass], want_logits: bool = False, flags: int = 0,
+                       logits_out=None):
+        """pie_forward_static: as forward, over the library's static device scratch."""
+        return self.forward(passes, want_logits, flags, logits_out, _entry="pie_forward_static")
+
     def forward(self, passes: Sequence[Pass], want_logits: bool = False, flags: int = 0,
-                logits_out=None):
+                logits_out=None, _entry: str = "pie_forward"):
         """Returns (tokens int32[R], logits float32[R, V] or None)."""
         arr, keep = self._marshal(passes)
         if os.environ.get("PIE_SYNC_DEBUG"):
@@ -345,9 +354,9 @@ class PieRuntime:
         elif want_logits and R:
             logits = np.empty((R, self.shape.vocab), dtype=np.float32)
             logits_ptr = logits.ctypes.data
-        check(N.lib().pie_forward(self.ctx, arr.ctypes.data_as(ctypes.POINTER(N.pie_pass)), len(passes),
-                                  toks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                                  logits_ptr, flags))
+        check(getattr(N.lib(), _entry)(self.ctx, arr.ctypes.data_as(ctypes.POINTER(N.pie_pass)), len(passes),
+                                       toks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                       logits_ptr, flags))
         del keep
         return toks[:R], logits
 
