@@ -38,39 +38,75 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(shape, recipe, n_seq=4, n_layers=8):
-    """The oracle's decode step on a bounded sample, scaled to a full step:
-    `n_seq` decode rows (context 2048, synthetic bf16 K/V) through `n_layers`
-    layers plus the head, timed on the host cores."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(shape, recipe, decode_rows=1, decode_steps=2, ctx=64, prefill_tokens=256, prefill_layers=2):
+    """The oracle timed on the host cores, on bounded samples of the workload.
+
+    decode: its incremental path (oracle.run.Session: token-major, contiguous
+    per-layer KV), every layer's weights resident in host memory; `decode_rows`
+    sequences with a `ctx`-token context (not timed) each take `decode_steps`
+    one-token steps through all layers and the head.
+    prefill: its layer-major pass (oracle.run.forward_chunks) over one
+    `prefill_tokens`-token prompt through the first `prefill_layers` layers,
+    scaled to all layers (the head is one readout row, timed apart)."""
     import synth
-    from oracle.model import Numerics, head_logits, layer_forward
-    from oracle.run import SynthWeights
-    w = SynthWeights(recipe)
-    num = Numerics(exact=False, kv_dtype=shape.kv_dtype)
-    rng = np.random.default_rng(3)
-    from oracle.numerics import round_bf16
-    ctxK = [round_bf16(rng.standard_normal((PROMPT, shape.n_kv_heads, shape.head_dim))) for _ in range(n_seq)]
-    ctxV = [round_bf16(rng.standard_normal((PROMPT, shape.n_kv_heads, shape.head_dim))) for _ in range(n_seq)]
-    h0 = [w.embed_rows(np.array([7 + s])).astype(np.float64) for s in range(n_seq)]
-    layers = [w.layer(l) for l in range(n_layers)]
+    from oracle.model import head_logits
+    from oracle.run import Chunk, Session, SynthWeights, default_numerics, forward_chunks
+    num = default_numerics(shape)
+    w = SynthWeights(recipe, cache_layers=True)
+    t0 = time.perf_counter()
+    for l in range(shape.n_layers):
+        w.layer(l)
     head, fin = w.head(), w.final_norm()
+    t_draw = time.perf_counter() - t0
+    # decode, incremental
+    sess = []
+    for r in range(decode_rows):
+        s = Session(w, num)
+        s.step(synth.prompt_tokens(2, 900 + r, ctx, shape.vocab), readout=[])
+        sess.append(s)
+    feed = synth.prompt_tokens(2, 950, decode_rows * decode_steps, shape.vocab)
     t0 = time.perf_counter()
-    for s in range(n_seq):
-        h = h0[s]
-        for l in range(n_layers):
-            h, _, _ = layer_forward(layers[l], h, np.array([PROMPT]), ctxK[s], ctxV[s], shape, num, l)
-    t_layers = time.perf_counter() - t0
+    for k in range(decode_steps):
+        for r, s in enumerate(sess):
+            s.step([int(feed[k * decode_rows + r])])
+    t_dec = time.perf_counter() - t0
+    del sess
+    # prefill, layer-major, over the first layers of the same resident weights
+    cut = synth.first_layers(shape, prefill_layers)
+    wc = SynthWeights(synth.WeightRecipe(cut, weight_seed=recipe.weight_seed, std=recipe.std,
+                                         gain_std=recipe.gain_std))
+    wc._layers = {l: w.layer(l) for l in range(prefill_layers)}
+    wc._cache_layers = True
+    wc._head, wc._final = head, fin
+    toks = synth.prompt_tokens(2, 990, prefill_tokens, shape.vocab)
     t0 = time.perf_counter()
-    for s in range(n_seq):
-        head_logits(h0[s], fin, head, shape, num)
+    h = forward_chunks(wc, [Chunk(toks, np.arange(prefill_tokens), -1, [])], num, want_hidden=True)[1][0]
+    t_pre = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    head_logits(h[-1:], fin, head, shape, num)
     t_head = time.perf_counter() - t0
-    per_row_step = t_layers / n_seq / n_layers * shape.n_layers + t_head / n_seq
+    prefill_s = t_pre * shape.n_layers / prefill_layers + t_head
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
-    return {"value": round(1.0 / per_row_step, 4), "unit": "decode tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "%d decode rows at context %d through %d of %d layers + lm_head (float64 "
-                      "numpy, synthetic K/V), scaled to one 64-row step; %.1f s of CPU work" %
-                      (n_seq, PROMPT, n_layers, shape.n_layers, t_layers + t_head)}
+    threads = min(threads, len(os.sched_getaffinity(0)))
+    return {"value": round(decode_rows * decode_steps / t_dec, 4), "unit": "decode tokens/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": "decode: %d sequence(s) x %d one-token steps through all %d layers and the head on the "
+                      "oracle's incremental path (float64 numpy, context %d tokens, weights resident), %.1f s; "
+                      "prefill: one %d-token prompt through %d of %d layers on its layer-major pass, scaled "
+                      "to all layers, %.1f s (weights drawn beforehand in %.1f s, not timed)" %
+                      (decode_rows, decode_steps, shape.n_layers, ctx, t_dec, prefill_tokens, prefill_layers,
+                       shape.n_layers, t_pre + t_head, t_draw),
+            "prefill_value": round(prefill_tokens / prefill_s, 2), "prefill_unit": "prefill tokens/s"}
 
 
 # ---------------------------------------------------------------- profiles
