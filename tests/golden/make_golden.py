@@ -62,7 +62,7 @@ def run(w, chunks, num):
     """The oracle's logits for the chunks and, for the cut models (cheap), the
     same run with every weight product in float32: the twin's difference over
     exactly the stored rows bounds the GPU's (tests/parity.py)."""
-    logits, twin = run(w, chunks, num)
+    logits = forward_chunks(w, chunks, num)
     if LAYERS is None:
         return logits, None
     import oracle.model as om

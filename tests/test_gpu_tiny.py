@@ -603,3 +603,42 @@ def test_no_launch_flag_is_refused_on_a_gpu_context(torch_cuda):
         rt.forward([Pass(ws, [1, 2, 3], [2], [(0, 1.0, 0)])], flags=N.PIE_FLAG_NO_LAUNCH)
     assert rt.ws_info(ws)["len"] == 0 and rt.pool_stats() == before
     rt.close()
+
+
+MID = synth.ModelShape("mid-2l", n_layers=2, d_model=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, d_ffn=2048,
+                       vocab=4096)
+
+
+@pytest.mark.parametrize("kv", [synth.KV_BF16, synth.KV_E4M3])
+def test_mid_decode_split_qkv_and_split_attention(torch_cuda, kv):
+    """A 2-layer model of width 1024, whose decode-sized QKV projection runs
+    split-K (partials summed by the reduce kernel, which applies RoPE and
+    appends K/V): three sequences (40, 300 and 1100 tokens, the long one cut
+    into several attention pieces merged by the combine kernel), three
+    teacher-fed decode steps, bf16 or e4m3 KV, against the oracle."""
+    from paged_kv_forward_amd.runtime import Pass
+    shape = dataclasses.replace(MID, kv_dtype=kv)
+    recipe = synth.WeightRecipe(shape, weight_seed=7, gain_std=0.02)
+    lens = [40, 300, 1100]
+    prompts = [synth.prompt_tokens(1, 600 + s, lens[s], shape.vocab) for s in range(3)]
+    teach = [synth.prompt_tokens(1, 610 + s, 3, shape.vocab) for s in range(3)]
+    w = SynthWeights(recipe, cache_layers=True)
+    num = default_numerics(shape)
+    say("mid kv=%d: oracle" % kv)
+    ref = []
+    for s in range(3):
+        sess = Session(w, num)
+        sess.step(prompts[s], readout=[])
+        ref.append([sess.step([int(teach[s][k])])[0] for k in range(3)])
+    rt = make_runtime(shape, recipe, torch_cuda, max_rows=1500, max_seqs=4, max_readout=4, max_ctx=1200, pages=256)
+    ws = [rt.alloc() for _ in range(3)]
+    rt.forward([Pass(ws[s], prompts[s]) for s in range(3)])
+    rep = Report()
+    for k in range(3):
+        toks, lg = rt.forward([Pass(ws[s], [int(teach[s][k])], [0], [(0, 1.0, 0)]) for s in range(3)],
+                              want_logits=True)
+        for s in range(3):
+            t, m = apply(ref[s][k], 0)
+            rep.add(toks[s], t, m, tau_for(0, 1.0), lg[s], ref[s][k], ("mid", k, s))
+    rep.check()
+    rt.close()
