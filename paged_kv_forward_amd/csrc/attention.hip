@@ -11,9 +11,11 @@
 // operands of each MFMA (any fixed assignment of k values to slots gives the
 // same sum): in k-step i of Q*K^T group g takes head-dim group 4i + g (8
 // values), for P*V group g takes tokens 4g..4g+3 of both pages.
-// Softmax is online (running max and sum per row, in log2 units), in fp32;
-// P enters the P*V MFMA as two bf16 parts, hi = bf16(P) and lo = bf16(P - hi),
-// so the product sees P to about 16 significant bits.
+// Softmax is online (running max and sum per row, in log2 units), in fp32.
+// In decode and the e4m3 prefill, P enters the P*V MFMA as two bf16 parts,
+// hi = bf16(P) and lo = bf16(P - hi), so the product sees P to about 16
+// significant bits; the bf16 prefill converts V to fp16 instead and takes P
+// in fp16 (11 bits), see attn_prefill_h_kernel.
 //
 // Memory: K and V are read with streaming (non-temporal) loads, each load
 // instruction covering whole 128-byte lines (K's page layout makes a k-step's
@@ -699,6 +701,311 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- prefill, bf16 KV
+//
+// The bf16-KV form of the prefill kernel, built around the cost of the
+// softmax: a wave64 VALU instruction holds the 16-lane SIMD for 4 cycles, a
+// quarter of a 16x16x32 MFMA, so at 8 waves per CU the vector instructions
+// per score, not LDS or memory, set the pace.  Same work split, grid and
+// three-stage LDS ring as attn_prefill_kernel; what changes:
+//  - The online softmax runs once per stage of four pages (64 keys) rather
+//    than per pair: one cross-lane max (lane-swap instructions, no LDS), one
+//    rescale of O per row block, and the scale folded into the exponent as
+//    one FMA per score.
+//  - P enters P*V in fp16 (11 significant bits; bf16 has 8) and V is
+//    converted to fp16 as it is staged: it comes through registers (two
+//    16-byte loads per thread per stage) rather than straight into LDS, and
+//    its slots past a page's valid count are written as zeros there.  bf16 ->
+//    fp16 is exact for magnitudes in [2^-14, 65504]; smaller ones keep an
+//    absolute error below 2^-25, and a V entry of 65520 or more would become
+//    infinite (activations of this model family stay many orders below).
+//  - Row sums come from the matrix core: a ninth P*V block whose A operand is
+//    all ones sums the same fp16 P that weighs V, in fp32.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16h(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+
+// Two floats -> packed fp16 (a in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
+}
+
+// Max over lanes l, l ^ 16, l ^ 32 and l ^ 48: each lane-swap instruction
+// returns its two operands with half of their 16-lane rows exchanged, so the
+// pair at lane l holds the values of lanes l and l ^ 32 (then l ^ 16).
+// (maximum, not fmaxf: no NaN reaches it, and fmaxf would first quiet every
+// operand with an extra instruction)
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// v *= a in place.  Written as assembly so that the registers of v stay the
+// same on both sides of the rarely taken branch that rescales: as plain code
+// the compiler copied all of O to fresh registers on every pair instead.
+__device__ __forceinline__ void scale_in_place(f32x4& v, float a) {
+  float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+  asm volatile("v_mul_f32 %0, %4, %0\n\tv_mul_f32 %1, %4, %1\n\tv_mul_f32 %2, %4, %2\n\tv_mul_f32 %3, %4, %3"
+               : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
+               : "v"(a));
+  v = f32x4{x0, x1, x2, x3};
+}
+
+// Headroom of the lazy reference maximum, in log2 units: P = 2^(s c - m)
+// may reach 2^8 (fp16 holds it exactly enough; sums stay far from fp32 range).
+constexpr float LAZY_LOG2 = 8.f;
+
+// One pair of pages (K blocks kp0, kp1 and V blocks vp0, vp1 of sb, V in
+// fp16) for RB row blocks.  m_ref is a reference maximum per row that moves
+// only when some score of the wave exceeds it by more than 2^LAZY_LOG2 (a
+// ballot, no cross-lane reduction); then it becomes the row's true maximum
+// and O is rescaled.  Any reference works for the softmax so long as no P
+// overflows: the sums, weighed by the same P, cancel it.  FULL: both pages
+// hold 16 tokens visible to every row of the wave.
+template <int HD, int RB, bool FULL>
+__device__ __forceinline__ void prefill_pair_h(const uint8_t* sb, int kp0, int kp1, int vp0, int vp1, int valid0,
+                                               int valid1, int start0, int start1, const uint4 (&qf)[RB][HD / 32],
+                                               f32x4 (&oacc)[RB][HD / 16 + 1], float (&m_ref)[RB],
+                                               float (&t_raw)[RB], const int (&qidx)[RB], float c, int vl,
+                                               int lane) {
+  constexpr int STEPS = HD / 32, DB = HD / 16, PAGE_B = PS * HD * 2;
+  const int g = lane >> 4;
+  // S^T per page: lane (g, n) holds the scores of query row n for tokens
+  // 4g .. 4g + 3 of the page
+  f32x4 s[RB][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint4 kf[STEPS];
+    const uint8_t* kb = sb + (j ? kp1 : kp0) * PAGE_B + lane * 16;
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) kf[i] = *reinterpret_cast<const uint4*>(kb + i * 1024);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < STEPS; ++i) acc = mfma16(kf[i], qf[rb][i], acc);
+      s[rb][j] = acc;
+    }
+  }
+  uint4 ph[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if constexpr (!FULL) {
+      const int qi = qidx[rb];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 4 * g + i;
+        s[rb][0][i] = tok < valid0 && start0 + tok <= qi ? s[rb][0][i] : -INFINITY;
+        s[rb][1][i] = tok < valid1 && start1 + tok <= qi ? s[rb][1][i] : -INFINITY;
+      }
+    }
+    const float mx = max3f(max3f(s[rb][0][0], s[rb][0][1], s[rb][0][2]), max3f(s[rb][0][3], s[rb][1][0], s[rb][1][1]),
+                           __builtin_elementwise_maximum(s[rb][1][2], s[rb][1][3]));
+    // c > 0, so max(s) c = max(s c): the test is on raw scores against
+    // t_raw = (m_ref + LAZY_LOG2) / c; a row still at -inf moves on any key
+    if (__builtin_amdgcn_ballot_w64(mx > t_raw[rb])) {  // wave-uniform, rare
+      const float m_new = __builtin_elementwise_maximum(m_ref[rb], max_over_groups(mx) * c);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_ref[rb] - m_new);
+      m_ref[rb] = m_new;
+      t_raw[rb] = m_new == -INFINITY ? -INFINITY : (m_new + LAZY_LOG2) / c;
+#pragma unroll
+      for (int b = 0; b <= DB; ++b) scale_in_place(oacc[rb][b], alpha);
+    }
+    const float nm = -m_ref[rb];
+    float p[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (FULL) p[j][i] = exp2_fast(fmaf(s[rb][j][i], c, nm));
+        else p[j][i] = nm == INFINITY ? 0.f : exp2_fast(fmaf(s[rb][j][i], c, nm));  // no key seen yet
+      }
+    // B operand of P*V: the 8 k-slots of lane group g are tokens 4g .. 4g + 3
+    // of the first page, then of the second
+    ph[rb] = make_uint4(pack_h2(p[0][0], p[0][1]), pack_h2(p[0][2], p[0][3]), pack_h2(p[1][0], p[1][1]),
+                        pack_h2(p[1][2], p[1][3]));
+  }
+  const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // fp16 1.0
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) oacc[rb][DB] = mfma16h(ones, ph[rb], oacc[rb][DB]);
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    const uint2 a0 = *reinterpret_cast<const uint2*>(sb + vp0 * PAGE_B + b * 16 * PS * 2 + vl);
+    const uint2 a1 = *reinterpret_cast<const uint2*>(sb + vp1 * PAGE_B + b * 16 * PS * 2 + vl);
+    const uint4 vf = make_uint4(a0.x, a0.y, a1.x, a1.y);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) oacc[rb][b] = mfma16h(vf, ph[rb], oacc[rb][b]);
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(PF_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
+  constexpr int RB = PREFILL_ROWS / (16 * PF_WAVES);
+  constexpr int DB = HD / 16;
+  constexpr int PAGE_B = PS * HD * 2;            // bytes of one page's K (or V) for one KV head
+  constexpr int SP = 4, NS = 3;                  // pages per stage, stages in the ring
+  constexpr int STAGE_B = SP * 2 * PAGE_B;
+  constexpr int PB_L = PAGE_B / 1024;            // 1 KiB loads per K (or V) block of a page
+  constexpr int HL = PB_L / 2;                   // K loads and V loads per wave per stage
+  static_assert(SP * 2 == PF_WAVES && HL >= 1, "two waves per page: half of its K and half of its V each");
+  __shared__ __attribute__((aligned(1024))) uint8_t skv[NS][STAGE_B];
+  const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4;
+  const int4 it = a.items[blockIdx.y];
+  const int kvh = blockIdx.x;
+  const int s = it.x, tb = it.y, nt = it.z;
+  const int G = a.nq / a.nkv;
+  const int row0 = a.seq_row0[s] + tb;
+  const int ctx = a.seq_ctx[s] + tb;  // logical index of the item's first token
+
+  uint4 qf[RB][HD / 32];
+  int qidx[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = wave * (RB * 16) + rb * 16 + n;
+    const int tq = r / G, h = r % G;
+    const bool ok = tq < nt;
+    qidx[rb] = ok ? ctx + tq : -1;
+    load_q<HD>(qf[rb], a.q + ((size_t)(row0 + (ok ? tq : 0)) * a.nq + kvh * G + h) * HD, ok, g);
+  }
+  const bool wave_live = wave * (RB * 16) / G < nt;
+  const int q_first = ctx + wave * (RB * 16) / G;
+  const int qmax = ctx + nt - 1;
+
+  f32x4 oacc[RB][DB + 1];
+  float m_ref[RB], t_raw[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_ref[rb] = t_raw[rb] = -INFINITY;
+#pragma unroll
+    for (int b = 0; b <= DB; ++b) oacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float c = a.sm_scale * LOG2E;
+  // V operand offset of this lane: row n of a 16-row block, tokens 4g ..; the
+  // vswz swap depends on bit 3 of the row, i.e. on n only, so every block's
+  // operand sits a fixed distance from it
+  const int vl = vswz((n * PS + 4 * g) * 2);
+  const uint32_t kofs = (uint32_t)(kvh * PS * HD) * 2;
+  const uint32_t vofs = (uint32_t)(a.nkv * PS * HD + kvh * HD * PS) * 2;
+  const uint32_t page_bytes = (uint32_t)a.page_stride * 2;
+  const uint8_t* kv = reinterpret_cast<const uint8_t*>(a.kv_layer);
+  const_i32_t* pg_id = (const_i32_t*)a.pg_id;
+  const_i32_t* pg_valid = (const_i32_t*)a.pg_valid;
+  const_i32_t* pg_start = (const_i32_t*)a.pg_start;
+  const int e_begin = a.seq_pg0[s];
+  int e_end = a.seq_pg0[s + 1];
+  while (e_end > e_begin && a.pg_start[e_end - 1] > qmax) --e_end;
+  const int n_stages = (e_end - e_begin + SP - 1) / SP;
+  __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
+
+  // This wave's share of a stage: page wave / 2 of it, 1 KiB blocks
+  // part0 .. part0 + HL - 1 of both its K and its V.  Stages past the end
+  // use a zero-size descriptor (zeros, no memory access).
+  const int pj = wave >> 1, part0 = (wave & 1) * HL;
+  auto issue = [&](int st) {
+    const int e = e_begin + st * SP + pj;
+    const bool live = st < n_stages && e < e_end;
+    const int pg = live ? pg_id[e] : 0;
+    const i32x4_t r = page_words(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
+    uint8_t* kd = &skv[st % NS][(2 * pj) * PAGE_B];
+#pragma unroll
+    for (int k = 0; k < HL; ++k) {
+      const int d = (part0 + k) * 1024 + lane * 16;
+      dma16(r, kd + (part0 + k) * 1024, kofs + (uint32_t)d, 0u);
+      // V rows are stored with their 16-byte halves swizzled (vswz, an involution)
+      dma16(r, kd + PAGE_B + (part0 + k) * 1024, vofs + (uint32_t)vswz(d), 0u);
+    }
+  };
+  // The V chunks this lane loaded (LDS bytes d of its page's V block, which
+  // hold source bytes vswz(d)), from bf16 to fp16 in place; token slots at
+  // or past the page's valid count become zeros.
+  auto convert_v = [&](int st) {
+    const int e = e_begin + st * SP + pj;
+    const int nv = st < n_stages && e < e_end ? pg_valid[e] : 0;
+    uint8_t* vd = &skv[st % NS][(2 * pj + 1) * PAGE_B];
+#pragma unroll
+    for (int k = 0; k < HL; ++k) {
+      const int d = (part0 + k) * 1024 + lane * 16;
+      const int t0 = ((vswz(d) % 32) / 16) * 8;  // first token of the chunk (a V row is 16 tokens)
+      const uint4 raw = *reinterpret_cast<const uint4*>(vd + d);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float lo = __uint_as_float(w[q] << 16), hi = __uint_as_float(w[q] & 0xffff0000u);
+        if (nv < PS) {  // wave-uniform: slots past the valid count may hold anything
+          lo = t0 + 2 * q < nv ? lo : 0.f;
+          hi = t0 + 2 * q + 1 < nv ? hi : 0.f;
+        }
+        o[q] = pack_h2(lo, hi);
+      }
+      *reinterpret_cast<uint4*>(vd + d) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+
+  if (n_stages > 0) {
+    // Stages st + 1 and st + 2 are in flight while stage st is computed; at
+    // the end of iteration st the wave waits for all but its 2 HL loads of
+    // stage st + 2, so stage st + 1 has landed, and converts its V share.
+    issue(0);
+    issue(1);
+    __builtin_amdgcn_s_waitcnt(PF_WAIT(2 * HL));
+    convert_v(0);
+    for (int st = 0; st < n_stages; ++st) {
+      // this wave's LDS writes are done (the ring's loads may still be in
+      // flight); after the barrier every wave's are, and the slot of stage
+      // st - 1 is free
+      __builtin_amdgcn_s_waitcnt(PF_WAIT(63));
+      asm volatile("s_barrier" ::: "memory");
+      issue(st + 2);
+      if (wave_live) {
+        const int eb = e_begin + st * SP;
+        const uint8_t* sb = skv[st % NS];
+#pragma unroll
+        for (int j0 = 0; j0 < SP; j0 += 2) {
+          const int e0 = eb + j0, e1 = eb + j0 + 1;
+          const int v0 = e0 < e_end ? pg_valid[e0] : 0, v1 = e1 < e_end ? pg_valid[e1] : 0;
+          const int s0 = e0 < e_end ? pg_start[e0] : 0, s1 = e1 < e_end ? pg_start[e1] : 0;
+          if (v0 == PS && v1 == PS && max(s0, s1) + PS - 1 <= q_first)
+            prefill_pair_h<HD, RB, true>(sb, 2 * j0, 2 * j0 + 2, 2 * j0 + 1, 2 * j0 + 3, v0, v1, s0, s1, qf, oacc,
+                                         m_ref, t_raw, qidx, c, vl, lane);
+          else
+            prefill_pair_h<HD, RB, false>(sb, 2 * j0, 2 * j0 + 2, 2 * j0 + 1, 2 * j0 + 3, v0, v1, s0, s1, qf, oacc,
+                                          m_ref, t_raw, qidx, c, vl, lane);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(PF_WAIT(2 * HL));
+      convert_v(st + 1);  // slot (st + 1) % NS: no wave reads it before the next barrier
+    }
+    // no load into this workgroup's LDS may still be in flight when it ends
+    __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (qidx[rb] < 0) continue;
+    const int r = wave * (RB * 16) + rb * 16 + n;
+    const int tq = r / G, h = r % G;
+    const float inv = 1.f / oacc[rb][DB][0];
+    uint16_t* o = a.o + ((size_t)(row0 + tq) * a.nq + kvh * G + h) * HD;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      uint2 w = make_uint2(pack_bf2(oacc[rb][b][0] * inv, oacc[rb][b][1] * inv),
+                           pack_bf2(oacc[rb][b][2] * inv, oacc[rb][b][3] * inv));
+      *reinterpret_cast<uint2*>(o + 16 * b + 4 * g) = w;
+    }
+  }
+}
+
 void launch_attn_decode(const AttnArgs& a, hipStream_t st) {
   if (a.n_items == 0) return;
   dim3 grid(a.n_items, a.nkv);
@@ -728,10 +1035,10 @@ void launch_attn_prefill(const AttnArgs& a0, hipStream_t st) {
     dim3 grid(a.nkv, a.n_items);
     if (a.hd == 128) {
       if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<128, true>), grid, dim3(PF_NT), 0, st, a);
-      else hipLaunchKernelGGL((attn_prefill_kernel<128, false>), grid, dim3(PF_NT), 0, st, a);
+      else hipLaunchKernelGGL(attn_prefill_h_kernel<128>, grid, dim3(PF_NT), 0, st, a);
     } else {
       if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<64, true>), grid, dim3(PF_NT), 0, st, a);
-      else hipLaunchKernelGGL((attn_prefill_kernel<64, false>), grid, dim3(PF_NT), 0, st, a);
+      else hipLaunchKernelGGL(attn_prefill_h_kernel<64>, grid, dim3(PF_NT), 0, st, a);
     }
   }
 }
