@@ -722,6 +722,10 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(AttnArgs a) {
 //  - Row sums come from the matrix core: a ninth P*V block whose A operand is
 //    all ones sums the same fp16 P that weighs V, in fp32.
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// Page ids a prefill workgroup keeps in LDS (16 KiB: sequences of up to
+// 65536 tokens at 16 per page).
+constexpr int PF_PT_MAX = 4096;
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16h(const uint4& a, const uint4& b, f32x4 c) {
@@ -765,28 +769,45 @@ __device__ __forceinline__ void scale_in_place(f32x4& v, float a) {
 // may reach 2^8 (fp16 holds it exactly enough; sums stay far from fp32 range).
 constexpr float LAZY_LOG2 = 8.f;
 
-// One pair of pages (K blocks kp0, kp1 and V blocks vp0, vp1 of sb, V in
-// fp16) for RB row blocks.  m_ref is a reference maximum per row that moves
-// only when some score of the wave exceeds it by more than 2^LAZY_LOG2 (a
-// ballot, no cross-lane reduction); then it becomes the row's true maximum
-// and O is rescaled.  Any reference works for the softmax so long as no P
-// overflows: the sums, weighed by the same P, cancel it.  FULL: both pages
-// hold 16 tokens visible to every row of the wave.
-template <int HD, int RB, bool FULL>
-__device__ __forceinline__ void prefill_pair_h(const uint8_t* sb, int kp0, int kp1, int vp0, int vp1, int valid0,
-                                               int valid1, int start0, int start1, const uint4 (&qf)[RB][HD / 32],
-                                               f32x4 (&oacc)[RB][HD / 16 + 1], float (&m_ref)[RB],
-                                               float (&t_raw)[RB], const int (&qidx)[RB], float c, int vl,
-                                               int lane) {
-  constexpr int STEPS = HD / 32, DB = HD / 16, PAGE_B = PS * HD * 2;
-  const int g = lane >> 4;
-  // S^T per page: lane (g, n) holds the scores of query row n for tokens
-  // 4g .. 4g + 3 of the page
-  f32x4 s[RB][2];
+// One pair of pages (32 keys) in four pieces: scores (qk_pair), their check
+// against the reference maximum (check_pair, with the rare rescale),
+// probabilities (exp_pair) and P*V (pv_pair).  The reference maximum m_ref
+// of a row moves only when some score of the wave exceeds it by more than
+// 2^LAZY_LOG2 (a ballot, no cross-lane reduction); then it becomes the
+// row's true maximum and O is rescaled.  Any reference works for the
+// softmax so long as no P overflows: the sums, weighed by the same P,
+// cancel it.
+// Token order within a pair: the two 16x16 score MFMAs of a pair
+// take their 16 rows from both pages, row r of MFMA j being token
+// 8 ((r / 4) % 2) + 4 j + r % 4 of page r / 8.  Lane group g then holds (in
+// MFMA 0, then 1) the scores of tokens 8 (g % 2) .. + 7 of page g / 2 in
+// order, which is also the P*V operand order; so each V operand is one
+// contiguous 16-byte read (k-slots only need to match between operands).
+// koff: this lane's K row of MFMA 0, head-dim group g, page and token as
+// above, from the pair's first K block.
+__device__ __forceinline__ int pipe_koff(int lane, int page_b) {
+  const int t = lane & 15, g = lane >> 4;
+  return 2 * (t >> 3) * page_b + (g * 16 + 8 * ((t >> 2) & 1) + (t & 3)) * 16;
+}
+
+// V operand of this lane, block 0: row n of page g / 2 of the pair, tokens
+// 8 (g % 2) .., under the vswz swap of rows with bit 3 set.
+__device__ __forceinline__ int pipe_voff(int lane, int page_b) {
+  const int n = lane & 15, g = lane >> 4;
+  return 2 * (g >> 1) * page_b + n * 32 + ((16 * (g & 1)) ^ (((n >> 3) & 1) << 4));
+}
+
+// (The scheduling barriers bound the LDS reads in flight: at four waves per
+// SIMD a wave has 128 registers, and left alone the compiler read every
+// operand of a pair ahead and spilled.)
+template <int HD, int RB, bool PIN = true>
+__device__ __forceinline__ void qk_pair(const uint8_t* sb, int kp0, const uint4 (&qf)[RB][HD / 32],
+                                        f32x4 (&s)[RB][2], int koff) {
+  constexpr int STEPS = HD / 32, PAGE_B = PS * HD * 2;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     uint4 kf[STEPS];
-    const uint8_t* kb = sb + (j ? kp1 : kp0) * PAGE_B + lane * 16;
+    const uint8_t* kb = sb + kp0 * PAGE_B + koff + j * 64;
 #pragma unroll
     for (int i = 0; i < STEPS; ++i) kf[i] = *reinterpret_cast<const uint4*>(kb + i * 1024);
 #pragma unroll
@@ -796,69 +817,169 @@ __device__ __forceinline__ void prefill_pair_h(const uint8_t* sb, int kp0, int k
       for (int i = 0; i < STEPS; ++i) acc = mfma16(kf[i], qf[rb][i], acc);
       s[rb][j] = acc;
     }
+    if (PIN) __builtin_amdgcn_sched_barrier(0);
   }
-  uint4 ph[RB];
+}
+
+// masked: scores of keys past a page's valid count or after a row's own
+// position become -inf (vld, stt: valid count and first position of the
+// pair's two pages; qidx: the row's position, -1 for an unused row).  Rows
+// that have seen no key yet stay at -inf.  (One code path for every pair,
+// the masking behind a wave-uniform branch: with a second copy of the pair
+// for masked stages the compiler hoisted the two copies' common LDS reads
+// above the branch and spilled.)
+template <int HD, int RB>
+__device__ __forceinline__ void check_pair(f32x4 (&s)[RB][2], f32x4 (&oacc)[RB][HD / 16 + 1], float (&m_ref)[RB],
+                                           float (&t_raw)[RB], float c, bool masked, int vld0, int vld1, int stt0,
+                                           int stt1, const int (&qidx)[RB], int lane) {
+  constexpr int DB = HD / 16;
+  if (masked) {
+    // token 8 (g % 2) + k of the lane's page is visible iff k < lim (one
+    // per-lane limit, so each test is against an inline constant)
+    const int g = lane >> 4;
+    const int vld = (g >> 1) ? vld1 : vld0, stt = (g >> 1) ? stt1 : stt0;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int lim = min(vld, qidx[rb] - stt + 1) - 8 * (g & 1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[rb][j][i] = 4 * j + i < lim ? s[rb][j][i] : -INFINITY;
+    }
+  }
+  float mx[RB];
+  bool up = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    if constexpr (!FULL) {
-      const int qi = qidx[rb];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 4 * g + i;
-        s[rb][0][i] = tok < valid0 && start0 + tok <= qi ? s[rb][0][i] : -INFINITY;
-        s[rb][1][i] = tok < valid1 && start1 + tok <= qi ? s[rb][1][i] : -INFINITY;
-      }
-    }
-    const float mx = max3f(max3f(s[rb][0][0], s[rb][0][1], s[rb][0][2]), max3f(s[rb][0][3], s[rb][1][0], s[rb][1][1]),
-                           __builtin_elementwise_maximum(s[rb][1][2], s[rb][1][3]));
+    mx[rb] = max3f(max3f(s[rb][0][0], s[rb][0][1], s[rb][0][2]), max3f(s[rb][0][3], s[rb][1][0], s[rb][1][1]),
+                   __builtin_elementwise_maximum(s[rb][1][2], s[rb][1][3]));
     // c > 0, so max(s) c = max(s c): the test is on raw scores against
     // t_raw = (m_ref + LAZY_LOG2) / c; a row still at -inf moves on any key
-    if (__builtin_amdgcn_ballot_w64(mx > t_raw[rb])) {  // wave-uniform, rare
-      const float m_new = __builtin_elementwise_maximum(m_ref[rb], max_over_groups(mx) * c);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_ref[rb] - m_new);
+    up = up || mx[rb] > t_raw[rb];
+  }
+  if (__builtin_amdgcn_ballot_w64(up)) {  // wave-uniform, rare: every row block moves to its true maximum
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float m_new = __builtin_elementwise_maximum(m_ref[rb], max_over_groups(mx[rb]) * c);
+      const bool seen = m_new != -INFINITY;
+      const float alpha = seen ? exp2_fast(m_ref[rb] - m_new) : 1.f;
       m_ref[rb] = m_new;
-      t_raw[rb] = m_new == -INFINITY ? -INFINITY : (m_new + LAZY_LOG2) / c;
+      t_raw[rb] = seen ? (m_new + LAZY_LOG2) / c : -INFINITY;
 #pragma unroll
       for (int b = 0; b <= DB; ++b) scale_in_place(oacc[rb][b], alpha);
     }
-    const float nm = -m_ref[rb];
+  }
+}
+
+template <int HD, int RB>
+__device__ __forceinline__ void exp_pair(const f32x4 (&s)[RB][2], const float (&m_ref)[RB], float c,
+                                         uint4 (&ph)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    // a row that has seen no key (m_ref = -inf) weighs nothing
+    const float nm = m_ref[rb] == -INFINITY ? -INFINITY : -m_ref[rb];
     float p[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (FULL) p[j][i] = exp2_fast(fmaf(s[rb][j][i], c, nm));
-        else p[j][i] = nm == INFINITY ? 0.f : exp2_fast(fmaf(s[rb][j][i], c, nm));  // no key seen yet
-      }
-    // B operand of P*V: the 8 k-slots of lane group g are tokens 4g .. 4g + 3
-    // of the first page, then of the second
+      for (int i = 0; i < 4; ++i) p[j][i] = exp2_fast(fmaf(s[rb][j][i], c, nm));
+    // B operand of P*V: lane group g's 8 k-slots are tokens 8 (g % 2) .. + 7
+    // of page g / 2 (MFMA 0 gave the first four, MFMA 1 the next)
     ph[rb] = make_uint4(pack_h2(p[0][0], p[0][1]), pack_h2(p[0][2], p[0][3]), pack_h2(p[1][0], p[1][1]),
                         pack_h2(p[1][2], p[1][3]));
   }
+}
+
+template <int HD, int RB, bool PIN = true>
+__device__ __forceinline__ void pv_pair(const uint8_t* sb, int vp0, const uint4 (&ph)[RB],
+                                        f32x4 (&oacc)[RB][HD / 16 + 1], int voff) {
+  constexpr int DB = HD / 16, PAGE_B = PS * HD * 2;
   const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // fp16 1.0
+  const uint8_t* vb = sb + vp0 * PAGE_B + voff;
+  uint4 vf[2];
+  vf[0] = *reinterpret_cast<const uint4*>(vb);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) oacc[rb][DB] = mfma16h(ones, ph[rb], oacc[rb][DB]);
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
-    const uint2 a0 = *reinterpret_cast<const uint2*>(sb + vp0 * PAGE_B + b * 16 * PS * 2 + vl);
-    const uint2 a1 = *reinterpret_cast<const uint2*>(sb + vp1 * PAGE_B + b * 16 * PS * 2 + vl);
-    const uint4 vf = make_uint4(a0.x, a0.y, a1.x, a1.y);
+    // operand b + 1 in flight while block b's MFMAs issue
+    if (b + 1 < DB) vf[(b + 1) & 1] = *reinterpret_cast<const uint4*>(vb + (b + 1) * 16 * PS * 2);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) oacc[rb][b] = mfma16h(vf, ph[rb], oacc[rb][b]);
+    for (int rb = 0; rb < RB; ++rb) oacc[rb][b] = mfma16h(vf[b & 1], ph[rb], oacc[rb][b]);
+    if (PIN) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
+// One step of the software pipeline: probabilities and P*V of the older
+// pair (scores s_old, V blocks ev0 and ev0 + 2 of se) in the same
+// straight-line block as the scores and check of the newer one (K blocks
+// qk0, qk0 + 2 of sq), so that the matrix core runs one pair's MFMAs while
+// the vector unit works on the other's softmax.  Without it a wave's pair is
+// MFMAs, then softmax, then MFMAs, and the two waves of a SIMD, in step with
+// each other, leave one unit idle while the other works.
+template <int HD, int RB, bool HQ>
+__device__ __forceinline__ void pipe_step(const uint8_t* sq, int qk0, f32x4 (&s_new)[RB][2], bool masked,
+                                          const int (&pv)[2], const int (&ps)[2], const uint8_t* se, int ev0,
+                                          const f32x4 (&s_old)[RB][2], const uint4 (&qf)[RB][HD / 32],
+                                          f32x4 (&oacc)[RB][HD / 16 + 1], float (&m_ref)[RB], float (&t_raw)[RB],
+                                          const int (&qidx)[RB], float c, int koff, int voff, int lane) {
+  constexpr int STEPS = HD / 32, DB = HD / 16;
+  uint4 ph[RB];
+  exp_pair<HD, RB>(s_old, m_ref, c, ph);
+  if constexpr (HQ) qk_pair<HD, RB, false>(sq, qk0, qf, s_new, koff);
+  pv_pair<HD, RB, false>(se, ev0, ph, oacc, voff);
+  // Issue order: the pair's K reads, then each score MFMA followed by three
+  // vector instructions of the older pair's softmax, then the P*V MFMAs with
+  // the V reads two blocks ahead.  (Left alone, the compiler put all the
+  // exponentials in one run ahead of the MFMAs.)
+  if constexpr (HQ) {
+    __builtin_amdgcn_sched_group_barrier(0x100, STEPS, 0);  // K reads, first score MFMA
+#pragma unroll
+    for (int i = 0; i < 2 * RB * STEPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (i == 1) __builtin_amdgcn_sched_group_barrier(0x100, STEPS, 0);  // K reads, second score MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);  // three VALU (transcendental ones included)
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V reads of blocks 0 and 1
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);  // row sums and block 0
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    if (b > 0) __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+    if (b + 2 < DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
+  }
+  // after P*V of the older pair: a rescale covers it too
+  if constexpr (HQ) check_pair<HD, RB>(s_new, oacc, m_ref, t_raw, c, masked, pv[0], pv[1], ps[0], ps[1], qidx, lane);
+}
+
+// 8 waves of two 16-row blocks each (188 registers, two waves per SIMD).
+// Sixteen waves of one block each measured 8% slower: every wave reads all of
+// a stage's K and V from LDS, so that doubles the operand reads.  No
+// register may spill here: a reload is a vector memory load, and since the
+// compiler does not see the ring's LDS-bound loads it waits for all of them
+// before it.
+constexpr int PH_WAVES = 8, PH_NT = 64 * PH_WAVES;
+
 template <int HD>
-__global__ __launch_bounds__(PF_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
-  constexpr int RB = PREFILL_ROWS / (16 * PF_WAVES);
+__global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
+  constexpr int RB = PREFILL_ROWS / (16 * PH_WAVES);
   constexpr int DB = HD / 16;
   constexpr int PAGE_B = PS * HD * 2;            // bytes of one page's K (or V) for one KV head
-  constexpr int SP = 4, NS = 3;                  // pages per stage, stages in the ring
+  // pages per stage, stages in the ring: four, since a stage's last pair is
+  // finished after the barrier that lets stage + 3 load
+  constexpr int SP = 4, NS = 4;
   constexpr int STAGE_B = SP * 2 * PAGE_B;
   constexpr int PB_L = PAGE_B / 1024;            // 1 KiB loads per K (or V) block of a page
   constexpr int HL = PB_L / 2;                   // K loads and V loads per wave per stage
-  static_assert(SP * 2 == PF_WAVES && HL >= 1, "two waves per page: half of its K and half of its V each");
+  constexpr int LPW = 2 * HL;                    // loads per wave per stage
+  static_assert(PH_WAVES == 2 * SP && HL >= 1, "two waves per page: half of its K and half of its V each");
   __shared__ __attribute__((aligned(1024))) uint8_t skv[NS][STAGE_B];
+  // The sequence's page ids, so that the ring reads them from LDS: a scalar
+  // load in the loop makes the next LDS wait wait for it too (scalar loads
+  // complete out of order, so such a wait is for everything), and a miss
+  // cost about 1600 cycles per stage.  Longer page tables use scalar loads.
+  __shared__ int s_pid[PF_PT_MAX];
   const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4;
   const int4 it = a.items[blockIdx.y];
   const int kvh = blockIdx.x;
@@ -878,7 +999,6 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     load_q<HD>(qf[rb], a.q + ((size_t)(row0 + (ok ? tq : 0)) * a.nq + kvh * G + h) * HD, ok, g);
   }
   const bool wave_live = wave * (RB * 16) / G < nt;
-  const int q_first = ctx + wave * (RB * 16) / G;
   const int qmax = ctx + nt - 1;
 
   f32x4 oacc[RB][DB + 1];
@@ -890,10 +1010,7 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     for (int b = 0; b <= DB; ++b) oacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float c = a.sm_scale * LOG2E;
-  // V operand offset of this lane: row n of a 16-row block, tokens 4g ..; the
-  // vswz swap depends on bit 3 of the row, i.e. on n only, so every block's
-  // operand sits a fixed distance from it
-  const int vl = vswz((n * PS + 4 * g) * 2);
+  const int koff = pipe_koff(lane, PAGE_B), voff = pipe_voff(lane, PAGE_B);
   const uint32_t kofs = (uint32_t)(kvh * PS * HD) * 2;
   const uint32_t vofs = (uint32_t)(a.nkv * PS * HD + kvh * HD * PS) * 2;
   const uint32_t page_bytes = (uint32_t)a.page_stride * 2;
@@ -905,16 +1022,40 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   int e_end = a.seq_pg0[s + 1];
   while (e_end > e_begin && a.pg_start[e_end - 1] > qmax) --e_end;
   const int n_stages = (e_end - e_begin + SP - 1) / SP;
+  const bool pt_lds = e_end - e_begin <= PF_PT_MAX;
+  if (pt_lds)
+    for (int i = threadIdx.x; i < e_end - e_begin; i += PH_NT) s_pid[i] = a.pg_id[e_begin + i];
+
+  // Leading stages whose four pages are complete and precede the item's
+  // first token need no masking for any row.  (Pages are checked 64 at a
+  // time, one per lane; the first page that fails ends the run.)
+  int n_full = 0;
+  for (int e0 = e_begin;; e0 += 64) {
+    const int e = e0 + lane;
+    const bool ok = e < e_end && a.pg_valid[e] == PS && a.pg_start[e] + PS - 1 <= ctx;
+    const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
+    if (bad) {
+      n_full = (e0 - e_begin + (int)__builtin_ctzll(bad)) / SP;
+      break;
+    }
+  }
   __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
 
   // This wave's share of a stage: page wave / 2 of it, 1 KiB blocks
-  // part0 .. part0 + HL - 1 of both its K and its V.  Stages past the end
-  // use a zero-size descriptor (zeros, no memory access).
+  // part0 .. part0 + HL - 1 of both its K and its V, so that every wave
+  // converts the same share of V (with whole blocks per wave, half of the
+  // waves converted and the others waited at the barrier).  Stages past the
+  // end use a zero-size descriptor (zeros, no memory access).  Page ids and
+  // valid counts come in as arguments, read a stage ahead.
   const int pj = wave >> 1, part0 = (wave & 1) * HL;
-  auto issue = [&](int st) {
-    const int e = e_begin + st * SP + pj;
-    const bool live = st < n_stages && e < e_end;
-    const int pg = live ? pg_id[e] : 0;
+  auto live_entry = [&](int st) { return st < n_stages && e_begin + st * SP + pj < e_end; };
+  auto entry = [&](int st) { return min(e_begin + st * SP + pj, e_end - 1); };  // clamped: always readable
+  auto page_id = [&](int st) {
+    return pt_lds ? __builtin_amdgcn_readfirstlane(s_pid[entry(st) - e_begin]) : pg_id[entry(st)];
+  };
+  auto issue = [&](int st, int pg_raw) {
+    const bool live = live_entry(st);
+    const int pg = live ? pg_raw : 0;
     const i32x4_t r = page_words(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
     uint8_t* kd = &skv[st % NS][(2 * pj) * PAGE_B];
 #pragma unroll
@@ -928,9 +1069,8 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   // The V chunks this lane loaded (LDS bytes d of its page's V block, which
   // hold source bytes vswz(d)), from bf16 to fp16 in place; token slots at
   // or past the page's valid count become zeros.
-  auto convert_v = [&](int st) {
-    const int e = e_begin + st * SP + pj;
-    const int nv = st < n_stages && e < e_end ? pg_valid[e] : 0;
+  auto convert_v = [&](int st, int nv_raw) {
+    const int nv = live_entry(st) ? nv_raw : 0;
     uint8_t* vd = &skv[st % NS][(2 * pj + 1) * PAGE_B];
 #pragma unroll
     for (int k = 0; k < HL; ++k) {
@@ -952,40 +1092,75 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     }
   };
 
+  // valid counts and first positions of a stage's pair q, read only for
+  // stages after the run of complete ones
+  auto pair_meta = [&](int st, int q, int (&pv)[2], int (&ps)[2]) {
+    pv[0] = pv[1] = PS;
+    ps[0] = ps[1] = 0;
+    if (st >= n_full) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = e_begin + st * SP + 2 * q + j;
+        pv[j] = e < e_end ? pg_valid[e] : 0;
+        ps[j] = e < e_end ? pg_start[e] : 0;
+      }
+    }
+  };
+
   if (n_stages > 0) {
-    // Stages st + 1 and st + 2 are in flight while stage st is computed; at
-    // the end of iteration st the wave waits for all but its 2 HL loads of
-    // stage st + 2, so stage st + 1 has landed, and converts its V share.
-    issue(0);
-    issue(1);
-    __builtin_amdgcn_s_waitcnt(PF_WAIT(2 * HL));
-    convert_v(0);
+    // Ring: right after the barrier that opens stage st the wave issues
+    // stage st + 2; in the middle of stage st it waits for all but its LPW
+    // loads of stage st + 2, so stage st + 1 has landed, and converts its V
+    // share; a barrier then opens stage st + 1.
+    __syncthreads();  // the page-id table is written (no ring load in flight yet)
+    issue(0, page_id(0));
+    issue(1, page_id(1));
+    int pid = page_id(2);
+    const int nv0 = pg_valid[entry(0)];
+    int nvn = pg_valid[entry(1)];
+    __builtin_amdgcn_s_waitcnt(PF_WAIT(LPW));
+    convert_v(0, nv0);
+    __builtin_amdgcn_s_waitcnt(PF_WAIT(63));
+    asm volatile("s_barrier" ::: "memory");
+    issue(2, pid);
+    pid = page_id(3);
+    // Pair 2st + 1's scores go with pair 2st's softmax and P*V, pair
+    // 2st + 2's (next stage) with pair 2st + 1's, which is why a stage's
+    // last pair is finished after the next stage's barrier.  The last stage
+    // is peeled so that no branch holds two copies of a step.
+    f32x4 sa[RB][2], sb2[RB][2];
+    int pv[2], ps[2];
+    if (wave_live) {
+      pair_meta(0, 0, pv, ps);
+      qk_pair<HD, RB>(skv[0], 0, qf, sa, koff);
+      check_pair<HD, RB>(sa, oacc, m_ref, t_raw, c, n_full == 0, pv[0], pv[1], ps[0], ps[1], qidx, lane);
+    }
     for (int st = 0; st < n_stages; ++st) {
-      // this wave's LDS writes are done (the ring's loads may still be in
-      // flight); after the barrier every wave's are, and the slot of stage
-      // st - 1 is free
+      const uint8_t* sb = skv[st % NS];
+      const bool last = st + 1 == n_stages;
+      if (wave_live) {
+        pair_meta(st, 1, pv, ps);
+        pipe_step<HD, RB, true>(sb, 4, sb2, st >= n_full, pv, ps, sb, 1, sa, qf, oacc, m_ref, t_raw, qidx, c, koff,
+                                voff, lane);
+      }
+      __builtin_amdgcn_s_waitcnt(PF_WAIT(LPW));
+      convert_v(st + 1, nvn);  // slot (st + 1) % NS: no wave reads it before the next barrier
+      // stages before n_full hold complete pages; later ones need their count
+      nvn = st + 2 < n_full ? PS : pg_valid[entry(st + 2)];
       __builtin_amdgcn_s_waitcnt(PF_WAIT(63));
       asm volatile("s_barrier" ::: "memory");
-      issue(st + 2);
+      issue(st + 3, pid);
+      pid = page_id(st + 4);
+      if (last) break;
       if (wave_live) {
-        const int eb = e_begin + st * SP;
-        const uint8_t* sb = skv[st % NS];
-#pragma unroll
-        for (int j0 = 0; j0 < SP; j0 += 2) {
-          const int e0 = eb + j0, e1 = eb + j0 + 1;
-          const int v0 = e0 < e_end ? pg_valid[e0] : 0, v1 = e1 < e_end ? pg_valid[e1] : 0;
-          const int s0 = e0 < e_end ? pg_start[e0] : 0, s1 = e1 < e_end ? pg_start[e1] : 0;
-          if (v0 == PS && v1 == PS && max(s0, s1) + PS - 1 <= q_first)
-            prefill_pair_h<HD, RB, true>(sb, 2 * j0, 2 * j0 + 2, 2 * j0 + 1, 2 * j0 + 3, v0, v1, s0, s1, qf, oacc,
-                                         m_ref, t_raw, qidx, c, vl, lane);
-          else
-            prefill_pair_h<HD, RB, false>(sb, 2 * j0, 2 * j0 + 2, 2 * j0 + 1, 2 * j0 + 3, v0, v1, s0, s1, qf, oacc,
-                                          m_ref, t_raw, qidx, c, vl, lane);
-        }
+        pair_meta(st + 1, 0, pv, ps);
+        pipe_step<HD, RB, true>(skv[(st + 1) % NS], 0, sa, st + 1 >= n_full, pv, ps, sb, 5, sb2, qf, oacc, m_ref,
+                                t_raw, qidx, c, koff, voff, lane);
       }
-      __builtin_amdgcn_s_waitcnt(PF_WAIT(2 * HL));
-      convert_v(st + 1);  // slot (st + 1) % NS: no wave reads it before the next barrier
     }
+    if (wave_live)  // the last pair: no next one to start
+      pipe_step<HD, RB, false>(skv[0], 0, sa, false, pv, ps, skv[(n_stages - 1) % NS], 5, sb2, qf, oacc, m_ref,
+                               t_raw, qidx, c, koff, voff, lane);
     // no load into this workgroup's LDS may still be in flight when it ends
     __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
   }
@@ -1035,10 +1210,10 @@ void launch_attn_prefill(const AttnArgs& a0, hipStream_t st) {
     dim3 grid(a.nkv, a.n_items);
     if (a.hd == 128) {
       if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<128, true>), grid, dim3(PF_NT), 0, st, a);
-      else hipLaunchKernelGGL(attn_prefill_h_kernel<128>, grid, dim3(PF_NT), 0, st, a);
+      else hipLaunchKernelGGL(attn_prefill_h_kernel<128>, grid, dim3(PH_NT), 0, st, a);
     } else {
       if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<64, true>), grid, dim3(PF_NT), 0, st, a);
-      else hipLaunchKernelGGL(attn_prefill_h_kernel<64>, grid, dim3(PF_NT), 0, st, a);
+      else hipLaunchKernelGGL(attn_prefill_h_kernel<64>, grid, dim3(PH_NT), 0, st, a);
     }
   }
 }
