@@ -642,3 +642,47 @@ def test_mid_decode_split_qkv_and_split_attention(torch_cuda, kv):
             rep.add(toks[s], t, m, tau_for(0, 1.0), lg[s], ref[s][k], ("mid", k, s))
     rep.check()
     rt.close()
+
+
+def test_mid_prefill_fork_at_partial_page_and_chunked(torch_cuda):
+    """Prefill at head dim 128 with masking away from the diagonal: a
+    150-token prefix (its last page holds 6 tokens) forked twice, the
+    children's suffixes (300 and 133 tokens) prefilled in one launch, so that
+    their page tables hold a partly filled page in the middle; and a
+    370-token prompt prefilled as 200 + 170 tokens, whose second chunk starts
+    inside a page.  Readouts spread over each chunk (first token, both sides
+    of a 64-token item boundary, the last token), against the oracle."""
+    from paged_kv_forward_amd.runtime import Pass
+    shape = MID
+    recipe = synth.WeightRecipe(shape, weight_seed=9, gain_std=0.02)
+    pre = synth.prompt_tokens(1, 700, 150, shape.vocab)
+    sufs = [synth.prompt_tokens(1, 701, 300, shape.vocab), synth.prompt_tokens(1, 702, 133, shape.vocab)]
+    longp = synth.prompt_tokens(1, 703, 370, shape.vocab)
+    reads = [[0, 63, 64, 150, 299], [0, 5, 6, 70, 132]]
+    rq = [0, 7, 8, 100, 169]
+    w = SynthWeights(recipe, cache_layers=True)
+    num = default_numerics(shape)
+    say("mid prefill fork/chunked: oracle")
+    tree = [Chunk(pre, np.arange(150), -1, []),
+            Chunk(sufs[0], 150 + np.arange(300), 0, reads[0]),
+            Chunk(sufs[1], 150 + np.arange(133), 0, reads[1]),
+            Chunk(longp[:200], np.arange(200), -1, []),
+            Chunk(longp[200:], 200 + np.arange(170), 3, rq)]
+    ref = forward_chunks(w, tree, num)
+    rt = make_runtime(shape, recipe, torch_cuda, max_rows=1500, max_seqs=4, max_readout=16, max_ctx=1200, pages=256)
+    p, q = rt.alloc(), rt.alloc()
+    rt.forward([Pass(p, pre), Pass(q, longp[:200])])
+    kids = [rt.fork(p) for _ in range(2)]
+    passes = [Pass(kids[b], sufs[b], reads[b], [(0, 1.0, 0)] * len(reads[b])) for b in range(2)]
+    passes.append(Pass(q, longp[200:], rq, [(0, 1.0, 0)] * len(rq)))
+    toks, logits = rt.forward(passes, want_logits=True)
+    assert rt.pool_stats()["kv_bytes_copied"] == 0
+    rep = Report()
+    row = 0
+    for ci, rs in ((1, reads[0]), (2, reads[1]), (4, rq)):
+        for k, r in enumerate(rs):
+            t, m = apply(ref[ci][k], 0)
+            rep.add(toks[row], t, m, tau_for(0, 1.0), logits[row], ref[ci][k], ("chunk", ci, r))
+            row += 1
+    rep.check()
+    rt.close()
