@@ -164,7 +164,7 @@ def summarize_prefill(trace, prof):
                 proj = "down" if prev == "gate_up" else "o"
             dur[proj].append(us)
             prev = proj
-        elif k.startswith("pie::attn_prefill_kernel"):
+        elif k.startswith("pie::attn_prefill"):  # attn_prefill_h_kernel (bf16 KV) or attn_prefill_kernel (e4m3)
             attn.append(us)
             prev = "attn"
     rows = ["# Prefill kernels of the benchmark run (Llama-3.1-8B shape, 8192 rows per launch)", "",
@@ -540,9 +540,15 @@ def main():
     nxt = np.zeros(N_SEQ, dtype=np.int32)
     gemm_classes = ["gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down"]
     n_launch = N_SEQ // PREFILL_SEQS_PER_LAUNCH
+    t_untimed, n_untimed = None, 0
     for b in range(0, N_SEQ, PREFILL_SEQS_PER_LAUNCH):
         if b // PREFILL_SEQS_PER_LAUNCH == n_launch - PREFILL_TIMED_LAUNCHES:
-            # the last launches run with HIP events around every GEMM launch
+            # prefill tokens/s is taken over the launches before this point:
+            # the event records of the profiled ones below add gaps
+            torch.cuda.synchronize()
+            t_untimed, n_untimed = time.perf_counter() - t0, b
+            # the last launches run with HIP events around every GEMM and
+            # prefill-attention launch
             rt.profile_enable(gemm_classes + ["attn_prefill"])
         ss = range(b, b + PREFILL_SEQS_PER_LAUNCH)
         toks, _ = rt.forward([Pass(ws[s], prompts[s], [PROMPT - 1], [(0, 1.0, 0)]) for s in ss])
@@ -565,13 +571,14 @@ def main():
         "unit": "TFLOP/s", "frac": round(tot_flop / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "flops_per_launch": tot_flop, "gemm_ms_per_launch": round(tot_ms, 3),
         "by_projection_tflops": {c[5:]: round(gemm_flop[c] / (gemm_ms[c] * 1e-3) / 1e12, 1) for c in gemm_classes},
+        # all layers of one prefill launch
         "attn_prefill_ms_per_launch": round(pf["attn_prefill"][0] / PREFILL_TIMED_LAUNCHES, 3),
         # causal attention: scores and P.V, 2 x 2 flops per (query, key <= query) pair per head dim
         "attn_prefill_tflops": round(4.0 * shape.n_q_heads * shape.head_dim * (PROMPT * (PROMPT + 1) / 2)
                                      * PREFILL_SEQS_PER_LAUNCH * shape.n_layers
                                      / (pf["attn_prefill"][0] / PREFILL_TIMED_LAUNCHES * 1e-3) / 1e12, 1),
-        "timed_over": "the last %d prefill launches (%d rows each), HIP events around every GEMM launch"
-                      % (PREFILL_TIMED_LAUNCHES, T_pf)}
+        "timed_over": "the last %d prefill launches (%d rows each), HIP events around every GEMM and "
+                      "prefill-attention launch" % (PREFILL_TIMED_LAUNCHES, T_pf)}
 
     ws_arr = np.array(ws, dtype=np.uint64)
 
@@ -695,7 +702,11 @@ def main():
         "step_hbm": {"bytes_per_step": int(step_bytes),
                      "achieved_gbs": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "prefill_tokens_per_s": round(N_SEQ * PROMPT / t_prefill, 1),
+        # the launches before the profiled ones (whose event records add gaps)
+        "prefill_tokens_per_s": round(n_untimed * PROMPT / t_untimed, 1),
+        "prefill_tokens_per_s_over": "%d of %d prefill launches (%d sequences of %d tokens each), before the "
+                                     "profiled ones" % (n_untimed // PREFILL_SEQS_PER_LAUNCH, n_launch,
+                                                        PREFILL_SEQS_PER_LAUNCH, PROMPT),
         "prefill_gemm": prefill_gemm,
     }
     out["ms_per_step_by_kernel"] = breakdown

@@ -777,17 +777,21 @@ constexpr float LAZY_LOG2 = 8.f;
 // row's true maximum and O is rescaled.  Any reference works for the
 // softmax so long as no P overflows: the sums, weighed by the same P,
 // cancel it.
-// Token order within a pair: the two 16x16 score MFMAs of a pair
-// take their 16 rows from both pages, row r of MFMA j being token
-// 8 ((r / 4) % 2) + 4 j + r % 4 of page r / 8.  Lane group g then holds (in
-// MFMA 0, then 1) the scores of tokens 8 (g % 2) .. + 7 of page g / 2 in
-// order, which is also the P*V operand order; so each V operand is one
-// contiguous 16-byte read (k-slots only need to match between operands).
-// koff: this lane's K row of MFMA 0, head-dim group g, page and token as
-// above, from the pair's first K block.
-__device__ __forceinline__ int pipe_koff(int lane, int page_b) {
-  const int t = lane & 15, g = lane >> 4;
-  return 2 * (t >> 3) * page_b + (g * 16 + 8 * ((t >> 2) & 1) + (t & 3)) * 16;
+// Token order within a pair: the two 16x16 score MFMAs of a pair take their
+// 16 rows from both pages, row r of MFMA j being token
+// 8 ((r / 4) % 2) + 4 (p ^ j) + r % 4 of page p = r / 8.  Lane group g then
+// holds (in MFMA 0, then 1) the scores of tokens 8 (g % 2) .. + 7 of page
+// g / 2: in order for the first page, halves swapped (+4 .. +7 first) for
+// the second, whose V the conversion stores with the same swap.  So each
+// P*V operand is one contiguous 16-byte read (k-slots only need to match
+// between operands), and the K reads of one MFMA cover all 64 LDS banks:
+// with the same tokens from both pages (8 KiB apart) they hit half of the
+// banks twice.
+// koff0 / koff1: this lane's K row of MFMA 0 / 1, head-dim group g, from the
+// pair's first K block.
+__device__ __forceinline__ int pipe_koff(int lane, int page_b, int j) {
+  const int t = lane & 15, g = lane >> 4, p = t >> 3;
+  return 2 * p * page_b + (g * 16 + 8 * ((t >> 2) & 1) + 4 * (p ^ j) + (t & 3)) * 16;
 }
 
 // V operand of this lane, block 0: row n of page g / 2 of the pair, tokens
@@ -802,12 +806,12 @@ __device__ __forceinline__ int pipe_voff(int lane, int page_b) {
 // operand of a pair ahead and spilled.)
 template <int HD, int RB, bool PIN = true>
 __device__ __forceinline__ void qk_pair(const uint8_t* sb, int kp0, const uint4 (&qf)[RB][HD / 32],
-                                        f32x4 (&s)[RB][2], int koff) {
+                                        f32x4 (&s)[RB][2], int koff0, int koff1) {
   constexpr int STEPS = HD / 32, PAGE_B = PS * HD * 2;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     uint4 kf[STEPS];
-    const uint8_t* kb = sb + kp0 * PAGE_B + koff + j * 64;
+    const uint8_t* kb = sb + kp0 * PAGE_B + (j ? koff1 : koff0);
 #pragma unroll
     for (int i = 0; i < STEPS; ++i) kf[i] = *reinterpret_cast<const uint4*>(kb + i * 1024);
 #pragma unroll
@@ -834,17 +838,20 @@ __device__ __forceinline__ void check_pair(f32x4 (&s)[RB][2], f32x4 (&oacc)[RB][
                                            int stt1, const int (&qidx)[RB], int lane) {
   constexpr int DB = HD / 16;
   if (masked) {
-    // token 8 (g % 2) + k of the lane's page is visible iff k < lim (one
-    // per-lane limit, so each test is against an inline constant)
+    // token 8 (g % 2) + k of the lane's page is visible iff k < lim (per-lane
+    // limits, so each test is against an inline constant)
     const int g = lane >> 4;
     const int vld = (g >> 1) ? vld1 : vld0, stt = (g >> 1) ? stt1 : stt0;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+      // MFMA j holds tokens 8 (g % 2) + 4 ((g / 2) ^ j) + i
       const int lim = min(vld, qidx[rb] - stt + 1) - 8 * (g & 1);
+      const int lim0 = lim - 4 * (g >> 1), lim1 = lim - 4 * ((g >> 1) ^ 1);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[rb][j][i] = 4 * j + i < lim ? s[rb][j][i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        s[rb][0][i] = i < lim0 ? s[rb][0][i] : -INFINITY;
+        s[rb][1][i] = i < lim1 ? s[rb][1][i] : -INFINITY;
+      }
     }
   }
   float mx[RB];
@@ -884,7 +891,8 @@ __device__ __forceinline__ void exp_pair(const f32x4 (&s)[RB][2], const float (&
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[j][i] = exp2_fast(fmaf(s[rb][j][i], c, nm));
     // B operand of P*V: lane group g's 8 k-slots are tokens 8 (g % 2) .. + 7
-    // of page g / 2 (MFMA 0 gave the first four, MFMA 1 the next)
+    // of page g / 2 (first page: MFMA 0 gave the first four, MFMA 1 the next;
+    // second page: the other way round, as its V is stored)
     ph[rb] = make_uint4(pack_h2(p[0][0], p[0][1]), pack_h2(p[0][2], p[0][3]), pack_h2(p[1][0], p[1][1]),
                         pack_h2(p[1][2], p[1][3]));
   }
@@ -922,11 +930,12 @@ __device__ __forceinline__ void pipe_step(const uint8_t* sq, int qk0, f32x4 (&s_
                                           const int (&pv)[2], const int (&ps)[2], const uint8_t* se, int ev0,
                                           const f32x4 (&s_old)[RB][2], const uint4 (&qf)[RB][HD / 32],
                                           f32x4 (&oacc)[RB][HD / 16 + 1], float (&m_ref)[RB], float (&t_raw)[RB],
-                                          const int (&qidx)[RB], float c, int koff, int voff, int lane) {
+                                          const int (&qidx)[RB], float c, int koff0, int koff1, int voff,
+                                          int lane) {
   constexpr int STEPS = HD / 32, DB = HD / 16;
   uint4 ph[RB];
   exp_pair<HD, RB>(s_old, m_ref, c, ph);
-  if constexpr (HQ) qk_pair<HD, RB, false>(sq, qk0, qf, s_new, koff);
+  if constexpr (HQ) qk_pair<HD, RB, false>(sq, qk0, qf, s_new, koff0, koff1);
   pv_pair<HD, RB, false>(se, ev0, ph, oacc, voff);
   // Issue order: the pair's K reads, then each score MFMA followed by three
   // vector instructions of the older pair's softmax, then the P*V MFMAs with
@@ -1010,7 +1019,7 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     for (int b = 0; b <= DB; ++b) oacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float c = a.sm_scale * LOG2E;
-  const int koff = pipe_koff(lane, PAGE_B), voff = pipe_voff(lane, PAGE_B);
+  const int koff0 = pipe_koff(lane, PAGE_B, 0), koff1 = pipe_koff(lane, PAGE_B, 1), voff = pipe_voff(lane, PAGE_B);
   const uint32_t kofs = (uint32_t)(kvh * PS * HD) * 2;
   const uint32_t vofs = (uint32_t)(a.nkv * PS * HD + kvh * HD * PS) * 2;
   const uint32_t page_bytes = (uint32_t)a.page_stride * 2;
@@ -1088,7 +1097,10 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
         }
         o[q] = pack_h2(lo, hi);
       }
-      *reinterpret_cast<uint4*>(vd + d) = make_uint4(o[0], o[1], o[2], o[3]);
+      // the second page of a pair holds its 8-token groups halves swapped
+      // (see the token order above)
+      *reinterpret_cast<uint4*>(vd + d) =
+          (pj & 1) ? make_uint4(o[2], o[3], o[0], o[1]) : make_uint4(o[0], o[1], o[2], o[3]);
     }
   };
 
@@ -1132,7 +1144,7 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     int pv[2], ps[2];
     if (wave_live) {
       pair_meta(0, 0, pv, ps);
-      qk_pair<HD, RB>(skv[0], 0, qf, sa, koff);
+      qk_pair<HD, RB>(skv[0], 0, qf, sa, koff0, koff1);
       check_pair<HD, RB>(sa, oacc, m_ref, t_raw, c, n_full == 0, pv[0], pv[1], ps[0], ps[1], qidx, lane);
     }
     for (int st = 0; st < n_stages; ++st) {
@@ -1140,8 +1152,8 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
       const bool last = st + 1 == n_stages;
       if (wave_live) {
         pair_meta(st, 1, pv, ps);
-        pipe_step<HD, RB, true>(sb, 4, sb2, st >= n_full, pv, ps, sb, 1, sa, qf, oacc, m_ref, t_raw, qidx, c, koff,
-                                voff, lane);
+        pipe_step<HD, RB, true>(sb, 4, sb2, st >= n_full, pv, ps, sb, 1, sa, qf, oacc, m_ref, t_raw, qidx, c, koff0,
+                                koff1, voff, lane);
       }
       __builtin_amdgcn_s_waitcnt(PF_WAIT(LPW));
       convert_v(st + 1, nvn);  // slot (st + 1) % NS: no wave reads it before the next barrier
@@ -1155,12 +1167,12 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
       if (wave_live) {
         pair_meta(st + 1, 0, pv, ps);
         pipe_step<HD, RB, true>(skv[(st + 1) % NS], 0, sa, st + 1 >= n_full, pv, ps, sb, 5, sb2, qf, oacc, m_ref,
-                                t_raw, qidx, c, koff, voff, lane);
+                                t_raw, qidx, c, koff0, koff1, voff, lane);
       }
     }
     if (wave_live)  // the last pair: no next one to start
       pipe_step<HD, RB, false>(skv[0], 0, sa, false, pv, ps, skv[(n_stages - 1) % NS], 5, sb2, qf, oacc, m_ref,
-                               t_raw, qidx, c, koff, voff, lane);
+                               t_raw, qidx, c, koff0, koff1, voff, lane);
     // no load into this workgroup's LDS may still be in flight when it ends
     __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
   }
