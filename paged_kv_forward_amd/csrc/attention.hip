@@ -723,9 +723,10 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(AttnArgs a) {
 //    all ones sums the same fp16 P that weighs V, in fp32.
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
-// Page ids a prefill workgroup keeps in LDS (16 KiB: sequences of up to
-// 65536 tokens at 16 per page).
-constexpr int PF_PT_MAX = 4096;
+// Page ids a prefill workgroup keeps in LDS (8 KiB: sequences of up to
+// 32768 tokens at 16 per page; longer ones read their page ids with scalar
+// loads).
+constexpr int PF_PT_MAX = 2048;
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16h(const uint4& a, const uint4& b, f32x4 c) {

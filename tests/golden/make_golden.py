@@ -7,7 +7,7 @@ run it layer-major in one pass (weights drawn once per layer); the GPU test
 feeds the same tokens.  By the incremental-decode invariant of the oracle,
 reading out row i of that chunk equals decoding token by token.
 
-    python tests/golden/make_golden.py c2 [c3 c4 c4long c5 c5ctx512] [c2:1 ...]
+    python tests/golden/make_golden.py c2 [c3 c4 c4long c5 c5ctx512 tinylong] [c2:1 ...]
 
 "cN:L" writes the same case for the model cut to its first L layers
 (<name>_first<L>.npz).  The checked rows follow the sampling plan of the
@@ -261,6 +261,32 @@ def c5ctx512():
     """The 70B decode with every prompt cut to its first 512 tokens: four
     sequences, 96 decode steps each (388 readouts)."""
     c5(decode_steps=96, seqs=(0, 10, 21, 31), ctx=512, name="c5_decode_70b_ctx512")
+
+
+def tinylong():
+    """The tiny model prefilling one 33000-token prompt (more pages than the
+    prefill attention kernel keeps in LDS, 2063 against 2048): read out at 3
+    rows of its last 232 tokens, which the GPU test prefills as the fifth
+    launch after four of 8192 tokens.  The oracle runs it in 2048-token
+    chunks (same KV, by its chunk-boundary invariant)."""
+    recipe = synth.WeightRecipe(synth.TINY, weight_seed=99, gain_std=0.02)
+    shape = recipe.shape
+    L, last0, reads = 33000, 4 * 8192, [0, 100, 231]
+    toks = synth.prompt_tokens(1, 800, L, shape.vocab)
+    w = SynthWeights(recipe, cache_layers=True)
+    num = default_numerics(shape)
+    tree, b = [], 0
+    while b < last0:
+        e = min(b + 2048, last0)
+        tree.append(Chunk(toks[b:e], np.arange(b, e), len(tree) - 1, []))
+        b = e
+    tree.append(Chunk(toks[last0:], np.arange(last0, L), len(tree) - 1, reads))
+    t0 = time.time()
+    out = forward_chunks(w, tree, num)[-1]
+    print("tinylong oracle %.0f s" % (time.time() - t0), flush=True)
+    rows = [dict(seq=0, step=r, kind=0, temp=1.0, seed=0, lane=i, logits=out[i]) for i, r in enumerate(reads)]
+    finish("tiny_long_prefill", rows, [0, 1, 2], shape.vocab,
+           {"prompt_len": L, "last_chunk": last0, "prompt_seed": 800})
 
 
 if __name__ == "__main__":

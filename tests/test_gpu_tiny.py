@@ -686,3 +686,34 @@ def test_mid_prefill_fork_at_partial_page_and_chunked(torch_cuda):
             row += 1
     rep.check()
     rt.close()
+
+
+def test_tiny_prefill_past_the_page_id_table(torch_cuda):
+    """A 33000-token prompt: 2063 pages, more than the 2048 page ids the bf16
+    prefill attention keeps in LDS, so its last launch reads page ids with
+    scalar loads.  Four launches of 8192 tokens, then the last 232 with three
+    readouts, against stored oracle values (tests/golden/tiny_long_prefill.npz,
+    written by tests/golden/make_golden.py tinylong)."""
+    import os
+    from paged_kv_forward_amd.runtime import Pass
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "tiny_long_prefill.npz")
+    if not os.path.exists(path):
+        pytest.skip("stored oracle values tiny_long_prefill not generated")
+    g = np.load(path, allow_pickle=False)
+    recipe = RECIPES["gains_spread"]
+    shape = recipe.shape
+    L, last0 = int(g["meta_prompt_len"]), int(g["meta_last_chunk"])
+    toks = synth.prompt_tokens(1, int(g["meta_prompt_seed"]), L, shape.vocab)
+    reads = [int(r) for r in g["row_step"]]
+    rt = make_runtime(shape, recipe, torch_cuda, max_rows=8192, max_seqs=2, max_readout=4, max_ctx=L + 16,
+                      pages=L // 16 + 8)
+    ws = rt.alloc()
+    for b in range(0, last0, 8192):
+        rt.forward([Pass(ws, toks[b:b + 8192])])
+    out, logits = rt.forward([Pass(ws, toks[last0:], reads, [(0, 1.0, 0)] * len(reads))], want_logits=True)
+    rep = Report()
+    for i, r in enumerate(reads):
+        rep.add(out[i], int(g["token"][i]), float(g["margin"][i]), tau_for(0, 1.0), logits[i], g["logits_full"][i],
+                ("long", r))
+    rep.check()
+    rt.close()
