@@ -703,30 +703,34 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- prefill, bf16 KV
 //
-// The bf16-KV form of the prefill kernel, built around the cost of the
-// softmax: a wave64 VALU instruction holds the 16-lane SIMD for 4 cycles, a
-// quarter of a 16x16x32 MFMA, so at 8 waves per CU the vector instructions
-// per score, not LDS or memory, set the pace.  Same work split, grid and
-// three-stage LDS ring as attn_prefill_kernel; what changes:
-//  - The online softmax runs once per stage of four pages (64 keys) rather
-//    than per pair: one cross-lane max (lane-swap instructions, no LDS), one
-//    rescale of O per row block, and the scale folded into the exponent as
-//    one FMA per score.
-//  - P enters P*V in fp16 (11 significant bits; bf16 has 8) and V is
-//    converted to fp16 as it is staged: it comes through registers (two
-//    16-byte loads per thread per stage) rather than straight into LDS, and
-//    its slots past a page's valid count are written as zeros there.  bf16 ->
-//    fp16 is exact for magnitudes in [2^-14, 65504]; smaller ones keep an
-//    absolute error below 2^-25, and a V entry of 65520 or more would become
-//    infinite (activations of this model family stay many orders below).
-//  - Row sums come from the matrix core: a ninth P*V block whose A operand is
-//    all ones sums the same fp16 P that weighs V, in fp32.
+// The bf16-KV prefill kernel, built around the cost of the softmax: a wave64
+// VALU instruction holds the 16-lane SIMD for 4 cycles, a quarter of a
+// 16x16x32 MFMA, so at 8 waves per CU the vector instructions per score, not
+// LDS or memory, set the pace.  Same work split and grid as
+// attn_prefill_kernel (256 query rows of one KV head per workgroup, 8 waves
+// of two 16-row blocks); what differs:
+//  - Pages pass through a four-stage LDS ring, K and V both loaded straight
+//    into LDS; each wave converts the V chunks it loaded to fp16 in place
+//    (two waves per page, each with half of its K and half of its V, so the
+//    conversion is evenly shared).  Slots past a page's valid count become
+//    zeros there.  bf16 -> fp16 is exact for magnitudes in [2^-14, 65504];
+//    smaller ones keep an absolute error below 2^-25, and a V entry of 65520
+//    or more would become infinite (activations of this model family stay
+//    many orders below).
+//  - Per pair of pages (32 keys): P enters P*V in fp16 (11 significant bits;
+//    bf16 has 8); the running maximum is a lazy reference checked with a
+//    ballot (check_pair), so the cross-lane max and the rescale of O run only
+//    when it moves; the scale is folded into the exponent as one FMA per
+//    score; row sums come from a ninth P*V block against an all-ones operand.
+//  - Software pipeline (pipe_step): the next pair's scores are computed in
+//    the same straight-line block as this pair's softmax and P*V, so one
+//    unit works while the other does; a stage's last pair is finished after
+//    the barrier that opens the next stage, hence the fourth stage.
+//  - Page ids come from an LDS table filled once per workgroup, not from
+//    scalar loads in the loop.
+//  - One pair body serves complete and masked stages (masking behind a
+//    wave-uniform flag), and no register spills: see the kernel's notes.
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-
-// Page ids a prefill workgroup keeps in LDS (8 KiB: sequences of up to
-// 32768 tokens at 16 per page; longer ones read their page ids with scalar
-// loads).
-constexpr int PF_PT_MAX = 2048;
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16h(const uint4& a, const uint4& b, f32x4 c) {
@@ -970,6 +974,10 @@ __device__ __forceinline__ void pipe_step(const uint8_t* sq, int qk0, f32x4 (&s_
 // compiler does not see the ring's LDS-bound loads it waits for all of them
 // before it.
 constexpr int PH_WAVES = 8, PH_NT = 64 * PH_WAVES;
+// Page ids a prefill workgroup keeps in LDS (8 KiB: sequences of up to
+// 32768 tokens at 16 per page; longer ones read their page ids with scalar
+// loads).
+constexpr int PF_PT_MAX = 2048;
 
 template <int HD>
 __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {

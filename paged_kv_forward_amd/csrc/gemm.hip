@@ -1266,6 +1266,261 @@ __global__ __launch_bounds__(RN_NT) void skinny_reduce_norm_kernel(GemmArgs g, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode QKV projection in one launch: narrow tiles, no split-K.  With
+// split-K the projection needs a second kernel to sum the partials, apply
+// RoPE and append k and v, and at decode sizes every launch costs a few
+// microseconds of ramp and drain on top of its bytes.  Here a workgroup owns
+// 32 output columns over the whole K range, chosen so that RoPE needs no
+// other workgroup: for q and k, 16 columns of one head and their 16 rotation
+// partners half a head further on; for v, 32 consecutive columns (at the
+// Llama-3.1-8B shape: 160 + 32 = 192 workgroups).  Every workgroup reads all
+// of A (64 rows x K bf16, from L2 after the first reader) besides its 32
+// columns of weights.
+//  - Eight waves; wave w takes the 64-wide K chunks w, w + 8, ... counted
+//    from a per-workgroup starting chunk, and keeps a ring of NQ_DEPTH chunks
+//    in registers.  A chunk is 8 loads of A, each 8 whole rows of 128 bytes
+//    (lane l: row 8i + l / 8, bytes 16 (l & 7)), and 4 loads of weights (two
+//    16-row panels x two 32-k halves, each one contiguous KiB of the tiled
+//    layout, already in MFMA operand order).  A then goes through a private
+//    8 KiB LDS slot of the wave (rows swizzled as in gemm_dma_kernel) into
+//    MFMA fragments; loading the fragments straight from memory (16 rows x
+//    64 bytes per load) measured 35% slower.
+//  - The eight waves' partial tiles are summed in wave order through LDS;
+//    then RoPE, the q stores and the k / v page-slot stores, as the split-K
+//    reduce does them.
+constexpr int NQ_WAVES = 8, NQ_NT = 64 * NQ_WAVES, NQ_DEPTH = 3;
+constexpr int NQ_LDC = 36;  // fp32 per row of a wave's 64 x 32 partial tile (float4-aligned, padded)
+constexpr int NQ_LDS = NQ_WAVES * 64 * NQ_LDC * 4 + NQ_WAVES * 8192;
+
+__host__ __device__ inline int qkv_narrow_units(int qw, int kw) { return (qw + kw) / 32 + kw / 32; }
+
+template <bool F8>
+__global__ __launch_bounds__(NQ_NT, 1) void gemm_qkv_narrow_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NQ_LDS];
+  const int lane = threadIdx.x & 63, wave = wave_id(), r16 = lane & 15, gq = lane >> 4;
+  const int HD = g.hd, qw = g.nq * HD, kw = g.nkv * HD;
+  const int n_rope = (qw + kw) / 32, u = blockIdx.x;
+  const bool rope = u < n_rope;
+  // the two 16-column panels of this workgroup (QKV output columns cA.., cB..)
+  const int cA = rope ? (u / (HD / 32)) * HD + (u % (HD / 32)) * 16 : qw + kw + (u - n_rope) * 32;
+  const int cB = rope ? cA + HD / 2 : cA + 16;
+  const int sg = cA < qw ? 0 : (cA < qw + kw ? 1 : 2);
+  const int kc = g.K / 64;
+  uint32_t pb[2];  // element offset of each panel in K chunk 0 of the segment's packed matrix
+  {
+    const int a = cA - g.seg_n0[sg], b = cB - g.seg_n0[sg];
+    pb[0] = (uint32_t)(a >> 6) * (uint32_t)kc * 4096u + (uint32_t)((a >> 4) & 3) * 1024u;
+    pb[1] = (uint32_t)(b >> 6) * (uint32_t)kc * 4096u + (uint32_t)((b >> 4) & 3) * 1024u;
+  }
+  const int seg_rows = g.seg_n0[sg + 1] - g.seg_n0[sg];
+  const __amdgpu_buffer_rsrc_t rw = F8 ? make_rsrc(g.w8[sg], (uint32_t)packed_elems(seg_rows, g.K))
+                                       : make_rsrc(g.w[sg], (uint32_t)(packed_elems(seg_rows, g.K) * 2));
+  // FP8: the panels' block scales, one per 128 rows x 128 k
+  const int kb8 = fp8_scale_blocks(g.K);
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(F8 ? g.s8[sg] : nullptr, F8 ? (uint32_t)(fp8_scale_blocks(seg_rows) * kb8 * 4) : 0u);
+  uint32_t srow[2];
+  srow[0] = (uint32_t)((cA - g.seg_n0[sg]) >> 7) * (uint32_t)kb8;
+  srow[1] = (uint32_t)((cB - g.seg_n0[sg]) >> 7) * (uint32_t)kb8;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, (uint32_t)((size_t)g.M * g.lda * 2));
+  // Workgroups start at different K chunks: all of them read the same A, and
+  // in step they would all queue on the few L2 channels that hold one chunk
+  // (its 64 rows are a row stride apart).  Workgroups are dispatched to the
+  // XCDs round robin, so the ones sharing an L2 (equal u mod 8) are spread
+  // evenly over the chunks.
+  const int per_xcd = (gridDim.x + 7) / 8;
+  const int rot = (int)(((u >> 3) * kc) / per_xcd);
+  // K chunk of this wave's iteration it (-1 past the end)
+  auto chunk = [&](int it) {
+    const int jr = wave + it * NQ_WAVES;
+    return jr < kc ? (jr + rot < kc ? jr + rot : jr + rot - kc) : -1;
+  };
+  // A load i covers rows 8i .. 8i + 7; rows past M read row M - 1 (their
+  // outputs are never stored)
+  uint32_t a_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    a_off[i] = (uint32_t)(min(i * 8 + (lane >> 3), g.M - 1) * g.lda * 2) + (uint32_t)(lane & 7) * 16u;
+  // bf16: b[ks][p] the panels' two k halves as loaded; FP8: b[0][p] holds
+  // panel p's 16 codes (both halves) and s[p] its block scale, converted to
+  // bf16 when the chunk is consumed (exactly: a code times its power-of-two
+  // scale is a bf16 value), so both forms add the same products in the same
+  // order
+  struct Slot {
+    uint4 a[8], b[2][2];
+    float s[2];
+  };
+  // Past K every offset is out of range: the loads read zeros.
+  auto load = [&](Slot& sl, int it) {
+    const int j = chunk(it);
+    const bool live = j >= 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sl.a[i] = bload16(ra, live ? a_off[i] + (uint32_t)j * 128u : OOB);
+    if constexpr (F8) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        sl.b[0][p] = bload16(rw, live ? pb[p] + (uint32_t)j * 4096u + (uint32_t)lane * 16u : OOB);
+        sl.s[p] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(srs, live ? (srow[p] + (uint32_t)j / 2u) * 4u : OOB, 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          sl.b[ks][p] =
+              bload16(rw, live ? (pb[p] + (uint32_t)j * 4096u + (uint32_t)ks * 512u + (uint32_t)lane * 8u) * 2u : OOB);
+    }
+  };
+  uint8_t* xs = smem + NQ_WAVES * 64 * NQ_LDC * 4 + wave * 8192;
+  const int a_sw = dg_swz(r16);  // the swizzle depends on the row mod 16 only
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) acc[a][0] = acc[a][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Fully unrolled over the most chunks a wave can have (K <= 4096), so that
+  // the compiler's waits are exact: in a rolled loop it waited for every
+  // load in flight at the top of each pass.  Iterations past the wave's
+  // last chunk load zeros and add nothing.
+  constexpr int IT_MAX = 64 / NQ_WAVES;
+  Slot ring[NQ_DEPTH];
+#pragma unroll
+  for (int d = 0; d < NQ_DEPTH; ++d) load(ring[d], d);
+#pragma unroll
+  for (int it = 0; it < IT_MAX; ++it) {
+    Slot& sl = ring[it % NQ_DEPTH];
+    // A through the wave's LDS slot into fragments (the wave's LDS accesses
+    // complete in order, so the next chunk's writes never pass these reads)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * 8 + (lane >> 3);
+      *reinterpret_cast<uint4*>(xs + r * 128 + (((lane & 7) ^ dg_swz(r)) * 16)) = sl.a[i];
+    }
+    uint4 af[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        af[ks][a] = *reinterpret_cast<const uint4*>(xs + (a * 16 + r16) * 128 + (((ks * 4 + gq) ^ a_sw) * 16));
+    uint4 bf[2][2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if constexpr (F8) {
+        const uint4 c = sl.b[0][p];
+        const uint2 p0 = fp8x4_to_bf16(c.x, sl.s[p]), p1 = fp8x4_to_bf16(c.y, sl.s[p]);
+        const uint2 p2 = fp8x4_to_bf16(c.z, sl.s[p]), p3 = fp8x4_to_bf16(c.w, sl.s[p]);
+        bf[0][p] = make_uint4(p0.x, p0.y, p1.x, p1.y);
+        bf[1][p] = make_uint4(p2.x, p2.y, p3.x, p3.y);
+      } else {
+        bf[0][p] = sl.b[0][p];
+        bf[1][p] = sl.b[1][p];
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) acc[a][p] = mfma16(af[ks][a], bf[ks][p], acc[a][p]);
+    if (it + NQ_DEPTH < IT_MAX) load(sl, it + NQ_DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+
+  float* sP = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sP[(wave * 64 + a * 16 + 4 * gq + i) * NQ_LDC + p * 16 + r16] = acc[a][p][i];
+  __syncthreads();
+  // four consecutive columns of one row, summed over the waves in wave order
+  auto col4 = [&](int row, int c) {
+    float4 v = *reinterpret_cast<const float4*>(&sP[row * NQ_LDC + c]);
+#pragma unroll
+    for (int w = 1; w < NQ_WAVES; ++w) {
+      const float4 x = *reinterpret_cast<const float4*>(&sP[(w * 64 + row) * NQ_LDC + c]);
+      v.x += x.x;
+      v.y += x.y;
+      v.z += x.z;
+      v.w += x.w;
+    }
+    return v;
+  };
+  const int tid = threadIdx.x;
+  constexpr int P = KV_PAGE;
+  if (rope) {
+    // a unit is one row's 8 consecutive rotation pairs: columns cA + 8h ..
+    // and their partners cB + 8h ..
+    if (tid >= 128) return;
+    const int row = tid >> 1, h = tid & 1, m = row;
+    if (m >= g.M) return;
+    const int d = cA % HD + 8 * h;  // rotation index (< HD / 2)
+    const float4* cs4 = reinterpret_cast<const float4*>(reinterpret_cast<const float2*>(g.rope_cs) +
+                                                        (size_t)m * (HD / 2) + d);
+    float4 c4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c4[i] = cs4[i];  // (cos, sin) of pairs 2i, 2i + 1
+    const float4 a0 = col4(row, 8 * h), a1 = col4(row, 8 * h + 4);
+    const float4 b0 = col4(row, 16 + 8 * h), b1 = col4(row, 16 + 8 * h + 4);
+    const float x1[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float x2[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    float o1[8], o2[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float c = (i & 1) ? c4[i >> 1].z : c4[i >> 1].x, sn = (i & 1) ? c4[i >> 1].w : c4[i >> 1].y;
+      o1[i] = x1[i] * c - x2[i] * sn;
+      o2[i] = x2[i] * c + x1[i] * sn;
+    }
+    if (sg == 0) {
+      uint16_t* q = g.q_out + (size_t)m * qw;
+      *reinterpret_cast<uint4*>(q + cA + 8 * h) = make_uint4(pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3]),
+                                                             pack_bf2(o1[4], o1[5]), pack_bf2(o1[6], o1[7]));
+      *reinterpret_cast<uint4*>(q + cB + 8 * h) = make_uint4(pack_bf2(o2[0], o2[1]), pack_bf2(o2[2], o2[3]),
+                                                             pack_bf2(o2[4], o2[5]), pack_bf2(o2[6], o2[7]));
+      return;
+    }
+    const int kh = (cA - qw) / HD, sl = g.slot[m];
+    const size_t base = (size_t)(sl / P) * g.page_stride + (size_t)kh * P * HD + (size_t)(sl % P) * 8;
+    const size_t i1 = base + (size_t)(d >> 3) * P * 8, i2 = base + (size_t)((d + HD / 2) >> 3) * P * 8;
+    if (g.kv_e4m3) {
+      const float sc = g.kv_scale[kh];
+      uint32_t w1[2] = {0u, 0u}, w2[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w1[i >> 2] |= (uint32_t)f2e4m3(o1[i] / sc) << (8 * (i & 3));
+        w2[i >> 2] |= (uint32_t)f2e4m3(o2[i] / sc) << (8 * (i & 3));
+      }
+      uint8_t* kv = reinterpret_cast<uint8_t*>(g.kv_layer);
+      *reinterpret_cast<uint2*>(kv + i1) = make_uint2(w1[0], w1[1]);
+      *reinterpret_cast<uint2*>(kv + i2) = make_uint2(w2[0], w2[1]);
+    } else {
+      uint16_t* kv = reinterpret_cast<uint16_t*>(g.kv_layer);
+      *reinterpret_cast<uint4*>(kv + i1) = make_uint4(pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3]),
+                                                      pack_bf2(o1[4], o1[5]), pack_bf2(o1[6], o1[7]));
+      *reinterpret_cast<uint4*>(kv + i2) = make_uint4(pack_bf2(o2[0], o2[1]), pack_bf2(o2[2], o2[3]),
+                                                      pack_bf2(o2[4], o2[5]), pack_bf2(o2[6], o2[7]));
+    }
+    return;
+  }
+  // v, layout [kv head][HD][token] in a page: one element per row (the rows
+  // of a decode step belong to different sequences)
+  const int c = tid & 31, vc = cA - qw - kw + c, kvh = vc / HD, dd = vc % HD;
+  const size_t col = (size_t)g.nkv * P * HD + (size_t)kvh * HD * P + (size_t)dd * P;
+  const float sc = g.kv_e4m3 ? g.kv_scale[g.nkv + kvh] : 1.f;
+  for (int row = tid >> 5; row < g.M; row += NQ_NT / 32) {
+    float v = sP[row * NQ_LDC + c];
+#pragma unroll
+    for (int w = 1; w < NQ_WAVES; ++w) v += sP[(w * 64 + row) * NQ_LDC + c];
+    const int sl = g.slot[row];
+    const size_t idx = (size_t)(sl / P) * g.page_stride + col + (sl % P);
+    if (g.kv_e4m3) reinterpret_cast<uint8_t*>(g.kv_layer)[idx] = f2e4m3(v / sc);
+    else reinterpret_cast<uint16_t*>(g.kv_layer)[idx] = f2bf(v);
+  }
+}
+
 // x[m, :] = bf16(y[m, :] * rsqrt(sum_sq[m] / d + eps) * gain), one workgroup per row.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ y, const float* __restrict__ ss,
                                                       int n_ss, const uint16_t* __restrict__ gain, int d,
@@ -1355,9 +1610,25 @@ static void launch_t(const GemmArgs& g0, hipStream_t st) {
 
 // Weights stream with non-temporal loads, except the QKV projection's: at its
 // size (50 MB at the 8B shape) plain loads measured slightly faster.
+// The narrow QKV kernel replaces split-K + reduce when every workgroup's
+// copy of A stays small (at most 64 x 4096 bf16) and its grid fits one round
+// of the 256 compute units.
+static bool qkv_narrow_fits(const GemmArgs& g) {
+  const int qw = g.nq * g.hd, kw = g.nkv * g.hd;
+  return g.M >= 1 && g.M <= 64 && g.K % 64 == 0 && g.K <= 4096 && (g.hd == 64 || g.hd == 128) &&
+         g.page_size == KV_PAGE && g.lda % 8 == 0 && ((uintptr_t)g.a & 15) == 0 &&
+         (size_t)g.M * g.lda * 2 < ((size_t)1 << 32) && qkv_narrow_units(qw, kw) <= 256;
+}
+
 template <int EPI>
 static void launch_skinny(const GemmArgs& g0, hipStream_t st) {
   GemmArgs g = g0;
+  if (EPI == EPI_QKV && qkv_narrow_fits(g)) {
+    const dim3 grid(qkv_narrow_units(g.nq * g.hd, g.nkv * g.hd));
+    if (g.f8) hipLaunchKernelGGL(gemm_qkv_narrow_kernel<true>, grid, dim3(NQ_NT), 0, st, g);
+    else hipLaunchKernelGGL(gemm_qkv_narrow_kernel<false>, grid, dim3(NQ_NT), 0, st, g);
+    return;
+  }
   if (EPI == EPI_SWIGLU && g.f8 && g.splits <= 1 && skinny_swiglu_cols_wide(g.N) > 64) {
     g.cw = skinny_swiglu_cols_wide(g.N);
     const dim3 gw((g.N + g.cw - 1) / g.cw);
