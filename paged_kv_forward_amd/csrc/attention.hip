@@ -117,15 +117,21 @@ __device__ __forceinline__ void load_pair(PairRaw<HD, E4M3>& f, const AttnArgs& 
   }
 }
 
+// Two e4m3 codes (bytes 0, 1 of c, or 2, 3 with HI) as two bf16 in one
+// gfx950 conversion instruction, unit scale.  Exact: a code has at most 4
+// significant bits and its exponent range sits inside bf16's (checked on the
+// GPU against the bit-level decode for every code that is not NaN; the KV
+// quantiser saturates and never writes a NaN code).  The scales of K and V
+// are applied to the scores and the output instead, once per value.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16(uint32_t c) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, HI));
+}
+
 __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
-  uint32_t w[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t src = j < 2 ? c.x : c.y;
-    const uint32_t b0 = (src >> (16 * (j & 1))) & 0xffu, b1 = (src >> (16 * (j & 1) + 8)) & 0xffu;
-    w[j] = e4m3_to_bf16(b0) | (e4m3_to_bf16(b1) << 16);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return make_uint4(e4m3x2_to_bf16<false>(c.x), e4m3x2_to_bf16<true>(c.x), e4m3x2_to_bf16<false>(c.y),
+                    e4m3x2_to_bf16<true>(c.y));
 }
 
 // 4 V^T tokens (4g .. 4g+3) as 2 bf16x2 words with slots >= nvalid zeroed
@@ -138,8 +144,8 @@ __device__ __forceinline__ uint2 v4_bf16(T raw, int nvalid) {
     uint32_t c = raw;
     const uint32_t keep = nvalid >= 4 ? 0xffffffffu : (nvalid <= 0 ? 0u : ((1u << (8 * nvalid)) - 1u));
     c &= keep;
-    w0 = e4m3_to_bf16(c & 0xffu) | (e4m3_to_bf16((c >> 8) & 0xffu) << 16);
-    w1 = e4m3_to_bf16((c >> 16) & 0xffu) | (e4m3_to_bf16(c >> 24) << 16);
+    w0 = e4m3x2_to_bf16<false>(c);
+    w1 = e4m3x2_to_bf16<true>(c);
   } else {
     w0 = raw.x;
     w1 = raw.y;

@@ -60,14 +60,6 @@ __device__ __forceinline__ uint8_t f2e4m3(float x) {
   return (uint8_t)(sign | code);
 }
 
-// E4M3FN code -> bf16 bits (exact: every finite code is a bf16 value).
-__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
-  uint32_t s = (c & 0x80u) << 8;
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  uint32_t normal = ((e + 120u) << 7) | (m << 4);
-  uint32_t sub = __float_as_uint((float)m * 0.001953125f) >> 16;  // m * 2^-9
-  return s | (e ? normal : sub);
-}
 
 // ---------------------------------------------------------------- MFMA
 
