@@ -969,12 +969,14 @@ constexpr int SK_LDX = SK_GK + 8;                // bf16 per LDS row (16-byte pa
 constexpr int SK_XP = 64 * SK_GK / 8 / SK_NT;    // 16-byte activation pieces per thread per group (8)
 constexpr int SK_LDS = 2 * 64 * SK_LDX * 2 > 64 * SK_LDC * 4 ? 2 * 64 * SK_LDX * 2 : 64 * SK_LDC * 4;
 
-// Four e4m3 codes (one 32-bit word) times a power-of-two scale -> four bf16
-// (exact: a code has at most 4 significant bits).
+// Four e4m3 codes (one 32-bit word) times a power-of-two scale -> four bf16,
+// two per gfx950 scaled conversion instruction.  Exact: a code has at most 4
+// significant bits, and with a power-of-two scale the product is a bf16
+// value (checked on the GPU against the bit-level decode times 2^e for every
+// code that is not NaN and every e in [-40, 20]).
 __device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t w, float s) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  return make_uint2(pack_bf2(a.x * s, a.y * s), pack_bf2(b.x * s, b.y * s));
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, true)));
 }
 
 // W2 (FP8 gate/up only, no split-K): each wave owns two 16-row panels, so a
