@@ -519,16 +519,20 @@ def test_tiny_prefix_lookup_reuses_pages_exactly(torch_cuda):
     rt.close()
 
 
+@pytest.mark.parametrize("d_ffn", [688, 704])
 @pytest.mark.parametrize("lens", [(150, 150), (600,), (257, 64)])
-def test_tiny_large_prefill_tiles_with_ragged_edges(torch_cuda, lens):
+def test_tiny_large_prefill_tiles_with_ragged_edges(torch_cuda, lens, d_ffn):
     """Prefill launches of 256 rows or more use the 256 x 256 GEMM tiles: at the
     tiny shape their row and column edges are ragged (300, 600 and 321 rows;
-    gate/up width 688 = 5 x 128 + 48), the down projection's K (688) is not a
-    multiple of 64 (register-staged tile) and the others' K (256) is (tiles
-    loaded straight into LDS).  Last-row logits of every sequence against the
-    oracle."""
+    gate/up width 688 = 5 x 128 + 48 or 704), and the others' K (256) is a
+    multiple of 64 (tiles loaded straight into LDS).  The down projection's K
+    is 688, not a multiple of 64 (register-staged tile), or 704 = 11 x 64: an
+    odd number of K stages, which the straight-to-LDS loop, run in pairs of
+    stages, finishes with a stage of zeros.  Last-row logits of every
+    sequence against the oracle."""
     from paged_kv_forward_amd.runtime import Pass
-    recipe = RECIPES["gains_spread"]
+    base = RECIPES["gains_spread"]
+    recipe = dataclasses.replace(base, shape=dataclasses.replace(base.shape, d_ffn=d_ffn))
     shape = recipe.shape
     rt = make_runtime(shape, recipe, torch_cuda, max_rows=1024)
     prompts = [synth.prompt_tokens(1, 60 + i, n, shape.vocab) for i, n in enumerate(lens)]
@@ -541,7 +545,7 @@ def test_tiny_large_prefill_tiles_with_ragged_edges(torch_cuda, lens):
         ref = Session(w, default_numerics(shape)).step(list(pr))[0]
         tok, margin = apply(ref, 0, 1.0, 0, 0)
         rep.add(toks[i], tok, margin, tau_for(0, 1.0), lg[i], ref, tag=("prefill", len(pr)))
-    rep.check(max_excluded_frac=1.0)  # one or two rows: the logits carry the check
+    rep.check(max_excluded_frac=1.0, min_compared=0)  # one or two rows: the logits carry the check
     rt.close()
 
 
