@@ -12,10 +12,11 @@
 // same sum): in k-step i of Q*K^T group g takes head-dim group 4i + g (8
 // values), for P*V group g takes tokens 4g..4g+3 of both pages.
 // Softmax is online (running max and sum per row, in log2 units), in fp32.
-// In decode and the e4m3 prefill, P enters the P*V MFMA as two bf16 parts,
-// hi = bf16(P) and lo = bf16(P - hi), so the product sees P to about 16
-// significant bits; the bf16 prefill converts V to fp16 instead and takes P
-// in fp16 (11 bits), see attn_prefill_h_kernel.
+// In decode, P enters the P*V MFMA as two bf16 parts, hi = bf16(P) and
+// lo = bf16(P - hi), so the product sees P to about 16 significant bits; the
+// prefill kernels take V in fp16 instead (e4m3 codes convert to it exactly,
+// bf16 values as attn_prefill_h_kernel states) and P in fp16 (11 bits), one
+// product per V block.
 //
 // Memory: K and V are read with streaming (non-temporal) loads, each load
 // instruction covering whole 128-byte lines (K's page layout makes a k-step's
@@ -129,6 +130,26 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16(uint32_t c) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, HI));
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16h(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+
+// Two floats -> packed fp16 (a in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
+}
+
+// Two e4m3 codes as two fp16, the same way.  Also exact: every e4m3 value,
+// subnormals included, is an fp16 normal or zero.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16(uint32_t c) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, HI));
+}
+
 __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
   return make_uint4(e4m3x2_to_bf16<false>(c.x), e4m3x2_to_bf16<true>(c.x), e4m3x2_to_bf16<false>(c.y),
                     e4m3x2_to_bf16<true>(c.y));
@@ -153,6 +174,12 @@ __device__ __forceinline__ uint2 v4_bf16(T raw, int nvalid) {
     w1 &= nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0xffffu : 0u);
   }
   return make_uint2(w0, w1);
+}
+
+// 4 e4m3 V^T tokens as 2 fp16x2 words, slots >= nvalid zeroed (as v4_bf16).
+__device__ __forceinline__ uint2 v4_f16(uint32_t c, int nvalid) {
+  c &= nvalid >= 4 ? 0xffffffffu : (nvalid <= 0 ? 0u : ((1u << (8 * nvalid)) - 1u));
+  return make_uint2(e4m3x2_to_f16<false>(c), e4m3x2_to_f16<true>(c));
 }
 
 // Online-softmax update of RB row blocks with one pair of entries.
@@ -494,19 +521,37 @@ __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* 
       // O is rescaled only when some row's running max moved (alpha != 1);
       // multiplying by 1 changes nothing, so skipping it is exact
       rescale[rb] = __builtin_amdgcn_ballot_w64(alpha[rb] != 1.f) != 0;
+      if constexpr (E4M3) {
+        // e4m3 V is exact in fp16, so P enters one fp16 product; the row sum
+        // adds the same rounded weights, so each row's output stays a convex
+        // combination of its V rows
+        ph[rb] = make_uint4(pack_h2(p[0], p[1]), pack_h2(p[2], p[3]), pack_h2(p[4], p[5]), pack_h2(p[6], p[7]));
+        const f16x2_t r0 = __builtin_bit_cast(f16x2_t, ph[rb].x), r1 = __builtin_bit_cast(f16x2_t, ph[rb].y);
+        const f16x2_t r2 = __builtin_bit_cast(f16x2_t, ph[rb].z), r3 = __builtin_bit_cast(f16x2_t, ph[rb].w);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          p[j] = (float)r0[j];
+          p[2 + j] = (float)r1[j];
+          p[4 + j] = (float)r2[j];
+          p[6 + j] = (float)r3[j];
+        }
+      }
       const float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       l_run[rb] = l_run[rb] * alpha[rb] + ps;
       m_run[rb] = m_new;
-      ph[rb] = make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]), pack_bf2(p[6], p[7]));
-      const uint32_t hw[4] = {ph[rb].x, ph[rb].y, ph[rb].z, ph[rb].w};
-      float lo[8];
+      if constexpr (!E4M3) {
+        // bf16 V: P as a bf16 pair (high part and remainder), two products
+        ph[rb] = make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]), pack_bf2(p[6], p[7]));
+        const uint32_t hw[4] = {ph[rb].x, ph[rb].y, ph[rb].z, ph[rb].w};
+        float lo[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lo[2 * j] = p[2 * j] - bf2f(hw[j] & 0xffffu);
-        lo[2 * j + 1] = p[2 * j + 1] - bf2f(hw[j] >> 16);
+        for (int j = 0; j < 4; ++j) {
+          lo[2 * j] = p[2 * j] - bf2f(hw[j] & 0xffffu);
+          lo[2 * j + 1] = p[2 * j + 1] - bf2f(hw[j] >> 16);
+        }
+        pl[rb] = make_uint4(pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(lo[4], lo[5]),
+                            pack_bf2(lo[6], lo[7]));
       }
-      pl[rb] = make_uint4(pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(lo[4], lo[5]),
-                          pack_bf2(lo[6], lo[7]));
     }
   }
 #pragma unroll
@@ -514,8 +559,8 @@ __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* 
     const int off = ((16 * b + n) * PS + 4 * g) * EB;
     uint2 a0, a1;
     if constexpr (E4M3) {
-      a0 = v4_bf16<true>(*reinterpret_cast<const uint32_t*>(vb0 + off), FULL ? 4 : valid0 - 4 * g);
-      a1 = v4_bf16<true>(*reinterpret_cast<const uint32_t*>(vb1 + off), FULL ? 4 : valid1 - 4 * g);
+      a0 = v4_f16(*reinterpret_cast<const uint32_t*>(vb0 + off), FULL ? 4 : valid0 - 4 * g);
+      a1 = v4_f16(*reinterpret_cast<const uint32_t*>(vb1 + off), FULL ? 4 : valid1 - 4 * g);
     } else if constexpr (FULL) {
       a0 = *reinterpret_cast<const uint2*>(vb0 + vswz(off));
       a1 = *reinterpret_cast<const uint2*>(vb1 + vswz(off));
@@ -527,8 +572,12 @@ __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* 
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (rescale[rb]) oacc[rb][b] *= alpha[rb];
-      oacc[rb][b] = mfma16(vf, ph[rb], oacc[rb][b]);
-      oacc[rb][b] = mfma16(vf, pl[rb], oacc[rb][b]);
+      if constexpr (E4M3) {
+        oacc[rb][b] = mfma16h(vf, ph[rb], oacc[rb][b]);
+      } else {
+        oacc[rb][b] = mfma16(vf, ph[rb], oacc[rb][b]);
+        oacc[rb][b] = mfma16(vf, pl[rb], oacc[rb][b]);
+      }
     }
   }
 }
@@ -736,19 +785,6 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(AttnArgs a) {
 //    scalar loads in the loop.
 //  - One pair body serves complete and masked stages (masking behind a
 //    wave-uniform flag), and no register spills: see the kernel's notes.
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4 mfma16h(const uint4& a, const uint4& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
-                                                0, 0, 0);
-}
-
-// Two floats -> packed fp16 (a in the low half), round to nearest even.
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
-}
-
 // Max over lanes l, l ^ 16, l ^ 32 and l ^ 48: each lane-swap instruction
 // returns its two operands with half of their 16-lane rows exchanged, so the
 // pair at lane l holds the values of lanes l and l ^ 32 (then l ^ 16).
