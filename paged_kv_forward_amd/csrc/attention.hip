@@ -1137,21 +1137,27 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
       const int d = (part0 + k) * 1024 + lane * 16;
       const int t0 = ((vswz(d) % 32) / 16) * 8;  // first token of the chunk (a V row is 16 tokens)
       const uint4 raw = *reinterpret_cast<const uint4*>(vd + d);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      if (nv < PS) {  // wave-uniform: slots past the valid count may hold anything
+        // bf16 word q holds tokens t0 + 2q, t0 + 2q + 1: keep the first
+        // clamp(nv - t0 - 2q, 0, 2) halves (bf16 zero converts to fp16 zero)
+        asm volatile("" ::: "memory");  // a real branch: complete pages skip this
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int keep = min(max(nv - t0 - 2 * q, 0), 2);
+          w[q] &= (uint32_t)(0xffffffffull >> (16 * (2 - keep)));
+        }
+      }
       uint32_t o[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float lo = __uint_as_float(w[q] << 16), hi = __uint_as_float(w[q] & 0xffff0000u);
-        if (nv < PS) {  // wave-uniform: slots past the valid count may hold anything
-          lo = t0 + 2 * q < nv ? lo : 0.f;
-          hi = t0 + 2 * q + 1 < nv ? hi : 0.f;
-        }
-        o[q] = pack_h2(lo, hi);
-      }
+      for (int q = 0; q < 4; ++q)
+        o[q] = pack_h2(__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xffff0000u));
       // the second page of a pair holds its 8-token groups halves swapped
-      // (see the token order above)
-      *reinterpret_cast<uint4*>(vd + d) =
-          (pj & 1) ? make_uint4(o[2], o[3], o[0], o[1]) : make_uint4(o[0], o[1], o[2], o[3]);
+      // (see the token order above): two 8-byte stores, their places chosen
+      // by the wave's page parity
+      const int sw = (pj & 1) * 8;
+      *reinterpret_cast<uint2*>(vd + d + sw) = make_uint2(o[0], o[1]);
+      *reinterpret_cast<uint2*>(vd + d + (8 - sw)) = make_uint2(o[2], o[3]);
     }
   };
 
