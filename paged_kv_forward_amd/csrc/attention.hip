@@ -979,31 +979,74 @@ __device__ __forceinline__ void pipe_step(const uint8_t* sq, int qk0, f32x4 (&s_
                                           f32x4 (&oacc)[RB][HD / 16 + 1], float (&m_ref)[RB], float (&t_raw)[RB],
                                           const int (&qidx)[RB], float c, int koff0, int koff1, int voff,
                                           int lane) {
-  constexpr int STEPS = HD / 32, DB = HD / 16;
-  uint4 ph[RB];
-  exp_pair<HD, RB>(s_old, m_ref, c, ph);
-  if constexpr (HQ) qk_pair<HD, RB, false>(sq, qk0, qf, s_new, koff0, koff1);
-  pv_pair<HD, RB, false>(se, ev0, ph, oacc, voff);
-  // Issue order: the pair's K reads, then each score MFMA followed by three
-  // vector instructions of the older pair's softmax, then the P*V MFMAs with
-  // the V reads two blocks ahead.  (Left alone, the compiler put all the
-  // exponentials in one run ahead of the MFMAs.)
-  if constexpr (HQ) {
-    __builtin_amdgcn_sched_group_barrier(0x100, STEPS, 0);  // K reads, first score MFMA
+  constexpr int STEPS = HD / 32, DB = HD / 16, PAGE_B = PS * HD * 2, NE = 8 * RB;
+  // Issue order, fixed with scheduling fences: the pair's K reads, then each
+  // score MFMA followed by one probability (an FMA and an exponential) of
+  // the older pair, so that the vector unit works while the matrix core
+  // runs; then the P*V MFMAs with the V reads two blocks ahead.  Consecutive
+  // score MFMAs go to different accumulators (i outer), so none waits for
+  // the one before.  (Scheduling-group hints were not followed here: the
+  // compiler put every exponential ahead of the MFMAs.)
+  float nm[RB];
 #pragma unroll
-    for (int i = 0; i < 2 * RB * STEPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      if (i == 1) __builtin_amdgcn_sched_group_barrier(0x100, STEPS, 0);  // K reads, second score MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);  // three VALU (transcendental ones included)
+  for (int rb = 0; rb < RB; ++rb) nm[rb] = m_ref[rb] == -INFINITY ? -INFINITY : -m_ref[rb];
+  float p[NE];
+  // probability e: row block e / 8, MFMA (e / 4) % 2 of the pair, value e % 4
+  auto prob = [&](int e) { p[e] = exp2_fast(fmaf(s_old[e / 8][(e / 4) & 1][e & 3], c, nm[e / 8])); };
+  const uint8_t* vb = se + ev0 * PAGE_B + voff;
+  constexpr int VB = 16 * PS * 2;  // bytes between V blocks
+  uint4 vf[3];
+  if constexpr (HQ) {
+    uint4 kf[2][STEPS];  // read in the order the MFMAs use them
+    const uint8_t* kb0 = sq + qk0 * PAGE_B + koff0;
+    const uint8_t* kb1 = sq + qk0 * PAGE_B + koff1;
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+      kf[0][i] = *reinterpret_cast<const uint4*>(kb0 + i * 1024);
+      kf[1][i] = *reinterpret_cast<const uint4*>(kb1 + i * 1024);
     }
+    f32x4 acc[RB][2];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < 2 * RB * STEPS; ++m) {
+      const int i = m / (2 * RB), j = (m / RB) & 1, rb = m % RB;
+      acc[rb][j] = mfma16(kf[j][i], qf[rb][i], i == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[rb][j]);
+      if (m < NE) prob(m);
+      if (m == 2 * RB * STEPS - 6) vf[0] = *reinterpret_cast<const uint4*>(vb);
+      if (m == 2 * RB * STEPS - 3) vf[1] = *reinterpret_cast<const uint4*>(vb + VB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int e = 2 * RB * STEPS; e < NE; ++e) prob(e);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) s_new[rb][j] = acc[rb][j];
+  } else {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) prob(e);
+    vf[0] = *reinterpret_cast<const uint4*>(vb);
+    vf[1] = *reinterpret_cast<const uint4*>(vb + VB);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V reads of blocks 0 and 1
-  __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);  // row sums and block 0
+  // B operand of P*V: lane group g's 8 k-slots are tokens 8 (g % 2) .. + 7
+  // of page g / 2 (first page: MFMA 0 gave the first four, MFMA 1 the next;
+  // second page: the other way round, as its V is stored)
+  uint4 ph[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    ph[rb] = make_uint4(pack_h2(p[8 * rb], p[8 * rb + 1]), pack_h2(p[8 * rb + 2], p[8 * rb + 3]),
+                        pack_h2(p[8 * rb + 4], p[8 * rb + 5]), pack_h2(p[8 * rb + 6], p[8 * rb + 7]));
+  __builtin_amdgcn_sched_barrier(0);
+  const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // fp16 1.0
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) oacc[rb][DB] = mfma16h(ones, ph[rb], oacc[rb][DB]);
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
-    if (b > 0) __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
-    if (b + 2 < DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
+    // operands b + 1 and b + 2 in flight while block b's MFMAs issue
+    if (b + 2 < DB) vf[(b + 2) % 3] = *reinterpret_cast<const uint4*>(vb + (b + 2) * VB);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) oacc[rb][b] = mfma16h(vf[b % 3], ph[rb], oacc[rb][b]);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // after P*V of the older pair: a rescale covers it too
   if constexpr (HQ) check_pair<HD, RB>(s_new, oacc, m_ref, t_raw, c, masked, pv[0], pv[1], ps[0], ps[1], qidx, lane);
