@@ -589,6 +589,21 @@ __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* 
 // all its rows; each wave runs the online softmax over its 32 rows.  Rows see
 // entries up to their own logical index (causal in append order); pages past
 // the workgroup's last row are skipped.
+// End of a sequence's page entries once the pages that start after logical
+// index qmax are dropped (no row of the workgroup sees them).  Page starts
+// ascend, so 64 entries are tested per vector load, from the end: one or two
+// loads where a walk back one scalar load at a time took one dependent load
+// per dropped page (up to 127 for the first rows of a 2048-token prompt).
+__device__ __forceinline__ int drop_pages_after(const int* pg_start, int e_begin, int e_end, int qmax, int lane) {
+  for (;;) {
+    const int e = e_end - 1 - lane;
+    const bool past = e >= e_begin && pg_start[e] > qmax;
+    const uint64_t keep = __builtin_amdgcn_ballot_w64(!past);
+    if (keep) return e_end - (int)__builtin_ctzll(keep);
+    e_end -= 64;
+  }
+}
+
 constexpr int PF_WAVES = 8, PF_NT = 64 * PF_WAVES;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -677,7 +692,7 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(AttnArgs a) {
   const_i32_t* pg_start = (const_i32_t*)a.pg_start;
   const int e_begin = a.seq_pg0[s];
   int e_end = a.seq_pg0[s + 1];
-  while (e_end > e_begin && a.pg_start[e_end - 1] > qmax) --e_end;
+  e_end = drop_pages_after(a.pg_start, e_begin, e_end, qmax, lane);
   const int n_stages = (e_end - e_begin + SP - 1) / SP;
   // everything loaded above has landed before the ring's loads are counted
   __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
@@ -1123,7 +1138,7 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   const_i32_t* pg_start = (const_i32_t*)a.pg_start;
   const int e_begin = a.seq_pg0[s];
   int e_end = a.seq_pg0[s + 1];
-  while (e_end > e_begin && a.pg_start[e_end - 1] > qmax) --e_end;
+  e_end = drop_pages_after(a.pg_start, e_begin, e_end, qmax, lane);
   const int n_stages = (e_end - e_begin + SP - 1) / SP;
   const bool pt_lds = e_end - e_begin <= PF_PT_MAX;
   if (pt_lds)
