@@ -1105,6 +1105,23 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   const int G = a.nq / a.nkv;
   const int row0 = a.seq_row0[s] + tb;
   const int ctx = a.seq_ctx[s] + tb;  // logical index of the item's first token
+  const int qmax = ctx + nt - 1;
+  const int e_begin = a.seq_pg0[s], e_all = a.seq_pg0[s + 1];
+
+  // The first 128 page entries (start, valid count, page id; entry
+  // e_begin + 64 k + lane in slot k), loaded before q and waited for together
+  // with it: one round trip for the tables and q, where loading each table
+  // after the previous one was needed took four (about 5 us per workgroup).
+  // Indexes are clamped into the sequence's entries (a launched item has at
+  // least one page) and the values outside it ignored.
+  int t_start[2], t_valid[2], t_id[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = max(min(e_begin + 64 * k + lane, e_all - 1), 0);
+    t_start[k] = a.pg_start[e];
+    t_valid[k] = a.pg_valid[e];
+    t_id[k] = a.pg_id[e];
+  }
 
   uint4 qf[RB][HD / 32];
   int qidx[RB];
@@ -1117,7 +1134,6 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     load_q<HD>(qf[rb], a.q + ((size_t)(row0 + (ok ? tq : 0)) * a.nq + kvh * G + h) * HD, ok, g);
   }
   const bool wave_live = wave * (RB * 16) / G < nt;
-  const int qmax = ctx + nt - 1;
 
   f32x4 oacc[RB][DB + 1];
   float m_ref[RB], t_raw[RB];
@@ -1136,26 +1152,46 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   const_i32_t* pg_id = (const_i32_t*)a.pg_id;
   const_i32_t* pg_valid = (const_i32_t*)a.pg_valid;
   const_i32_t* pg_start = (const_i32_t*)a.pg_start;
-  const int e_begin = a.seq_pg0[s];
-  int e_end = a.seq_pg0[s + 1];
-  e_end = drop_pages_after(a.pg_start, e_begin, e_end, qmax, lane);
+  __builtin_amdgcn_s_waitcnt(PF_WAIT(0));  // tables and q
+  // Pages that start after qmax serve no row of the workgroup.  Page starts
+  // ascend, so the entries kept are a prefix: counted from the tables when
+  // it ends inside them, else scanned from the sequence's end.
+  int e_end;
+  {
+    const uint64_t in0 = __builtin_amdgcn_ballot_w64(e_begin + lane < e_all && t_start[0] <= qmax);
+    const uint64_t in1 = __builtin_amdgcn_ballot_w64(e_begin + 64 + lane < e_all && t_start[1] <= qmax);
+    if (~in0) e_end = e_begin + __builtin_popcountll(in0);
+    else if (~in1) e_end = e_begin + 64 + __builtin_popcountll(in1);
+    else e_end = drop_pages_after(a.pg_start, e_begin, e_all, qmax, lane);
+  }
   const int n_stages = (e_end - e_begin + SP - 1) / SP;
   const bool pt_lds = e_end - e_begin <= PF_PT_MAX;
-  if (pt_lds)
-    for (int i = threadIdx.x; i < e_end - e_begin; i += PH_NT) s_pid[i] = a.pg_id[e_begin + i];
+  if (pt_lds) {
+    if (wave == 0) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (64 * k + lane < e_end - e_begin) s_pid[64 * k + lane] = t_id[k];
+    }
+    for (int i = 128 + threadIdx.x; i < e_end - e_begin; i += PH_NT) s_pid[i] = a.pg_id[e_begin + i];
+  }
 
   // Leading stages whose four pages are complete and precede the item's
   // first token need no masking for any row.  (Pages are checked 64 at a
-  // time, one per lane; the first page that fails ends the run.)
-  int n_full = 0;
-  for (int e0 = e_begin;; e0 += 64) {
+  // time, one per lane, the first 128 from the tables; the first page that
+  // fails ends the run.)
+  int n_full = -1;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = e_begin + 64 * k + lane;
+    const bool ok = e < e_end && t_valid[k] == PS && t_start[k] + PS - 1 <= ctx;
+    const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
+    if (n_full < 0 && bad) n_full = (64 * k + (int)__builtin_ctzll(bad)) / SP;
+  }
+  for (int e0 = e_begin + 128; n_full < 0; e0 += 64) {
     const int e = e0 + lane;
     const bool ok = e < e_end && a.pg_valid[e] == PS && a.pg_start[e] + PS - 1 <= ctx;
     const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
-    if (bad) {
-      n_full = (e0 - e_begin + (int)__builtin_ctzll(bad)) / SP;
-      break;
-    }
+    if (bad) n_full = (e0 - e_begin + (int)__builtin_ctzll(bad)) / SP;
   }
   __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
 
