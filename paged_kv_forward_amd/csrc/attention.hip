@@ -1328,19 +1328,34 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
   }
 
+  // Output through LDS: each wave writes its rows (normalised, bf16) to a
+  // region of the ring, then stores them as whole 16-byte pieces, lanes in
+  // row order.  The rows of one token are the G query heads of this KV head,
+  // adjacent in the output, so one store instruction covers whole runs of
+  // G x HD x 2 bytes; straight from the MFMA layout each lane held 8 bytes
+  // of 16 different rows per store (about 2.4 us per workgroup).
+  constexpr int RS = HD * 2 + 16;        // LDS row stride (padded: the 16 rows of a write hit distinct banks)
+  constexpr int CH = HD * 2 / 16;        // 16-byte pieces per row
+  constexpr int WR = RB * 16;            // rows per wave
+  static_assert(PH_WAVES * WR * RS <= NS * STAGE_B, "the output staging fits in the ring");
+  __syncthreads();  // every wave is done with the ring
+  uint8_t* so = &skv[0][0] + wave * WR * RS;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    if (qidx[rb] < 0) continue;
-    const int r = wave * (RB * 16) + rb * 16 + n;
-    const int tq = r / G, h = r % G;
-    const float inv = 1.f / oacc[rb][DB][0];
-    uint16_t* o = a.o + ((size_t)(row0 + tq) * a.nq + kvh * G + h) * HD;
+    const float inv = 1.f / oacc[rb][DB][0];  // unused rows (inf, nan) are never stored
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      uint2 w = make_uint2(pack_bf2(oacc[rb][b][0] * inv, oacc[rb][b][1] * inv),
-                           pack_bf2(oacc[rb][b][2] * inv, oacc[rb][b][3] * inv));
-      *reinterpret_cast<uint2*>(o + 16 * b + 4 * g) = w;
-    }
+    for (int b = 0; b < DB; ++b)
+      *reinterpret_cast<uint2*>(so + (rb * 16 + n) * RS + (16 * b + 4 * g) * 2) =
+          make_uint2(pack_bf2(oacc[rb][b][0] * inv, oacc[rb][b][1] * inv),
+                     pack_bf2(oacc[rb][b][2] * inv, oacc[rb][b][3] * inv));
+  }
+#pragma unroll
+  for (int k = 0; k < WR * CH / 64; ++k) {
+    const int rr = k * (64 / CH) + lane / CH, col = lane % CH;
+    const uint4 v = *reinterpret_cast<const uint4*>(so + rr * RS + col * 16);
+    const int r = wave * WR + rr;
+    const int tq = r / G, h = r % G;
+    if (tq < nt) *reinterpret_cast<uint4*>(a.o + ((size_t)(row0 + tq) * a.nq + kvh * G + h) * HD + col * 8) = v;
   }
 }
 
