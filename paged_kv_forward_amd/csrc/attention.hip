@@ -1022,6 +1022,10 @@ __device__ __forceinline__ void pipe_step(const uint8_t* sq, int qk0, f32x4 (&s_
     }
     f32x4 acc[RB][2];
     __builtin_amdgcn_sched_barrier(0);
+    // this wave's issue priority up while its scores and probabilities
+    // interleave, down for the P*V MFMAs: the other wave of the SIMD, in
+    // its own P*V phase, then fills the matrix core between them (+6%)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int m = 0; m < 2 * RB * STEPS; ++m) {
       const int i = m / (2 * RB), j = (m / RB) & 1, rb = m % RB;
@@ -1051,6 +1055,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* sq, int qk0, f32x4 (&s_
   for (int rb = 0; rb < RB; ++rb)
     ph[rb] = make_uint4(pack_h2(p[8 * rb], p[8 * rb + 1]), pack_h2(p[8 * rb + 2], p[8 * rb + 3]),
                         pack_h2(p[8 * rb + 4], p[8 * rb + 5]), pack_h2(p[8 * rb + 6], p[8 * rb + 7]));
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
   const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // fp16 1.0
 #pragma unroll
