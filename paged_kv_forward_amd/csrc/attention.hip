@@ -1104,39 +1104,79 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   // cost about 1600 cycles per stage.  Longer page tables use scalar loads.
   __shared__ int s_pid[PF_PT_MAX];
   const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4;
-  const int4 it = a.items[blockIdx.y];
   const int kvh = blockIdx.x;
-  const int s = it.x, tb = it.y, nt = it.z;
+  // Persistent over items: round r takes item r P + y, or r P + P - 1 - y in
+  // odd rounds (P = gridDim.y workgroups per KV head, y = blockIdx.y), so
+  // that with items sorted longest first every workgroup gets a similar
+  // total; no workgroup is launched per item, so none waits for one to be
+  // dispatched.  Every wave runs the same rounds (the barriers match).
   const int G = a.nq / a.nkv;
-  const int row0 = a.seq_row0[s] + tb;
-  const int ctx = a.seq_ctx[s] + tb;  // logical index of the item's first token
-  const int qmax = ctx + nt - 1;
-  const int e_begin = a.seq_pg0[s], e_all = a.seq_pg0[s + 1];
-
+  const int P = gridDim.y;
+  auto item_at = [&](int r) { return r * P + ((r & 1) ? P - 1 - (int)blockIdx.y : (int)blockIdx.y); };
   // The first 128 page entries (start, valid count, page id; entry
-  // e_begin + 64 k + lane in slot k), loaded before q and waited for together
-  // with it: one round trip for the tables and q, where loading each table
-  // after the previous one was needed took four (about 5 us per workgroup).
-  // Indexes are clamped into the sequence's entries (a launched item has at
-  // least one page) and the values outside it ignored.
+  // e_begin + 64 k + lane in slot k) and q, loaded in one round trip (loading
+  // each table after the previous one was needed took four, about 5 us per
+  // item).  For every item after the first they are loaded while the
+  // previous item's output is written.  Indexes are clamped into the
+  // sequence's entries (an item has at least one page) and the values
+  // outside it ignored.
   int t_start[2], t_valid[2], t_id[2];
+  uint4 qf[RB][HD / 32];
+  auto fetch = [&](int4 itv, int r0, int eb, int ea) {
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int e = max(min(e_begin + 64 * k + lane, e_all - 1), 0);
-    t_start[k] = a.pg_start[e];
-    t_valid[k] = a.pg_valid[e];
-    t_id[k] = a.pg_id[e];
+    for (int k = 0; k < 2; ++k) {
+      const int e = max(min(eb + 64 * k + lane, ea - 1), 0);
+      t_start[k] = a.pg_start[e];
+      t_valid[k] = a.pg_valid[e];
+      t_id[k] = a.pg_id[e];
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = wave * (RB * 16) + rb * 16 + n;
+      const int tq = r / G, h = r % G;
+      const bool ok = tq < itv.z;
+      load_q<HD>(qf[rb], a.q + ((size_t)(r0 + itv.y + (ok ? tq : 0)) * a.nq + kvh * G + h) * HD, ok, g);
+    }
+  };
+  int4 it = a.items[item_at(0)];  // grid.y <= the item count: round 0 always has an item
+  int seq_row0 = a.seq_row0[it.x], seq_ctx = a.seq_ctx[it.x];
+  int pg0 = a.seq_pg0[it.x], pg1 = a.seq_pg0[it.x + 1];
+  fetch(it, seq_row0, pg0, pg1);
+  // Persistent over items: round r takes item r P + y, or r P + P - 1 - y in
+  // odd rounds (P = gridDim.y workgroups per KV head, y = blockIdx.y), so
+  // that with items sorted longest first every workgroup gets a similar
+  // total; no workgroup is launched per item, so none waits for one to be
+  // dispatched.  Every wave runs the same rounds (the barriers match).
+  for (int round = 0;; ++round) {
+  // lane-derived offsets are recomputed each round rather than held in
+  // registers across rounds (that spilled)
+  int lane_r = lane;
+  asm volatile("" : "+v"(lane_r));
+  const int lane = lane_r, n = lane & 15, g = lane >> 4;
+  const int s = it.x, tb = it.y, nt = it.z;
+  const int row0 = seq_row0 + tb;
+  const int ctx = seq_ctx + tb;  // logical index of the item's first token
+  const int qmax = ctx + nt - 1;
+  const int e_begin = pg0, e_all = pg1;
+  // the next round's item and sequence (scalars, in registers long before
+  // this round's output)
+  const int yn = item_at(round + 1);
+  const bool more = yn < a.n_items;
+  int4 it_n = it;
+  int seq_row0_n = 0, seq_ctx_n = 0, pg0_n = 0, pg1_n = 0;
+  if (more) {
+    it_n = a.items[yn];
+    seq_row0_n = a.seq_row0[it_n.x];
+    seq_ctx_n = a.seq_ctx[it_n.x];
+    pg0_n = a.seq_pg0[it_n.x];
+    pg1_n = a.seq_pg0[it_n.x + 1];
   }
 
-  uint4 qf[RB][HD / 32];
   int qidx[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = wave * (RB * 16) + rb * 16 + n;
-    const int tq = r / G, h = r % G;
-    const bool ok = tq < nt;
-    qidx[rb] = ok ? ctx + tq : -1;
-    load_q<HD>(qf[rb], a.q + ((size_t)(row0 + (ok ? tq : 0)) * a.nq + kvh * G + h) * HD, ok, g);
+    qidx[rb] = r / G < nt ? ctx + r / G : -1;
   }
   const bool wave_live = wave * (RB * 16) / G < nt;
 
@@ -1343,6 +1383,7 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   constexpr int CH = HD * 2 / 16;        // 16-byte pieces per row
   constexpr int WR = RB * 16;            // rows per wave
   static_assert(PH_WAVES * WR * RS <= NS * STAGE_B, "the output staging fits in the ring");
+  if (more) fetch(it_n, seq_row0_n, pg0_n, pg1_n);  // q is no longer needed: the next item's goes in its place
   __syncthreads();  // every wave is done with the ring
   uint8_t* so = &skv[0][0] + wave * WR * RS;
 #pragma unroll
@@ -1361,6 +1402,14 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     const int r = wave * WR + rr;
     const int tq = r / G, h = r % G;
     if (tq < nt) *reinterpret_cast<uint4*>(a.o + ((size_t)(row0 + tq) * a.nq + kvh * G + h) * HD + col * 8) = v;
+  }
+  __syncthreads();  // the staging reads are done before the next round writes LDS
+  if (!more) break;
+  it = it_n;
+  seq_row0 = seq_row0_n;
+  seq_ctx = seq_ctx_n;
+  pg0 = pg0_n;
+  pg1 = pg1_n;
   }
 }
 
@@ -1385,18 +1434,34 @@ void launch_attn_combine(const AttnArgs& a, hipStream_t st) {
 // longer lists go out as several launches over consecutive slices.
 constexpr int MAX_GRID_Y = 65535;
 
+// Compute units of the current device (cached per device).
+static int n_compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 void launch_attn_prefill(const AttnArgs& a0, hipStream_t st) {
   for (int i0 = 0; i0 < a0.n_items; i0 += MAX_GRID_Y) {
     AttnArgs a = a0;
     a.items = a0.items + i0;
     a.n_items = min(MAX_GRID_Y, a0.n_items - i0);
     dim3 grid(a.nkv, a.n_items);
+    // the bf16 kernel is persistent: one workgroup per compute unit at most
+    // (one fits per unit), each taking several items in turn
+    dim3 grid_p(a.nkv, std::max(1, std::min(a.n_items, (n_compute_units() + a.nkv - 1) / a.nkv)));
     if (a.hd == 128) {
       if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<128, true>), grid, dim3(PF_NT), 0, st, a);
-      else hipLaunchKernelGGL(attn_prefill_h_kernel<128>, grid, dim3(PH_NT), 0, st, a);
+      else hipLaunchKernelGGL(attn_prefill_h_kernel<128>, grid_p, dim3(PH_NT), 0, st, a);
     } else {
       if (a.kv_e4m3) hipLaunchKernelGGL((attn_prefill_kernel<64, true>), grid, dim3(PF_NT), 0, st, a);
-      else hipLaunchKernelGGL(attn_prefill_h_kernel<64>, grid, dim3(PH_NT), 0, st, a);
+      else hipLaunchKernelGGL(attn_prefill_h_kernel<64>, grid_p, dim3(PH_NT), 0, st, a);
     }
   }
 }
