@@ -1261,13 +1261,25 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     for (int k = 0; k < HL; ++k) {
       const int d = (part0 + k) * 1024 + lane * 16;
       dma16(r, kd + (part0 + k) * 1024, kofs + (uint32_t)d, 0u);
-      // V rows are stored with their 16-byte halves swizzled (vswz, an involution)
-      dma16(r, kd + PAGE_B + (part0 + k) * 1024, vofs + (uint32_t)vswz(d), 0u);
     }
   };
-  // The V chunks this lane loaded (LDS bytes d of its page's V block, which
-  // hold source bytes vswz(d)), from bf16 to fp16 in place; token slots at
-  // or past the page's valid count become zeros.
+  // V comes through registers, one stage ahead: this lane's chunks of its
+  // page's V block (the chunk for LDS bytes d is source bytes vswz(d): V
+  // rows are stored with their 16-byte halves swizzled, an involution), so
+  // that the conversion need not read them back from LDS.
+  uint4 vreg[HL];
+  auto load_v = [&](int st, int pg_raw) {
+    const bool live = live_entry(st);
+    const int pg = live ? pg_raw : 0;
+    const __amdgpu_buffer_rsrc_t r = page_rsrc(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
+#pragma unroll
+    for (int k = 0; k < HL; ++k) {
+      const int d = (part0 + k) * 1024 + lane * 16;
+      vreg[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, vofs + (uint32_t)vswz(d), 0, 0));
+    }
+  };
+  // The loaded V chunks from bf16 to fp16 into the stage's LDS V block;
+  // token slots at or past the page's valid count become zeros.
   auto convert_v = [&](int st, int nv_raw) {
     const int nv = live_entry(st) ? nv_raw : 0;
     uint8_t* vd = &skv[st % NS][(2 * pj + 1) * PAGE_B];
@@ -1275,7 +1287,7 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     for (int k = 0; k < HL; ++k) {
       const int d = (part0 + k) * 1024 + lane * 16;
       const int t0 = ((vswz(d) % 32) / 16) * 8;  // first token of the chunk (a V row is 16 tokens)
-      const uint4 raw = *reinterpret_cast<const uint4*>(vd + d);
+      const uint4 raw = vreg[k];
       uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
       if (nv < PS) {  // wave-uniform: slots past the valid count may hold anything
         // bf16 word q holds tokens t0 + 2q, t0 + 2q + 1: keep the first
@@ -1321,16 +1333,20 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
     // loads of stage st + 2, so stage st + 1 has landed, and converts its V
     // share; a barrier then opens stage st + 1.
     __syncthreads();  // the page-id table is written (no ring load in flight yet)
-    issue(0, page_id(0));
-    issue(1, page_id(1));
-    int pid = page_id(2);
+    const int pid0 = page_id(0), pid1 = page_id(1);
+    issue(0, pid0);
+    issue(1, pid1);
+    load_v(0, pid0);
+    int pid = page_id(2), pidv = pid1;  // next K stage's page, next V stage's page
     const int nv0 = pg_valid[entry(0)];
     int nvn = pg_valid[entry(1)];
-    __builtin_amdgcn_s_waitcnt(PF_WAIT(LPW));
+    __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
     convert_v(0, nv0);
     __builtin_amdgcn_s_waitcnt(PF_WAIT(63));
     asm volatile("s_barrier" ::: "memory");
     issue(2, pid);
+    load_v(1, pidv);
+    pidv = pid;
     pid = page_id(3);
     // Pair 2st + 1's scores go with pair 2st's softmax and P*V, pair
     // 2st + 2's (next stage) with pair 2st + 1's, which is why a stage's
@@ -1351,13 +1367,16 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
         pipe_step<HD, RB, true>(sb, 4, sb2, st >= n_full, pv, ps, sb, 1, sa, qf, oacc, m_ref, t_raw, qidx, c, koff0,
                                 koff1, voff, lane);
       }
-      __builtin_amdgcn_s_waitcnt(PF_WAIT(LPW));
+      // V of stage st + 1 (in registers) and K up to stage st + 2 have landed
+      __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
       convert_v(st + 1, nvn);  // slot (st + 1) % NS: no wave reads it before the next barrier
       // stages before n_full hold complete pages; later ones need their count
       nvn = st + 2 < n_full ? PS : pg_valid[entry(st + 2)];
       __builtin_amdgcn_s_waitcnt(PF_WAIT(63));
       asm volatile("s_barrier" ::: "memory");
       issue(st + 3, pid);
+      load_v(st + 2, pidv);
+      pidv = pid;
       pid = page_id(st + 4);
       if (last) break;
       if (wave_live) {
