@@ -468,6 +468,7 @@ __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* 
   uint4 ph[RB], pl[RB];
   float alpha[RB];
   bool rescale[RB];
+  __builtin_amdgcn_s_setprio(1);  // scores and softmax ahead of the other wave's P*V (+0.8% at the 70B shape)
   {
     uint4 kf[2][STEPS];
 #pragma unroll
@@ -554,6 +555,7 @@ __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* 
       }
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
     const int off = ((16 * b + n) * PS + 4 * g) * EB;
