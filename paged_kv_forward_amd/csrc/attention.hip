@@ -778,25 +778,31 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(AttnArgs a) {
 // The bf16-KV prefill kernel, built around the cost of the softmax: a wave64
 // VALU instruction holds the 16-lane SIMD for 4 cycles, a quarter of a
 // 16x16x32 MFMA, so at 8 waves per CU the vector instructions per score, not
-// LDS or memory, set the pace.  Same work split and grid as
-// attn_prefill_kernel (256 query rows of one KV head per workgroup, 8 waves
-// of two 16-row blocks); what differs:
-//  - Pages pass through a four-stage LDS ring, K and V both loaded straight
-//    into LDS; each wave converts the V chunks it loaded to fp16 in place
-//    (two waves per page, each with half of its K and half of its V, so the
-//    conversion is evenly shared).  Slots past a page's valid count become
-//    zeros there.  bf16 -> fp16 is exact for magnitudes in [2^-14, 65504];
-//    smaller ones keep an absolute error below 2^-25, and a V entry of 65520
-//    or more would become infinite (activations of this model family stay
-//    many orders below).
+// LDS or memory, set the pace.  Same work split as attn_prefill_kernel (256
+// query rows of one KV head per item, 8 waves of two 16-row blocks); what
+// differs:
+//  - Persistent: one workgroup per compute unit takes items in rounds
+//    (snake order over the longest-first list); the next item's tables and
+//    q load while the current item's output is written, and the output goes
+//    through LDS so that each store covers whole rows.
+//  - Pages pass through a four-stage LDS ring: K loaded straight into LDS
+//    three stages ahead, V into registers one stage ahead and converted to
+//    fp16 into the ring (two waves per page, each with half of its K and
+//    half of its V, so the conversion is evenly shared).  Slots past a
+//    page's valid count become zeros there.  bf16 -> fp16 is exact for
+//    magnitudes in [2^-14, 65504]; smaller ones keep an absolute error below
+//    2^-25, and a V entry of 65520 or more would become infinite
+//    (activations of this model family stay many orders below).
 //  - Per pair of pages (32 keys): P enters P*V in fp16 (11 significant bits;
 //    bf16 has 8); the running maximum is a lazy reference checked with a
 //    ballot (check_pair), so the cross-lane max and the rescale of O run only
 //    when it moves; the scale is folded into the exponent as one FMA per
 //    score; row sums come from a ninth P*V block against an all-ones operand.
 //  - Software pipeline (pipe_step): the next pair's scores are computed in
-//    the same straight-line block as this pair's softmax and P*V, so one
-//    unit works while the other does; a stage's last pair is finished after
+//    the same straight-line block as this pair's softmax and P*V, each score
+//    MFMA followed by one probability under scheduling fences, with the
+//    wave's priority raised for that phase and lowered for P*V, so that the
+//    two waves of a SIMD alternate; a stage's last pair is finished after
 //    the barrier that opens the next stage, hence the fourth stage.
 //  - Page ids come from an LDS table filled once per workgroup, not from
 //    scalar loads in the loop.
