@@ -419,7 +419,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int s = c.x, p0 = c.y, np = min(c.z, MAXP);
   const int G = a.nq / a.nkv, HD = a.hd;
   const int row = a.seq_row0[s];
-  if (threadIdx.x < G) {
+  if ((int)threadIdx.x < G) {
     const int n = threadIdx.x;
     float M = -INFINITY;
     for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_ml[(((size_t)(p0 + p) * a.nkv + kvh) * 16 + n) * 2]);
@@ -1103,7 +1103,6 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   constexpr int STAGE_B = SP * 2 * PAGE_B;
   constexpr int PB_L = PAGE_B / 1024;            // 1 KiB loads per K (or V) block of a page
   constexpr int HL = PB_L / 2;                   // K loads and V loads per wave per stage
-  constexpr int LPW = 2 * HL;                    // loads per wave per stage
   static_assert(PH_WAVES == 2 * SP && HL >= 1, "two waves per page: half of its K and half of its V each");
   __shared__ __attribute__((aligned(1024))) uint8_t skv[NS][STAGE_B];
   // The sequence's page ids, so that the ring reads them from LDS: a scalar
@@ -1161,7 +1160,7 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   int lane_r = lane;
   asm volatile("" : "+v"(lane_r));
   const int lane = lane_r, n = lane & 15, g = lane >> 4;
-  const int s = it.x, tb = it.y, nt = it.z;
+  const int tb = it.y, nt = it.z;
   const int row0 = seq_row0 + tb;
   const int ctx = seq_ctx + tb;  // logical index of the item's first token
   const int qmax = ctx + nt - 1;
