@@ -1016,6 +1016,10 @@ __device__ __forceinline__ void pipe_step(const uint8_t* sq, int qk0, f32x4 (&s_
   float p[NE];
   // probability e: row block e / 8, MFMA (e / 4) % 2 of the pair, value e % 4
   auto prob = [&](int e) { p[e] = exp2_fast(fmaf(s_old[e / 8][(e / 4) & 1][e & 3], c, nm[e / 8])); };
+  // beside the score MFMAs, each exponential's FMA goes one MFMA earlier, so
+  // that the exponential does not wait for it (+1.6%)
+  float xs[NE];
+  auto pre = [&](int e) { xs[e] = fmaf(s_old[e / 8][(e / 4) & 1][e & 3], c, nm[e / 8]); };
   const uint8_t* vb = se + ev0 * PAGE_B + voff;
   constexpr int VB = 16 * PS * 2;  // bytes between V blocks
   uint4 vf[3];
@@ -1038,7 +1042,9 @@ __device__ __forceinline__ void pipe_step(const uint8_t* sq, int qk0, f32x4 (&s_
     for (int m = 0; m < 2 * RB * STEPS; ++m) {
       const int i = m / (2 * RB), j = (m / RB) & 1, rb = m % RB;
       acc[rb][j] = mfma16(kf[j][i], qf[rb][i], i == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[rb][j]);
-      if (m < NE) prob(m);
+      if (m == 0) pre(0);
+      if (m + 1 < NE) pre(m + 1);
+      if (m < NE) p[m] = exp2_fast(xs[m]);
       if (m == 2 * RB * STEPS - 6) vf[0] = *reinterpret_cast<const uint4*>(vb);
       if (m == 2 * RB * STEPS - 3) vf[1] = *reinterpret_cast<const uint4*>(vb + VB);
       __builtin_amdgcn_sched_barrier(0);
