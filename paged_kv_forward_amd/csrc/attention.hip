@@ -1086,7 +1086,8 @@ __device__ __forceinline__ void pipe_step(const uint8_t* sq, int qk0, f32x4 (&s_
   if constexpr (HQ) check_pair<HD, RB>(s_new, oacc, m_ref, t_raw, c, masked, pv[0], pv[1], ps[0], ps[1], qidx, lane);
 }
 
-// 8 waves of two 16-row blocks each (188 registers, two waves per SIMD).
+// 8 waves of two 16-row blocks each (at most 256 registers: two waves per
+// SIMD; the kernel uses about 240).
 // Sixteen waves of one block each measured 8% slower: every wave reads all of
 // a stage's K and V from LDS, so that doubles the operand reads.  No
 // register may spill here: a reload is a vector memory load, and since the
