@@ -1119,11 +1119,6 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   __shared__ int s_pid[PF_PT_MAX];
   const int lane = threadIdx.x & 63, wave = wave_id(), n = lane & 15, g = lane >> 4;
   const int kvh = blockIdx.x;
-  // Persistent over items: round r takes item r P + y, or r P + P - 1 - y in
-  // odd rounds (P = gridDim.y workgroups per KV head, y = blockIdx.y), so
-  // that with items sorted longest first every workgroup gets a similar
-  // total; no workgroup is launched per item, so none waits for one to be
-  // dispatched.  Every wave runs the same rounds (the barriers match).
   const int G = a.nq / a.nkv;
   const int P = gridDim.y;
   auto item_at = [&](int r) { return r * P + ((r & 1) ? P - 1 - (int)blockIdx.y : (int)blockIdx.y); };
@@ -1160,7 +1155,8 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   // odd rounds (P = gridDim.y workgroups per KV head, y = blockIdx.y), so
   // that with items sorted longest first every workgroup gets a similar
   // total; no workgroup is launched per item, so none waits for one to be
-  // dispatched.  Every wave runs the same rounds (the barriers match).
+  // dispatched.  Every wave runs the same rounds (the barriers match).  The
+  // round's body (not indented) runs to the end of the kernel.
   for (int round = 0;; ++round) {
   // lane-derived offsets are recomputed each round rather than held in
   // registers across rounds (that spilled)
