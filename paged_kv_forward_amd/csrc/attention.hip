@@ -584,13 +584,6 @@ __device__ __forceinline__ void prefill_pair(const uint8_t* kb0, const uint8_t* 
   }
 }
 
-// One workgroup (8 waves, PREFILL_ROWS query rows: PREFILL_ROWS / G tokens x
-// the G query heads of one KV head) per (item, KV head).  The K and V of the
-// sequence pass through LDS four pages (64 tokens) at a time, double
-// buffered, so every page is read from memory once per workgroup and serves
-// all its rows; each wave runs the online softmax over its 32 rows.  Rows see
-// entries up to their own logical index (causal in append order); pages past
-// the workgroup's last row are skipped.
 // End of a sequence's page entries once the pages that start after logical
 // index qmax are dropped (no row of the workgroup sees them).  Page starts
 // ascend, so 64 entries are tested per vector load, from the end: one or two
@@ -606,6 +599,13 @@ __device__ __forceinline__ int drop_pages_after(const int* pg_start, int e_begin
   }
 }
 
+// One workgroup (8 waves, PREFILL_ROWS query rows: PREFILL_ROWS / G tokens x
+// the G query heads of one KV head) per (item, KV head).  The K and V of the
+// sequence pass through LDS four pages (64 tokens) at a time, double
+// buffered, so every page is read from memory once per workgroup and serves
+// all its rows; each wave runs the online softmax over its 32 rows.  Rows see
+// entries up to their own logical index (causal in append order); pages past
+// the workgroup's last row are skipped.
 constexpr int PF_WAVES = 8, PF_NT = 64 * PF_WAVES;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
