@@ -1155,290 +1155,289 @@ __global__ __launch_bounds__(PH_NT, 1) void attn_prefill_h_kernel(AttnArgs a) {
   // odd rounds (P = gridDim.y workgroups per KV head, y = blockIdx.y), so
   // that with items sorted longest first every workgroup gets a similar
   // total; no workgroup is launched per item, so none waits for one to be
-  // dispatched.  Every wave runs the same rounds (the barriers match).  The
-  // round's body (not indented) runs to the end of the kernel.
+  // dispatched.  Every wave runs the same rounds (the barriers match).
   for (int round = 0;; ++round) {
-  // lane-derived offsets are recomputed each round rather than held in
-  // registers across rounds (that spilled)
-  int lane_r = lane;
-  asm volatile("" : "+v"(lane_r));
-  const int lane = lane_r, n = lane & 15, g = lane >> 4;
-  const int tb = it.y, nt = it.z;
-  const int row0 = seq_row0 + tb;
-  const int ctx = seq_ctx + tb;  // logical index of the item's first token
-  const int qmax = ctx + nt - 1;
-  const int e_begin = pg0, e_all = pg1;
-  // the next round's item and sequence (scalars, in registers long before
-  // this round's output)
-  const int yn = item_at(round + 1);
-  const bool more = yn < a.n_items;
-  int4 it_n = it;
-  int seq_row0_n = 0, seq_ctx_n = 0, pg0_n = 0, pg1_n = 0;
-  if (more) {
-    it_n = a.items[yn];
-    seq_row0_n = a.seq_row0[it_n.x];
-    seq_ctx_n = a.seq_ctx[it_n.x];
-    pg0_n = a.seq_pg0[it_n.x];
-    pg1_n = a.seq_pg0[it_n.x + 1];
-  }
-
-  int qidx[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = wave * (RB * 16) + rb * 16 + n;
-    qidx[rb] = r / G < nt ? ctx + r / G : -1;
-  }
-  const bool wave_live = wave * (RB * 16) / G < nt;
-
-  f32x4 oacc[RB][DB + 1];
-  float m_ref[RB], t_raw[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_ref[rb] = t_raw[rb] = -INFINITY;
-#pragma unroll
-    for (int b = 0; b <= DB; ++b) oacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const float c = a.sm_scale * LOG2E;
-  const int koff0 = pipe_koff(lane, PAGE_B, 0), koff1 = pipe_koff(lane, PAGE_B, 1), voff = pipe_voff(lane, PAGE_B);
-  const uint32_t kofs = (uint32_t)(kvh * PS * HD) * 2;
-  const uint32_t vofs = (uint32_t)(a.nkv * PS * HD + kvh * HD * PS) * 2;
-  const uint32_t page_bytes = (uint32_t)a.page_stride * 2;
-  const uint8_t* kv = reinterpret_cast<const uint8_t*>(a.kv_layer);
-  const_i32_t* pg_id = (const_i32_t*)a.pg_id;
-  const_i32_t* pg_valid = (const_i32_t*)a.pg_valid;
-  const_i32_t* pg_start = (const_i32_t*)a.pg_start;
-  __builtin_amdgcn_s_waitcnt(PF_WAIT(0));  // tables and q
-  // Pages that start after qmax serve no row of the workgroup.  Page starts
-  // ascend, so the entries kept are a prefix: counted from the tables when
-  // it ends inside them, else scanned from the sequence's end.
-  int e_end;
-  {
-    const uint64_t in0 = __builtin_amdgcn_ballot_w64(e_begin + lane < e_all && t_start[0] <= qmax);
-    const uint64_t in1 = __builtin_amdgcn_ballot_w64(e_begin + 64 + lane < e_all && t_start[1] <= qmax);
-    if (~in0) e_end = e_begin + __builtin_popcountll(in0);
-    else if (~in1) e_end = e_begin + 64 + __builtin_popcountll(in1);
-    else e_end = drop_pages_after(a.pg_start, e_begin, e_all, qmax, lane);
-  }
-  const int n_stages = (e_end - e_begin + SP - 1) / SP;
-  const bool pt_lds = e_end - e_begin <= PF_PT_MAX;
-  if (pt_lds) {
-    if (wave == 0) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        if (64 * k + lane < e_end - e_begin) s_pid[64 * k + lane] = t_id[k];
+    // lane-derived offsets are recomputed each round rather than held in
+    // registers across rounds (that spilled)
+    int lane_r = lane;
+    asm volatile("" : "+v"(lane_r));
+    const int lane = lane_r, n = lane & 15, g = lane >> 4;
+    const int tb = it.y, nt = it.z;
+    const int row0 = seq_row0 + tb;
+    const int ctx = seq_ctx + tb;  // logical index of the item's first token
+    const int qmax = ctx + nt - 1;
+    const int e_begin = pg0, e_all = pg1;
+    // the next round's item and sequence (scalars, in registers long before
+    // this round's output)
+    const int yn = item_at(round + 1);
+    const bool more = yn < a.n_items;
+    int4 it_n = it;
+    int seq_row0_n = 0, seq_ctx_n = 0, pg0_n = 0, pg1_n = 0;
+    if (more) {
+      it_n = a.items[yn];
+      seq_row0_n = a.seq_row0[it_n.x];
+      seq_ctx_n = a.seq_ctx[it_n.x];
+      pg0_n = a.seq_pg0[it_n.x];
+      pg1_n = a.seq_pg0[it_n.x + 1];
     }
-    for (int i = 128 + threadIdx.x; i < e_end - e_begin; i += PH_NT) s_pid[i] = a.pg_id[e_begin + i];
-  }
 
-  // Leading stages whose four pages are complete and precede the item's
-  // first token need no masking for any row.  (Pages are checked 64 at a
-  // time, one per lane, the first 128 from the tables; the first page that
-  // fails ends the run.)
-  int n_full = -1;
+    int qidx[RB];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int e = e_begin + 64 * k + lane;
-    const bool ok = e < e_end && t_valid[k] == PS && t_start[k] + PS - 1 <= ctx;
-    const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
-    if (n_full < 0 && bad) n_full = (64 * k + (int)__builtin_ctzll(bad)) / SP;
-  }
-  for (int e0 = e_begin + 128; n_full < 0; e0 += 64) {
-    const int e = e0 + lane;
-    const bool ok = e < e_end && a.pg_valid[e] == PS && a.pg_start[e] + PS - 1 <= ctx;
-    const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
-    if (bad) n_full = (e0 - e_begin + (int)__builtin_ctzll(bad)) / SP;
-  }
-  __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = wave * (RB * 16) + rb * 16 + n;
+      qidx[rb] = r / G < nt ? ctx + r / G : -1;
+    }
+    const bool wave_live = wave * (RB * 16) / G < nt;
 
-  // This wave's share of a stage: page wave / 2 of it, 1 KiB blocks
-  // part0 .. part0 + HL - 1 of both its K and its V, so that every wave
-  // converts the same share of V (with whole blocks per wave, half of the
-  // waves converted and the others waited at the barrier).  Stages past the
-  // end use a zero-size descriptor (zeros, no memory access).  Page ids and
-  // valid counts come in as arguments, read a stage ahead.
-  const int pj = wave >> 1, part0 = (wave & 1) * HL;
-  auto live_entry = [&](int st) { return st < n_stages && e_begin + st * SP + pj < e_end; };
-  auto entry = [&](int st) { return min(e_begin + st * SP + pj, e_end - 1); };  // clamped: always readable
-  auto page_id = [&](int st) {
-    return pt_lds ? __builtin_amdgcn_readfirstlane(s_pid[entry(st) - e_begin]) : pg_id[entry(st)];
-  };
-  auto issue = [&](int st, int pg_raw) {
-    const bool live = live_entry(st);
-    const int pg = live ? pg_raw : 0;
-    const i32x4_t r = page_words(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
-    uint8_t* kd = &skv[st % NS][(2 * pj) * PAGE_B];
+    f32x4 oacc[RB][DB + 1];
+    float m_ref[RB], t_raw[RB];
 #pragma unroll
-    for (int k = 0; k < HL; ++k) {
-      const int d = (part0 + k) * 1024 + lane * 16;
-      dma16(r, kd + (part0 + k) * 1024, kofs + (uint32_t)d, 0u);
+    for (int rb = 0; rb < RB; ++rb) {
+      m_ref[rb] = t_raw[rb] = -INFINITY;
+#pragma unroll
+      for (int b = 0; b <= DB; ++b) oacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  };
-  // V comes through registers, one stage ahead: this lane's chunks of its
-  // page's V block (the chunk for LDS bytes d is source bytes vswz(d): V
-  // rows are stored with their 16-byte halves swizzled, an involution), so
-  // that the conversion need not read them back from LDS.
-  uint4 vreg[HL];
-  auto load_v = [&](int st, int pg_raw) {
-    const bool live = live_entry(st);
-    const int pg = live ? pg_raw : 0;
-    const __amdgpu_buffer_rsrc_t r = page_rsrc(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
-#pragma unroll
-    for (int k = 0; k < HL; ++k) {
-      const int d = (part0 + k) * 1024 + lane * 16;
-      vreg[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, vofs + (uint32_t)vswz(d), 0, 0));
+    const float c = a.sm_scale * LOG2E;
+    const int koff0 = pipe_koff(lane, PAGE_B, 0), koff1 = pipe_koff(lane, PAGE_B, 1), voff = pipe_voff(lane, PAGE_B);
+    const uint32_t kofs = (uint32_t)(kvh * PS * HD) * 2;
+    const uint32_t vofs = (uint32_t)(a.nkv * PS * HD + kvh * HD * PS) * 2;
+    const uint32_t page_bytes = (uint32_t)a.page_stride * 2;
+    const uint8_t* kv = reinterpret_cast<const uint8_t*>(a.kv_layer);
+    const_i32_t* pg_id = (const_i32_t*)a.pg_id;
+    const_i32_t* pg_valid = (const_i32_t*)a.pg_valid;
+    const_i32_t* pg_start = (const_i32_t*)a.pg_start;
+    __builtin_amdgcn_s_waitcnt(PF_WAIT(0));  // tables and q
+    // Pages that start after qmax serve no row of the workgroup.  Page starts
+    // ascend, so the entries kept are a prefix: counted from the tables when
+    // it ends inside them, else scanned from the sequence's end.
+    int e_end;
+    {
+      const uint64_t in0 = __builtin_amdgcn_ballot_w64(e_begin + lane < e_all && t_start[0] <= qmax);
+      const uint64_t in1 = __builtin_amdgcn_ballot_w64(e_begin + 64 + lane < e_all && t_start[1] <= qmax);
+      if (~in0) e_end = e_begin + __builtin_popcountll(in0);
+      else if (~in1) e_end = e_begin + 64 + __builtin_popcountll(in1);
+      else e_end = drop_pages_after(a.pg_start, e_begin, e_all, qmax, lane);
     }
-  };
-  // The loaded V chunks from bf16 to fp16 into the stage's LDS V block;
-  // token slots at or past the page's valid count become zeros.
-  auto convert_v = [&](int st, int nv_raw) {
-    const int nv = live_entry(st) ? nv_raw : 0;
-    uint8_t* vd = &skv[st % NS][(2 * pj + 1) * PAGE_B];
+    const int n_stages = (e_end - e_begin + SP - 1) / SP;
+    const bool pt_lds = e_end - e_begin <= PF_PT_MAX;
+    if (pt_lds) {
+      if (wave == 0) {
 #pragma unroll
-    for (int k = 0; k < HL; ++k) {
-      const int d = (part0 + k) * 1024 + lane * 16;
-      const int t0 = ((vswz(d) % 32) / 16) * 8;  // first token of the chunk (a V row is 16 tokens)
-      const uint4 raw = vreg[k];
-      uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-      if (nv < PS) {  // wave-uniform: slots past the valid count may hold anything
-        // bf16 word q holds tokens t0 + 2q, t0 + 2q + 1: keep the first
-        // clamp(nv - t0 - 2q, 0, 2) halves (bf16 zero converts to fp16 zero)
-        asm volatile("" ::: "memory");  // a real branch: complete pages skip this
+        for (int k = 0; k < 2; ++k)
+          if (64 * k + lane < e_end - e_begin) s_pid[64 * k + lane] = t_id[k];
+      }
+      for (int i = 128 + threadIdx.x; i < e_end - e_begin; i += PH_NT) s_pid[i] = a.pg_id[e_begin + i];
+    }
+
+    // Leading stages whose four pages are complete and precede the item's
+    // first token need no masking for any row.  (Pages are checked 64 at a
+    // time, one per lane, the first 128 from the tables; the first page that
+    // fails ends the run.)
+    int n_full = -1;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int keep = min(max(nv - t0 - 2 * q, 0), 2);
-          w[q] &= (uint32_t)(0xffffffffull >> (16 * (2 - keep)));
+    for (int k = 0; k < 2; ++k) {
+      const int e = e_begin + 64 * k + lane;
+      const bool ok = e < e_end && t_valid[k] == PS && t_start[k] + PS - 1 <= ctx;
+      const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
+      if (n_full < 0 && bad) n_full = (64 * k + (int)__builtin_ctzll(bad)) / SP;
+    }
+    for (int e0 = e_begin + 128; n_full < 0; e0 += 64) {
+      const int e = e0 + lane;
+      const bool ok = e < e_end && a.pg_valid[e] == PS && a.pg_start[e] + PS - 1 <= ctx;
+      const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
+      if (bad) n_full = (e0 - e_begin + (int)__builtin_ctzll(bad)) / SP;
+    }
+    __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
+
+    // This wave's share of a stage: page wave / 2 of it, 1 KiB blocks
+    // part0 .. part0 + HL - 1 of both its K and its V, so that every wave
+    // converts the same share of V (with whole blocks per wave, half of the
+    // waves converted and the others waited at the barrier).  Stages past the
+    // end use a zero-size descriptor (zeros, no memory access).  Page ids and
+    // valid counts come in as arguments, read a stage ahead.
+    const int pj = wave >> 1, part0 = (wave & 1) * HL;
+    auto live_entry = [&](int st) { return st < n_stages && e_begin + st * SP + pj < e_end; };
+    auto entry = [&](int st) { return min(e_begin + st * SP + pj, e_end - 1); };  // clamped: always readable
+    auto page_id = [&](int st) {
+      return pt_lds ? __builtin_amdgcn_readfirstlane(s_pid[entry(st) - e_begin]) : pg_id[entry(st)];
+    };
+    auto issue = [&](int st, int pg_raw) {
+      const bool live = live_entry(st);
+      const int pg = live ? pg_raw : 0;
+      const i32x4_t r = page_words(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
+      uint8_t* kd = &skv[st % NS][(2 * pj) * PAGE_B];
+#pragma unroll
+      for (int k = 0; k < HL; ++k) {
+        const int d = (part0 + k) * 1024 + lane * 16;
+        dma16(r, kd + (part0 + k) * 1024, kofs + (uint32_t)d, 0u);
+      }
+    };
+    // V comes through registers, one stage ahead: this lane's chunks of its
+    // page's V block (the chunk for LDS bytes d is source bytes vswz(d): V
+    // rows are stored with their 16-byte halves swizzled, an involution), so
+    // that the conversion need not read them back from LDS.
+    uint4 vreg[HL];
+    auto load_v = [&](int st, int pg_raw) {
+      const bool live = live_entry(st);
+      const int pg = live ? pg_raw : 0;
+      const __amdgpu_buffer_rsrc_t r = page_rsrc(kv + (size_t)pg * page_bytes, live ? page_bytes : 0u);
+#pragma unroll
+      for (int k = 0; k < HL; ++k) {
+        const int d = (part0 + k) * 1024 + lane * 16;
+        vreg[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, vofs + (uint32_t)vswz(d), 0, 0));
+      }
+    };
+    // The loaded V chunks from bf16 to fp16 into the stage's LDS V block;
+    // token slots at or past the page's valid count become zeros.
+    auto convert_v = [&](int st, int nv_raw) {
+      const int nv = live_entry(st) ? nv_raw : 0;
+      uint8_t* vd = &skv[st % NS][(2 * pj + 1) * PAGE_B];
+#pragma unroll
+      for (int k = 0; k < HL; ++k) {
+        const int d = (part0 + k) * 1024 + lane * 16;
+        const int t0 = ((vswz(d) % 32) / 16) * 8;  // first token of the chunk (a V row is 16 tokens)
+        const uint4 raw = vreg[k];
+        uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        if (nv < PS) {  // wave-uniform: slots past the valid count may hold anything
+          // bf16 word q holds tokens t0 + 2q, t0 + 2q + 1: keep the first
+          // clamp(nv - t0 - 2q, 0, 2) halves (bf16 zero converts to fp16 zero)
+          asm volatile("" ::: "memory");  // a real branch: complete pages skip this
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int keep = min(max(nv - t0 - 2 * q, 0), 2);
+            w[q] &= (uint32_t)(0xffffffffull >> (16 * (2 - keep)));
+          }
+        }
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = pack_h2(__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xffff0000u));
+        // the second page of a pair holds its 8-token groups halves swapped
+        // (see the token order above): two 8-byte stores, their places chosen
+        // by the wave's page parity
+        const int sw = (pj & 1) * 8;
+        *reinterpret_cast<uint2*>(vd + d + sw) = make_uint2(o[0], o[1]);
+        *reinterpret_cast<uint2*>(vd + d + (8 - sw)) = make_uint2(o[2], o[3]);
+      }
+    };
+
+    // valid counts and first positions of a stage's pair q, read only for
+    // stages after the run of complete ones
+    auto pair_meta = [&](int st, int q, int (&pv)[2], int (&ps)[2]) {
+      pv[0] = pv[1] = PS;
+      ps[0] = ps[1] = 0;
+      if (st >= n_full) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int e = e_begin + st * SP + 2 * q + j;
+          pv[j] = e < e_end ? pg_valid[e] : 0;
+          ps[j] = e < e_end ? pg_start[e] : 0;
         }
       }
-      uint32_t o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = pack_h2(__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xffff0000u));
-      // the second page of a pair holds its 8-token groups halves swapped
-      // (see the token order above): two 8-byte stores, their places chosen
-      // by the wave's page parity
-      const int sw = (pj & 1) * 8;
-      *reinterpret_cast<uint2*>(vd + d + sw) = make_uint2(o[0], o[1]);
-      *reinterpret_cast<uint2*>(vd + d + (8 - sw)) = make_uint2(o[2], o[3]);
-    }
-  };
+    };
 
-  // valid counts and first positions of a stage's pair q, read only for
-  // stages after the run of complete ones
-  auto pair_meta = [&](int st, int q, int (&pv)[2], int (&ps)[2]) {
-    pv[0] = pv[1] = PS;
-    ps[0] = ps[1] = 0;
-    if (st >= n_full) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int e = e_begin + st * SP + 2 * q + j;
-        pv[j] = e < e_end ? pg_valid[e] : 0;
-        ps[j] = e < e_end ? pg_start[e] : 0;
-      }
-    }
-  };
-
-  if (n_stages > 0) {
-    // Ring: right after the barrier that opens stage st the wave issues
-    // stage st + 2; in the middle of stage st it waits for all but its LPW
-    // loads of stage st + 2, so stage st + 1 has landed, and converts its V
-    // share; a barrier then opens stage st + 1.
-    __syncthreads();  // the page-id table is written (no ring load in flight yet)
-    const int pid0 = page_id(0), pid1 = page_id(1);
-    issue(0, pid0);
-    issue(1, pid1);
-    load_v(0, pid0);
-    int pid = page_id(2), pidv = pid1;  // next K stage's page, next V stage's page
-    const int nv0 = pg_valid[entry(0)];
-    int nvn = pg_valid[entry(1)];
-    __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
-    convert_v(0, nv0);
-    __builtin_amdgcn_s_waitcnt(PF_WAIT(63));
-    asm volatile("s_barrier" ::: "memory");
-    issue(2, pid);
-    load_v(1, pidv);
-    pidv = pid;
-    pid = page_id(3);
-    // Pair 2st + 1's scores go with pair 2st's softmax and P*V, pair
-    // 2st + 2's (next stage) with pair 2st + 1's, which is why a stage's
-    // last pair is finished after the next stage's barrier.  The last stage
-    // is peeled so that no branch holds two copies of a step.
-    f32x4 sa[RB][2], sb2[RB][2];
-    int pv[2], ps[2];
-    if (wave_live) {
-      pair_meta(0, 0, pv, ps);
-      qk_pair<HD, RB>(skv[0], 0, qf, sa, koff0, koff1);
-      check_pair<HD, RB>(sa, oacc, m_ref, t_raw, c, n_full == 0, pv[0], pv[1], ps[0], ps[1], qidx, lane);
-    }
-    for (int st = 0; st < n_stages; ++st) {
-      const uint8_t* sb = skv[st % NS];
-      const bool last = st + 1 == n_stages;
-      if (wave_live) {
-        pair_meta(st, 1, pv, ps);
-        pipe_step<HD, RB, true>(sb, 4, sb2, st >= n_full, pv, ps, sb, 1, sa, qf, oacc, m_ref, t_raw, qidx, c, koff0,
-                                koff1, voff, lane);
-      }
-      // V of stage st + 1 (in registers) and K up to stage st + 2 have landed
+    if (n_stages > 0) {
+      // Ring: right after the barrier that opens stage st the wave issues
+      // stage st + 2; in the middle of stage st it waits for all but its LPW
+      // loads of stage st + 2, so stage st + 1 has landed, and converts its V
+      // share; a barrier then opens stage st + 1.
+      __syncthreads();  // the page-id table is written (no ring load in flight yet)
+      const int pid0 = page_id(0), pid1 = page_id(1);
+      issue(0, pid0);
+      issue(1, pid1);
+      load_v(0, pid0);
+      int pid = page_id(2), pidv = pid1;  // next K stage's page, next V stage's page
+      const int nv0 = pg_valid[entry(0)];
+      int nvn = pg_valid[entry(1)];
       __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
-      convert_v(st + 1, nvn);  // slot (st + 1) % NS: no wave reads it before the next barrier
-      // stages before n_full hold complete pages; later ones need their count
-      nvn = st + 2 < n_full ? PS : pg_valid[entry(st + 2)];
+      convert_v(0, nv0);
       __builtin_amdgcn_s_waitcnt(PF_WAIT(63));
       asm volatile("s_barrier" ::: "memory");
-      issue(st + 3, pid);
-      load_v(st + 2, pidv);
+      issue(2, pid);
+      load_v(1, pidv);
       pidv = pid;
-      pid = page_id(st + 4);
-      if (last) break;
+      pid = page_id(3);
+      // Pair 2st + 1's scores go with pair 2st's softmax and P*V, pair
+      // 2st + 2's (next stage) with pair 2st + 1's, which is why a stage's
+      // last pair is finished after the next stage's barrier.  The last stage
+      // is peeled so that no branch holds two copies of a step.
+      f32x4 sa[RB][2], sb2[RB][2];
+      int pv[2], ps[2];
       if (wave_live) {
-        pair_meta(st + 1, 0, pv, ps);
-        pipe_step<HD, RB, true>(skv[(st + 1) % NS], 0, sa, st + 1 >= n_full, pv, ps, sb, 5, sb2, qf, oacc, m_ref,
-                                t_raw, qidx, c, koff0, koff1, voff, lane);
+        pair_meta(0, 0, pv, ps);
+        qk_pair<HD, RB>(skv[0], 0, qf, sa, koff0, koff1);
+        check_pair<HD, RB>(sa, oacc, m_ref, t_raw, c, n_full == 0, pv[0], pv[1], ps[0], ps[1], qidx, lane);
       }
+      for (int st = 0; st < n_stages; ++st) {
+        const uint8_t* sb = skv[st % NS];
+        const bool last = st + 1 == n_stages;
+        if (wave_live) {
+          pair_meta(st, 1, pv, ps);
+          pipe_step<HD, RB, true>(sb, 4, sb2, st >= n_full, pv, ps, sb, 1, sa, qf, oacc, m_ref, t_raw, qidx, c, koff0,
+                                  koff1, voff, lane);
+        }
+        // V of stage st + 1 (in registers) and K up to stage st + 2 have landed
+        __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
+        convert_v(st + 1, nvn);  // slot (st + 1) % NS: no wave reads it before the next barrier
+        // stages before n_full hold complete pages; later ones need their count
+        nvn = st + 2 < n_full ? PS : pg_valid[entry(st + 2)];
+        __builtin_amdgcn_s_waitcnt(PF_WAIT(63));
+        asm volatile("s_barrier" ::: "memory");
+        issue(st + 3, pid);
+        load_v(st + 2, pidv);
+        pidv = pid;
+        pid = page_id(st + 4);
+        if (last) break;
+        if (wave_live) {
+          pair_meta(st + 1, 0, pv, ps);
+          pipe_step<HD, RB, true>(skv[(st + 1) % NS], 0, sa, st + 1 >= n_full, pv, ps, sb, 5, sb2, qf, oacc, m_ref,
+                                  t_raw, qidx, c, koff0, koff1, voff, lane);
+        }
+      }
+      if (wave_live)  // the last pair: no next one to start
+        pipe_step<HD, RB, false>(skv[0], 0, sa, false, pv, ps, skv[(n_stages - 1) % NS], 5, sb2, qf, oacc, m_ref,
+                                 t_raw, qidx, c, koff0, koff1, voff, lane);
+      // no load into this workgroup's LDS may still be in flight when it ends
+      __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
     }
-    if (wave_live)  // the last pair: no next one to start
-      pipe_step<HD, RB, false>(skv[0], 0, sa, false, pv, ps, skv[(n_stages - 1) % NS], 5, sb2, qf, oacc, m_ref,
-                               t_raw, qidx, c, koff0, koff1, voff, lane);
-    // no load into this workgroup's LDS may still be in flight when it ends
-    __builtin_amdgcn_s_waitcnt(PF_WAIT(0));
-  }
 
-  // Output through LDS: each wave writes its rows (normalised, bf16) to a
-  // region of the ring, then stores them as whole 16-byte pieces, lanes in
-  // row order.  The rows of one token are the G query heads of this KV head,
-  // adjacent in the output, so one store instruction covers whole runs of
-  // G x HD x 2 bytes; straight from the MFMA layout each lane held 8 bytes
-  // of 16 different rows per store (about 2.4 us per workgroup).
-  constexpr int RS = HD * 2 + 16;        // LDS row stride (padded: the 16 rows of a write hit distinct banks)
-  constexpr int CH = HD * 2 / 16;        // 16-byte pieces per row
-  constexpr int WR = RB * 16;            // rows per wave
-  static_assert(PH_WAVES * WR * RS <= NS * STAGE_B, "the output staging fits in the ring");
-  if (more) fetch(it_n, seq_row0_n, pg0_n, pg1_n);  // q is no longer needed: the next item's goes in its place
-  __syncthreads();  // every wave is done with the ring
-  uint8_t* so = &skv[0][0] + wave * WR * RS;
+    // Output through LDS: each wave writes its rows (normalised, bf16) to a
+    // region of the ring, then stores them as whole 16-byte pieces, lanes in
+    // row order.  The rows of one token are the G query heads of this KV head,
+    // adjacent in the output, so one store instruction covers whole runs of
+    // G x HD x 2 bytes; straight from the MFMA layout each lane held 8 bytes
+    // of 16 different rows per store (about 2.4 us per workgroup).
+    constexpr int RS = HD * 2 + 16;        // LDS row stride (padded: the 16 rows of a write hit distinct banks)
+    constexpr int CH = HD * 2 / 16;        // 16-byte pieces per row
+    constexpr int WR = RB * 16;            // rows per wave
+    static_assert(PH_WAVES * WR * RS <= NS * STAGE_B, "the output staging fits in the ring");
+    if (more) fetch(it_n, seq_row0_n, pg0_n, pg1_n);  // q is no longer needed: the next item's goes in its place
+    __syncthreads();  // every wave is done with the ring
+    uint8_t* so = &skv[0][0] + wave * WR * RS;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float inv = 1.f / oacc[rb][DB][0];  // unused rows (inf, nan) are never stored
+    for (int rb = 0; rb < RB; ++rb) {
+      const float inv = 1.f / oacc[rb][DB][0];  // unused rows (inf, nan) are never stored
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
-      *reinterpret_cast<uint2*>(so + (rb * 16 + n) * RS + (16 * b + 4 * g) * 2) =
-          make_uint2(pack_bf2(oacc[rb][b][0] * inv, oacc[rb][b][1] * inv),
-                     pack_bf2(oacc[rb][b][2] * inv, oacc[rb][b][3] * inv));
-  }
+      for (int b = 0; b < DB; ++b)
+        *reinterpret_cast<uint2*>(so + (rb * 16 + n) * RS + (16 * b + 4 * g) * 2) =
+            make_uint2(pack_bf2(oacc[rb][b][0] * inv, oacc[rb][b][1] * inv),
+                       pack_bf2(oacc[rb][b][2] * inv, oacc[rb][b][3] * inv));
+    }
 #pragma unroll
-  for (int k = 0; k < WR * CH / 64; ++k) {
-    const int rr = k * (64 / CH) + lane / CH, col = lane % CH;
-    const uint4 v = *reinterpret_cast<const uint4*>(so + rr * RS + col * 16);
-    const int r = wave * WR + rr;
-    const int tq = r / G, h = r % G;
-    if (tq < nt) *reinterpret_cast<uint4*>(a.o + ((size_t)(row0 + tq) * a.nq + kvh * G + h) * HD + col * 8) = v;
-  }
-  __syncthreads();  // the staging reads are done before the next round writes LDS
-  if (!more) break;
-  it = it_n;
-  seq_row0 = seq_row0_n;
-  seq_ctx = seq_ctx_n;
-  pg0 = pg0_n;
-  pg1 = pg1_n;
+    for (int k = 0; k < WR * CH / 64; ++k) {
+      const int rr = k * (64 / CH) + lane / CH, col = lane % CH;
+      const uint4 v = *reinterpret_cast<const uint4*>(so + rr * RS + col * 16);
+      const int r = wave * WR + rr;
+      const int tq = r / G, h = r % G;
+      if (tq < nt) *reinterpret_cast<uint4*>(a.o + ((size_t)(row0 + tq) * a.nq + kvh * G + h) * HD + col * 8) = v;
+    }
+    __syncthreads();  // the staging reads are done before the next round writes LDS
+    if (!more) break;
+    it = it_n;
+    seq_row0 = seq_row0_n;
+    seq_ctx = seq_ctx_n;
+    pg0 = pg0_n;
+    pg1 = pg1_n;
   }
 }
 
